@@ -1,0 +1,163 @@
+/*
+ * gdn_oracle.c -- plain, slow fp64 CPU oracle for the Gated DeltaNet token mixer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library's product path may call,
+ * link or load this file; only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code with the HIP kernels.
+ *
+ * What it computes.  The pages name the mixer without writing it out: the
+ * Qwen3.5-0.8B chat guide (soniqo.audio, section "Architektur") describes the
+ * DeltaNet layers as linear attention with a gated-delta-rule recurrence
+ * followed by RMSNormGated; the Qwen3.6 card of the Core AI model zoo (intro)
+ * gives the grouped value heads (each key/query head shared by two value
+ * heads); the Swiftlet post (section "How It Works") stresses the fixed-size
+ * recurrent state.  The recurrence used here is the published gated delta rule
+ * (Yang, Kautz, Hatamizadeh, "Gated Delta Networks", ICLR 2025):
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T ,   o_t = S_t q_t
+ *
+ * with S_t a d_v x d_k matrix (row i <-> value dim, column j <-> key dim),
+ * a_t = exp(g_t) the decay and b_t = beta_t the write strength, both per
+ * (token, value head).  The readout uses the state AFTER the token's update
+ * and is multiplied by `scale`.  Value head h reads key/query head h / (HV/H).
+ *
+ * RMSNormGated, per (token, value head) group of d_v values:
+ *     y = x / sqrt(mean(x^2) + eps) * w * silu(z),   silu(z) = z / (1 + e^-z)
+ *
+ * Everything is computed in double from float32 inputs (bf16 inputs arrive as
+ * exactly representable float32 values).  No chunking and no reordering beyond
+ * the plain loops below; the (sequence, head) recurrences are independent and
+ * run in parallel with OpenMP.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int gdn_oracle_version(void) { return 1; }
+
+int gdn_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * One (sequence n, value head h) recurrence over tokens t0 .. t1-1.
+ *   q, k  : [T, H, dk]     float32, token-major
+ *   v     : [T, HV, dv]
+ *   g, bt : [T, HV]        log-decay and beta
+ *   S     : [dv, dk]       in: initial state, out: final state (double)
+ *   o     : [T, HV, dv]    outputs for this head's rows (double)
+ *   sk    : [dv]           scratch
+ */
+static void recur_one(const float* q, const float* k, const float* v, const float* g,
+                      const float* bt, long t0, long t1, int H, int HV, int dk, int dv,
+                      int h, double scale, double* S, double* o, double* sk) {
+    const int hk = h / (HV / H);          /* grouped value heads: key head of h */
+    for (long t = t0; t < t1; ++t) {
+        const float* kt = k + ((size_t)t * H + hk) * dk;
+        const float* qt = q + ((size_t)t * H + hk) * dk;
+        const float* vt = v + ((size_t)t * HV + h) * dv;
+        const double a = exp((double)g[(size_t)t * HV + h]);
+        const double b = (double)bt[(size_t)t * HV + h];
+
+        /* sk = S_{t-1} k_t */
+        for (int i = 0; i < dv; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * (double)kt[j];
+            sk[i] = acc;
+        }
+        /* S_t = a S_{t-1} - a b (S_{t-1} k_t) k_t^T + b v_t k_t^T */
+        for (int i = 0; i < dv; ++i) {
+            for (int j = 0; j < dk; ++j) {
+                double s = S[(size_t)i * dk + j];
+                double upd = a * s;
+                upd -= a * b * sk[i] * (double)kt[j];
+                upd += b * (double)vt[i] * (double)kt[j];
+                S[(size_t)i * dk + j] = upd;
+            }
+        }
+        /* o_t = scale * S_t q_t */
+        double* ot = o + ((size_t)t * HV + h) * dv;
+        for (int i = 0; i < dv; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * (double)qt[j];
+            ot[i] = scale * acc;
+        }
+    }
+}
+
+/*
+ * The whole packed batch.
+ *   cu_seqlens : [N+1] int32, sequence n holds tokens cu[n] .. cu[n+1]-1
+ *   s0         : [N, HV, dv, dk] double, or NULL for zero initial states
+ *   o          : [T, HV, dv] double (written for every token)
+ *   s_final    : [N, HV, dv, dk] double, or NULL
+ *   nthreads   : OpenMP threads (<= 0: the runtime's default)
+ * Returns 0, or -1 on invalid sizes or a failed allocation.
+ */
+int gdn_oracle_recurrence(const float* q, const float* k, const float* v, const float* g,
+                          const float* beta, const int32_t* cu_seqlens, int N, int H, int HV,
+                          int dk, int dv, double scale, const double* s0, double* o,
+                          double* s_final, int nthreads) {
+    if (N < 0 || H <= 0 || HV <= 0 || HV % H != 0 || dk <= 0 || dv <= 0) return -1;
+    const long pairs = (long)N * HV;
+    const size_t ssz = (size_t)dv * dk;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+    for (long p = 0; p < pairs; ++p) {
+        const int n = (int)(p / HV), h = (int)(p % HV);
+        double* S = (double*)malloc(ssz * sizeof(double));
+        double* sk = (double*)malloc((size_t)dv * sizeof(double));
+        if (!S || !sk) {
+            failed = 1;
+        } else {
+            if (s0)
+                memcpy(S, s0 + (size_t)p * ssz, ssz * sizeof(double));
+            else
+                memset(S, 0, ssz * sizeof(double));
+            recur_one(q, k, v, g, beta, cu_seqlens[n], cu_seqlens[n + 1], H, HV, dk, dv, h,
+                      scale, S, o, sk);
+            if (s_final) memcpy(s_final + (size_t)p * ssz, S, ssz * sizeof(double));
+        }
+        free(S);
+        free(sk);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * RMSNormGated over groups of dv values.
+ *   x : [groups, dv] double      z : [groups, dv] float32     w : [dv] float32
+ *   y : [groups, dv] double
+ * y = x / sqrt(mean(x^2) + eps) * w * z * sigmoid(z)
+ */
+int gdn_oracle_rmsnorm_gated(const double* x, const float* z, const float* w, long groups,
+                             int dv, double eps, double* y) {
+    if (groups < 0 || dv <= 0) return -1;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (long r = 0; r < groups; ++r) {
+        const double* xr = x + (size_t)r * dv;
+        const float* zr = z + (size_t)r * dv;
+        double ss = 0.0;
+        for (int i = 0; i < dv; ++i) ss += xr[i] * xr[i];
+        const double inv = 1.0 / sqrt(ss / dv + eps);
+        for (int i = 0; i < dv; ++i) {
+            const double zi = (double)zr[i];
+            const double gate = zi / (1.0 + exp(-zi));
+            y[(size_t)r * dv + i] = xr[i] * inv * (double)w[i] * gate;
+        }
+    }
+    return 0;
+}
