@@ -1,0 +1,348 @@
+"""Benchmark of the Gated DeltaNet token mixer (libgdn) on one MI355X.
+
+Default workload (one "step"): the Qwen3.5-0.8B DeltaNet decode job over the
+18 DeltaNet layers of the model (18 of 24 layers; Qwen3.5-0.8B chat guide,
+section "Architektur").  32 sequences, 16 key/query heads, 16 value heads,
+d_k = d_v = 128, bf16 q/k/v, fp32 state.  Per layer: a 512-token chunked
+prefill of every sequence from a zero state (gdn_prefill_chunked) followed by
+RMSNormGated of its outputs; then 256 decode steps, each advancing all 18
+layer-states by one token (gdn_decode_step + gdn_rmsnorm_gated per layer).
+Every layer has its own state (18 x 32 MiB = 576 MiB, more than the 256 MB
+Infinity Cache) and its own inputs, all resident in HBM before timing starts.
+The launch sequence of a step is captured once in HIP graphs and replayed.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill2|prefill3|prefill4]
+
+Prints one JSON line.  ``value`` = tokens per second per DeltaNet layer over
+the whole job: 32 x (512 + 256) tokens x 18 layers / job time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN tokens/s (prefill, decode) + % HBM/MFMA roofline, 1×MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must move / compute, not what a kernel does)
+# ---------------------------------------------------------------------------
+
+def decode_bytes_per_token(H, HV, dk, dv, in_bytes=2, o_bytes=4):
+    """HBM bytes per token per layer: read + write the fp32 state of every value
+    head, read q, k (per key head) and v, g, beta, write o."""
+    return (HV * dk * dv * 4 * 2 + H * dk * in_bytes * 2 + HV * dv * in_bytes
+            + HV * 8 + HV * dv * o_bytes)
+
+
+def prefill_bytes(T, N, H, HV, dk, dv, in_bytes=2, o_bytes=4, s0=False):
+    """HBM bytes of one prefill call: q, k, v, g, beta in, o out, final state
+    out (and initial state in when given)."""
+    b = T * (H * dk * in_bytes * 2 + HV * dv * in_bytes + HV * 8 + HV * dv * o_bytes)
+    b += N * HV * dk * dv * 4 * (2 if s0 else 1)
+    return b
+
+
+def prefill_flops(T, H, HV, dk, dv, C=64):
+    """Flops of the chunked form per call, full C x C tiles: per key head and
+    token K K^T and Q K^T (2 C dk each); per value head and token the
+    triangular solve (C^2 / 3), U = T diag(b)(V - diag(gamma) K S^T)
+    (2 dk dv + 2 C dv), O = diag(gamma) Q S^T + P U (2 dk dv + 2 C dv) and the
+    state update U^T K (2 dk dv)."""
+    per_k = 2 * C * dk * 2
+    per_v = C * C / 3 + (2 * dk * dv + 2 * C * dv) * 2 + 2 * dk * dv
+    return T * (H * per_k + HV * per_v)
+
+
+def norm_bytes(rows, HV, dv, x_bytes=4, z_bytes=2, y_bytes=4):
+    return rows * HV * dv * (x_bytes + z_bytes + y_bytes) + dv * 4
+
+
+# ---------------------------------------------------------------------------
+
+def graph_capture(fn):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # one eager run on the capture stream first
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return g, s
+
+
+def cpu_baseline_decode_job(layers_sample: int, N, T, H, HV, d, steps, seed=0):
+    """The fp64 oracle on a bounded sample of the decode job: ``layers_sample``
+    layers, each a T-token prefill of N sequences, RMSNormGated, then ``steps``
+    decode steps with RMSNormGated.  Returns (tokens/s per layer, seconds,
+    threads)."""
+    import gdn_inputs as gi
+    import oracle
+    orc = oracle.load()
+    data = []
+    for l in range(layers_sample):
+        x = gi.make_prefill([T] * N, H, HV, d, d, seed=seed + l, stream=1001)
+        dd = gi.make_decode(steps, N, H, HV, d, d, seed=seed + l, stream=2001, decay_stream=1001)
+        data.append((x, dd))
+    t0 = time.perf_counter()
+    for x, dd in data:
+        o, S = orc.recurrence(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens)
+        orc.rmsnorm_gated(o, x.z, x.w)
+        for t in range(steps):
+            od, S = orc.decode(dd.q[t], dd.k[t], dd.v[t], dd.g[t], dd.beta[t], S)
+            orc.rmsnorm_gated(od, dd.z[t], dd.w)
+    dt = time.perf_counter() - t0
+    return N * (T + steps) * layers_sample / dt, dt, orc.max_threads()
+
+
+def run_decode_job(args):
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    import gdn_inputs as gi
+
+    N, H, HV, d, T, steps, L = 32, 16, 16, 128, 512, 256, args.layers
+    if args.decode_steps:
+        steps = args.decode_steps
+    dev = torch.device("cuda", 0)
+    bf = torch.bfloat16
+    log(f"decode job: N={N} H={H} HV={HV} d={d} prefill T={T} steps={steps} layers={L}")
+    head_scale = gi.decay_scale(0, 1001, HV, "qwen")
+    layers = []
+    for l in range(L):
+        q, k, v, g, b, z = gi.device_tokens((N * T,), H, HV, d, d, seed=1000 + l,
+                                            head_scale=head_scale, device=dev)
+        dq, dk_, dv_, dg, db, dz = gi.device_tokens((steps, N), H, HV, d, d, seed=5000 + l,
+                                                    head_scale=head_scale, device=dev)
+        layers.append(dict(q=q, k=k, v=v, g=g, b=b, z=z, dq=dq, dk=dk_, dv=dv_, dg=dg, db=db,
+                           dz=dz, state=torch.zeros(N, HV, d, d, device=dev),
+                           o=torch.empty(N * T, HV, d, device=dev),
+                           y=torch.empty(N * T, HV, d, device=dev),
+                           od=torch.empty(N, HV, d, device=dev),
+                           yd=torch.empty(N, HV, d, device=dev)))
+    w = torch.ones(d, device=dev)
+    cu = torch.arange(0, N * T + 1, T, dtype=torch.int32, device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(N, N * T, H, HV, d, d), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def prefill_phase():
+        for Ly in layers:
+            gdn.prefill_chunked(Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu,
+                                final_state=Ly["state"], o=Ly["o"], workspace=ws)
+            gdn.rmsnorm_gated(Ly["o"], Ly["z"], w, y=Ly["y"])
+
+    def decode_phase():
+        for t in range(steps):
+            for Ly in layers:
+                gdn.decode_step(Ly["dq"][t], Ly["dk"][t], Ly["dv"][t], Ly["dg"][t], Ly["db"][t],
+                                Ly["state"], o=Ly["od"])
+                gdn.rmsnorm_gated(Ly["od"], Ly["dz"][t], w, y=Ly["yd"])
+
+    def decode_only():
+        for t in range(steps):
+            for Ly in layers:
+                gdn.decode_step(Ly["dq"][t], Ly["dk"][t], Ly["dv"][t], Ly["dg"][t], Ly["db"][t],
+                                Ly["state"], o=Ly["od"])
+
+    t0 = time.perf_counter()
+    g_pf, s = graph_capture(prefill_phase)
+    g_dec, _ = graph_capture(decode_phase)
+    log(f"graphs captured in {time.perf_counter() - t0:.1f}s")
+
+    for _ in range(args.warmup):
+        g_pf.replay()
+        g_dec.replay()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    with torch.cuda.stream(s):
+        for i in range(args.steps):
+            ev[i][0].record(s)
+            g_pf.replay()
+            ev[i][1].record(s)
+            g_dec.replay()
+            ev[i][2].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    pf_ms = sum(a.elapsed_time(b) for a, b, _ in ev)
+    dec_ms = sum(b.elapsed_time(c) for _, b, c in ev)
+    job_ms = (pf_ms + dec_ms) / args.steps
+    ms_per_step = max(job_ms, wall * 1e3 / args.steps)
+
+    tokens = N * (T + steps) * L
+    value = tokens / (ms_per_step * 1e-3)
+    pf_tok_s = N * T * L / (pf_ms / args.steps * 1e-3)
+    dec_tok_s = N * steps * L / (dec_ms / args.steps * 1e-3)
+
+    # dominant kernel: the decode step, timed alone with HIP events on the
+    # stream it is launched on (the same 18-layer rotation, same inputs)
+    g_do, _ = graph_capture(decode_only)
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        g_do.replay()
+        e0.record(s)
+        for _ in range(reps):
+            g_do.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    dec_launch_us = e0.elapsed_time(e1) * 1e3 / (reps * steps * L)
+    bytes_launch = decode_bytes_per_token(H, HV, d, d) * N
+    achieved = bytes_launch / (dec_launch_us * 1e-6) / 1e9
+
+    # prefill kernels: one layer's call timed alone
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    Ly = layers[0]
+    with torch.cuda.stream(s):
+        pe0.record(s)
+        for _ in range(5):
+            gdn.prefill_chunked(Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu,
+                                final_state=Ly["state"], o=Ly["o"], workspace=ws)
+        pe1.record(s)
+    torch.cuda.synchronize()
+    pf_call_us = pe0.elapsed_time(pe1) * 1e3 / 5
+    pf_b = prefill_bytes(N * T, N, H, HV, d, d)
+    pf_f = prefill_flops(N * T, H, HV, d, d)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s per DeltaNet layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwen3.5-0.8b-deltanet-decode-job", "sequences": N,
+                   "qk_heads": H, "v_heads": HV, "d_k": d, "d_v": d,
+                   "prefill_tokens_per_seq": T, "decode_steps": steps, "layers": L,
+                   "inputs": "bf16", "state": "f32", "outputs": "f32"},
+        "phases": {"prefill_tokens_per_s_per_layer": round(pf_tok_s, 1),
+                   "decode_tokens_per_s_per_layer": round(dec_tok_s, 1),
+                   "prefill_ms_per_step": round(pf_ms / args.steps, 4),
+                   "decode_ms_per_step": round(dec_ms / args.steps, 4),
+                   "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(dec_launch_us, 3),
+                     "algorithmic_bytes_per_launch": bytes_launch},
+        "roofline_prefill": {"call_us": round(pf_call_us, 2),
+                             "hbm_achieved_GBs": round(pf_b / (pf_call_us * 1e-6) / 1e9, 1),
+                             "hbm_frac": round(pf_b / (pf_call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "tflops": round(pf_f / (pf_call_us * 1e-6) / 1e12, 2),
+                             "mfma_bf16_frac": round(pf_f / (pf_call_us * 1e-6) / 1e12 /
+                                                     BF16_PEAK_TFLOPS, 5),
+                             "algorithmic_bytes": pf_b, "algorithmic_flops": pf_f},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a sample of the job")
+        v_cpu, secs, thr = cpu_baseline_decode_job(args.cpu_layers, N, T, H, HV, d, steps)
+        out["cpu_baseline"] = {"value": round(v_cpu, 1), "unit": "tokens/s per DeltaNet layer",
+                               "cores": thr, "kind": "oracle",
+                               "sample": f"{args.cpu_layers} layer(s) of the job: 32 x 512-token "
+                                         f"prefill + {steps} decode steps + RMSNormGated, fp64, "
+                                         f"{secs:.1f} s"}
+    return out
+
+
+def run_prefill(args, cfg: int):
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    import gdn_inputs as gi
+
+    w = gi.WORKLOADS[cfg]
+    H, HV, d = w["H"], w["HV"], w["dk"]
+    lengths = gi.config_lengths(0) if cfg == 4 else np.array([w["T"]] * w["N"])
+    N, T = len(lengths), int(np.sum(lengths))
+    dev = torch.device("cuda", 0)
+    head_scale = gi.decay_scale(0, 1000 + cfg, HV, "qwen")
+    q, k, v, g, b, _ = gi.device_tokens((T,), H, HV, d, d, seed=cfg, head_scale=head_scale,
+                                        device=dev, with_z=False)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).to(dev)
+    s0 = None
+    if w.get("s0_std"):
+        s0 = torch.randn(N, HV, d, d, device=dev) * w["s0_std"]
+    o = torch.empty(T, HV, d, device=dev)
+    sf = torch.empty(N, HV, d, d, device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(N, T, H, HV, d, d), dtype=torch.uint8, device=dev)
+    call = lambda: gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf, o=o,
+                                       workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+    pb = prefill_bytes(T, N, H, HV, d, d, s0=s0 is not None)
+    pfl = prefill_flops(T, H, HV, d, d)
+    return {
+        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s (one layer)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "sequences": N, "tokens": T,
+                   "lengths": [int(x) for x in lengths], "qk_heads": H, "v_heads": HV,
+                   "d_k": d, "d_v": d, "chunk": 64},
+        "roofline": {"kernel": "prefill (chunk_table + prep + scan)", "bound": "hbm",
+                     "achieved": round(pb / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(pb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "tflops": round(pfl / (ms * 1e-3) / 1e12, 2),
+                     "mfma_bf16_frac": round(pfl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill2", "prefill3", "prefill4"])
+    ap.add_argument("--layers", type=int, default=18)
+    ap.add_argument("--decode-steps", type=int, default=0)
+    ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: libgdn has no multi-GPU path (every "
+                  "(sequence, head) recurrence is independent; see the sharding notes). "
+                  "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import gated_delta_rule_decode_amd as gdn
+    gdn.lib()  # loud failure without the HIP library
+    if args.workload == "decode":
+        out = run_decode_job(args)
+    else:
+        out = run_prefill(args, int(args.workload[-1]))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

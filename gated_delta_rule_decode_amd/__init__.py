@@ -1,0 +1,224 @@
+"""libgdn -- the Gated DeltaNet token mixer on MI355X (gfx950): Python binding.
+
+Thin ctypes marshalling over the C ABI declared in include/gdn.h.  Every step
+of the computation runs in the HIP kernels of libgdn.so; torch supplies device
+memory and the current stream only.  If libgdn.so is missing, every call
+raises (there is no fallback path).
+
+    decode_step(q, k, v, g, beta, state, ...)          -> o
+    prefill_chunked(q, k, v, g, beta, cu_seqlens, ...) -> (o, final_state)
+    rmsnorm_gated(x, z, w, ...)                        -> y
+    prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk=64)
+
+Layouts (row-major, contiguous): q, k [tokens, H, dk]; v [tokens, HV, dv];
+g, beta [tokens, HV] fp32; state [N, HV, dv, dk] fp32; o [tokens, HV, dv].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libgdn.so")
+
+GDN_F32 = 0
+GDN_BF16 = 1
+STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPPORTED",
+          3: "GDN_ERROR_WORKSPACE", 4: "GDN_ERROR_HIP"}
+
+# every symbol include/gdn.h declares
+EXPORTS = ("gdn_version", "gdn_status_string", "gdn_decode_step", "gdn_prefill_workspace_bytes",
+           "gdn_prefill_chunked", "gdn_rmsnorm_gated")
+
+__all__ = ["decode_step", "prefill_chunked", "rmsnorm_gated", "prefill_workspace_bytes",
+           "GDNError", "lib", "LIBRARY", "EXPORTS", "version"]
+
+
+class GDNError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+        self.status = status
+
+
+_LIB: Optional[ctypes.CDLL] = None
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError(f"libgdn.so is not built ({LIBRARY}); run "
+                              "`python -m gated_delta_rule_decode_amd.build`")
+        L = ctypes.CDLL(LIBRARY)
+        L.gdn_version.restype = _i
+        L.gdn_version.argtypes = []
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_status_string.argtypes = [_i]
+        L.gdn_decode_step.restype = _i
+        L.gdn_decode_step.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                      _i, _f, _vp]
+        L.gdn_prefill_workspace_bytes.restype = _sz
+        L.gdn_prefill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+        L.gdn_prefill_chunked.restype = _i
+        L.gdn_prefill_chunked.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
+                                          _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]
+        L.gdn_rmsnorm_gated.restype = _i
+        L.gdn_rmsnorm_gated.argtypes = [_vp, _i, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp]
+        _LIB = L
+    return _LIB
+
+
+def version() -> int:
+    return int(lib().gdn_version())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise GDNError(fn, status)
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return GDN_F32
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name: str, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def decode_step(q, k, v, g, beta, state, *, o=None, scale: float = 1.0, out_dtype=None):
+    """Advance N sequences by one token in place.
+
+    q, k [N, H, dk], v [N, HV, dv] (same dtype, fp32 or bf16); g, beta [N, HV]
+    fp32; state [N, HV, dv, dk] fp32 (updated in place).  Returns o [N, HV, dv]
+    (fp32 unless ``out_dtype`` or a preallocated ``o`` says otherwise)."""
+    torch = _torch()
+    f32 = torch.float32
+    N, H, dk = q.shape
+    HV, dv = v.shape[1], v.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(g, "g", f32)
+    _dev(beta, "beta", f32)
+    _dev(state, "state", f32)
+    if k.shape != q.shape or v.shape[0] != N or g.shape != (N, HV) or beta.shape != (N, HV) \
+            or state.shape != (N, HV, dv, dk):
+        raise ValueError("inconsistent decode shapes")
+    if o is None:
+        o = torch.empty((N, HV, dv), dtype=out_dtype or f32, device=q.device)
+    _dev(o, "o")
+    if o.shape != (N, HV, dv):
+        raise ValueError("o shape")
+    st = lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta),
+                               _ptr(state), _ptr(o), _dtype_code(o), N, H, HV, dk, dv,
+                               float(scale), _stream(q.device))
+    _check("gdn_decode_step", st)
+    return o
+
+
+def prefill_workspace_bytes(N: int, T_total: int, H: int, HV: int, dk: int, dv: int,
+                            chunk: int = 64) -> int:
+    return int(lib().gdn_prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk))
+
+
+def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_state=None,
+                    o=None, scale: float = 1.0, chunk: int = 64, workspace=None,
+                    out_dtype=None, return_final_state: bool = True) -> Tuple:
+    """Chunked prefill of a packed batch.
+
+    q, k [T, H, dk], v [T, HV, dv]; g, beta [T, HV] fp32; cu_seqlens [N+1]
+    int32 on the device; initial_state [N, HV, dv, dk] fp32 or None (zeros).
+    Returns (o [T, HV, dv], final_state [N, HV, dv, dk] or None)."""
+    torch = _torch()
+    f32 = torch.float32
+    T, H, dk = q.shape
+    HV, dv = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(g, "g", f32)
+    _dev(beta, "beta", f32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if k.shape != q.shape or v.shape[0] != T or g.shape != (T, HV) or beta.shape != (T, HV):
+        raise ValueError("inconsistent prefill shapes")
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", f32)
+        if initial_state.shape != (N, HV, dv, dk):
+            raise ValueError("initial_state shape")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((N, HV, dv, dk), dtype=f32, device=q.device)
+    if final_state is not None:
+        _dev(final_state, "final_state", f32)
+    if o is None:
+        o = torch.empty((T, HV, dv), dtype=out_dtype or f32, device=q.device)
+    _dev(o, "o")
+    need = prefill_workspace_bytes(N, T, H, HV, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    st = lib().gdn_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+        _ptr(initial_state), _ptr(final_state), _ptr(o), _dtype_code(o), H, HV, dk, dv, chunk,
+        float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device))
+    _check("gdn_prefill_chunked", st)
+    return o, final_state
+
+
+def rmsnorm_gated(x, z, w, *, y=None, eps: float = 1e-6, out_dtype=None):
+    """y = x / sqrt(mean(x^2) + eps) * w * silu(z) over the last axis (dv).
+
+    x, z [..., HV, dv]; w [dv]; y may be x itself (in place) if dtypes match."""
+    torch = _torch()
+    _dev(x, "x")
+    _dev(z, "z")
+    _dev(w, "w")
+    dv = x.shape[-1]
+    HV = x.shape[-2] if x.dim() >= 2 else 1
+    rows = x.numel() // (HV * dv) if x.numel() else 0
+    if z.shape != x.shape or w.shape != (dv,):
+        raise ValueError("inconsistent norm shapes")
+    if y is None:
+        y = torch.empty(x.shape, dtype=out_dtype or torch.float32, device=x.device)
+    _dev(y, "y")
+    if y.shape != x.shape:
+        raise ValueError("y shape")
+    st = lib().gdn_rmsnorm_gated(_ptr(x), _dtype_code(x), _ptr(z), _dtype_code(z), _ptr(w),
+                                 _dtype_code(w), _ptr(y), _dtype_code(y), rows, HV, dv,
+                                 float(eps), _stream(x.device))
+    _check("gdn_rmsnorm_gated", st)
+    return y

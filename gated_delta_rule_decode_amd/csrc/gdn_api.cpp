@@ -1,0 +1,156 @@
+// gdn_api.cpp -- the C ABI of libgdn: host-side validation and dispatch.
+//
+// Every check runs on the host before anything is enqueued; a failing check
+// returns its status with no HIP call made and no output touched.  See
+// include/gdn.h for the contract of each entry point.
+#include "gdn.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "gdn_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_dtype(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+gdn_status heads_status(int H, int HV, int dk, int dv) {
+    if (H <= 0 || HV <= 0 || dk <= 0 || dv <= 0) return GDN_ERROR_INVALID_VALUE;
+    if (HV % H != 0) return GDN_ERROR_INVALID_VALUE;
+    if (!supported_d(dk) || !supported_d(dv)) return GDN_ERROR_NOT_SUPPORTED;
+    return GDN_SUCCESS;
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_HIP; }
+
+}  // namespace
+
+namespace gdn {
+
+PrefillLayout prefill_layout(int N, int T, int HV) {
+    PrefillLayout L{};
+    // upper bound on sum_n ceil(len_n / 64) given sum_n len_n = T
+    const size_t maxc = ((size_t)T + (size_t)N * (kChunk - 1)) / kChunk;
+    L.max_chunks = (int)maxc;
+    size_t off = 0;
+    L.chunk_off = off;
+    off = align256(off + ((size_t)N + 1) * sizeof(int32_t));
+    L.ws_T = off;
+    off = align256(off + maxc * HV * kChunk * kChunk * sizeof(float));
+    L.ws_G = off;
+    off = align256(off + maxc * HV * kChunk * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+int gdn_version(void) { return kVersion; }
+
+const char* gdn_status_string(int status) {
+    switch (status) {
+        case GDN_SUCCESS: return "GDN_SUCCESS";
+        case GDN_ERROR_INVALID_VALUE: return "GDN_ERROR_INVALID_VALUE";
+        case GDN_ERROR_NOT_SUPPORTED: return "GDN_ERROR_NOT_SUPPORTED";
+        case GDN_ERROR_WORKSPACE: return "GDN_ERROR_WORKSPACE";
+        case GDN_ERROR_HIP: return "GDN_ERROR_HIP";
+        default: return "GDN_UNKNOWN_STATUS";
+    }
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                           const float* g, const float* beta, float* state, void* o,
+                           gdn_dtype o_dtype, int N, int H, int HV, int dk, int dv, float scale,
+                           void* stream) {
+    if (N < 0) return GDN_ERROR_INVALID_VALUE;
+    gdn_status st = heads_status(H, HV, dk, dv);
+    if (st != GDN_SUCCESS) return st;
+    if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return GDN_ERROR_NOT_SUPPORTED;
+    if (N == 0) return GDN_SUCCESS;
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
+        return GDN_ERROR_INVALID_VALUE;
+    if ((size_t)N * HV > (size_t)(1u << 31) / (size_t)dv) return GDN_ERROR_NOT_SUPPORTED;
+    gdn::DecodeArgs a{q, k, v, g, beta, state, o, in_dtype == GDN_BF16, o_dtype == GDN_BF16,
+                      N, H, HV, dk, dv, scale, static_cast<hipStream_t>(stream)};
+    return from_hip(gdn::launch_decode(a));
+}
+
+size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv, int chunk) {
+    if (N < 0 || T_total < 0) return 0;
+    if (heads_status(H, HV, dk, dv) != GDN_SUCCESS || chunk != gdn::kChunk) return 0;
+    if (N == 0 || T_total == 0) return 0;
+    return gdn::prefill_layout(N, T_total, HV).total;
+}
+
+gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                               const float* g, const float* beta, const int32_t* cu_seqlens,
+                               int N, int T_total, const float* initial_state,
+                               float* final_state, void* o, gdn_dtype o_dtype, int H, int HV,
+                               int dk, int dv, int chunk, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (N < 0 || T_total < 0) return GDN_ERROR_INVALID_VALUE;
+    gdn_status st = heads_status(H, HV, dk, dv);
+    if (st != GDN_SUCCESS) return st;
+    if (chunk != gdn::kChunk) return GDN_ERROR_NOT_SUPPORTED;
+    if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return GDN_ERROR_NOT_SUPPORTED;
+    if (N == 0) return GDN_SUCCESS;
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return GDN_ERROR_INVALID_VALUE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t state_elems = (size_t)N * HV * dv * dk;
+    if (T_total == 0) {
+        if (!final_state || final_state == initial_state) return GDN_SUCCESS;
+        return from_hip(gdn::launch_state_copy(initial_state, final_state, state_elems, s));
+    }
+    if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return GDN_ERROR_INVALID_VALUE;
+    const gdn::PrefillLayout L = gdn::prefill_layout(N, T_total, HV);
+    if ((size_t)L.max_chunks * HV > (size_t)(1u << 31) / (gdn::kChunk * gdn::kChunk))
+        return GDN_ERROR_NOT_SUPPORTED;
+    if (!workspace || workspace_bytes < L.total) return GDN_ERROR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN_ERROR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    gdn::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
+    a.s0 = initial_state; a.s_final = final_state; a.o = o;
+    a.in_bf16 = in_dtype == GDN_BF16; a.o_bf16 = o_dtype == GDN_BF16;
+    a.N = N; a.T = T_total; a.H = H; a.HV = HV; a.dk = dk; a.dv = dv; a.scale = scale;
+    a.chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
+    a.ws_T = reinterpret_cast<float*>(ws + L.ws_T);
+    a.ws_G = reinterpret_cast<float*>(ws + L.ws_G);
+    a.max_chunks = L.max_chunks;
+    a.stream = s;
+    return from_hip(gdn::launch_prefill(a));
+}
+
+gdn_status gdn_rmsnorm_gated(const void* x, gdn_dtype x_dtype, const void* z, gdn_dtype z_dtype,
+                             const void* w, gdn_dtype w_dtype, void* y, gdn_dtype y_dtype,
+                             int rows, int HV, int dv, float eps, void* stream) {
+    if (rows < 0 || HV <= 0 || dv <= 0 || !(eps >= 0.f)) return GDN_ERROR_INVALID_VALUE;
+    if (!supported_d(dv)) return GDN_ERROR_NOT_SUPPORTED;
+    if (!valid_dtype(x_dtype) || !valid_dtype(z_dtype) || !valid_dtype(w_dtype) ||
+        !valid_dtype(y_dtype))
+        return GDN_ERROR_NOT_SUPPORTED;
+    if (rows == 0) return GDN_SUCCESS;
+    if (!x || !z || !w || !y) return GDN_ERROR_INVALID_VALUE;
+    if (!aligned16(x) || !aligned16(z) || !aligned16(w) || !aligned16(y))
+        return GDN_ERROR_INVALID_VALUE;
+    if (x == y && x_dtype != y_dtype) return GDN_ERROR_INVALID_VALUE;
+    const long groups = (long)rows * HV;
+    if ((size_t)groups * dv >= ((size_t)1 << 40)) return GDN_ERROR_NOT_SUPPORTED;
+    gdn::NormArgs a{x, z, w, y, x_dtype == GDN_BF16, z_dtype == GDN_BF16, w_dtype == GDN_BF16,
+                    y_dtype == GDN_BF16, groups, dv, eps, static_cast<hipStream_t>(stream)};
+    return from_hip(gdn::launch_rmsnorm_gated(a));
+}
+
+}  // extern "C"

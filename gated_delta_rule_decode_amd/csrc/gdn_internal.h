@@ -1,0 +1,75 @@
+// gdn_internal.h -- host-side argument bundles and kernel launchers shared by
+// the C-ABI layer (gdn_api.cpp) and the kernel translation units.  Arguments
+// reaching a launcher have already been validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kChunk = 64;
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* state;
+    void* o;
+    bool in_bf16;
+    bool o_bf16;
+    int N, H, HV, dk, dv;
+    float scale;
+    hipStream_t stream;
+};
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const int32_t* cu_seqlens;
+    const float* s0;   // may be null (zeros)
+    float* s_final;    // may be null
+    void* o;
+    bool in_bf16;
+    bool o_bf16;
+    int N, T, H, HV, dk, dv;
+    float scale;
+    // workspace carve-up (device pointers into the caller's buffer)
+    int32_t* chunk_off;  // [N + 1]
+    float* ws_T;         // [max_chunks, HV, 64, 64]  (I + A)^-1 diag(beta)
+    float* ws_G;         // [max_chunks, HV, 64]      in-chunk cumulative log-decay
+    int max_chunks;
+    hipStream_t stream;
+};
+
+struct NormArgs {
+    const void* x;
+    const void* z;
+    const void* w;
+    void* y;
+    bool x_bf16, z_bf16, w_bf16, y_bf16;
+    long groups;
+    int dv;
+    float eps;
+    hipStream_t stream;
+};
+
+// Workspace layout of gdn_prefill_chunked (byte offsets, 256-aligned).
+struct PrefillLayout {
+    size_t chunk_off, ws_T, ws_G, total;
+    int max_chunks;
+};
+PrefillLayout prefill_layout(int N, int T, int HV);
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream);
+hipError_t launch_rmsnorm_gated(const NormArgs& a);
+
+}  // namespace gdn

@@ -243,3 +243,39 @@ def workload(cfg: int, seed: int = 0) -> PrefillInputs:
     return make_prefill(lengths, w["H"], w["HV"], w["dk"], w["dv"], dtype=w["dtype"],
                         decay=w["decay"], s0_std=w.get("s0_std", 0.0), seed=seed,
                         stream=1000 + cfg)
+
+
+# ---------------------------------------------------------------------------
+# device-side draws (benchmark): the same recipe, drawn with torch on the GPU
+# ---------------------------------------------------------------------------
+
+def device_tokens(lead, H, HV, dk, dv, *, seed: int, head_scale, device, dtype=None,
+                  with_z: bool = True):
+    """q, k, v, g, beta (and z) for tokens with leading shape ``lead``, drawn
+    on ``device`` with a seeded torch.Generator: q, k L2-normalised in fp32
+    then rounded to ``dtype`` (bf16 by default); v, z ~ N(0,1) in ``dtype``;
+    g = -head_scale * softplus(x), beta = sigmoid(x') in fp32.  head_scale is
+    the per-value-head exp(A_h) ([HV] float64 numpy array)."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    lead = tuple(lead)
+    f32 = torch.float32
+
+    def unit(shape):
+        x = torch.randn(shape, generator=gen, device=device, dtype=f32)
+        return (x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)).to(dtype)
+
+    q = unit(lead + (H, dk))
+    k = unit(lead + (H, dk))
+    v = torch.randn(lead + (HV, dv), generator=gen, device=device, dtype=f32).to(dtype)
+    sc = torch.as_tensor(np.asarray(head_scale, np.float32), device=device)
+    xg = torch.randn(lead + (HV,), generator=gen, device=device, dtype=f32)
+    g = (-sc * torch.nn.functional.softplus(xg)).contiguous()
+    xb = torch.randn(lead + (HV,), generator=gen, device=device, dtype=f32)
+    beta = torch.sigmoid(xb).contiguous()
+    z = None
+    if with_z:
+        z = torch.randn(lead + (HV, dv), generator=gen, device=device, dtype=f32).to(dtype)
+    return q, k, v, g, beta, z

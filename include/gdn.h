@@ -1,0 +1,147 @@
+/*
+ * gdn.h -- libgdn: the Gated DeltaNet token mixer on AMD Instinct MI355X (gfx950).
+ *
+ * The mixer is the linear-attention layer of the Qwen3.5 / Qwen3.6 hybrid
+ * decoders: the Qwen3.5-0.8B chat guide (soniqo.audio, section "Architektur")
+ * describes 18 of its 24 layers as linear attention with a gated-delta-rule
+ * recurrence followed by RMSNormGated; the Qwen3.6-35B-A3B card of the Core AI
+ * model zoo (intro) runs 32 value heads over 16 key heads, each key/query head
+ * shared by two value heads; the Swiftlet post ("How It Works") notes the
+ * fixed-size recurrent state.  The recurrence is the gated delta rule (Yang,
+ * Kautz, Hatamizadeh, "Gated Delta Networks", ICLR 2025), per sequence and
+ * value head:
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T        a_t = exp(g_t)
+ *     o_t = scale * S_t q_t                                         b_t = beta_t
+ *
+ * S_t is d_v x d_k (row i <-> value dim, column j <-> key dim); the readout uses
+ * the state after the token's update.  Value head h reads key/query head
+ * h / (HV / H) (consecutive value heads share a key head).
+ *
+ * Conventions for every call
+ *  - Pointers are device pointers unless stated.  Tensors are dense, row-major,
+ *    with the layouts given per argument, and 16-byte aligned.
+ *  - The caller owns all memory, including the prefill workspace.  The library
+ *    allocates nothing, keeps no global state and is reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued and the call returns without synchronising.
+ *  - Arguments are validated on the host before anything is enqueued.  On an
+ *    error nothing is enqueued and no output is touched.  A kernel launch
+ *    failure returns GDN_ERROR_HIP; device faults surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this interface.
+ *  - Supported: d_k, d_v in {16, 32, 64, 128}; HV a multiple of H; chunk 64;
+ *    q/k/v in GDN_F32 or GDN_BF16; outputs in GDN_F32 or GDN_BF16.  Other
+ *    values return GDN_ERROR_NOT_SUPPORTED.  g and beta are fp32.
+ *  - Preconditions not checked (documented): finite inputs; cu_seqlens
+ *    non-decreasing with cu_seqlens[0] = 0 and cu_seqlens[N] = T_total.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_SUCCESS = 0,
+    GDN_ERROR_INVALID_VALUE = 1, /* null pointer, bad size, misaligned pointer */
+    GDN_ERROR_NOT_SUPPORTED = 2, /* a head size, chunk or dtype outside the list above */
+    GDN_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    GDN_ERROR_HIP = 4            /* the HIP runtime reported an error at launch */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,  /* IEEE binary32 */
+    GDN_BF16 = 1  /* bfloat16 (upper 16 bits of binary32) */
+} gdn_dtype;
+
+/* Library version as an integer (major * 10000 + minor * 100 + patch). */
+int gdn_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* gdn_status_string(int status);
+
+/*
+ * gdn_decode_step -- advance every sequence by one token against its resident
+ * state, in place.  This is the single-step decoder that owns its recurrent
+ * state and is advanced one token per call (Qwen3.5-0.8B Core ML card on
+ * aimarketly.com, section "Model").
+ *
+ *   q, k     [N, H, dk]      in_dtype   query and key of the token
+ *   v        [N, HV, dv]     in_dtype   value
+ *   g        [N, HV]         fp32       log-decay, a = exp(g) (g <= 0 expected)
+ *   beta     [N, HV]         fp32       write strength b
+ *   state    [N, HV, dv, dk] fp32       S_{t-1} in, S_t out (read fully before
+ *                                       any element is written; one lane owns
+ *                                       each element)
+ *   o        [N, HV, dv]     o_dtype    o_t = scale * S_t q_t
+ *   N >= 0 sequences (N == 0 is a successful no-op).
+ */
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                           const float* g, const float* beta, float* state, void* o,
+                           gdn_dtype o_dtype, int N, int H, int HV, int dk, int dv,
+                           float scale, void* stream);
+
+/*
+ * gdn_prefill_workspace_bytes -- device workspace that gdn_prefill_chunked
+ * needs for this problem (a multiple of 256 bytes; 0 when T_total == 0).
+ * Returns 0 for sizes that gdn_prefill_chunked would reject.
+ */
+size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv,
+                                   int chunk);
+
+/*
+ * gdn_prefill_chunked -- a whole packed batch of prompts in the chunked
+ * (WY / UT-transform) form, returning every output and the final states.
+ * The result equals running the recurrence token by token (up to rounding);
+ * chunks restart at every sequence start, so no token influences another
+ * sequence.  Incremental use is exact: prefill(A) then prefill(B) from the
+ * returned state equals prefill(A+B), as the Swiftlet post's correctness
+ * section requires of incremental decoding.
+ *
+ *   q, k          [T_total, H, dk]    in_dtype  packed tokens of all sequences
+ *   v             [T_total, HV, dv]   in_dtype
+ *   g, beta       [T_total, HV]       fp32
+ *   cu_seqlens    [N + 1]             int32     device; sequence n holds tokens
+ *                                               cu_seqlens[n] .. cu_seqlens[n+1]-1
+ *                                               (zero-length sequences allowed)
+ *   initial_state [N, HV, dv, dk]     fp32      or NULL for zero states
+ *   final_state   [N, HV, dv, dk]     fp32      or NULL; may equal initial_state
+ *   o             [T_total, HV, dv]   o_dtype
+ *   chunk         must be 64
+ *   workspace     device memory of workspace_bytes >= gdn_prefill_workspace_bytes(...)
+ *   N == 0 or T_total == 0 only copies initial_state to final_state (zeros if
+ *   NULL) and is otherwise a no-op.
+ */
+gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                               const float* g, const float* beta, const int32_t* cu_seqlens,
+                               int N, int T_total, const float* initial_state,
+                               float* final_state, void* o, gdn_dtype o_dtype, int H, int HV,
+                               int dk, int dv, int chunk, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_rmsnorm_gated -- RMSNormGated, the norm that closes each DeltaNet layer
+ * (Qwen3.5-0.8B chat guide, section "Architektur").  Per (row, head) group of
+ * dv values:
+ *
+ *     y = x / sqrt(mean(x^2) + eps) * w * silu(z),   silu(z) = z / (1 + e^-z)
+ *
+ *   x   [rows, HV, dv]  x_dtype      (usually the mixer output o)
+ *   z   [rows, HV, dv]  z_dtype      gate input
+ *   w   [dv]            w_dtype      weight shared by all heads
+ *   y   [rows, HV, dv]  y_dtype      may alias x when y_dtype == x_dtype
+ *   rows >= 0 (0 is a successful no-op), eps >= 0.
+ */
+gdn_status gdn_rmsnorm_gated(const void* x, gdn_dtype x_dtype, const void* z, gdn_dtype z_dtype,
+                             const void* w, gdn_dtype w_dtype, void* y, gdn_dtype y_dtype,
+                             int rows, int HV, int dv, float eps, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports every declared symbol and validates its
+arguments on the host.  No call here reaches a kernel launch: every call either
+fails validation (which happens before any HIP call) or is an N == 0 no-op."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_decode_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+FAKE = 0x10000  # an aligned non-null address; validation fails before any use
+MISALIGNED = 0x10004
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gdn.LIBRARY):
+        import gated_delta_rule_decode_amd.build as b
+        b.build()
+    return gdn.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(gdn.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(L):
+    assert gdn.version() == 100
+    for code, name in gdn.STATUS.items():
+        assert L.gdn_status_string(code).decode() == name
+    assert L.gdn_status_string(99).decode() == "GDN_UNKNOWN_STATUS"
+
+
+def _decode(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=1, g=FAKE, beta=FAKE, state=FAKE, o=FAKE, o_dt=0,
+             N=2, H=2, HV=4, dk=128, dv=128, scale=1.0)
+    a.update(kw)
+    return L.gdn_decode_step(a["q"], a["k"], a["v"], a["in_dt"], a["g"], a["beta"], a["state"],
+                             a["o"], a["o_dt"], a["N"], a["H"], a["HV"], a["dk"], a["dv"],
+                             a["scale"], None)
+
+
+def test_decode_validation(L):
+    assert _decode(L, N=0) == 0                      # no-op
+    assert _decode(L, N=0, q=None) == 0              # no-op ignores pointers
+    assert _decode(L, N=-1) == 1
+    assert _decode(L, q=None) == 1
+    assert _decode(L, state=None) == 1
+    assert _decode(L, o=MISALIGNED) == 1
+    assert _decode(L, HV=3) == 1                     # HV % H != 0
+    assert _decode(L, H=0) == 1
+    assert _decode(L, dk=96) == 2
+    assert _decode(L, dv=256) == 2
+    assert _decode(L, in_dt=7) == 2
+    assert _decode(L, o_dt=-1) == 2
+
+
+def _prefill(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=1, g=FAKE, beta=FAKE, cu=FAKE, N=2, T=100, s0=None,
+             sf=FAKE, o=FAKE, o_dt=0, H=2, HV=4, dk=128, dv=128, chunk=64, scale=1.0,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.gdn_prefill_chunked(a["q"], a["k"], a["v"], a["in_dt"], a["g"], a["beta"], a["cu"],
+                                 a["N"], a["T"], a["s0"], a["sf"], a["o"], a["o_dt"], a["H"],
+                                 a["HV"], a["dk"], a["dv"], a["chunk"], a["scale"], a["ws"],
+                                 a["wsb"], None)
+
+
+def test_prefill_validation(L):
+    assert _prefill(L, N=0) == 0
+    assert _prefill(L, N=-1) == 1
+    assert _prefill(L, T=-5) == 1
+    assert _prefill(L, chunk=32) == 2
+    assert _prefill(L, dk=48) == 2
+    assert _prefill(L, HV=5) == 1
+    assert _prefill(L, cu=None) == 1
+    assert _prefill(L, o=None) == 1
+    assert _prefill(L, k=MISALIGNED) == 1
+    assert _prefill(L, s0=MISALIGNED) == 1
+    assert _prefill(L, ws=None) == 3
+    need = gdn.prefill_workspace_bytes(2, 100, 2, 4, 128, 128)
+    assert _prefill(L, wsb=need - 1) == 3
+    assert _prefill(L, ws=FAKE + 16) == 3            # workspace must be 256-aligned
+    assert _prefill(L, o_dt=3) == 2
+
+
+def test_prefill_workspace_bytes(L):
+    f = gdn.prefill_workspace_bytes
+    assert f(0, 100, 2, 4, 128, 128) == 0
+    assert f(2, 0, 2, 4, 128, 128) == 0
+    assert f(2, 100, 2, 4, 128, 128, 32) == 0
+    assert f(2, 100, 2, 4, 96, 128) == 0
+    for N, T, HV in ((1, 1, 1), (4, 16384, 16), (8, 131072, 32), (3, 65, 2)):
+        maxc = (T + N * 63) // 64
+        al = lambda x: (x + 255) // 256 * 256
+        want = al(4 * (N + 1)) + al(maxc * HV * 64 * 64 * 4) + al(maxc * HV * 64 * 4)
+        assert f(N, T, 1, HV, 128, 128) == want
+        assert f(N, T, 1, HV, 128, 128) % 256 == 0
+
+
+def _norm(L, **kw):
+    a = dict(x=FAKE, xd=0, z=FAKE, zd=1, w=FAKE, wd=0, y=FAKE, yd=0, rows=4, HV=2, dv=128,
+             eps=1e-6)
+    a.update(kw)
+    return L.gdn_rmsnorm_gated(a["x"], a["xd"], a["z"], a["zd"], a["w"], a["wd"], a["y"], a["yd"],
+                               a["rows"], a["HV"], a["dv"], a["eps"], None)
+
+
+def test_norm_validation(L):
+    assert _norm(L, rows=0) == 0
+    assert _norm(L, rows=-1) == 1
+    assert _norm(L, eps=-1.0) == 1
+    assert _norm(L, eps=float("nan")) == 1
+    assert _norm(L, z=None) == 1
+    assert _norm(L, y=MISALIGNED) == 1
+    assert _norm(L, dv=80) == 2
+    assert _norm(L, zd=5) == 2
+    assert _norm(L, yd=1) == 1                       # y aliases x with another dtype
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(2, 2, 16)
+    with pytest.raises(ValueError):
+        gdn.rmsnorm_gated(x, x, torch.ones(16))
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "LIBRARY", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gdn, "_LIB", None)
+    with pytest.raises(ImportError):
+        gdn.lib()
