@@ -28,16 +28,17 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
           3: "GDN_ERROR_WORKSPACE", 4: "GDN_ERROR_HIP"}
 
 # every symbol include/gdn.h declares
-EXPORTS = ("gdn_version", "gdn_status_string", "gdn_decode_step", "gdn_prefill_workspace_bytes",
-           "gdn_prefill_chunked", "gdn_rmsnorm_gated")
+EXPORTS = ("gdn_version", "gdn_status_string", "gdn_last_hip_error", "gdn_decode_step",
+           "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_rmsnorm_gated")
 
 __all__ = ["decode_step", "prefill_chunked", "rmsnorm_gated", "prefill_workspace_bytes",
            "GDNError", "lib", "LIBRARY", "EXPORTS", "version"]
 
 
 class GDNError(RuntimeError):
-    def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        msg = f"{fn} returned {STATUS.get(status, status)}"
+        super().__init__(msg + (f" ({detail})" if detail else ""))
         self.status = status
 
 
@@ -52,11 +53,18 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIBRARY):
             raise ImportError(f"libgdn.so is not built ({LIBRARY}); run "
                               "`python -m gated_delta_rule_decode_amd.build`")
+        # torch ships its own HIP runtime (same soname, libamdhip64.so.7).
+        # Loading torch first makes libgdn.so bind to that runtime; loaded the
+        # other way round, the process would hold two HIP runtimes and the
+        # second would find no device.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIBRARY)
         L.gdn_version.restype = _i
         L.gdn_version.argtypes = []
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_status_string.argtypes = [_i]
+        L.gdn_last_hip_error.restype = ctypes.c_char_p
+        L.gdn_last_hip_error.argtypes = []
         L.gdn_decode_step.restype = _i
         L.gdn_decode_step.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                       _i, _f, _vp]
@@ -77,7 +85,8 @@ def version() -> int:
 
 def _check(fn: str, status: int):
     if status != 0:
-        raise GDNError(fn, status)
+        detail = lib().gdn_last_hip_error().decode() if status == 4 else ""
+        raise GDNError(fn, status, detail)
 
 
 # ---------------------------------------------------------------------------

@@ -27,7 +27,16 @@ gdn_status heads_status(int H, int HV, int dk, int dv) {
     return GDN_SUCCESS;
 }
 
-gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_HIP; }
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+gdn_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return GDN_SUCCESS;
+    t_last_hip_error = e;
+    return GDN_ERROR_HIP;
+}
+
+// drop an error that earlier HIP calls left pending on this thread
+void clear_pending() { (void)hipGetLastError(); }
 
 }  // namespace
 
@@ -55,6 +64,8 @@ extern "C" {
 
 int gdn_version(void) { return kVersion; }
 
+const char* gdn_last_hip_error(void) { return hipGetErrorName(t_last_hip_error); }
+
 const char* gdn_status_string(int status) {
     switch (status) {
         case GDN_SUCCESS: return "GDN_SUCCESS";
@@ -79,6 +90,7 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtyp
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
         return GDN_ERROR_INVALID_VALUE;
     if ((size_t)N * HV > (size_t)(1u << 31) / (size_t)dv) return GDN_ERROR_NOT_SUPPORTED;
+    clear_pending();
     gdn::DecodeArgs a{q, k, v, g, beta, state, o, in_dtype == GDN_BF16, o_dtype == GDN_BF16,
                       N, H, HV, dk, dv, scale, static_cast<hipStream_t>(stream)};
     return from_hip(gdn::launch_decode(a));
@@ -109,6 +121,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     const size_t state_elems = (size_t)N * HV * dv * dk;
     if (T_total == 0) {
         if (!final_state || final_state == initial_state) return GDN_SUCCESS;
+        clear_pending();
         return from_hip(gdn::launch_state_copy(initial_state, final_state, state_elems, s));
     }
     if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERROR_INVALID_VALUE;
@@ -130,6 +143,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     a.ws_G = reinterpret_cast<float*>(ws + L.ws_G);
     a.max_chunks = L.max_chunks;
     a.stream = s;
+    clear_pending();
     return from_hip(gdn::launch_prefill(a));
 }
 
@@ -148,6 +162,7 @@ gdn_status gdn_rmsnorm_gated(const void* x, gdn_dtype x_dtype, const void* z, gd
     if (x == y && x_dtype != y_dtype) return GDN_ERROR_INVALID_VALUE;
     const long groups = (long)rows * HV;
     if ((size_t)groups * dv >= ((size_t)1 << 40)) return GDN_ERROR_NOT_SUPPORTED;
+    clear_pending();
     gdn::NormArgs a{x, z, w, y, x_dtype == GDN_BF16, z_dtype == GDN_BF16, w_dtype == GDN_BF16,
                     y_dtype == GDN_BF16, groups, dv, eps, static_cast<hipStream_t>(stream)};
     return from_hip(gdn::launch_rmsnorm_gated(a));

@@ -65,6 +65,15 @@ int gdn_version(void);
 const char* gdn_status_string(int status);
 
 /*
+ * Name of the HIP error behind the most recent GDN_ERROR_HIP returned on the
+ * calling thread ("hipSuccess" if there was none).  Static string, never NULL.
+ * Before launching, each entry point clears a HIP error that earlier calls
+ * left pending on this thread, so GDN_ERROR_HIP always refers to libgdn's
+ * own launches.
+ */
+const char* gdn_last_hip_error(void);
+
+/*
  * gdn_decode_step -- advance every sequence by one token against its resident
  * state, in place.  This is the single-step decoder that owns its recurrent
  * state and is advanced one token per call (Qwen3.5-0.8B Core ML card on

@@ -144,3 +144,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "_LIB", None)
     with pytest.raises(ImportError):
         gdn.lib()
+
+
+def test_library_binds_to_torch_hip_runtime():
+    """libgdn.so must share torch's HIP runtime (one runtime per process)."""
+    gdn.lib()
+    maps = open("/proc/self/maps").read()
+    runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(runtimes) == 1, runtimes
