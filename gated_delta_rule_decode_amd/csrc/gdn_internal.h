@@ -69,6 +69,8 @@ PrefillLayout prefill_layout(int N, int T, int HV);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
+bool prefill_mfma_eligible(const PrefillArgs& a);
+hipError_t launch_prefill_mfma(const PrefillArgs& a);
 hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream);
 hipError_t launch_rmsnorm_gated(const NormArgs& a);
 

@@ -292,14 +292,10 @@ hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStre
 
 template <int DK, int BV, typename Tin, typename Tout>
 static hipError_t launch_prefill_t(const PrefillArgs& A) {
-    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, A.stream, A.cu_seqlens, A.N,
-                       A.T, A.chunk_off);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     hipLaunchKernelGGL((prep_kernel<DK, Tin>), dim3(A.max_chunks, A.HV), dim3(256), 0, A.stream,
                        static_cast<const Tin*>(A.k), A.g, A.beta, A.cu_seqlens, A.chunk_off, A.N,
                        A.T, A.H, A.HV, A.max_chunks, A.ws_T, A.ws_G);
-    err = hipGetLastError();
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int tiles = A.dv / BV;
     hipLaunchKernelGGL((scan_kernel<DK, BV, Tin, Tout>), dim3((unsigned)(A.N * A.HV * tiles)),
@@ -326,7 +322,15 @@ static hipError_t launch_prefill_io(const PrefillArgs& A) {
     }
 }
 
+// Chunk table, then the bf16-MFMA kernels where they apply (bf16 inputs,
+// d_k in {64, 128}, d_v a multiple of 32) and the fp32 vector-unit kernels
+// above for every other supported shape and for fp32 inputs.
 hipError_t launch_prefill(const PrefillArgs& A) {
+    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, A.stream, A.cu_seqlens, A.N,
+                       A.T, A.chunk_off);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (prefill_mfma_eligible(A)) return launch_prefill_mfma(A);
     if (A.in_bf16) {
         return A.o_bf16 ? launch_prefill_io<bf16_t, bf16_t>(A) : launch_prefill_io<bf16_t, float>(A);
     }
