@@ -90,10 +90,11 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
     int HV, int max_chunks, float* __restrict__ wsT, float* __restrict__ wsG) {
     constexpr int C = kChunk;
     constexpr int KP = DK + 8;  // padded bf16 row
+    constexpr int AP = C + 4;   // padded fp32 row (16-byte aligned rows)
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
-    __shared__ float Am[C][C + 1];
-    __shared__ float Tm[C][C + 1];
-    __shared__ float Xb[3][16][17];
+    __shared__ __attribute__((aligned(16))) float Am[C * AP];
+    __shared__ __attribute__((aligned(16))) float Tm[C * AP];
+    __shared__ __attribute__((aligned(16))) float Xm[32 * 36];
     __shared__ float Gs[C], Bs[C];
 
     const int c = blockIdx.x, hk = blockIdx.y, tid = threadIdx.x;
@@ -107,11 +108,12 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
     const int L = min(C, e0 - t0);
     const int ratio = HV / H;
 
-    // K chunk -> LDS (zero rows past the sequence end)
+    // K chunk -> LDS (rows past the sequence end are zero)
     for (int idx = tid; idx < C * DK / 8; idx += 256) {
         const int t = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (t < L) val = *reinterpret_cast<const uint4*>(k + ((size_t)(t0 + t) * H + hk) * DK + c8);
+        uint4 val = *reinterpret_cast<const uint4*>(
+            k + ((size_t)(t0 + min(t, L - 1)) * H + hk) * DK + c8);
+        if (t >= L) val = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(&Ks[t * KP + c8]) = val;
     }
     __syncthreads();
@@ -135,71 +137,139 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
     for (int hv = hk * ratio; hv < (hk + 1) * ratio; ++hv) {
         // G = in-chunk inclusive cumsum of g (wave 0), beta
         if (w == 0) {
-            float gv = l < L ? g[(size_t)(t0 + l) * HV + hv] : 0.f;
+            float gv = g[(size_t)(t0 + min(l, L - 1)) * HV + hv];
+            float bv = beta[(size_t)(t0 + min(l, L - 1)) * HV + hv];
+            if (l >= L) gv = 0.f, bv = 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float up = __shfl_up(gv, off, 64);
                 if (l >= off) gv += up;
             }
             Gs[l] = gv;
-            Bs[l] = l < L ? beta[(size_t)(t0 + l) * HV + hv] : 0.f;
+            Bs[l] = bv;
         }
         __syncthreads();
-        // A (strictly lower part of the blocks this wave computed)
+        // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s})
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             if (sb <= w) {
+                const float Gsb = Gs[16 * sb + lr];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * w + 4 * lg + r, s = 16 * sb + lr;
-                    Am[t][s] = (s < t) ? Bs[t] * __expf(Gs[t] - Gs[s]) * kk[sb][r] : 0.f;
+                    Am[t * AP + s] = (s < t) ? Bs[t] * __expf(Gs[t] - Gsb) * kk[sb][r] : 0.f;
                 }
             }
         }
         __syncthreads();
-        // diagonal 16 x 16 blocks by forward substitution: wave b, lane j = column
-        if (lr == l) {  // lanes 0..15 of every wave
-            const int b = w;
+        // diagonal blocks T_bb = (I + A_bb)^-1 by forward substitution:
+        // wave b, lane j < 16 owns column j, rows of A_bb preloaded
+        if (l < 16) {
+            const int o = 16 * w;
             float col[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                float v = (t == lr) ? 1.f : 0.f;
+                float arow[16];
 #pragma unroll
-                for (int x = 0; x < t; ++x) v -= Am[16 * b + t][16 * b + x] * col[x];
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    if (4 * q4 < t) {
+                        const float4 a4 = *reinterpret_cast<const float4*>(&Am[(o + t) * AP + o + 4 * q4]);
+                        arow[4 * q4] = a4.x; arow[4 * q4 + 1] = a4.y;
+                        arow[4 * q4 + 2] = a4.z; arow[4 * q4 + 3] = a4.w;
+                    }
+                }
+                float v = (t == l) ? 1.f : 0.f;
+#pragma unroll
+                for (int x = 0; x < t; ++x) v -= arow[x] * col[x];
                 col[t] = v;
             }
 #pragma unroll
-            for (int t = 0; t < 16; ++t) Tm[16 * b + t][16 * b + lr] = col[t];
+            for (int t = 0; t < 16; ++t) Tm[(o + t) * AP + o + l] = col[t];
         }
         __syncthreads();
-        // off-diagonal blocks, block row by block row
-        for (int i = 1; i < 4; ++i) {
-            // X_j = sum_{k=j}^{i-1} A_ik T_kj for j < i
-            for (int e = tid; e < i * 256; e += 256) {
-                const int j = e >> 8, rho = (e >> 4) & 15, kap = e & 15;
-                float acc = 0.f;
-                for (int kb = j; kb < i; ++kb) {
+        // 16-block merges: T_10 = -T_11 (A_10 T_00), T_32 = -T_33 (A_32 T_22)
+        {
 #pragma unroll
-                    for (int x = 0; x < 16; ++x)
-                        acc += Am[16 * i + rho][16 * kb + x] * Tm[16 * kb + x][16 * j + kap];
-                }
-                Xb[j][rho][kap] = acc;
-            }
-            __syncthreads();
-            // T_ij = -T_ii X_j
-            for (int e = tid; e < i * 256; e += 256) {
-                const int j = e >> 8, rho = (e >> 4) & 15, kap = e & 15;
+            for (int half = 0; half < 2; ++half) {
+                const int e = tid + 256 * half;
+                const int j = (e >> 8) * 2, i = j + 1;  // (1,0) or (3,2)
+                const int rho = (e >> 4) & 15, kap = e & 15;
                 float acc = 0.f;
-                for (int x = 0; x <= rho; ++x) acc += Tm[16 * i + rho][16 * i + x] * Xb[j][x][kap];
-                Tm[16 * i + rho][16 * j + kap] = -acc;
+#pragma unroll
+                for (int x = 0; x < 16; ++x)
+                    acc += (x >= kap) ? Am[(16 * i + rho) * AP + 16 * j + x] *
+                                            Tm[(16 * j + x) * AP + 16 * j + kap]
+                                      : 0.f;
+                Xm[(16 * (e >> 8) + rho) * 36 + kap] = acc;
             }
-            __syncthreads();
         }
+        __syncthreads();
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int e = tid + 256 * half;
+            const int j = (e >> 8) * 2, i = j + 1;
+            const int rho = (e >> 4) & 15, kap = e & 15;
+            float acc = 0.f;
+#pragma unroll
+            for (int x = 0; x < 16; ++x)
+                acc += (x <= rho) ? Tm[(16 * i + rho) * AP + 16 * i + x] *
+                                        Xm[(16 * (e >> 8) + x) * 36 + kap]
+                                  : 0.f;
+            Tm[(16 * i + rho) * AP + 16 * j + kap] = -acc;
+        }
+        __syncthreads();
+        // 32-block merge on MFMA: X = A[32:64, 0:32] T[0:32, 0:32]; T[32:64, 0:32] = -T_B X
+        {
+            const int tb = w >> 1, jb = w & 1;
+            float av[8], bv[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                av[x] = Am[(32 + 16 * tb + lr) * AP + 8 * lg + x];
+                const int xr = 8 * lg + x, cc = 16 * jb + lr;
+                bv[x] = (xr >= cc || (xr >> 4) > (cc >> 4)) ? Tm[xr * AP + cc] : 0.f;
+            }
+            bf8_t ah, al, bh, bl;
+            split8(av, ah, al);
+            split8(bv, bh, bl);
+            f4_t xa = f4_t{0.f, 0.f, 0.f, 0.f};
+            xa = mfma(ah, bh, xa);
+            xa = mfma(ah, bl, xa);
+            xa = mfma(al, bh, xa);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xm[(16 * tb + 4 * lg + r) * 36 + 16 * jb + lr] = xa[r];
+        }
+        __syncthreads();
+        {
+            const int tb = w >> 1, jb = w & 1;
+            float av[8], bv[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const int rr = 16 * tb + lr, xc = 8 * lg + x;  // T_B row rr, column xc (lower)
+                av[x] = (xc <= rr) ? Tm[(32 + rr) * AP + 32 + xc] : 0.f;
+                bv[x] = Xm[(8 * lg + x) * 36 + 16 * jb + lr];
+            }
+            bf8_t ah, al, bh, bl;
+            split8(av, ah, al);
+            split8(bv, bh, bl);
+            f4_t ta = f4_t{0.f, 0.f, 0.f, 0.f};
+            ta = mfma(ah, bh, ta);
+            ta = mfma(ah, bl, ta);
+            ta = mfma(al, bh, ta);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Tm[(32 + 16 * tb + 4 * lg + r) * AP + 16 * jb + lr] = -ta[r];
+        }
+        __syncthreads();
         // T' = T diag(b) (lower triangle; zeros above), and G
         float* To = wsT + ((size_t)c * HV + hv) * C * C;
-        for (int idx = tid; idx < C * C; idx += 256) {
-            const int t = idx >> 6, s = idx & 63;
-            To[idx] = (s <= t) ? Tm[t][s] * Bs[s] : 0.f;
+        for (int idx = tid; idx < C * C / 4; idx += 256) {
+            const int t = idx >> 4, s4 = 4 * (idx & 15);
+            float4 out;
+            out.x = (s4 + 0 <= t) ? Tm[t * AP + s4 + 0] * Bs[s4 + 0] : 0.f;
+            out.y = (s4 + 1 <= t) ? Tm[t * AP + s4 + 1] * Bs[s4 + 1] : 0.f;
+            out.z = (s4 + 2 <= t) ? Tm[t * AP + s4 + 2] * Bs[s4 + 2] : 0.f;
+            out.w = (s4 + 3 <= t) ? Tm[t * AP + s4 + 3] * Bs[s4 + 3] : 0.f;
+            *reinterpret_cast<float4*>(To + t * C + s4) = out;
         }
         if (tid < C) wsG[((size_t)c * HV + hv) * C + tid] = Gs[tid];
         __syncthreads();
@@ -209,8 +279,15 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
 // ---------------------------------------------------------------------------
 // scan: sequential over chunks, state tile in MFMA accumulators
 // ---------------------------------------------------------------------------
+// 8 wavefronts.  Wave w owns output tile (tb = w / 2, ib = w % 2): rows
+// 16 tb .. 16 tb + 15 of the chunk (tokens) and columns 16 ib .. 16 ib + 15
+// of the state tile's 32 rows (value dims) in K S^T, Q S^T, X, U and O, and
+// state tiles S^T[16 jb .. +15][16 ibS .. +15] for (jb, ibS) in its share.
+// Products whose accumulators are written to LDS are taken in the
+// orientation that gives each lane 4 consecutive elements of the stored
+// layout (P^T = K Q^T, S'^T = K^T U'), so every LDS store is 8 bytes.
 template <int DK, typename Tout>
-__global__ __launch_bounds__(256) void scan_mfma_kernel(
+__global__ __launch_bounds__(512) void scan_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int N, int T, int H,
     int HV, int dv, int max_chunks, const float* __restrict__ wsT, const float* __restrict__ wsG,
@@ -218,9 +295,9 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(
     constexpr int C = kChunk;
     constexpr int BV = 32;
     constexpr int KP = DK + 8;   // padded row of K, Q, S (bf16)
-    constexpr int TP = C + 8;    // padded row of transposed [*, C] tiles (bf16)
-    constexpr int NJB = DK / 16 / 4;  // 16-column blocks of S per wave
-    constexpr int KQ_LOADS = C * DK / 8 / 256;  // uint4 per thread for K (and for Q)
+    constexpr int TP = C + 8;    // padded row of the [*, C] tiles (bf16)
+    constexpr int KQ_LOADS = DK / 64;   // uint4 per lane for K (and for Q)
+    constexpr int NST = DK / 64;        // state tiles per wave
 
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
     __shared__ __attribute__((aligned(16))) __bf16 Qs[C * KP];
@@ -239,6 +316,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int tb = w >> 1, ib = w & 1;
     const int tiles = dv / BV;
     // XCD-aware mapping: workgroup b runs on XCD b % 8; all tiles of a chain
     // get the same b % 8 and neighbouring dispatch slots
@@ -251,31 +329,30 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(
     const int hk = h / (HV / H);
     const size_t sbase = ((size_t)chain * dv + (size_t)tile * BV) * DK;
 
-    // state tiles owned by this wave: rows 16 ib + 4 lg + r, columns 16 (NJB w + jj) + lr
-    f4_t sacc[2][NJB];
+    // state: sacc[x][r] = S[i = 16 ibS + lr][j = 16 jb + 4 lg + r], tile index w + 8 x
+    f4_t sacc[NST];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int jj = 0; jj < NJB; ++jj) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ib + 4 * lg + r, j = 16 * (NJB * w + jj) + lr;
-                sacc[ib][jj][r] = s0 ? s0[sbase + (size_t)i * DK + j] : 0.f;
-            }
+    for (int x = 0; x < NST; ++x) {
+        const int ti = w + 8 * x, jb = ti >> 1, ibS = ti & 1;
+        const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * jb + 4 * lg;
+        if (s0) {
+            const float4 v4 = *reinterpret_cast<const float4*>(s0 + off);
+            sacc[x] = f4_t{v4.x, v4.y, v4.z, v4.w};
+        } else {
+            sacc[x] = f4_t{0.f, 0.f, 0.f, 0.f};
         }
+    }
     auto store_state_lds = [&]() {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+        for (int x = 0; x < NST; ++x) {
+            const int ti = w + 8 * x, jb = ti >> 1, ibS = ti & 1;
+            const int off = (16 * ibS + lr) * KP + 16 * jb + 4 * lg;
+            __bf16 hi[4], lo[4];
 #pragma unroll
-            for (int jj = 0; jj < NJB; ++jj)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * ib + 4 * lg + r, j = 16 * (NJB * w + jj) + lr;
-                    __bf16 hi, lo;
-                    split1(sacc[ib][jj][r], hi, lo);
-                    Sh[i * KP + j] = hi;
-                    Sl[i * KP + j] = lo;
-                }
+            for (int r = 0; r < 4; ++r) split1(sacc[x][r], hi[r], lo[r]);
+            *reinterpret_cast<uint2*>(&Sh[off]) = *reinterpret_cast<const uint2*>(hi);
+            *reinterpret_cast<uint2*>(&Sl[off]) = *reinterpret_cast<const uint2*>(lo);
+        }
     };
     store_state_lds();
 
@@ -285,29 +362,24 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(
     int nch = chunk_off[n + 1] - c_first;
     if (c_first + nch > max_chunks) nch = max(0, max_chunks - c_first);
 
-    // ---- prefetch registers ----
+    // ---- prefetch registers (branch-free: rows past the end are clamped on
+    //      load and zeroed on use, so no load waits for another) ----
     uint4 pk[KQ_LOADS], pq[KQ_LOADS];
-    float pT[2][8];     // T' row 16 w + lr, columns 32 kk + 8 lg .. +7
-    float pV[2][4];     // V[t = 16 w + 4 lg + r][i = 16 ib + lr]
-    float pG = 0.f;
+    float pT[2][8];     // T' row 16 tb + lr, columns 32 kk + 8 lg .. +7
+    uint16_t pV[4];     // V[t = 16 tb + 4 lg + r][i = 16 ib + lr], raw bf16
+    float pG = 0.f;     // G[l]
     auto prefetch = [&](int jc) {
         const int c = c_first + jc;
         const int t0 = sq + jc * C;
         const int L = min(C, eq - t0);
+        const size_t row = (size_t)(t0 + min(l, L - 1)) * H + hk;
 #pragma unroll
         for (int m = 0; m < KQ_LOADS; ++m) {
-            const int idx = tid + 256 * m;
-            const int t = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-            if (t < L) {
-                const size_t off = ((size_t)(t0 + t) * H + hk) * DK + c8;
-                pk[m] = *reinterpret_cast<const uint4*>(k + off);
-                pq[m] = *reinterpret_cast<const uint4*>(q + off);
-            } else {
-                pk[m] = make_uint4(0, 0, 0, 0);
-                pq[m] = make_uint4(0, 0, 0, 0);
-            }
+            const size_t off = row * DK + 8 * (w + 8 * m);
+            pk[m] = *reinterpret_cast<const uint4*>(k + off);
+            pq[m] = *reinterpret_cast<const uint4*>(q + off);
         }
-        const float* Tp = wsT + (((size_t)c * HV + h) * C + 16 * w + lr) * C + 8 * lg;
+        const float* Tp = wsT + (((size_t)c * HV + h) * C + 16 * tb + lr) * C + 8 * lg;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const float4 x0 = *reinterpret_cast<const float4*>(Tp + 32 * kk);
@@ -316,215 +388,194 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(
             pT[kk][4] = x1.x; pT[kk][5] = x1.y; pT[kk][6] = x1.z; pT[kk][7] = x1.w;
         }
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * lg + r;
-                pV[ib][r] = t < L ? bf16_to_f32(v[((size_t)(t0 + t) * HV + h) * dv + tile * BV +
-                                                  16 * ib + lr])
-                                  : 0.f;
-            }
-        if (tid < C) pG = wsG[((size_t)c * HV + h) * C + tid];
+        for (int r = 0; r < 4; ++r) {
+            const int t = min(16 * tb + 4 * lg + r, L - 1);
+            pV[r] = v[((size_t)(t0 + t) * HV + h) * dv + tile * BV + 16 * ib + lr];
+        }
+        pG = wsG[((size_t)c * HV + h) * C + l];
     };
     if (nch > 0) prefetch(0);
 
     for (int jc = 0; jc < nch; ++jc) {
         const int t0 = sq + jc * C;
         const int L = min(C, eq - t0);
-        // (1) chunk -> LDS: K, Q (row-major), K^T, G
+        // (1) chunk -> LDS: K, Q (row-major), K^T (token pairs packed per dword), G.
+        // Lane l holds token l; its partner l ^ 1 holds the neighbouring token.
+        const bool live = l < L;
 #pragma unroll
         for (int m = 0; m < KQ_LOADS; ++m) {
-            const int idx = tid + 256 * m;
-            const int t = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-            *reinterpret_cast<uint4*>(&Ks[t * KP + c8]) = pk[m];
-            *reinterpret_cast<uint4*>(&Qs[t * KP + c8]) = pq[m];
-            const uint32_t wds[4] = {pk[m].x, pk[m].y, pk[m].z, pk[m].w};
+            const int c8 = 8 * (w + 8 * m);
+            const uint4 kv = live ? pk[m] : make_uint4(0, 0, 0, 0);
+            const uint4 qv = live ? pq[m] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(&Ks[l * KP + c8]) = kv;
+            *reinterpret_cast<uint4*>(&Qs[l * KP + c8]) = qv;
+            const uint32_t own[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const uint16_t bits = static_cast<uint16_t>(wds[x >> 1] >> (16 * (x & 1)));
-                Kt[(c8 + x) * TP + t] = __builtin_bit_cast(__bf16, bits);
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t par = (uint32_t)__builtin_amdgcn_update_dpp(
+                    0, (int)own[p], kDppQuadXor1, 0xF, 0xF, false);
+                const bool even = (l & 1) == 0;
+                const uint32_t word = even ? ((own[p] & 0xFFFFu) | (par << 16))
+                                           : ((par >> 16) | (own[p] & 0xFFFF0000u));
+                const int j = c8 + 2 * p + (even ? 0 : 1);
+                *reinterpret_cast<uint32_t*>(&Kt[j * TP + (l & ~1)]) = word;
             }
         }
         if (tid < C) Gs[tid] = pG;
-        float cT[2][8], cV[2][4];
+        float cT[2][8], cV[4];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int x = 0; x < 8; ++x) cT[kk][x] = pT[kk][x];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) cV[ib][r] = pV[ib][r];
+        for (int r = 0; r < 4; ++r) cV[r] = (16 * tb + 4 * lg + r < L) ? bf16_to_f32(pV[r]) : 0.f;
         __syncthreads();
         if (jc + 1 < nch) prefetch(jc + 1);
 
-        // (2) K S^T, Q S^T (row block w), Q K^T -> P, X = V - diag(gamma) K S^T
-        f4_t ksa[2], qsa[2], pa[4];
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            ksa[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-            qsa[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) pa[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+        // (2) K S^T and Q S^T for tile (tb, ib); P^T tiles; X = V - diag(gamma) K S^T
+        f4_t ksa = f4_t{0.f, 0.f, 0.f, 0.f}, qsa = f4_t{0.f, 0.f, 0.f, 0.f};
+        f4_t pa[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
+        // P^T tiles (sb, tb) handled here: sb = ib and sb = ib + 2, when sb <= tb
+        const bool p0 = ib <= tb, p1 = ib + 2 <= tb;
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
             const int col = 32 * kk + 8 * lg;
-            const bf8_t ak = lds8(&Ks[(16 * w + lr) * KP + col]);
-            const bf8_t aq = lds8(&Qs[(16 * w + lr) * KP + col]);
+            const bf8_t ak = lds8(&Ks[(16 * tb + lr) * KP + col]);
+            const bf8_t aq = lds8(&Qs[(16 * tb + lr) * KP + col]);
+            const bf8_t bh = lds8(&Sh[(16 * ib + lr) * KP + col]);
+            const bf8_t bl = lds8(&Sl[(16 * ib + lr) * KP + col]);
+            ksa = mfma(ak, bh, ksa);
+            ksa = mfma(ak, bl, ksa);
+            qsa = mfma(aq, bh, qsa);
+            qsa = mfma(aq, bl, qsa);
+            if (p0) pa[0] = mfma(lds8(&Ks[(16 * ib + lr) * KP + col]), aq, pa[0]);
+            if (p1) pa[1] = mfma(lds8(&Ks[(16 * (ib + 2) + lr) * KP + col]), aq, pa[1]);
+        }
+        // pa[x][r] = P^T[s = 16 sb + 4 lg + r][t = 16 tb + lr]
+        {
+            const int t = 16 * tb + lr;
+            const float Gt = Gs[t];
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const bf8_t bh = lds8(&Sh[(16 * ib + lr) * KP + col]);
-                const bf8_t bl = lds8(&Sl[(16 * ib + lr) * KP + col]);
-                ksa[ib] = mfma(ak, bh, ksa[ib]);
-                ksa[ib] = mfma(ak, bl, ksa[ib]);
-                qsa[ib] = mfma(aq, bh, qsa[ib]);
-                qsa[ib] = mfma(aq, bl, qsa[ib]);
-            }
+            for (int x = 0; x < 2; ++x) {
+                const int sb = ib + 2 * x;
+                // tiles inside the k-range that the O product reads must be stored (zeros
+                // above the diagonal); others are never read
+                if ((sb >> 1) <= (tb >> 1)) {
+                    const bool comp = sb <= tb;
+                    __bf16 hi[4], lo[4];
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                if (sb <= w) {
-                    const bf8_t bk = lds8(&Ks[(16 * sb + lr) * KP + col]);
-                    pa[sb] = mfma(aq, bk, pa[sb]);
+                    for (int r = 0; r < 4; ++r) {
+                        const int s = 16 * sb + 4 * lg + r;
+                        const float pv = (comp && s <= t) ? pa[x][r] * __expf(Gt - Gs[s]) : 0.f;
+                        split1(pv, hi[r], lo[r]);
+                    }
+                    const int off = t * TP + 16 * sb + 4 * lg;
+                    *reinterpret_cast<uint2*>(&Ph[off]) = *reinterpret_cast<const uint2*>(hi);
+                    *reinterpret_cast<uint2*>(&Pl[off]) = *reinterpret_cast<const uint2*>(lo);
                 }
             }
         }
-        float Gt[4], gam[4];
+        float Gt4[4], gam[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            Gt[r] = Gs[16 * w + 4 * lg + r];
-            gam[r] = __expf(Gt[r]);
+            Gt4[r] = Gs[16 * tb + 4 * lg + r];
+            gam[r] = __expf(Gt4[r]);
         }
+        {
+            __bf16 hi[4], lo[4];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            const float Gsb = Gs[16 * sb + lr];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * lg + r, s = 16 * sb + lr;
-                const float p = (sb <= w && s <= t) ? pa[sb][r] * __expf(Gt[r] - Gsb) : 0.f;
-                __bf16 hi, lo;
-                split1(p, hi, lo);
-                Ph[t * TP + s] = hi;
-                Pl[t * TP + s] = lo;
-            }
+            for (int r = 0; r < 4; ++r) split1(cV[r] - gam[r] * ksa[r], hi[r], lo[r]);
+            const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
+            *reinterpret_cast<uint2*>(&Xh[off]) = *reinterpret_cast<const uint2*>(hi);
+            *reinterpret_cast<uint2*>(&Xl[off]) = *reinterpret_cast<const uint2*>(lo);
         }
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * lg + r, i = 16 * ib + lr;
-                const float x = cV[ib][r] - gam[r] * ksa[ib][r];
-                __bf16 hi, lo;
-                split1(x, hi, lo);
-                Xh[i * TP + t] = hi;
-                Xl[i * TP + t] = lo;
-            }
         __syncthreads();
 
-        // (3) U = T' X for row block w (T' is lower triangular: k-steps up to w / 2)
-        f4_t ua[2];
-        ua[0] = f4_t{0.f, 0.f, 0.f, 0.f};
-        ua[1] = f4_t{0.f, 0.f, 0.f, 0.f};
+        // (3) U = T' X for tile (tb, ib) (T' lower triangular: k-steps up to tb / 2)
+        f4_t ua = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            if (kk <= (w >> 1)) {
+            if (kk <= (tb >> 1)) {
                 bf8_t ah, al;
                 split8(cT[kk], ah, al);
                 const int col = 32 * kk + 8 * lg;
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const bf8_t bh = lds8(&Xh[(16 * ib + lr) * TP + col]);
-                    const bf8_t bl = lds8(&Xl[(16 * ib + lr) * TP + col]);
-                    ua[ib] = mfma(ah, bh, ua[ib]);
-                    ua[ib] = mfma(ah, bl, ua[ib]);
-                    ua[ib] = mfma(al, bh, ua[ib]);
-                }
+                const bf8_t bh = lds8(&Xh[(16 * ib + lr) * TP + col]);
+                const bf8_t bl = lds8(&Xl[(16 * ib + lr) * TP + col]);
+                ua = mfma(ah, bh, ua);
+                ua = mfma(ah, bl, ua);
+                ua = mfma(al, bh, ua);
             }
         }
         const float Gn = Gs[L - 1];
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+        {
+            __bf16 hi[4], lo[4], whi[4], wlo[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * lg + r, i = 16 * ib + lr;
-                __bf16 hi, lo;
-                split1(ua[ib][r], hi, lo);
-                Uh[i * TP + t] = hi;
-                Ul[i * TP + t] = lo;
-                split1(ua[ib][r] * __expf(Gn - Gt[r]), hi, lo);
-                Wh[i * TP + t] = hi;
-                Wl[i * TP + t] = lo;
+                split1(ua[r], hi[r], lo[r]);
+                split1(ua[r] * __expf(Gn - Gt4[r]), whi[r], wlo[r]);
             }
+            const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
+            *reinterpret_cast<uint2*>(&Uh[off]) = *reinterpret_cast<const uint2*>(hi);
+            *reinterpret_cast<uint2*>(&Ul[off]) = *reinterpret_cast<const uint2*>(lo);
+            *reinterpret_cast<uint2*>(&Wh[off]) = *reinterpret_cast<const uint2*>(whi);
+            *reinterpret_cast<uint2*>(&Wl[off]) = *reinterpret_cast<const uint2*>(wlo);
+        }
         __syncthreads();
 
-        // (4a) O = scale (diag(gamma) Q S^T + P U) for row block w
+        // (4a) O = scale (diag(gamma) Q S^T + P U) for tile (tb, ib)
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) qsa[ib][r] *= gam[r];
+        for (int r = 0; r < 4; ++r) qsa[r] *= gam[r];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            if (kk <= (w >> 1)) {
+            if (kk <= (tb >> 1)) {
                 const int col = 32 * kk + 8 * lg;
-                const bf8_t ah = lds8(&Ph[(16 * w + lr) * TP + col]);
-                const bf8_t al = lds8(&Pl[(16 * w + lr) * TP + col]);
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const bf8_t bh = lds8(&Uh[(16 * ib + lr) * TP + col]);
-                    const bf8_t bl = lds8(&Ul[(16 * ib + lr) * TP + col]);
-                    qsa[ib] = mfma(ah, bh, qsa[ib]);
-                    qsa[ib] = mfma(ah, bl, qsa[ib]);
-                    qsa[ib] = mfma(al, bh, qsa[ib]);
-                }
+                const bf8_t ah = lds8(&Ph[(16 * tb + lr) * TP + col]);
+                const bf8_t al = lds8(&Pl[(16 * tb + lr) * TP + col]);
+                const bf8_t bh = lds8(&Uh[(16 * ib + lr) * TP + col]);
+                const bf8_t bl = lds8(&Ul[(16 * ib + lr) * TP + col]);
+                qsa = mfma(ah, bh, qsa);
+                qsa = mfma(ah, bl, qsa);
+                qsa = mfma(al, bh, qsa);
             }
         }
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * lg + r;
-                if (t < L)
-                    io<Tout>::st(o + ((size_t)(t0 + t) * HV + h) * dv + tile * BV + 16 * ib + lr,
-                                 scale * qsa[ib][r]);
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tb + 4 * lg + r;
+            if (t < L)
+                io<Tout>::st(o + ((size_t)(t0 + t) * HV + h) * dv + tile * BV + 16 * ib + lr,
+                             scale * qsa[r]);
+        }
 
-        // (4b) S' = gamma_n S + U'^T K for the wave's state tiles
+        // (4b) S'^T = gamma_n S^T + K^T U' for the wave's state tiles
         const float gn = __expf(Gn);
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+        for (int x = 0; x < NST; ++x) {
+            const int ti = w + 8 * x, jb = ti >> 1, ibS = ti & 1;
 #pragma unroll
-            for (int jj = 0; jj < NJB; ++jj)
+            for (int r = 0; r < 4; ++r) sacc[x][r] *= gn;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sacc[ib][jj][r] *= gn;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int col = 32 * kk + 8 * lg;
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const bf8_t ah = lds8(&Wh[(16 * ib + lr) * TP + col]);
-                const bf8_t al = lds8(&Wl[(16 * ib + lr) * TP + col]);
-#pragma unroll
-                for (int jj = 0; jj < NJB; ++jj) {
-                    const bf8_t bk = lds8(&Kt[(16 * (NJB * w + jj) + lr) * TP + col]);
-                    sacc[ib][jj] = mfma(ah, bk, sacc[ib][jj]);
-                    sacc[ib][jj] = mfma(al, bk, sacc[ib][jj]);
-                }
+            for (int kk = 0; kk < 2; ++kk) {
+                const int col = 32 * kk + 8 * lg;
+                const bf8_t ak = lds8(&Kt[(16 * jb + lr) * TP + col]);
+                const bf8_t bh = lds8(&Wh[(16 * ibS + lr) * TP + col]);
+                const bf8_t bl = lds8(&Wl[(16 * ibS + lr) * TP + col]);
+                sacc[x] = mfma(ak, bh, sacc[x]);
+                sacc[x] = mfma(ak, bl, sacc[x]);
             }
         }
-        __syncthreads();
+        // Sh / Sl are read only in (2): each wave can refresh its part now
         store_state_lds();
+        __syncthreads();
     }
 
     if (sfin) {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int jj = 0; jj < NJB; ++jj)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * ib + 4 * lg + r, j = 16 * (NJB * w + jj) + lr;
-                    sfin[sbase + (size_t)i * DK + j] = sacc[ib][jj][r];
-                }
+        for (int x = 0; x < NST; ++x) {
+            const int ti = w + 8 * x, jb = ti >> 1, ibS = ti & 1;
+            const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * jb + 4 * lg;
+            *reinterpret_cast<float4*>(sfin + off) =
+                make_float4(sacc[x][0], sacc[x][1], sacc[x][2], sacc[x][3]);
+        }
     }
 }
 
@@ -538,7 +589,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& A) {
     const int tiles = A.dv / 32;
     const int chains = A.N * A.HV;
     const size_t blocks = (size_t)((chains + 7) / 8) * 8 * tiles;
-    hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(512), 0,
                        A.stream, static_cast<const bf16_t*>(A.q), static_cast<const bf16_t*>(A.k),
                        static_cast<const bf16_t*>(A.v), A.cu_seqlens, A.chunk_off, A.N, A.T, A.H,
                        A.HV, A.dv, A.max_chunks, A.ws_T, A.ws_G, A.s0, A.s_final,
