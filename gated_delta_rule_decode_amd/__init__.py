@@ -6,6 +6,7 @@ memory and the current stream only.  If libgdn.so is missing, every call
 raises (there is no fallback path).
 
     decode_step(q, k, v, g, beta, state, ...)          -> o
+    decode_step_norm(q, k, v, g, beta, state, z, w)    -> y (and o on request)
     prefill_chunked(q, k, v, g, beta, cu_seqlens, ...) -> (o, final_state)
     rmsnorm_gated(x, z, w, ...)                        -> y
     prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk=64)
@@ -29,9 +30,10 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_version", "gdn_status_string", "gdn_last_hip_error", "gdn_decode_step",
-           "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_rmsnorm_gated")
+           "gdn_decode_step_norm", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
+           "gdn_rmsnorm_gated")
 
-__all__ = ["decode_step", "prefill_chunked", "rmsnorm_gated", "prefill_workspace_bytes",
+__all__ = ["decode_step", "decode_step_norm", "prefill_chunked", "rmsnorm_gated", "prefill_workspace_bytes",
            "GDNError", "lib", "LIBRARY", "EXPORTS", "version"]
 
 
@@ -68,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_step.restype = _i
         L.gdn_decode_step.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                       _i, _f, _vp]
+        L.gdn_decode_step_norm.restype = _i
+        L.gdn_decode_step_norm.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _i,
+                                           _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _vp]
         L.gdn_prefill_workspace_bytes.restype = _sz
         L.gdn_prefill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
         L.gdn_prefill_chunked.restype = _i
@@ -157,6 +162,42 @@ def decode_step(q, k, v, g, beta, state, *, o=None, scale: float = 1.0, out_dtyp
                                float(scale), _stream(q.device))
     _check("gdn_decode_step", st)
     return o
+
+
+def decode_step_norm(q, k, v, g, beta, state, z, w, *, y=None, o=None, scale: float = 1.0,
+                     eps: float = 1e-6, out_dtype=None, return_o: bool = False):
+    """decode_step followed by RMSNormGated of each head in one kernel.
+
+    z [N, HV, dv] (fp32 or bf16), w [dv].  Returns y, or (y, o) with
+    ``return_o`` (o is then written as well)."""
+    torch = _torch()
+    f32 = torch.float32
+    N, H, dk = q.shape
+    HV, dv = v.shape[1], v.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(g, "g", f32)
+    _dev(beta, "beta", f32)
+    _dev(state, "state", f32)
+    _dev(z, "z")
+    _dev(w, "w")
+    if k.shape != q.shape or v.shape[0] != N or g.shape != (N, HV) or beta.shape != (N, HV) \
+            or state.shape != (N, HV, dv, dk) or z.shape != (N, HV, dv) or w.shape != (dv,):
+        raise ValueError("inconsistent decode shapes")
+    if y is None:
+        y = torch.empty((N, HV, dv), dtype=out_dtype or f32, device=q.device)
+    _dev(y, "y")
+    if return_o and o is None:
+        o = torch.empty((N, HV, dv), dtype=f32, device=q.device)
+    if o is not None:
+        _dev(o, "o")
+    st = lib().gdn_decode_step_norm(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(state), _ptr(z),
+        _dtype_code(z), _ptr(w), _dtype_code(w), _ptr(y), _dtype_code(y), _ptr(o),
+        _dtype_code(o) if o is not None else GDN_F32, N, H, HV, dk, dv, float(scale),
+        float(eps), _stream(q.device))
+    _check("gdn_decode_step_norm", st)
+    return (y, o) if (return_o or o is not None) else y
 
 
 def prefill_workspace_bytes(N: int, T_total: int, H: int, HV: int, dk: int, dv: int,

@@ -77,22 +77,72 @@ const char* gdn_status_string(int status) {
     }
 }
 
+}  // extern "C"
+
+namespace {
+
+gdn_status decode_common(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                         const float* g, const float* beta, float* state, int N, int H, int HV,
+                         int dk, int dv) {
+    if (N < 0) return GDN_ERROR_INVALID_VALUE;
+    gdn_status st = heads_status(H, HV, dk, dv);
+    if (st != GDN_SUCCESS) return st;
+    if (!valid_dtype(in_dtype)) return GDN_ERROR_NOT_SUPPORTED;
+    if (N == 0) return GDN_SUCCESS;
+    if (!q || !k || !v || !g || !beta || !state) return GDN_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state))
+        return GDN_ERROR_INVALID_VALUE;
+    if ((size_t)N * HV > (size_t)(1u << 31) / (size_t)dv) return GDN_ERROR_NOT_SUPPORTED;
+    return GDN_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
 gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
                            const float* g, const float* beta, float* state, void* o,
                            gdn_dtype o_dtype, int N, int H, int HV, int dk, int dv, float scale,
                            void* stream) {
-    if (N < 0) return GDN_ERROR_INVALID_VALUE;
-    gdn_status st = heads_status(H, HV, dk, dv);
-    if (st != GDN_SUCCESS) return st;
-    if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return GDN_ERROR_NOT_SUPPORTED;
-    if (N == 0) return GDN_SUCCESS;
-    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERROR_INVALID_VALUE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
-        return GDN_ERROR_INVALID_VALUE;
-    if ((size_t)N * HV > (size_t)(1u << 31) / (size_t)dv) return GDN_ERROR_NOT_SUPPORTED;
+    gdn_status st = decode_common(q, k, v, in_dtype, g, beta, state, N, H, HV, dk, dv);
+    if (st != GDN_SUCCESS || N == 0) return st;
+    if (!valid_dtype(o_dtype)) return GDN_ERROR_NOT_SUPPORTED;
+    if (!o || !aligned16(o)) return GDN_ERROR_INVALID_VALUE;
     clear_pending();
-    gdn::DecodeArgs a{q, k, v, g, beta, state, o, in_dtype == GDN_BF16, o_dtype == GDN_BF16,
-                      N, H, HV, dk, dv, scale, static_cast<hipStream_t>(stream)};
+    gdn::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+    a.in_bf16 = in_dtype == GDN_BF16; a.o_bf16 = o_dtype == GDN_BF16;
+    a.N = N; a.H = H; a.HV = HV; a.dk = dk; a.dv = dv; a.scale = scale;
+    a.fuse_norm = false;
+    a.stream = static_cast<hipStream_t>(stream);
+    return from_hip(gdn::launch_decode(a));
+}
+
+gdn_status gdn_decode_step_norm(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                                const float* g, const float* beta, float* state, const void* z,
+                                gdn_dtype z_dtype, const void* w, gdn_dtype w_dtype, void* y,
+                                gdn_dtype y_dtype, void* o, gdn_dtype o_dtype, int N, int H,
+                                int HV, int dk, int dv, float scale, float eps, void* stream) {
+    gdn_status st = decode_common(q, k, v, in_dtype, g, beta, state, N, H, HV, dk, dv);
+    if (st != GDN_SUCCESS) return st;
+    if (!(eps >= 0.f)) return GDN_ERROR_INVALID_VALUE;
+    if (!valid_dtype(z_dtype) || !valid_dtype(w_dtype) || !valid_dtype(y_dtype) ||
+        !valid_dtype(o_dtype))
+        return GDN_ERROR_NOT_SUPPORTED;
+    if (N == 0) return GDN_SUCCESS;
+    if (!z || !w || !y || !aligned16(z) || !aligned16(w) || !aligned16(y))
+        return GDN_ERROR_INVALID_VALUE;
+    if (o && !aligned16(o)) return GDN_ERROR_INVALID_VALUE;
+    clear_pending();
+    gdn::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+    a.in_bf16 = in_dtype == GDN_BF16; a.o_bf16 = o_dtype == GDN_BF16;
+    a.N = N; a.H = H; a.HV = HV; a.dk = dk; a.dv = dv; a.scale = scale;
+    a.fuse_norm = true;
+    a.z = z; a.w = w; a.y = y;
+    a.z_bf16 = z_dtype == GDN_BF16; a.w_bf16 = w_dtype == GDN_BF16; a.y_bf16 = y_dtype == GDN_BF16;
+    a.eps = eps;
+    a.stream = static_cast<hipStream_t>(stream);
     return from_hip(gdn::launch_decode(a));
 }
 

@@ -18,11 +18,18 @@ struct DecodeArgs {
     const float* g;
     const float* beta;
     float* state;
-    void* o;
+    void* o;          // may be null when fuse_norm
     bool in_bf16;
     bool o_bf16;
     int N, H, HV, dk, dv;
     float scale;
+    // RMSNormGated fused after the update (gdn_decode_step_norm)
+    bool fuse_norm;
+    const void* z;
+    const void* w;
+    void* y;
+    bool z_bf16, w_bf16, y_bf16;
+    float eps;
     hipStream_t stream;
 };
 

@@ -95,6 +95,25 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtyp
                            float scale, void* stream);
 
 /*
+ * gdn_decode_step_norm -- gdn_decode_step followed by RMSNormGated of each
+ * head's outputs in the same kernel: the decode step and the norm that closes
+ * the DeltaNet layer (Qwen3.5-0.8B chat guide, section "Architektur"), without
+ * the round trip of o through memory and without a second launch.
+ *
+ *   q, k, v, g, beta, state   as gdn_decode_step
+ *   z        [N, HV, dv]     z_dtype    gate input of the norm
+ *   w        [dv]            w_dtype    norm weight shared by heads
+ *   y        [N, HV, dv]     y_dtype    y = o / sqrt(mean_dv(o^2) + eps) * w * silu(z)
+ *   o        [N, HV, dv]     o_dtype    the raw outputs too, or NULL to skip them
+ *   eps >= 0.
+ */
+gdn_status gdn_decode_step_norm(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                                const float* g, const float* beta, float* state, const void* z,
+                                gdn_dtype z_dtype, const void* w, gdn_dtype w_dtype, void* y,
+                                gdn_dtype y_dtype, void* o, gdn_dtype o_dtype, int N, int H,
+                                int HV, int dk, int dv, float scale, float eps, void* stream);
+
+/*
  * gdn_prefill_workspace_bytes -- device workspace that gdn_prefill_chunked
  * needs for this problem (a multiple of 256 bytes; 0 when T_total == 0).
  * Returns 0 for sizes that gdn_prefill_chunked would reject.

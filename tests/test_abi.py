@@ -152,3 +152,28 @@ def test_library_binds_to_torch_hip_runtime():
     maps = open("/proc/self/maps").read()
     runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(runtimes) == 1, runtimes
+
+
+def _decode_norm(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=1, g=FAKE, beta=FAKE, state=FAKE, z=FAKE, z_dt=1,
+             w=FAKE, w_dt=0, y=FAKE, y_dt=0, o=None, o_dt=0, N=2, H=2, HV=4, dk=128, dv=128,
+             scale=1.0, eps=1e-6)
+    a.update(kw)
+    return L.gdn_decode_step_norm(a["q"], a["k"], a["v"], a["in_dt"], a["g"], a["beta"],
+                                  a["state"], a["z"], a["z_dt"], a["w"], a["w_dt"], a["y"],
+                                  a["y_dt"], a["o"], a["o_dt"], a["N"], a["H"], a["HV"],
+                                  a["dk"], a["dv"], a["scale"], a["eps"], None)
+
+
+def test_decode_norm_validation(L):
+    assert _decode_norm(L, N=0) == 0
+    assert _decode_norm(L, N=-1) == 1
+    assert _decode_norm(L, z=None) == 1
+    assert _decode_norm(L, y=None) == 1
+    assert _decode_norm(L, w=MISALIGNED) == 1
+    assert _decode_norm(L, o=MISALIGNED) == 1
+    assert _decode_norm(L, eps=-1.0) == 1
+    assert _decode_norm(L, state=None) == 1
+    assert _decode_norm(L, dv=48) == 2
+    assert _decode_norm(L, z_dt=9) == 2
+    assert _decode_norm(L, HV=6, H=4) == 1

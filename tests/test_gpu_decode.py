@@ -203,3 +203,59 @@ def test_graph_replay_matches_eager():
         assert torch.equal(y, y_eager), f"replay {rep}: outputs differ"
         assert torch.equal(state, s_eager), f"replay {rep}: state differs"
         _ = (y * 2).sum().item()  # eager work between replays
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 16), (128, 128)])
+@pytest.mark.parametrize("dtype,zdt,ydt", [("bf16", "bf16", "f32"), ("f32", "f32", "f32"),
+                                           ("bf16", "bf16", "bf16")])
+def test_decode_step_norm_parity(orc, dk, dv, dtype, zdt, ydt):
+    """Fused decode + RMSNormGated against the oracle's decode then norm."""
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    T = {"f32": torch.float32, "bf16": torch.bfloat16}
+    d = gi.make_decode(5, 6, 2, 4, dk, dv, dtype=dtype, seed=50 + dk + dv)
+    r = np.random.default_rng(dk * dv)
+    S0 = (r.standard_normal((6, 4, dv, dk)) * 0.05).astype(np.float32)
+    w = r.standard_normal(dv).astype(np.float32)
+    z = d.z if zdt == "bf16" or dtype == "f32" else gi.round_bf16(d.z)
+    say(f"decode+norm dk={dk} dv={dv} {dtype} z={zdt} y={ydt}")
+    dt = torch_dtype(dtype)
+    q, k, v = dev(d.q, dt), dev(d.k, dt), dev(d.v, dt)
+    g, b = dev(d.g), dev(d.beta)
+    state = dev(S0)
+    wt = dev(w)
+    ys, os_ = [], []
+    for t in range(d.steps):
+        y, o = gdn.decode_step_norm(q[t], k[t], v[t], g[t], b[t], state, dev(z[t], T[zdt]), wt,
+                                    scale=dk ** -0.5, out_dtype=T[ydt], return_o=True)
+        ys.append(y)
+        os_.append(o)
+    o_ref, S_ref = _oracle_decode_chain(orc, d, S0, scale=dk ** -0.5)
+    y_ref = orc.rmsnorm_gated(o_ref, z, w)
+    f32 = dtype == "f32" and ydt == "f32"
+    assert_parity(host(torch.stack(os_)), host(state), o_ref, S_ref, f32=(dtype == "f32"),
+                  what=f"decode+norm o dk={dk} dv={dv}")
+    err = rel_l2(host(torch.stack(ys)), y_ref)
+    print(f"[parity] decode+norm y dk={dk} dv={dv} {dtype}/{zdt}/{ydt}: rel-L2 {err:.3e}")
+    assert err <= (2e-5 if f32 else (4e-3 if ydt == "bf16" else 2e-3)), err
+
+
+def test_decode_step_norm_without_o_matches_two_calls():
+    """o = NULL skips the raw outputs; y and the state equal decode_step then
+    rmsnorm_gated up to rounding of the norm's sum order."""
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    d = gi.make_decode(2, 8, 4, 8, 128, 128, seed=60)
+    S0 = (np.random.default_rng(6).standard_normal((8, 8, 128, 128)) * 0.02).astype(np.float32)
+    bf = torch.bfloat16
+    q, k, v, g, b, z = (dev(d.q, bf), dev(d.k, bf), dev(d.v, bf), dev(d.g), dev(d.beta),
+                        dev(d.z, bf))
+    w = torch.ones(128, device="cuda")
+    s1, s2 = dev(S0), dev(S0)
+    say("decode+norm without o vs two calls")
+    for t in range(d.steps):
+        y1 = gdn.decode_step_norm(q[t], k[t], v[t], g[t], b[t], s1, z[t], w)
+        o2 = gdn.decode_step(q[t], k[t], v[t], g[t], b[t], s2)
+        y2 = gdn.rmsnorm_gated(o2, z[t], w)
+        assert torch.equal(s1, s2)
+        assert rel_l2(host(y1), host(y2)) < 1e-6
