@@ -42,19 +42,29 @@ void clear_pending() { (void)hipGetLastError(); }
 
 namespace gdn {
 
-PrefillLayout prefill_layout(int N, int T, int HV) {
+PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk) {
     PrefillLayout L{};
     // upper bound on sum_n ceil(len_n / 64) given sum_n len_n = T
     const size_t maxc = ((size_t)T + (size_t)N * (kChunk - 1)) / kChunk;
     L.max_chunks = (int)maxc;
+    const size_t tile = (size_t)kChunk * kChunk;  // elements of a 64 x 64 tile
     size_t off = 0;
     L.chunk_off = off;
     off = align256(off + ((size_t)N + 1) * sizeof(int32_t));
-    L.ws_T = off;
-    off = align256(off + maxc * HV * kChunk * kChunk * sizeof(float));
     L.ws_G = off;
     off = align256(off + maxc * HV * kChunk * sizeof(float));
-    L.total = off;
+    // one region, used by either path
+    const size_t region = off;
+    L.ws_T = region;
+    const size_t valu_end = align256(region + maxc * HV * tile * sizeof(float));
+    const size_t plane = align256(maxc * HV * tile * sizeof(uint16_t));
+    L.ws_Th = region;
+    L.ws_Tl = region + plane;
+    L.ws_Ph = region + 2 * plane;
+    L.ws_Pl = region + 3 * plane;
+    L.ws_Kt = region + 4 * plane;
+    const size_t mfma_end = align256(L.ws_Kt + maxc * H * (size_t)dk * kChunk * sizeof(uint16_t));
+    L.total = valu_end > mfma_end ? valu_end : mfma_end;
     return L;
 }
 
@@ -150,7 +160,7 @@ size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, in
     if (N < 0 || T_total < 0) return 0;
     if (heads_status(H, HV, dk, dv) != GDN_SUCCESS || chunk != gdn::kChunk) return 0;
     if (N == 0 || T_total == 0) return 0;
-    return gdn::prefill_layout(N, T_total, HV).total;
+    return gdn::prefill_layout(N, T_total, H, HV, dk).total;
 }
 
 gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
@@ -177,7 +187,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return GDN_ERROR_INVALID_VALUE;
-    const gdn::PrefillLayout L = gdn::prefill_layout(N, T_total, HV);
+    const gdn::PrefillLayout L = gdn::prefill_layout(N, T_total, H, HV, dk);
     if ((size_t)L.max_chunks * HV > (size_t)(1u << 31) / (gdn::kChunk * gdn::kChunk))
         return GDN_ERROR_NOT_SUPPORTED;
     if (!workspace || workspace_bytes < L.total) return GDN_ERROR_WORKSPACE;
@@ -189,8 +199,13 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     a.in_bf16 = in_dtype == GDN_BF16; a.o_bf16 = o_dtype == GDN_BF16;
     a.N = N; a.T = T_total; a.H = H; a.HV = HV; a.dk = dk; a.dv = dv; a.scale = scale;
     a.chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
-    a.ws_T = reinterpret_cast<float*>(ws + L.ws_T);
     a.ws_G = reinterpret_cast<float*>(ws + L.ws_G);
+    a.ws_T = reinterpret_cast<float*>(ws + L.ws_T);
+    a.ws_Th = reinterpret_cast<uint16_t*>(ws + L.ws_Th);
+    a.ws_Tl = reinterpret_cast<uint16_t*>(ws + L.ws_Tl);
+    a.ws_Ph = reinterpret_cast<uint16_t*>(ws + L.ws_Ph);
+    a.ws_Pl = reinterpret_cast<uint16_t*>(ws + L.ws_Pl);
+    a.ws_Kt = reinterpret_cast<uint16_t*>(ws + L.ws_Kt);
     a.max_chunks = L.max_chunks;
     a.stream = s;
     clear_pending();

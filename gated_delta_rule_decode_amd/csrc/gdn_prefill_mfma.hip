@@ -4,8 +4,9 @@
 // 2025): per chunk of C = 64 tokens with cumulative log-decays G,
 //
 //     A_ts = b_t e^{G_t - G_s} k_t.k_s (s < t),   T' = (I + A)^-1 diag(b)
+//     P_ts = e^{G_t - G_s} q_t.k_s (s <= t)
 //     X    = V - diag(e^G) K S^T                  U  = T' X
-//     O    = scale (diag(e^G) Q S^T + P U),       P_ts = e^{G_t - G_s} q_t.k_s (s <= t)
+//     O    = scale (diag(e^G) Q S^T + P U)
 //     S'   = e^{G_n} S + U'^T K,                  U' = diag(e^{G_n - G}) U
 //
 // Every contraction runs on v_mfma_f32_16x16x32_bf16 (16 x 16 output tile,
@@ -20,17 +21,13 @@
 // Accumulation is fp32 and the state between chunks stays fp32 in the
 // accumulators of the update product.
 //
-// Kernels:
-//   prep_mfma  one workgroup per (chunk, key head): K K^T once on MFMA, then
-//              for each value head sharing that key head: G, A, the blocked
-//              triangular inverse (16 x 16 diagonal blocks by substitution,
-//              off-diagonal blocks by T_ij = -T_ii sum_k A_ik T_kj), and
-//              T' = T diag(b) to the workspace.
-//   scan_mfma  one workgroup per (sequence, value head, 32-row tile of S),
-//              sequential over the sequence's chunks, with the next chunk's
-//              K, Q, V, T', G prefetched into registers.  The tiles of one
-//              (sequence, head) run on one XCD so that their shared K, Q and
-//              T' reads hit the same L2.
+// Work split.  Everything that does not depend on the state runs
+// chunk-parallel in prep_mfma: per (chunk, key head) K K^T and Q K^T, and per
+// value head of that key head G, the triangular inverse, T' and P, stored
+// pre-split as hi/lo bf16 row-major tiles, plus K^T of the chunk.  The
+// sequential scan_mfma then only runs the state-dependent products, reading
+// its T', P, K, Q and K^T fragments straight from memory into registers one
+// chunk ahead; LDS holds just the state tile and the X, U, U' exchange tiles.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -47,6 +44,25 @@ __device__ __forceinline__ bf8_t lds8(const __bf16* p) {
     return *reinterpret_cast<const bf8_t*>(p);
 }
 
+__device__ __forceinline__ bf8_t gld8(const uint16_t* p) {
+    return __builtin_bit_cast(bf8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+// Raw buffer stores: an offset at or past num_records is dropped by the
+// hardware, which masks rows past a sequence's end without a branch (a branch
+// around a store would make the compiler wait for every outstanding load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v, float*) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)(off * 4), 0, 0);
+}
+__device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v, bf16_t*) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)(off * 2), 0, 0);
+}
+
+__device__ __forceinline__ bf8_t zero8() { return __builtin_bit_cast(bf8_t, make_uint4(0, 0, 0, 0)); }
+
 // fp32 x -> (hi, lo) with hi = bf16(x), lo = bf16(x - hi)
 __device__ __forceinline__ void split8(const float* x, bf8_t& hi, bf8_t& lo) {
 #pragma unroll
@@ -60,6 +76,15 @@ __device__ __forceinline__ void split8(const float* x, bf8_t& hi, bf8_t& lo) {
 __device__ __forceinline__ void split1(float x, __bf16& hi, __bf16& lo) {
     hi = static_cast<__bf16>(x);
     lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+// 4 consecutive floats -> 8-byte hi and lo words
+__device__ __forceinline__ void split4(const float* x, uint2& hi, uint2& lo) {
+    __bf16 h[4], o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) split1(x[r], h[r], o[r]);
+    hi = *reinterpret_cast<const uint2*>(h);
+    lo = *reinterpret_cast<const uint2*>(o);
 }
 
 __device__ __forceinline__ void seq_bounds_m(const int32_t* cu, int n, int T, int& s, int& e) {
@@ -81,64 +106,95 @@ __device__ __forceinline__ int find_seq_m(const int32_t* chunk_off, int N, int c
 }
 
 // ---------------------------------------------------------------------------
-// prep: K K^T, A, T' = (I + A)^-1 diag(b), G
+// prep: everything that does not depend on the state, chunk-parallel
 // ---------------------------------------------------------------------------
+// One workgroup (4 wavefronts) per (chunk, key head).  Wave w owns row block
+// w (tokens 16 w .. 16 w + 15) of K K^T and of P.  Outputs per value head:
+// T' and P as hi/lo bf16 row-major 64 x 64 tiles (zeros above the diagonal and
+// in rows / columns past the sequence end) and G; per key head: K^T (dk x 64).
 template <int DK>
-__global__ __launch_bounds__(256) void prep_mfma_kernel(
-    const bf16_t* __restrict__ k, const float* __restrict__ g, const float* __restrict__ beta,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int N, int T, int H,
-    int HV, int max_chunks, float* __restrict__ wsT, float* __restrict__ wsG) {
+__global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
     constexpr int KP = DK + 8;  // padded bf16 row
     constexpr int AP = C + 4;   // padded fp32 row (16-byte aligned rows)
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * KP];
     __shared__ __attribute__((aligned(16))) float Am[C * AP];
     __shared__ __attribute__((aligned(16))) float Tm[C * AP];
     __shared__ __attribute__((aligned(16))) float Xm[32 * 36];
     __shared__ float Gs[C], Bs[C];
 
+    const int H = A.H, HV = A.HV;
     const int c = blockIdx.x, hk = blockIdx.y, tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int total = min(chunk_off[N], max_chunks);
+    const int total = min(A.chunk_off[A.N], A.max_chunks);
     if (c >= total) return;
-    const int n = find_seq_m(chunk_off, N, c);
+    const int n = find_seq_m(A.chunk_off, A.N, c);
     int s0, e0;
-    seq_bounds_m(cu, n, T, s0, e0);
-    const int t0 = s0 + (c - chunk_off[n]) * C;
+    seq_bounds_m(A.cu_seqlens, n, A.T, s0, e0);
+    const int t0 = s0 + (c - A.chunk_off[n]) * C;
     const int L = min(C, e0 - t0);
     const int ratio = HV / H;
+    const bf16_t* k = static_cast<const bf16_t*>(A.k);
+    const bf16_t* q = static_cast<const bf16_t*>(A.q);
 
-    // K chunk -> LDS (rows past the sequence end are zero)
+    // K and Q chunk -> LDS (rows past the sequence end are zero)
     for (int idx = tid; idx < C * DK / 8; idx += 256) {
         const int t = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-        uint4 val = *reinterpret_cast<const uint4*>(
-            k + ((size_t)(t0 + min(t, L - 1)) * H + hk) * DK + c8);
-        if (t >= L) val = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&Ks[t * KP + c8]) = val;
+        const size_t off = ((size_t)(t0 + min(t, L - 1)) * H + hk) * DK + c8;
+        uint4 kv = *reinterpret_cast<const uint4*>(k + off);
+        uint4 qv = *reinterpret_cast<const uint4*>(q + off);
+        if (t >= L) kv = qv = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&Ks[t * KP + c8]) = kv;
+        *reinterpret_cast<uint4*>(&Qs[t * KP + c8]) = qv;
     }
     __syncthreads();
 
-    // K K^T for row block w and column blocks sb <= w
-    f4_t kk[4];
+    // K^T of the chunk -> workspace, [dk][64] bf16
+    {
+        uint16_t* Kt = A.ws_Kt + ((size_t)c * H + hk) * DK * C;
+        const uint16_t* Kr = reinterpret_cast<const uint16_t*>(Ks);
+        for (int idx = tid; idx < DK * C / 8; idx += 256) {
+            const int t8 = 8 * (idx % (C / 8)), j = idx / (C / 8);
+            uint32_t wd[4];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) kk[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-        const bf8_t a = lds8(&Ks[(16 * w + lr) * KP + 32 * ks + 8 * lg]);
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            if (sb <= w) {
-                const bf8_t b = lds8(&Ks[(16 * sb + lr) * KP + 32 * ks + 8 * lg]);
-                kk[sb] = mfma(a, b, kk[sb]);
-            }
+            for (int x = 0; x < 4; ++x)
+                wd[x] = (uint32_t)Kr[(t8 + 2 * x) * KP + j] |
+                        ((uint32_t)Kr[(t8 + 2 * x + 1) * KP + j] << 16);
+            *reinterpret_cast<uint4*>(Kt + (size_t)j * C + t8) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
         }
     }
 
+    // K K^T (row block w, column blocks sb <= w) and P^T = K Q^T (column block w)
+    f4_t kk[4], pq[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+        kk[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+        pq[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+        const int col = 32 * ks + 8 * lg;
+        const bf8_t ka = lds8(&Ks[(16 * w + lr) * KP + col]);
+        const bf8_t qa = lds8(&Qs[(16 * w + lr) * KP + col]);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            if (sb <= w) {
+                const bf8_t kb = lds8(&Ks[(16 * sb + lr) * KP + col]);
+                kk[sb] = mfma(ka, kb, kk[sb]);
+                pq[sb] = mfma(kb, qa, pq[sb]);
+            }
+        }
+    }
+    // kk[sb][r] = (K K^T)[t = 16 w + 4 lg + r][s = 16 sb + lr]
+    // pq[sb][r] = (Q K^T)[t = 16 w + lr][s = 16 sb + 4 lg + r]
+
     for (int hv = hk * ratio; hv < (hk + 1) * ratio; ++hv) {
+        const size_t tileoff = ((size_t)c * HV + hv) * C * C;
         // G = in-chunk inclusive cumsum of g (wave 0), beta
         if (w == 0) {
-            float gv = g[(size_t)(t0 + min(l, L - 1)) * HV + hv];
-            float bv = beta[(size_t)(t0 + min(l, L - 1)) * HV + hv];
+            float gv = A.g[(size_t)(t0 + min(l, L - 1)) * HV + hv];
+            float bv = A.beta[(size_t)(t0 + min(l, L - 1)) * HV + hv];
             if (l >= L) gv = 0.f, bv = 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -147,8 +203,28 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
             }
             Gs[l] = gv;
             Bs[l] = bv;
+            A.ws_G[((size_t)c * HV + hv) * C + l] = gv;
         }
         __syncthreads();
+        // P = tril(Q K^T) o e^{G_t - G_s}: row block w, all column blocks, hi / lo
+        {
+            const int t = 16 * w + lr;
+            const float Gt = Gs[t];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                float pv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * sb + 4 * lg + r;
+                    pv[r] = (sb <= w && s <= t) ? pq[sb][r] * __expf(Gt - Gs[s]) : 0.f;
+                }
+                uint2 hi, lo;
+                split4(pv, hi, lo);
+                const size_t off = tileoff + (size_t)t * C + 16 * sb + 4 * lg;
+                *reinterpret_cast<uint2*>(A.ws_Ph + off) = hi;
+                *reinterpret_cast<uint2*>(A.ws_Pl + off) = lo;
+            }
+        }
         // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s})
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
@@ -188,20 +264,18 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
         }
         __syncthreads();
         // 16-block merges: T_10 = -T_11 (A_10 T_00), T_32 = -T_33 (A_32 T_22)
-        {
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int e = tid + 256 * half;
-                const int j = (e >> 8) * 2, i = j + 1;  // (1,0) or (3,2)
-                const int rho = (e >> 4) & 15, kap = e & 15;
-                float acc = 0.f;
+        for (int half = 0; half < 2; ++half) {
+            const int e = tid + 256 * half;
+            const int j = (e >> 8) * 2, i = j + 1;  // (1,0) or (3,2)
+            const int rho = (e >> 4) & 15, kap = e & 15;
+            float acc = 0.f;
 #pragma unroll
-                for (int x = 0; x < 16; ++x)
-                    acc += (x >= kap) ? Am[(16 * i + rho) * AP + 16 * j + x] *
-                                            Tm[(16 * j + x) * AP + 16 * j + kap]
-                                      : 0.f;
-                Xm[(16 * (e >> 8) + rho) * 36 + kap] = acc;
-            }
+            for (int x = 0; x < 16; ++x)
+                acc += (x >= kap) ? Am[(16 * i + rho) * AP + 16 * j + x] *
+                                        Tm[(16 * j + x) * AP + 16 * j + kap]
+                                  : 0.f;
+            Xm[(16 * (e >> 8) + rho) * 36 + kap] = acc;
         }
         __syncthreads();
 #pragma unroll
@@ -226,7 +300,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
             for (int x = 0; x < 8; ++x) {
                 av[x] = Am[(32 + 16 * tb + lr) * AP + 8 * lg + x];
                 const int xr = 8 * lg + x, cc = 16 * jb + lr;
-                bv[x] = (xr >= cc || (xr >> 4) > (cc >> 4)) ? Tm[xr * AP + cc] : 0.f;
+                bv[x] = (xr >= cc) ? Tm[xr * AP + cc] : 0.f;
             }
             bf8_t ah, al, bh, bl;
             split8(av, ah, al);
@@ -260,18 +334,18 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
                 Tm[(32 + 16 * tb + 4 * lg + r) * AP + 16 * jb + lr] = -ta[r];
         }
         __syncthreads();
-        // T' = T diag(b) (lower triangle; zeros above), and G
-        float* To = wsT + ((size_t)c * HV + hv) * C * C;
+        // T' = T diag(b) (lower triangle; zeros above) as hi / lo
         for (int idx = tid; idx < C * C / 4; idx += 256) {
             const int t = idx >> 4, s4 = 4 * (idx & 15);
-            float4 out;
-            out.x = (s4 + 0 <= t) ? Tm[t * AP + s4 + 0] * Bs[s4 + 0] : 0.f;
-            out.y = (s4 + 1 <= t) ? Tm[t * AP + s4 + 1] * Bs[s4 + 1] : 0.f;
-            out.z = (s4 + 2 <= t) ? Tm[t * AP + s4 + 2] * Bs[s4 + 2] : 0.f;
-            out.w = (s4 + 3 <= t) ? Tm[t * AP + s4 + 3] * Bs[s4 + 3] : 0.f;
-            *reinterpret_cast<float4*>(To + t * C + s4) = out;
+            float tv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tv[r] = (s4 + r <= t) ? Tm[t * AP + s4 + r] * Bs[s4 + r] : 0.f;
+            uint2 hi, lo;
+            split4(tv, hi, lo);
+            *reinterpret_cast<uint2*>(A.ws_Th + tileoff + t * C + s4) = hi;
+            *reinterpret_cast<uint2*>(A.ws_Tl + tileoff + t * C + s4) = lo;
         }
-        if (tid < C) wsG[((size_t)c * HV + hv) * C + tid] = Gs[tid];
         __syncthreads();
     }
 }
@@ -279,29 +353,29 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(
 // ---------------------------------------------------------------------------
 // scan: sequential over chunks, state tile in MFMA accumulators
 // ---------------------------------------------------------------------------
-// 8 wavefronts.  Wave w owns output tile (tb = w / 2, ib = w % 2): rows
-// 16 tb .. 16 tb + 15 of the chunk (tokens) and columns 16 ib .. 16 ib + 15
-// of the state tile's 32 rows (value dims) in K S^T, Q S^T, X, U and O, and
-// state tiles S^T[16 jb .. +15][16 ibS .. +15] for (jb, ibS) in its share.
-// Products whose accumulators are written to LDS are taken in the
-// orientation that gives each lane 4 consecutive elements of the stored
-// layout (P^T = K Q^T, S'^T = K^T U'), so every LDS store is 8 bytes.
+// 4 wavefronts, one per SIMD.  Wave w owns the chunk's row block tb = w
+// (tokens 16 w .. 16 w + 15) in K S^T, Q S^T, X, U and O for both 16-column
+// halves ib = 0, 1 of the state tile's 32 rows, so its K, Q, T', P row
+// fragments are loaded once; and the state tiles S^T[16 jb .. +15][16 ibS ..]
+// for its DK/64 column blocks jb and both halves ibS.
+// Per chunk: (A) K S^T, Q S^T, X -> LDS; (B) U = T' X, U and U' -> LDS;
+// (C) O = gamma Q S^T + P U to memory and S' = gamma_n S + U'^T K -> LDS.
+// Operand fragments that come from memory are held in one register set: each
+// group is reloaded for the next chunk right after its last use in this one
+// (K, Q and G after (A), T' after (B), P after the output product, K^T after
+// the state update), so every load has a full chunk to arrive and the loads
+// are spread over the chunk instead of queueing at its start.  No branch
+// surrounds a load or store (masked rows use clamped loads and out-of-range
+// buffer stores), so the compiler waits for exactly the group it needs.
 template <int DK, typename Tout>
-__global__ __launch_bounds__(512) void scan_mfma_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int N, int T, int H,
-    int HV, int dv, int max_chunks, const float* __restrict__ wsT, const float* __restrict__ wsG,
-    const float* s0, float* sfin, Tout* __restrict__ o, float scale) {
+__global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
     constexpr int BV = 32;
-    constexpr int KP = DK + 8;   // padded row of K, Q, S (bf16)
+    constexpr int KP = DK + 8;   // padded row of S (bf16)
     constexpr int TP = C + 8;    // padded row of the [*, C] tiles (bf16)
-    constexpr int KQ_LOADS = DK / 64;   // uint4 per lane for K (and for Q)
-    constexpr int NST = DK / 64;        // state tiles per wave
+    constexpr int NKK = DK / 32;
+    constexpr int NJB = DK / 64;  // state column blocks per wave
 
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 Kt[DK * TP];
     __shared__ __attribute__((aligned(16))) __bf16 Sh[BV * KP];
     __shared__ __attribute__((aligned(16))) __bf16 Sl[BV * KP];
     __shared__ __attribute__((aligned(16))) __bf16 Xh[BV * TP];
@@ -310,13 +384,11 @@ __global__ __launch_bounds__(512) void scan_mfma_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 Ul[BV * TP];
     __shared__ __attribute__((aligned(16))) __bf16 Wh[BV * TP];
     __shared__ __attribute__((aligned(16))) __bf16 Wl[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Ph[C * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Pl[C * TP];
-    __shared__ float Gs[C];
 
+    const int H = A.H, HV = A.HV, dv = A.dv, N = A.N;
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int tb = w >> 1, ib = w & 1;
+    const int tb = w;
     const int tiles = dv / BV;
     // XCD-aware mapping: workgroup b runs on XCD b % 8; all tiles of a chain
     // get the same b % 8 and neighbouring dispatch slots
@@ -328,272 +400,298 @@ __global__ __launch_bounds__(512) void scan_mfma_kernel(
     const int n = chain / HV, h = chain - n * HV;
     const int hk = h / (HV / H);
     const size_t sbase = ((size_t)chain * dv + (size_t)tile * BV) * DK;
+    const bf16_t* kp = static_cast<const bf16_t*>(A.k);
+    const bf16_t* qp = static_cast<const bf16_t*>(A.q);
+    const bf16_t* vp = static_cast<const bf16_t*>(A.v);
+    Tout* op = static_cast<Tout*>(A.o);
 
-    // state: sacc[x][r] = S[i = 16 ibS + lr][j = 16 jb + 4 lg + r], tile index w + 8 x
-    f4_t sacc[NST];
+    // state: sacc[x][ibS][r] = S[i = 16 ibS + lr][j = 16 (NJB w + x) + 4 lg + r]
+    f4_t sacc[NJB][2];
 #pragma unroll
-    for (int x = 0; x < NST; ++x) {
-        const int ti = w + 8 * x, jb = ti >> 1, ibS = ti & 1;
-        const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * jb + 4 * lg;
-        if (s0) {
-            const float4 v4 = *reinterpret_cast<const float4*>(s0 + off);
-            sacc[x] = f4_t{v4.x, v4.y, v4.z, v4.w};
-        } else {
-            sacc[x] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < NJB; ++x)
+#pragma unroll
+        for (int ibS = 0; ibS < 2; ++ibS) {
+            const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * w + x) + 4 * lg;
+            if (A.s0) {
+                const float4 v4 = *reinterpret_cast<const float4*>(A.s0 + off);
+                sacc[x][ibS] = f4_t{v4.x, v4.y, v4.z, v4.w};
+            } else {
+                sacc[x][ibS] = f4_t{0.f, 0.f, 0.f, 0.f};
+            }
         }
-    }
     auto store_state_lds = [&]() {
 #pragma unroll
-        for (int x = 0; x < NST; ++x) {
-            const int ti = w + 8 * x, jb = ti >> 1, ibS = ti & 1;
-            const int off = (16 * ibS + lr) * KP + 16 * jb + 4 * lg;
-            __bf16 hi[4], lo[4];
+        for (int x = 0; x < NJB; ++x)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) split1(sacc[x][r], hi[r], lo[r]);
-            *reinterpret_cast<uint2*>(&Sh[off]) = *reinterpret_cast<const uint2*>(hi);
-            *reinterpret_cast<uint2*>(&Sl[off]) = *reinterpret_cast<const uint2*>(lo);
-        }
+            for (int ibS = 0; ibS < 2; ++ibS) {
+                const int off = (16 * ibS + lr) * KP + 16 * (NJB * w + x) + 4 * lg;
+                float sv[4] = {sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]};
+                uint2 hi, lo;
+                split4(sv, hi, lo);
+                *reinterpret_cast<uint2*>(&Sh[off]) = hi;
+                *reinterpret_cast<uint2*>(&Sl[off]) = lo;
+            }
     };
     store_state_lds();
 
     int sq, eq;
-    seq_bounds_m(cu, n, T, sq, eq);
-    const int c_first = chunk_off[n];
-    int nch = chunk_off[n + 1] - c_first;
-    if (c_first + nch > max_chunks) nch = max(0, max_chunks - c_first);
-
-    // ---- prefetch registers (branch-free: rows past the end are clamped on
-    //      load and zeroed on use, so no load waits for another) ----
-    uint4 pk[KQ_LOADS], pq[KQ_LOADS];
-    float pT[2][8];     // T' row 16 tb + lr, columns 32 kk + 8 lg .. +7
-    uint16_t pV[4];     // V[t = 16 tb + 4 lg + r][i = 16 ib + lr], raw bf16
-    float pG = 0.f;     // G[l]
-    auto prefetch = [&](int jc) {
-        const int c = c_first + jc;
-        const int t0 = sq + jc * C;
-        const int L = min(C, eq - t0);
-        const size_t row = (size_t)(t0 + min(l, L - 1)) * H + hk;
+    seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
+    const int c_first = A.chunk_off[n];
+    int nch = A.chunk_off[n + 1] - c_first;
+    if (c_first + nch > A.max_chunks) nch = max(0, A.max_chunks - c_first);
+    if (nch <= 0) {
+        if (A.s_final) {
 #pragma unroll
-        for (int m = 0; m < KQ_LOADS; ++m) {
-            const size_t off = row * DK + 8 * (w + 8 * m);
-            pk[m] = *reinterpret_cast<const uint4*>(k + off);
-            pq[m] = *reinterpret_cast<const uint4*>(q + off);
+            for (int x = 0; x < NJB; ++x)
+#pragma unroll
+                for (int ibS = 0; ibS < 2; ++ibS) {
+                    const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * w + x) + 4 * lg;
+                    *reinterpret_cast<float4*>(A.s_final + off) =
+                        make_float4(sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]);
+                }
         }
-        const float* Tp = wsT + (((size_t)c * HV + h) * C + 16 * tb + lr) * C + 8 * lg;
+        return;
+    }
+
+    // ---- operand fragments (one set; groups reloaded after their last use) ----
+    bf8_t kA[NKK], qA[NKK];      // K, Q row 16 tb + lr, k-step kk
+    bf8_t tH[2], tL[2];          // T' row 16 tb + lr, columns 32 kk + 8 lg ..
+    bf8_t pH[2], pL[2];          // P row 16 tb + lr
+    bf8_t ktA[NJB][2];           // K^T row 16 jb + lr, tokens 32 kk + 8 lg ..
+    uint32_t vr[2][4];           // V[t = 16 tb + 4 lg + r][i = 16 ib + lr], raw bf16 bits
+    float4 gR;                   // G[16 tb + 4 lg + r]
+    float gN;                    // G[L - 1]
+
+    auto chunk_t0 = [&](int jc) { return sq + jc * C; };
+    auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
+    auto load_kq_g = [&](int jc) {
+        const int t0 = chunk_t0(jc), L = chunk_L(jc);
+        const size_t krow = ((size_t)(t0 + min(16 * tb + lr, L - 1)) * H + hk) * DK + 8 * lg;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            kA[kk] = __builtin_bit_cast(bf8_t, *reinterpret_cast<const uint4*>(kp + krow + 32 * kk));
+            qA[kk] = __builtin_bit_cast(bf8_t, *reinterpret_cast<const uint4*>(qp + krow + 32 * kk));
+        }
+        const float* G = A.ws_G + ((size_t)(c_first + jc) * HV + h) * C;
+        gR = *reinterpret_cast<const float4*>(G + 16 * tb + 4 * lg);
+        gN = G[L - 1];
+    };
+    auto load_v = [&](int jc) {
+        const int t0 = chunk_t0(jc), L = chunk_L(jc);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = min(16 * tb + 4 * lg + r, L - 1);
+                vr[ib][r] = vp[((size_t)(t0 + t) * HV + h) * dv + tile * BV + 16 * ib + lr];
+            }
+    };
+    auto tile_off = [&](int jc) {
+        return (((size_t)(c_first + jc) * HV + h) * C + 16 * tb + lr) * C + 8 * lg;
+    };
+    auto load_t = [&](int jc) {
+        const size_t toff = tile_off(jc);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const float4 x0 = *reinterpret_cast<const float4*>(Tp + 32 * kk);
-            const float4 x1 = *reinterpret_cast<const float4*>(Tp + 32 * kk + 4);
-            pT[kk][0] = x0.x; pT[kk][1] = x0.y; pT[kk][2] = x0.z; pT[kk][3] = x0.w;
-            pT[kk][4] = x1.x; pT[kk][5] = x1.y; pT[kk][6] = x1.z; pT[kk][7] = x1.w;
+            tH[kk] = gld8(A.ws_Th + toff + 32 * kk);
+            tL[kk] = gld8(A.ws_Tl + toff + 32 * kk);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = min(16 * tb + 4 * lg + r, L - 1);
-            pV[r] = v[((size_t)(t0 + t) * HV + h) * dv + tile * BV + 16 * ib + lr];
-        }
-        pG = wsG[((size_t)c * HV + h) * C + l];
     };
-    if (nch > 0) prefetch(0);
+    auto load_p = [&](int jc) {
+        const size_t toff = tile_off(jc);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            pH[kk] = gld8(A.ws_Ph + toff + 32 * kk);
+            pL[kk] = gld8(A.ws_Pl + toff + 32 * kk);
+        }
+    };
+    auto load_kt = [&](int jc) {
+        const uint16_t* Kt = A.ws_Kt + ((size_t)(c_first + jc) * H + hk) * DK * C;
+#pragma unroll
+        for (int x = 0; x < NJB; ++x)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                ktA[x][kk] = gld8(Kt + (size_t)(16 * (NJB * w + x) + lr) * C + 32 * kk + 8 * lg);
+    };
+    load_kq_g(0);
+    load_v(0);
+    load_t(0);
+    load_p(0);
+    load_kt(0);
 
     for (int jc = 0; jc < nch; ++jc) {
-        const int t0 = sq + jc * C;
-        const int L = min(C, eq - t0);
-        // (1) chunk -> LDS: K, Q (row-major), K^T (token pairs packed per dword), G.
-        // Lane l holds token l; its partner l ^ 1 holds the neighbouring token.
-        const bool live = l < L;
+        const int nj = min(jc + 1, nch - 1);  // the last chunk re-reads itself
+        const int t0 = chunk_t0(jc);
+        const int L = chunk_L(jc);
+        const bool rowlive = 16 * tb + lr < L;  // K / Q row of this lane's A fragments
+        const float gr[4] = {gR.x, gR.y, gR.z, gR.w};
+        const float gNc = gN;
+        float gam[4];
 #pragma unroll
-        for (int m = 0; m < KQ_LOADS; ++m) {
-            const int c8 = 8 * (w + 8 * m);
-            const uint4 kv = live ? pk[m] : make_uint4(0, 0, 0, 0);
-            const uint4 qv = live ? pq[m] : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(&Ks[l * KP + c8]) = kv;
-            *reinterpret_cast<uint4*>(&Qs[l * KP + c8]) = qv;
-            const uint32_t own[4] = {kv.x, kv.y, kv.z, kv.w};
+        for (int r = 0; r < 4; ++r) gam[r] = __expf(gr[r]);
+
+        // (A) K S^T and Q S^T for row block tb, both column halves; X = V - diag(gamma) K S^T
+        f4_t ksa[2], qsa[2];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t par = (uint32_t)__builtin_amdgcn_update_dpp(
-                    0, (int)own[p], kDppQuadXor1, 0xF, 0xF, false);
-                const bool even = (l & 1) == 0;
-                const uint32_t word = even ? ((own[p] & 0xFFFFu) | (par << 16))
-                                           : ((par >> 16) | (own[p] & 0xFFFF0000u));
-                const int j = c8 + 2 * p + (even ? 0 : 1);
-                *reinterpret_cast<uint32_t*>(&Kt[j * TP + (l & ~1)]) = word;
+        for (int ib = 0; ib < 2; ++ib) {
+            ksa[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+            qsa[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int col = 32 * kk + 8 * lg;
+            const bf8_t ak = rowlive ? kA[kk] : zero8();
+            const bf8_t aq = rowlive ? qA[kk] : zero8();
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const bf8_t bh = lds8(&Sh[(16 * ib + lr) * KP + col]);
+                const bf8_t bl = lds8(&Sl[(16 * ib + lr) * KP + col]);
+                ksa[ib] = mfma(ak, bh, ksa[ib]);
+                qsa[ib] = mfma(aq, bh, qsa[ib]);
+                ksa[ib] = mfma(ak, bl, ksa[ib]);
+                qsa[ib] = mfma(aq, bl, qsa[ib]);
             }
         }
-        if (tid < C) Gs[tid] = pG;
-        float cT[2][8], cV[4];
+        load_kq_g(nj);
+        float vf[2][4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int x = 0; x < 8; ++x) cT[kk][x] = pT[kk][x];
+            for (int r = 0; r < 4; ++r) vf[ib][r] = __uint_as_float(vr[ib][r] << 16);
+        load_v(nj);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cV[r] = (16 * tb + 4 * lg + r < L) ? bf16_to_f32(pV[r]) : 0.f;
-        __syncthreads();
-        if (jc + 1 < nch) prefetch(jc + 1);
-
-        // (2) K S^T and Q S^T for tile (tb, ib); P^T tiles; X = V - diag(gamma) K S^T
-        f4_t ksa = f4_t{0.f, 0.f, 0.f, 0.f}, qsa = f4_t{0.f, 0.f, 0.f, 0.f};
-        f4_t pa[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
-        // P^T tiles (sb, tb) handled here: sb = ib and sb = ib + 2, when sb <= tb
-        const bool p0 = ib <= tb, p1 = ib + 2 <= tb;
+        for (int ib = 0; ib < 2; ++ib) {
+            float xv[4];
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            const int col = 32 * kk + 8 * lg;
-            const bf8_t ak = lds8(&Ks[(16 * tb + lr) * KP + col]);
-            const bf8_t aq = lds8(&Qs[(16 * tb + lr) * KP + col]);
-            const bf8_t bh = lds8(&Sh[(16 * ib + lr) * KP + col]);
-            const bf8_t bl = lds8(&Sl[(16 * ib + lr) * KP + col]);
-            ksa = mfma(ak, bh, ksa);
-            ksa = mfma(ak, bl, ksa);
-            qsa = mfma(aq, bh, qsa);
-            qsa = mfma(aq, bl, qsa);
-            if (p0) pa[0] = mfma(lds8(&Ks[(16 * ib + lr) * KP + col]), aq, pa[0]);
-            if (p1) pa[1] = mfma(lds8(&Ks[(16 * (ib + 2) + lr) * KP + col]), aq, pa[1]);
+            for (int r = 0; r < 4; ++r)
+                xv[r] = (16 * tb + 4 * lg + r < L) ? vf[ib][r] - gam[r] * ksa[ib][r] : 0.f;
+            uint2 hi, lo;
+            split4(xv, hi, lo);
+            const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
+            *reinterpret_cast<uint2*>(&Xh[off]) = hi;
+            *reinterpret_cast<uint2*>(&Xl[off]) = lo;
         }
-        // pa[x][r] = P^T[s = 16 sb + 4 lg + r][t = 16 tb + lr]
-        {
-            const int t = 16 * tb + lr;
-            const float Gt = Gs[t];
+        __syncthreads();
+
+        // (B) U = T' X for row block tb (T' is lower triangular: k-steps up to tb / 2)
+        f4_t ua[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int sb = ib + 2 * x;
-                // tiles inside the k-range that the O product reads must be stored (zeros
-                // above the diagonal); others are never read
-                if ((sb >> 1) <= (tb >> 1)) {
-                    const bool comp = sb <= tb;
-                    __bf16 hi[4], lo[4];
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk <= (tb >> 1)) {
+                const int col = 32 * kk + 8 * lg;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int s = 16 * sb + 4 * lg + r;
-                        const float pv = (comp && s <= t) ? pa[x][r] * __expf(Gt - Gs[s]) : 0.f;
-                        split1(pv, hi[r], lo[r]);
-                    }
-                    const int off = t * TP + 16 * sb + 4 * lg;
-                    *reinterpret_cast<uint2*>(&Ph[off]) = *reinterpret_cast<const uint2*>(hi);
-                    *reinterpret_cast<uint2*>(&Pl[off]) = *reinterpret_cast<const uint2*>(lo);
+                for (int ib = 0; ib < 2; ++ib) {
+                    const bf8_t bh = lds8(&Xh[(16 * ib + lr) * TP + col]);
+                    const bf8_t bl = lds8(&Xl[(16 * ib + lr) * TP + col]);
+                    ua[ib] = mfma(tH[kk], bh, ua[ib]);
+                    ua[ib] = mfma(tH[kk], bl, ua[ib]);
+                    ua[ib] = mfma(tL[kk], bh, ua[ib]);
                 }
             }
         }
-        float Gt4[4], gam[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            Gt4[r] = Gs[16 * tb + 4 * lg + r];
-            gam[r] = __expf(Gt4[r]);
-        }
+        load_t(nj);
         {
-            __bf16 hi[4], lo[4];
+            float dec[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) split1(cV[r] - gam[r] * ksa[r], hi[r], lo[r]);
-            const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
-            *reinterpret_cast<uint2*>(&Xh[off]) = *reinterpret_cast<const uint2*>(hi);
-            *reinterpret_cast<uint2*>(&Xl[off]) = *reinterpret_cast<const uint2*>(lo);
+            for (int r = 0; r < 4; ++r) dec[r] = __expf(gNc - gr[r]);
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                float uv[4], wv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uv[r] = ua[ib][r];
+                    wv[r] = ua[ib][r] * dec[r];
+                }
+                uint2 hi, lo;
+                const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
+                split4(uv, hi, lo);
+                *reinterpret_cast<uint2*>(&Uh[off]) = hi;
+                *reinterpret_cast<uint2*>(&Ul[off]) = lo;
+                split4(wv, hi, lo);
+                *reinterpret_cast<uint2*>(&Wh[off]) = hi;
+                *reinterpret_cast<uint2*>(&Wl[off]) = lo;
+            }
         }
         __syncthreads();
 
-        // (3) U = T' X for tile (tb, ib) (T' lower triangular: k-steps up to tb / 2)
-        f4_t ua = f4_t{0.f, 0.f, 0.f, 0.f};
+        // (C1) O = scale (diag(gamma) Q S^T + P U) for row block tb
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (kk <= (tb >> 1)) {
-                bf8_t ah, al;
-                split8(cT[kk], ah, al);
-                const int col = 32 * kk + 8 * lg;
-                const bf8_t bh = lds8(&Xh[(16 * ib + lr) * TP + col]);
-                const bf8_t bl = lds8(&Xl[(16 * ib + lr) * TP + col]);
-                ua = mfma(ah, bh, ua);
-                ua = mfma(ah, bl, ua);
-                ua = mfma(al, bh, ua);
-            }
-        }
-        const float Gn = Gs[L - 1];
-        {
-            __bf16 hi[4], lo[4], whi[4], wlo[4];
+        for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                split1(ua[r], hi[r], lo[r]);
-                split1(ua[r] * __expf(Gn - Gt4[r]), whi[r], wlo[r]);
-            }
-            const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
-            *reinterpret_cast<uint2*>(&Uh[off]) = *reinterpret_cast<const uint2*>(hi);
-            *reinterpret_cast<uint2*>(&Ul[off]) = *reinterpret_cast<const uint2*>(lo);
-            *reinterpret_cast<uint2*>(&Wh[off]) = *reinterpret_cast<const uint2*>(whi);
-            *reinterpret_cast<uint2*>(&Wl[off]) = *reinterpret_cast<const uint2*>(wlo);
-        }
-        __syncthreads();
-
-        // (4a) O = scale (diag(gamma) Q S^T + P U) for tile (tb, ib)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) qsa[r] *= gam[r];
+            for (int r = 0; r < 4; ++r) qsa[ib][r] *= gam[r];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             if (kk <= (tb >> 1)) {
                 const int col = 32 * kk + 8 * lg;
-                const bf8_t ah = lds8(&Ph[(16 * tb + lr) * TP + col]);
-                const bf8_t al = lds8(&Pl[(16 * tb + lr) * TP + col]);
-                const bf8_t bh = lds8(&Uh[(16 * ib + lr) * TP + col]);
-                const bf8_t bl = lds8(&Ul[(16 * ib + lr) * TP + col]);
-                qsa = mfma(ah, bh, qsa);
-                qsa = mfma(ah, bl, qsa);
-                qsa = mfma(al, bh, qsa);
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const bf8_t bh = lds8(&Uh[(16 * ib + lr) * TP + col]);
+                    const bf8_t bl = lds8(&Ul[(16 * ib + lr) * TP + col]);
+                    qsa[ib] = mfma(pH[kk], bh, qsa[ib]);
+                    qsa[ib] = mfma(pH[kk], bl, qsa[ib]);
+                    qsa[ib] = mfma(pL[kk], bh, qsa[ib]);
+                }
             }
         }
+        load_p(nj);
+        {
+            // rows t >= L land at or past the resource end and are dropped
+            const __amdgpu_buffer_rsrc_t orsrc =
+                out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tb + 4 * lg + r;
-            if (t < L)
-                io<Tout>::st(o + ((size_t)(t0 + t) * HV + h) * dv + tile * BV + 16 * ib + lr,
-                             scale * qsa[r]);
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tb + 4 * lg + r;
+                    out_store(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * ib + lr),
+                              A.scale * qsa[ib][r], op);
+                }
         }
-
-        // (4b) S'^T = gamma_n S^T + K^T U' for the wave's state tiles
-        const float gn = __expf(Gn);
+        // (C2) S'^T = gamma_n S^T + K^T U' for the wave's state tiles
+        const float gn = __expf(gNc);
 #pragma unroll
-        for (int x = 0; x < NST; ++x) {
-            const int ti = w + 8 * x, jb = ti >> 1, ibS = ti & 1;
+        for (int x = 0; x < NJB; ++x)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[x][r] *= gn;
+            for (int ibS = 0; ibS < 2; ++ibS) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int col = 32 * kk + 8 * lg;
-                const bf8_t ak = lds8(&Kt[(16 * jb + lr) * TP + col]);
-                const bf8_t bh = lds8(&Wh[(16 * ibS + lr) * TP + col]);
-                const bf8_t bl = lds8(&Wl[(16 * ibS + lr) * TP + col]);
-                sacc[x] = mfma(ak, bh, sacc[x]);
-                sacc[x] = mfma(ak, bl, sacc[x]);
+                for (int r = 0; r < 4; ++r) sacc[x][ibS][r] *= gn;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int col = 32 * kk + 8 * lg;
+                    const bf8_t bh = lds8(&Wh[(16 * ibS + lr) * TP + col]);
+                    const bf8_t bl = lds8(&Wl[(16 * ibS + lr) * TP + col]);
+                    sacc[x][ibS] = mfma(ktA[x][kk], bh, sacc[x][ibS]);
+                    sacc[x][ibS] = mfma(ktA[x][kk], bl, sacc[x][ibS]);
+                }
             }
-        }
-        // Sh / Sl are read only in (2): each wave can refresh its part now
+        load_kt(nj);
+        // Sh / Sl are read only in (A): each wave refreshes its part now
         store_state_lds();
         __syncthreads();
     }
 
-    if (sfin) {
+    if (A.s_final) {
 #pragma unroll
-        for (int x = 0; x < NST; ++x) {
-            const int ti = w + 8 * x, jb = ti >> 1, ibS = ti & 1;
-            const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * jb + 4 * lg;
-            *reinterpret_cast<float4*>(sfin + off) =
-                make_float4(sacc[x][0], sacc[x][1], sacc[x][2], sacc[x][3]);
-        }
+        for (int x = 0; x < NJB; ++x)
+#pragma unroll
+            for (int ibS = 0; ibS < 2; ++ibS) {
+                const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * w + x) + 4 * lg;
+                *reinterpret_cast<float4*>(A.s_final + off) =
+                    make_float4(sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]);
+            }
     }
 }
 
 template <int DK, typename Tout>
 static hipError_t launch_mfma_t(const PrefillArgs& A) {
-    hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.H), dim3(256), 0, A.stream,
-                       static_cast<const bf16_t*>(A.k), A.g, A.beta, A.cu_seqlens, A.chunk_off,
-                       A.N, A.T, A.H, A.HV, A.max_chunks, A.ws_T, A.ws_G);
+    hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.H), dim3(256), 0, A.stream, A);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int tiles = A.dv / 32;
     const int chains = A.N * A.HV;
     const size_t blocks = (size_t)((chains + 7) / 8) * 8 * tiles;
-    hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(512), 0,
-                       A.stream, static_cast<const bf16_t*>(A.q), static_cast<const bf16_t*>(A.k),
-                       static_cast<const bf16_t*>(A.v), A.cu_seqlens, A.chunk_off, A.N, A.T, A.H,
-                       A.HV, A.dv, A.max_chunks, A.ws_T, A.ws_G, A.s0, A.s_final,
-                       static_cast<Tout*>(A.o), A.scale);
+    hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(256), 0,
+                       A.stream, A);
     return hipGetLastError();
 }
 

@@ -104,12 +104,16 @@ def test_prefill_workspace_bytes(L):
     assert f(2, 0, 2, 4, 128, 128) == 0
     assert f(2, 100, 2, 4, 128, 128, 32) == 0
     assert f(2, 100, 2, 4, 96, 128) == 0
-    for N, T, HV in ((1, 1, 1), (4, 16384, 16), (8, 131072, 32), (3, 65, 2)):
+    al = lambda x: (x + 255) // 256 * 256
+    for N, T, H, HV, dk in ((1, 1, 1, 1, 16), (4, 16384, 16, 16, 128), (8, 131072, 16, 32, 128),
+                            (3, 65, 2, 2, 64)):
         maxc = (T + N * 63) // 64
-        al = lambda x: (x + 255) // 256 * 256
-        want = al(4 * (N + 1)) + al(maxc * HV * 64 * 64 * 4) + al(maxc * HV * 64 * 4)
-        assert f(N, T, 1, HV, 128, 128) == want
-        assert f(N, T, 1, HV, 128, 128) % 256 == 0
+        head = al(4 * (N + 1)) + al(maxc * HV * 64 * 4)
+        valu = al(maxc * HV * 64 * 64 * 4)
+        mfma = 4 * al(maxc * HV * 64 * 64 * 2) + maxc * H * dk * 64 * 2
+        want = head + max(valu, al(mfma))
+        assert f(N, T, H, HV, dk, 128) == want
+        assert f(N, T, H, HV, dk, 128) % 256 == 0
 
 
 def _norm(L, **kw):
