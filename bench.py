@@ -37,6 +37,23 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 
 
+# HBM traffic of the dominant kernel (fused decode + RMSNormGated, 0.8B decode
+# job shape) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by the same
+# counters read for a copy of known size; recorded in
+# profiles/decode_traffic_qwen35_08b.md together with the sha256 of the kernel
+# source it was measured on.  Reported only while that source is unchanged.
+DECODE_TRAFFIC = {"kernel_source_sha256": "368ed6c0e7a70c9134c2b00ee547d4ab39561258a86055a81f5ceff616e4eada",
+                  "bytes_per_launch": 68047522}
+
+
+def measured_traffic():
+    import hashlib
+    path = os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc", "gdn_decode.hip")
+    with open(path, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return DECODE_TRAFFIC["bytes_per_launch"] if sha == DECODE_TRAFFIC["kernel_source_sha256"] else None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -230,7 +247,7 @@ def run_decode_job(args):
                    "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
         "roofline": {"kernel": "decode_kernel (decode + RMSNormGated)", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(dec_launch_us, 3),
+                     "traffic": measured_traffic(), "avg_launch_us": round(dec_launch_us, 3),
                      "algorithmic_bytes_per_launch": bytes_launch},
         "roofline_prefill": {"call_us": round(pf_call_us, 2),
                              "hbm_achieved_GBs": round(pf_b / (pf_call_us * 1e-6) / 1e9, 1),
@@ -303,13 +320,37 @@ def run_prefill(args, cfg: int):
     }
 
 
+def run_copy(args):
+    """Calibration for the HBM-traffic counters: a plain device copy of known
+    size (256 MiB read + 256 MiB written per launch), timed like the rest."""
+    import torch
+    n = 64 * 1024 * 1024  # fp32 elements = 256 MiB
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 2 * n * 4
+    return {"metric": "device copy (counter calibration)", "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "bytes_per_launch": nbytes,
+            "read_bytes_per_launch": n * 4, "write_bytes_per_launch": n * 4}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill2", "prefill3", "prefill4"])
+                    choices=["decode", "prefill2", "prefill3", "prefill4", "copy"])
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--decode-steps", type=int, default=0)
     ap.add_argument("--cpu-layers", type=int, default=12)
@@ -326,6 +367,8 @@ def main():
     gdn.lib()  # loud failure without the HIP library
     if args.workload == "decode":
         out = run_decode_job(args)
+    elif args.workload == "copy":
+        out = run_copy(args)
     else:
         out = run_prefill(args, int(args.workload[-1]))
     print(json.dumps(out), flush=True)
