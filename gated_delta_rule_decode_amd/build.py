@@ -4,7 +4,7 @@
 
 Compiles every source under csrc/ to an object (in parallel) and links the
 shared library next to this file.  Device code is built for gfx950 only, with
-packed-fp32 instruction selection turned off.
+packed-fp32 instruction selection turned off and MFMA results kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -36,7 +36,10 @@ def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
             "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-munsafe-fp-atomics", "-ffp-contract=fast"]
+            "-munsafe-fp-atomics", "-ffp-contract=fast",
+            # MFMA accumulators in ordinary VGPRs: results feed vector code
+            # directly, without accumulator-register copies
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _compile(src: str) -> str:

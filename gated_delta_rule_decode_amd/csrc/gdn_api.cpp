@@ -43,6 +43,8 @@ void clear_pending() { (void)hipGetLastError(); }
 namespace gdn {
 
 PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk) {
+    (void)H;
+    (void)dk;
     PrefillLayout L{};
     // upper bound on sum_n ceil(len_n / 64) given sum_n len_n = T
     const size_t maxc = ((size_t)T + (size_t)N * (kChunk - 1)) / kChunk;
@@ -53,17 +55,14 @@ PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk) {
     off = align256(off + ((size_t)N + 1) * sizeof(int32_t));
     L.ws_G = off;
     off = align256(off + maxc * HV * kChunk * sizeof(float));
-    // one region, used by either path
+    // one region, used by either path: T' in fp32, or T' as hi and lo bf16 planes
     const size_t region = off;
     L.ws_T = region;
     const size_t valu_end = align256(region + maxc * HV * tile * sizeof(float));
     const size_t plane = align256(maxc * HV * tile * sizeof(uint16_t));
     L.ws_Th = region;
     L.ws_Tl = region + plane;
-    L.ws_Ph = region + 2 * plane;
-    L.ws_Pl = region + 3 * plane;
-    L.ws_Kt = region + 4 * plane;
-    const size_t mfma_end = align256(L.ws_Kt + maxc * H * (size_t)dk * kChunk * sizeof(uint16_t));
+    const size_t mfma_end = region + 2 * plane;
     L.total = valu_end > mfma_end ? valu_end : mfma_end;
     return L;
 }
@@ -203,9 +202,6 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     a.ws_T = reinterpret_cast<float*>(ws + L.ws_T);
     a.ws_Th = reinterpret_cast<uint16_t*>(ws + L.ws_Th);
     a.ws_Tl = reinterpret_cast<uint16_t*>(ws + L.ws_Tl);
-    a.ws_Ph = reinterpret_cast<uint16_t*>(ws + L.ws_Ph);
-    a.ws_Pl = reinterpret_cast<uint16_t*>(ws + L.ws_Pl);
-    a.ws_Kt = reinterpret_cast<uint16_t*>(ws + L.ws_Kt);
     a.max_chunks = L.max_chunks;
     a.stream = s;
     clear_pending();

@@ -52,12 +52,9 @@ struct PrefillArgs {
     float* ws_G;         // [max_chunks, HV, 64]      in-chunk cumulative log-decay
     // vector-unit path
     float* ws_T;         // [max_chunks, HV, 64, 64]  T' = (I + A)^-1 diag(beta), fp32
-    // MFMA path (same memory as ws_T): T' and P as hi + lo bf16, K^T per key head
+    // MFMA path (same memory as ws_T): T' as hi + lo bf16 planes
     uint16_t* ws_Th;     // [max_chunks, HV, 64, 64]
     uint16_t* ws_Tl;
-    uint16_t* ws_Ph;     // [max_chunks, HV, 64, 64]  P = tril(Q K^T) o e^{G_t - G_s}
-    uint16_t* ws_Pl;
-    uint16_t* ws_Kt;     // [max_chunks, H, dk, 64]   K^T of the chunk (zero past the end)
     int max_chunks;
     hipStream_t stream;
 };
@@ -76,7 +73,7 @@ struct NormArgs {
 
 // Workspace layout of gdn_prefill_chunked (byte offsets, 256-aligned).
 struct PrefillLayout {
-    size_t chunk_off, ws_G, ws_T, ws_Th, ws_Tl, ws_Ph, ws_Pl, ws_Kt, total;
+    size_t chunk_off, ws_G, ws_T, ws_Th, ws_Tl, total;
     int max_chunks;
 };
 PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk);

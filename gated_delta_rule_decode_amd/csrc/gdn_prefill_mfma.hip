@@ -21,13 +21,14 @@
 // Accumulation is fp32 and the state between chunks stays fp32 in the
 // accumulators of the update product.
 //
-// Work split.  Everything that does not depend on the state runs
-// chunk-parallel in prep_mfma: per (chunk, key head) K K^T and Q K^T, and per
-// value head of that key head G, the triangular inverse, T' and P, stored
-// pre-split as hi/lo bf16 row-major tiles, plus K^T of the chunk.  The
-// sequential scan_mfma then only runs the state-dependent products, reading
-// its T', P, K, Q and K^T fragments straight from memory into registers one
-// chunk ahead; LDS holds just the state tile and the X, U, U' exchange tiles.
+// Work split.  What does not depend on the state runs chunk-parallel in
+// prep_mfma: per (chunk, key head) K K^T, and per value head of that key head
+// G, the triangular inverse and T', stored pre-split as hi/lo bf16 row-major
+// tiles.  The sequential scan_mfma runs the rest: K S^T, Q S^T, the causal
+// Q K^T (computed again per chunk: it costs less MFMA time than the HBM bytes
+// of storing P), U = T' X, O and the state update.  It reads K, Q, V, G and T'
+// fragments straight from memory into registers one chunk ahead; LDS holds
+// the state tile, the X, U, U' exchange tiles and the chunk's K rows.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -63,28 +64,43 @@ __device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 __device__ __forceinline__ bf8_t zero8() { return __builtin_bit_cast(bf8_t, make_uint4(0, 0, 0, 0)); }
 
-// fp32 x -> (hi, lo) with hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ void split8(const float* x, bf8_t& hi, bf8_t& lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const __bf16 h = static_cast<__bf16>(x[j]);
-        hi[j] = h;
-        lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
-    }
-}
+// exponentials of log-decay differences: G is kept in log2 units (g log2 e),
+// so e^{G_t - G_s} is one hardware exp2
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ void split1(float x, __bf16& hi, __bf16& lo) {
-    hi = static_cast<__bf16>(x);
-    lo = static_cast<__bf16>(x - static_cast<float>(hi));
-}
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
-// 4 consecutive floats -> 8-byte hi and lo words
+// two floats -> packed hi and lo bf16 words (one conversion per word)
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{x0, x1}, bf2_t));
+    const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{x0 - h0, x1 - h1}, bf2_t));
+}
+// fp32 x -> (hi, lo) with hi = bf16(x), lo = bf16(x - hi): 4 or 8 values
 __device__ __forceinline__ void split4(const float* x, uint2& hi, uint2& lo) {
-    __bf16 h[4], o[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) split1(x[r], h[r], o[r]);
-    hi = *reinterpret_cast<const uint2*>(h);
-    lo = *reinterpret_cast<const uint2*>(o);
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
+}
+__device__ __forceinline__ void split8(const float* x, bf8_t& hi, bf8_t& lo) {
+    uint4 h, o;
+    split2(x[0], x[1], h.x, o.x);
+    split2(x[2], x[3], h.y, o.y);
+    split2(x[4], x[5], h.z, o.z);
+    split2(x[6], x[7], h.w, o.w);
+    hi = __builtin_bit_cast(bf8_t, h);
+    lo = __builtin_bit_cast(bf8_t, o);
+}
+
+// Raw buffer loads: the resource covers exactly the valid rows of a chunk, so
+// rows past a sequence end read as zero without a clamp or a select.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t in_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ bf8_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(bf8_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
 __device__ __forceinline__ void seq_bounds_m(const int32_t* cu, int n, int T, int& s, int& e) {
@@ -109,16 +125,15 @@ __device__ __forceinline__ int find_seq_m(const int32_t* chunk_off, int N, int c
 // prep: everything that does not depend on the state, chunk-parallel
 // ---------------------------------------------------------------------------
 // One workgroup (4 wavefronts) per (chunk, key head).  Wave w owns row block
-// w (tokens 16 w .. 16 w + 15) of K K^T and of P.  Outputs per value head:
-// T' and P as hi/lo bf16 row-major 64 x 64 tiles (zeros above the diagonal and
-// in rows / columns past the sequence end) and G; per key head: K^T (dk x 64).
+// w (tokens 16 w .. 16 w + 15) of K K^T.  Outputs per value head: T' as hi/lo
+// bf16 row-major 64 x 64 tiles (zeros above the diagonal and in rows /
+// columns past the sequence end) and G.
 template <int DK>
 __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
     constexpr int KP = DK + 8;  // padded bf16 row
     constexpr int AP = C + 4;   // padded fp32 row (16-byte aligned rows)
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * KP];
     __shared__ __attribute__((aligned(16))) float Am[C * AP];
     __shared__ __attribute__((aligned(16))) float Tm[C * AP];
     __shared__ __attribute__((aligned(16))) float Xm[32 * 36];
@@ -136,64 +151,40 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     const int L = min(C, e0 - t0);
     const int ratio = HV / H;
     const bf16_t* k = static_cast<const bf16_t*>(A.k);
-    const bf16_t* q = static_cast<const bf16_t*>(A.q);
 
-    // K and Q chunk -> LDS (rows past the sequence end are zero)
+    // K chunk -> LDS (rows past the sequence end are zero)
     for (int idx = tid; idx < C * DK / 8; idx += 256) {
         const int t = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
         const size_t off = ((size_t)(t0 + min(t, L - 1)) * H + hk) * DK + c8;
         uint4 kv = *reinterpret_cast<const uint4*>(k + off);
-        uint4 qv = *reinterpret_cast<const uint4*>(q + off);
-        if (t >= L) kv = qv = make_uint4(0, 0, 0, 0);
+        if (t >= L) kv = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(&Ks[t * KP + c8]) = kv;
-        *reinterpret_cast<uint4*>(&Qs[t * KP + c8]) = qv;
     }
     __syncthreads();
 
-    // K^T of the chunk -> workspace, [dk][64] bf16
-    {
-        uint16_t* Kt = A.ws_Kt + ((size_t)c * H + hk) * DK * C;
-        const uint16_t* Kr = reinterpret_cast<const uint16_t*>(Ks);
-        for (int idx = tid; idx < DK * C / 8; idx += 256) {
-            const int t8 = 8 * (idx % (C / 8)), j = idx / (C / 8);
-            uint32_t wd[4];
+    // K K^T (row block w, column blocks sb <= w)
+    f4_t kk[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
-                wd[x] = (uint32_t)Kr[(t8 + 2 * x) * KP + j] |
-                        ((uint32_t)Kr[(t8 + 2 * x + 1) * KP + j] << 16);
-            *reinterpret_cast<uint4*>(Kt + (size_t)j * C + t8) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        }
-    }
-
-    // K K^T (row block w, column blocks sb <= w) and P^T = K Q^T (column block w)
-    f4_t kk[4], pq[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-        kk[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
-        pq[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int sb = 0; sb < 4; ++sb) kk[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
         const int col = 32 * ks + 8 * lg;
         const bf8_t ka = lds8(&Ks[(16 * w + lr) * KP + col]);
-        const bf8_t qa = lds8(&Qs[(16 * w + lr) * KP + col]);
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             if (sb <= w) {
                 const bf8_t kb = lds8(&Ks[(16 * sb + lr) * KP + col]);
                 kk[sb] = mfma(ka, kb, kk[sb]);
-                pq[sb] = mfma(kb, qa, pq[sb]);
             }
         }
     }
     // kk[sb][r] = (K K^T)[t = 16 w + 4 lg + r][s = 16 sb + lr]
-    // pq[sb][r] = (Q K^T)[t = 16 w + lr][s = 16 sb + 4 lg + r]
 
     for (int hv = hk * ratio; hv < (hk + 1) * ratio; ++hv) {
         const size_t tileoff = ((size_t)c * HV + hv) * C * C;
         // G = in-chunk inclusive cumsum of g (wave 0), beta
         if (w == 0) {
-            float gv = A.g[(size_t)(t0 + min(l, L - 1)) * HV + hv];
+            float gv = A.g[(size_t)(t0 + min(l, L - 1)) * HV + hv] * kLog2e;
             float bv = A.beta[(size_t)(t0 + min(l, L - 1)) * HV + hv];
             if (l >= L) gv = 0.f, bv = 0.f;
 #pragma unroll
@@ -206,25 +197,6 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
             A.ws_G[((size_t)c * HV + hv) * C + l] = gv;
         }
         __syncthreads();
-        // P = tril(Q K^T) o e^{G_t - G_s}: row block w, all column blocks, hi / lo
-        {
-            const int t = 16 * w + lr;
-            const float Gt = Gs[t];
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                float pv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * sb + 4 * lg + r;
-                    pv[r] = (sb <= w && s <= t) ? pq[sb][r] * __expf(Gt - Gs[s]) : 0.f;
-                }
-                uint2 hi, lo;
-                split4(pv, hi, lo);
-                const size_t off = tileoff + (size_t)t * C + 16 * sb + 4 * lg;
-                *reinterpret_cast<uint2*>(A.ws_Ph + off) = hi;
-                *reinterpret_cast<uint2*>(A.ws_Pl + off) = lo;
-            }
-        }
         // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s})
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
@@ -233,7 +205,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * w + 4 * lg + r, s = 16 * sb + lr;
-                    Am[t * AP + s] = (s < t) ? Bs[t] * __expf(Gs[t] - Gsb) * kk[sb][r] : 0.f;
+                    Am[t * AP + s] = (s < t) ? Bs[t] * exp2f_(Gs[t] - Gsb) * kk[sb][r] : 0.f;
                 }
             }
         }
@@ -354,24 +326,31 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
 // scan: sequential over chunks, state tile in MFMA accumulators
 // ---------------------------------------------------------------------------
 // 4 wavefronts, one per SIMD.  Wave w owns the chunk's row block tb = w
-// (tokens 16 w .. 16 w + 15) in K S^T, Q S^T, X, U and O for both 16-column
-// halves ib = 0, 1 of the state tile's 32 rows, so its K, Q, T', P row
-// fragments are loaded once; and the state tiles S^T[16 jb .. +15][16 ibS ..]
-// for its DK/64 column blocks jb and both halves ibS.
-// Per chunk: (A) K S^T, Q S^T, X -> LDS; (B) U = T' X, U and U' -> LDS;
-// (C) O = gamma Q S^T + P U to memory and S' = gamma_n S + U'^T K -> LDS.
-// Operand fragments that come from memory are held in one register set: each
-// group is reloaded for the next chunk right after its last use in this one
-// (K, Q and G after (A), T' after (B), P after the output product, K^T after
-// the state update), so every load has a full chunk to arrive and the loads
-// are spread over the chunk instead of queueing at its start.  No branch
-// surrounds a load or store (masked rows use clamped loads and out-of-range
-// buffer stores), so the compiler waits for exactly the group it needs.
+// (tokens 16 w .. 16 w + 15) in K S^T, Q S^T, P, X, U and O for both 16-column
+// halves ib = 0, 1 of the state tile's 32 rows, and the state tiles
+// S^T[16 jb .. +15][16 ibS .. +15] for its DK/64 column blocks jb.
+// Per chunk:
+//   (A) K S^T, Q S^T, P^T = K Q^T (row block tb against column blocks <= tb);
+//       X = V - diag(gamma) K S^T -> LDS
+//   (B) U = T' X; U and U' -> LDS
+//   (C) O = gamma Q S^T + P U to memory, with P taken straight from the P^T
+//       accumulators (the contraction slots are ordered so that a lane's four
+//       accumulator values of two P^T tiles are its eight A-operand values,
+//       and U is read in the same order); S' = gamma_n S + K^T U' -> LDS;
+//       the next chunk's K rows and G go to the other half of a double buffer.
+// Operand fragments from memory (K, Q rows, G, V, T') are held in one register
+// set: each group is reloaded for the next chunk right after its last use, so
+// every load has about a chunk to arrive.  Loads go through buffer resources
+// that end at the chunk's last valid row: rows past a sequence end read as
+// zero, which masks K, Q, V, X and U without selects, and output rows past
+// the end are dropped by the store's resource.  No branch surrounds a memory
+// operation whose count differs between paths, so the compiler waits for
+// exactly the group it needs.
 template <int DK, typename Tout>
 __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
     constexpr int BV = 32;
-    constexpr int KP = DK + 8;   // padded row of S (bf16)
+    constexpr int KP = DK + 8;   // padded row of S and K (bf16)
     constexpr int TP = C + 8;    // padded row of the [*, C] tiles (bf16)
     constexpr int NKK = DK / 32;
     constexpr int NJB = DK / 64;  // state column blocks per wave
@@ -384,11 +363,14 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     __shared__ __attribute__((aligned(16))) __bf16 Ul[BV * TP];
     __shared__ __attribute__((aligned(16))) __bf16 Wh[BV * TP];
     __shared__ __attribute__((aligned(16))) __bf16 Wl[BV * TP];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C * KP];
+    __shared__ __attribute__((aligned(16))) float Gs[2][C];
 
     const int H = A.H, HV = A.HV, dv = A.dv, N = A.N;
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int tb = w;
+    const int tb = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index = row block
+    __builtin_assume(tb >= 0 && tb < 4);
+    const int l = tid & 63, lr = l & 15, lg = l >> 4;
     const int tiles = dv / BV;
     // XCD-aware mapping: workgroup b runs on XCD b % 8; all tiles of a chain
     // get the same b % 8 and neighbouring dispatch slots
@@ -405,13 +387,13 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     const bf16_t* vp = static_cast<const bf16_t*>(A.v);
     Tout* op = static_cast<Tout*>(A.o);
 
-    // state: sacc[x][ibS][r] = S[i = 16 ibS + lr][j = 16 (NJB w + x) + 4 lg + r]
+    // state: sacc[x][ibS][r] = S[i = 16 ibS + lr][j = 16 (NJB tb + x) + 4 lg + r]
     f4_t sacc[NJB][2];
 #pragma unroll
     for (int x = 0; x < NJB; ++x)
 #pragma unroll
         for (int ibS = 0; ibS < 2; ++ibS) {
-            const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * w + x) + 4 * lg;
+            const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * tb + x) + 4 * lg;
             if (A.s0) {
                 const float4 v4 = *reinterpret_cast<const float4*>(A.s0 + off);
                 sacc[x][ibS] = f4_t{v4.x, v4.y, v4.z, v4.w};
@@ -419,12 +401,22 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
                 sacc[x][ibS] = f4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
+    auto store_state = [&](float* dst) {
+#pragma unroll
+        for (int x = 0; x < NJB; ++x)
+#pragma unroll
+            for (int ibS = 0; ibS < 2; ++ibS) {
+                const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * tb + x) + 4 * lg;
+                *reinterpret_cast<float4*>(dst + off) =
+                    make_float4(sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]);
+            }
+    };
     auto store_state_lds = [&]() {
 #pragma unroll
         for (int x = 0; x < NJB; ++x)
 #pragma unroll
             for (int ibS = 0; ibS < 2; ++ibS) {
-                const int off = (16 * ibS + lr) * KP + 16 * (NJB * w + x) + 4 * lg;
+                const int off = (16 * ibS + lr) * KP + 16 * (NJB * tb + x) + 4 * lg;
                 float sv[4] = {sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]};
                 uint2 hi, lo;
                 split4(sv, hi, lo);
@@ -432,7 +424,6 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
                 *reinterpret_cast<uint2*>(&Sl[off]) = lo;
             }
     };
-    store_state_lds();
 
     int sq, eq;
     seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
@@ -440,37 +431,37 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     int nch = A.chunk_off[n + 1] - c_first;
     if (c_first + nch > A.max_chunks) nch = max(0, A.max_chunks - c_first);
     if (nch <= 0) {
-        if (A.s_final) {
-#pragma unroll
-            for (int x = 0; x < NJB; ++x)
-#pragma unroll
-                for (int ibS = 0; ibS < 2; ++ibS) {
-                    const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * w + x) + 4 * lg;
-                    *reinterpret_cast<float4*>(A.s_final + off) =
-                        make_float4(sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]);
-                }
-        }
+        if (A.s_final) store_state(A.s_final);
         return;
     }
+
+    // byte offsets of this lane's fragments inside a chunk (the same for every chunk)
+    const uint32_t qk_row = (uint32_t)H * DK * 2;  // bytes per token of q, k
+    const uint32_t v_row = (uint32_t)HV * dv * 2;  // bytes per token of v
+    const uint32_t kq_off = ((uint32_t)(16 * tb + lr) * H + hk) * DK * 2 + 16 * lg;
+    uint32_t v_off[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        v_off[r] = ((uint32_t)(16 * tb + 4 * lg + r) * HV + h) * dv * 2 + (tile * BV + lr) * 2;
+    const uint32_t t_off = ((16 * tb + lr) * C + 8 * lg) * 2;
 
     // ---- operand fragments (one set; groups reloaded after their last use) ----
     bf8_t kA[NKK], qA[NKK];      // K, Q row 16 tb + lr, k-step kk
     bf8_t tH[2], tL[2];          // T' row 16 tb + lr, columns 32 kk + 8 lg ..
-    bf8_t pH[2], pL[2];          // P row 16 tb + lr
-    bf8_t ktA[NJB][2];           // K^T row 16 jb + lr, tokens 32 kk + 8 lg ..
     uint32_t vr[2][4];           // V[t = 16 tb + 4 lg + r][i = 16 ib + lr], raw bf16 bits
-    float4 gR;                   // G[16 tb + 4 lg + r]
+    float4 gR;                   // G[16 tb + 4 lg + r]  (log2 units)
     float gN;                    // G[L - 1]
 
     auto chunk_t0 = [&](int jc) { return sq + jc * C; };
     auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
     auto load_kq_g = [&](int jc) {
         const int t0 = chunk_t0(jc), L = chunk_L(jc);
-        const size_t krow = ((size_t)(t0 + min(16 * tb + lr, L - 1)) * H + hk) * DK + 8 * lg;
+        const __amdgpu_buffer_rsrc_t rk = in_rsrc(kp + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
+        const __amdgpu_buffer_rsrc_t rq = in_rsrc(qp + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            kA[kk] = __builtin_bit_cast(bf8_t, *reinterpret_cast<const uint4*>(kp + krow + 32 * kk));
-            qA[kk] = __builtin_bit_cast(bf8_t, *reinterpret_cast<const uint4*>(qp + krow + 32 * kk));
+            kA[kk] = bload8(rk, kq_off + 64 * kk);
+            qA[kk] = bload8(rq, kq_off + 64 * kk);
         }
         const float* G = A.ws_G + ((size_t)(c_first + jc) * HV + h) * C;
         gR = *reinterpret_cast<const float4*>(G + 16 * tb + 4 * lg);
@@ -478,79 +469,76 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     };
     auto load_v = [&](int jc) {
         const int t0 = chunk_t0(jc), L = chunk_L(jc);
+        const __amdgpu_buffer_rsrc_t rv = in_rsrc(vp + (size_t)t0 * HV * dv, (uint32_t)L * v_row);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = min(16 * tb + 4 * lg + r, L - 1);
-                vr[ib][r] = vp[((size_t)(t0 + t) * HV + h) * dv + tile * BV + 16 * ib + lr];
-            }
-    };
-    auto tile_off = [&](int jc) {
-        return (((size_t)(c_first + jc) * HV + h) * C + 16 * tb + lr) * C + 8 * lg;
+            for (int r = 0; r < 4; ++r)
+                vr[ib][r] = __builtin_amdgcn_raw_buffer_load_b16(rv, (int)(v_off[r] + 32 * ib), 0, 0);
     };
     auto load_t = [&](int jc) {
-        const size_t toff = tile_off(jc);
+        const size_t tt = ((size_t)(c_first + jc) * HV + h) * C * C;
+        const __amdgpu_buffer_rsrc_t rh = in_rsrc(A.ws_Th + tt, C * C * 2);
+        const __amdgpu_buffer_rsrc_t rl = in_rsrc(A.ws_Tl + tt, C * C * 2);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            tH[kk] = gld8(A.ws_Th + toff + 32 * kk);
-            tL[kk] = gld8(A.ws_Tl + toff + 32 * kk);
+            tH[kk] = bload8(rh, t_off + 64 * kk);
+            tL[kk] = bload8(rl, t_off + 64 * kk);
         }
     };
-    auto load_p = [&](int jc) {
-        const size_t toff = tile_off(jc);
+    // K rows of row block tb and G of the chunk whose fragments are loaded -> LDS
+    auto stage_k_g = [&](int buf) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            pH[kk] = gld8(A.ws_Ph + toff + 32 * kk);
-            pL[kk] = gld8(A.ws_Pl + toff + 32 * kk);
-        }
+        for (int kk = 0; kk < NKK; ++kk)
+            *reinterpret_cast<bf8_t*>(&Ks[buf][(16 * tb + lr) * KP + 32 * kk + 8 * lg]) = kA[kk];
+        if (lr == 0) *reinterpret_cast<float4*>(&Gs[buf][16 * tb + 4 * lg]) = gR;
     };
-    auto load_kt = [&](int jc) {
-        const uint16_t* Kt = A.ws_Kt + ((size_t)(c_first + jc) * H + hk) * DK * C;
-#pragma unroll
-        for (int x = 0; x < NJB; ++x)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                ktA[x][kk] = gld8(Kt + (size_t)(16 * (NJB * w + x) + lr) * C + 32 * kk + 8 * lg);
-    };
+
     load_kq_g(0);
     load_v(0);
     load_t(0);
-    load_p(0);
-    load_kt(0);
+    store_state_lds();
+    stage_k_g(0);
+    __syncthreads();
 
     for (int jc = 0; jc < nch; ++jc) {
         const int nj = min(jc + 1, nch - 1);  // the last chunk re-reads itself
+        const int buf = jc & 1;
+        const __bf16* Kc = Ks[buf];
+        const float* Gc = Gs[buf];
         const int t0 = chunk_t0(jc);
         const int L = chunk_L(jc);
-        const bool rowlive = 16 * tb + lr < L;  // K / Q row of this lane's A fragments
         const float gr[4] = {gR.x, gR.y, gR.z, gR.w};
         const float gNc = gN;
         float gam[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) gam[r] = __expf(gr[r]);
+        for (int r = 0; r < 4; ++r) gam[r] = exp2f_(gr[r]);
 
-        // (A) K S^T and Q S^T for row block tb, both column halves; X = V - diag(gamma) K S^T
-        f4_t ksa[2], qsa[2];
+        // (A) K S^T, Q S^T (row block tb, both column halves) and P^T tiles
+        f4_t ksa[2], qsa[2], pa[4];
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             ksa[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
             qsa[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
+        for (int sb = 0; sb < 4; ++sb) pa[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const int col = 32 * kk + 8 * lg;
-            const bf8_t ak = rowlive ? kA[kk] : zero8();
-            const bf8_t aq = rowlive ? qA[kk] : zero8();
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
                 const bf8_t bh = lds8(&Sh[(16 * ib + lr) * KP + col]);
                 const bf8_t bl = lds8(&Sl[(16 * ib + lr) * KP + col]);
-                ksa[ib] = mfma(ak, bh, ksa[ib]);
-                qsa[ib] = mfma(aq, bh, qsa[ib]);
-                ksa[ib] = mfma(ak, bl, ksa[ib]);
-                qsa[ib] = mfma(aq, bl, qsa[ib]);
+                ksa[ib] = mfma(kA[kk], bh, ksa[ib]);
+                qsa[ib] = mfma(qA[kk], bh, qsa[ib]);
+                ksa[ib] = mfma(kA[kk], bl, ksa[ib]);
+                qsa[ib] = mfma(qA[kk], bl, qsa[ib]);
             }
+            // pa[sb][r] = (Q K^T)[t = 16 tb + lr][s = 16 sb + 4 lg + r]
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+                if (sb <= tb) pa[sb] = mfma(lds8(&Kc[(16 * sb + lr) * KP + col]), qA[kk], pa[sb]);
         }
         load_kq_g(nj);
         float vf[2][4];
@@ -559,17 +547,50 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) vf[ib][r] = __uint_as_float(vr[ib][r] << 16);
         load_v(nj);
+        // X = V - diag(gamma) K S^T (zero in rows past the end: V and K read as zero)
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             float xv[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                xv[r] = (16 * tb + 4 * lg + r < L) ? vf[ib][r] - gam[r] * ksa[ib][r] : 0.f;
+            for (int r = 0; r < 4; ++r) xv[r] = vf[ib][r] - gam[r] * ksa[ib][r];
             uint2 hi, lo;
             split4(xv, hi, lo);
             const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
             *reinterpret_cast<uint2*>(&Xh[off]) = hi;
             *reinterpret_cast<uint2*>(&Xl[off]) = lo;
+        }
+        // P = P^T values masked to s <= t and decayed, split into hi / lo: the
+        // A operand of k-step kk holds s = 32 kk + 4 lg + (0..3) from tile 2 kk
+        // and s = 32 kk + 16 + 4 lg + (0..3) from tile 2 kk + 1.  Tiles below
+        // the diagonal block need no mask; tiles above it are zero.
+        uint4 pHw[2], pLw[2];
+        {
+            const int t = 16 * tb + lr;
+            const float Gt = Gc[t];
+            float pv[4][4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * sb + 4 * lg]);
+                const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
+                if (sb < tb) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pv[sb][r] = pa[sb][r] * exp2f_(Gt - gs[r]);
+                } else if (sb == tb) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        pv[sb][r] = (4 * lg + r <= lr) ? pa[sb][r] * exp2f_(Gt - gs[r]) : 0.f;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pv[sb][r] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                split2(pv[2 * kk][0], pv[2 * kk][1], pHw[kk].x, pLw[kk].x);
+                split2(pv[2 * kk][2], pv[2 * kk][3], pHw[kk].y, pLw[kk].y);
+                split2(pv[2 * kk + 1][0], pv[2 * kk + 1][1], pHw[kk].z, pLw[kk].z);
+                split2(pv[2 * kk + 1][2], pv[2 * kk + 1][3], pHw[kk].w, pLw[kk].w);
+            }
         }
         __syncthreads();
 
@@ -593,7 +614,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
         {
             float dec[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dec[r] = __expf(gNc - gr[r]);
+            for (int r = 0; r < 4; ++r) dec[r] = exp2f_(gNc - gr[r]);
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
                 float uv[4], wv[4];
@@ -614,7 +635,8 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
         }
         __syncthreads();
 
-        // (C1) O = scale (diag(gamma) Q S^T + P U) for row block tb
+        // (C1) O = scale (diag(gamma) Q S^T + P U) for row block tb; U is read in
+        // the slot order of the P operand (two 8-byte pieces per k-step)
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -622,18 +644,24 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             if (kk <= (tb >> 1)) {
-                const int col = 32 * kk + 8 * lg;
+                const int col = 32 * kk + 4 * lg;
+                const bf8_t ph = __builtin_bit_cast(bf8_t, pHw[kk]);
+                const bf8_t pl = __builtin_bit_cast(bf8_t, pLw[kk]);
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
-                    const bf8_t bh = lds8(&Uh[(16 * ib + lr) * TP + col]);
-                    const bf8_t bl = lds8(&Ul[(16 * ib + lr) * TP + col]);
-                    qsa[ib] = mfma(pH[kk], bh, qsa[ib]);
-                    qsa[ib] = mfma(pH[kk], bl, qsa[ib]);
-                    qsa[ib] = mfma(pL[kk], bh, qsa[ib]);
+                    const int row = (16 * ib + lr) * TP;
+                    const uint2 h0 = *reinterpret_cast<const uint2*>(&Uh[row + col]);
+                    const uint2 h1 = *reinterpret_cast<const uint2*>(&Uh[row + col + 16]);
+                    const uint2 l0 = *reinterpret_cast<const uint2*>(&Ul[row + col]);
+                    const uint2 l1 = *reinterpret_cast<const uint2*>(&Ul[row + col + 16]);
+                    const bf8_t bh = __builtin_bit_cast(bf8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
+                    const bf8_t bl = __builtin_bit_cast(bf8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
+                    qsa[ib] = mfma(ph, bh, qsa[ib]);
+                    qsa[ib] = mfma(ph, bl, qsa[ib]);
+                    qsa[ib] = mfma(pl, bh, qsa[ib]);
                 }
             }
         }
-        load_p(nj);
         {
             // rows t >= L land at or past the resource end and are dropped
             const __amdgpu_buffer_rsrc_t orsrc =
@@ -647,10 +675,18 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
                               A.scale * qsa[ib][r], op);
                 }
         }
-        // (C2) S'^T = gamma_n S^T + K^T U' for the wave's state tiles
-        const float gn = __expf(gNc);
+        // (C2) S'^T = gamma_n S^T + K^T U' for the wave's state tiles; the K^T
+        // fragment (column j, tokens 32 kk + 8 lg .. +7) is gathered from the
+        // row-major K tile
+        const float gn = exp2f_(gNc);
 #pragma unroll
-        for (int x = 0; x < NJB; ++x)
+        for (int x = 0; x < NJB; ++x) {
+            const int j = 16 * (NJB * tb + x) + lr;
+            bf8_t ka[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int y = 0; y < 8; ++y) ka[kk][y] = Kc[(32 * kk + 8 * lg + y) * KP + j];
 #pragma unroll
             for (int ibS = 0; ibS < 2; ++ibS) {
 #pragma unroll
@@ -660,26 +696,19 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
                     const int col = 32 * kk + 8 * lg;
                     const bf8_t bh = lds8(&Wh[(16 * ibS + lr) * TP + col]);
                     const bf8_t bl = lds8(&Wl[(16 * ibS + lr) * TP + col]);
-                    sacc[x][ibS] = mfma(ktA[x][kk], bh, sacc[x][ibS]);
-                    sacc[x][ibS] = mfma(ktA[x][kk], bl, sacc[x][ibS]);
+                    sacc[x][ibS] = mfma(ka[kk], bh, sacc[x][ibS]);
+                    sacc[x][ibS] = mfma(ka[kk], bl, sacc[x][ibS]);
                 }
             }
-        load_kt(nj);
-        // Sh / Sl are read only in (A): each wave refreshes its part now
+        }
+        // Sh / Sl are read only in (A), and the other K / G buffer was last
+        // read in the previous chunk: both can be written before the barrier
         store_state_lds();
+        stage_k_g(buf ^ 1);
         __syncthreads();
     }
 
-    if (A.s_final) {
-#pragma unroll
-        for (int x = 0; x < NJB; ++x)
-#pragma unroll
-            for (int ibS = 0; ibS < 2; ++ibS) {
-                const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * w + x) + 4 * lg;
-                *reinterpret_cast<float4*>(A.s_final + off) =
-                    make_float4(sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]);
-            }
-    }
+    if (A.s_final) store_state(A.s_final);
 }
 
 template <int DK, typename Tout>
