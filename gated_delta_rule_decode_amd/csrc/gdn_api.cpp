@@ -44,7 +44,6 @@ namespace gdn {
 
 PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk) {
     (void)H;
-    (void)dk;
     PrefillLayout L{};
     // upper bound on sum_n ceil(len_n / 64) given sum_n len_n = T
     const size_t maxc = ((size_t)T + (size_t)N * (kChunk - 1)) / kChunk;
@@ -55,14 +54,18 @@ PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk) {
     off = align256(off + ((size_t)N + 1) * sizeof(int32_t));
     L.ws_G = off;
     off = align256(off + maxc * HV * kChunk * sizeof(float));
-    // one region, used by either path: T' in fp32, or T' as hi and lo bf16 planes
+    // one region, used by either path: T' in fp32 (vector-unit path), or R and
+    // Z^T as hi and lo bf16 planes (MFMA path)
     const size_t region = off;
     L.ws_T = region;
     const size_t valu_end = align256(region + maxc * HV * tile * sizeof(float));
-    const size_t plane = align256(maxc * HV * tile * sizeof(uint16_t));
-    L.ws_Th = region;
-    L.ws_Tl = region + plane;
-    const size_t mfma_end = region + 2 * plane;
+    const size_t rplane = align256(maxc * HV * tile * sizeof(uint16_t));
+    const size_t zplane = align256(maxc * HV * (size_t)dk * kChunk * sizeof(uint16_t));
+    L.ws_Rh = region;
+    L.ws_Rl = region + rplane;
+    L.ws_Zh = region + 2 * rplane;
+    L.ws_Zl = region + 2 * rplane + zplane;
+    const size_t mfma_end = region + 2 * rplane + 2 * zplane;
     L.total = valu_end > mfma_end ? valu_end : mfma_end;
     return L;
 }
@@ -200,8 +203,10 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     a.chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
     a.ws_G = reinterpret_cast<float*>(ws + L.ws_G);
     a.ws_T = reinterpret_cast<float*>(ws + L.ws_T);
-    a.ws_Th = reinterpret_cast<uint16_t*>(ws + L.ws_Th);
-    a.ws_Tl = reinterpret_cast<uint16_t*>(ws + L.ws_Tl);
+    a.ws_Rh = reinterpret_cast<uint16_t*>(ws + L.ws_Rh);
+    a.ws_Rl = reinterpret_cast<uint16_t*>(ws + L.ws_Rl);
+    a.ws_Zh = reinterpret_cast<uint16_t*>(ws + L.ws_Zh);
+    a.ws_Zl = reinterpret_cast<uint16_t*>(ws + L.ws_Zl);
     a.max_chunks = L.max_chunks;
     a.stream = s;
     clear_pending();

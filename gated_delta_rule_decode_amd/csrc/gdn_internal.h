@@ -52,9 +52,13 @@ struct PrefillArgs {
     float* ws_G;         // [max_chunks, HV, 64]      in-chunk cumulative log-decay
     // vector-unit path
     float* ws_T;         // [max_chunks, HV, 64, 64]  T' = (I + A)^-1 diag(beta), fp32
-    // MFMA path (same memory as ws_T): T' as hi + lo bf16 planes
-    uint16_t* ws_Th;     // [max_chunks, HV, 64, 64]
-    uint16_t* ws_Tl;
+    // MFMA path (same memory as ws_T), each as hi + lo bf16 planes:
+    //   R  = P T'                          [max_chunks, HV, 64, 64]   (row t, column c)
+    //   Zt = K^T diag(e^{G_n - G}) T'      [max_chunks, HV, dk, 64]   (row j, column c)
+    uint16_t* ws_Rh;
+    uint16_t* ws_Rl;
+    uint16_t* ws_Zh;
+    uint16_t* ws_Zl;
     int max_chunks;
     hipStream_t stream;
 };
@@ -73,7 +77,7 @@ struct NormArgs {
 
 // Workspace layout of gdn_prefill_chunked (byte offsets, 256-aligned).
 struct PrefillLayout {
-    size_t chunk_off, ws_G, ws_T, ws_Th, ws_Tl, total;
+    size_t chunk_off, ws_G, ws_T, ws_Rh, ws_Rl, ws_Zh, ws_Zl, total;
     int max_chunks;
 };
 PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk);

@@ -62,6 +62,19 @@ __device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t off
     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)(off * 2), 0, 0);
 }
 
+__device__ __forceinline__ void out_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v, float*) {
+    typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+    const u4_t d = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, (int)(off * 4), 0, 0);
+}
+__device__ __forceinline__ void out_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v, bf16_t*) {
+    typedef unsigned u2_t __attribute__((ext_vector_type(2)));
+    const u2_t d = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)(off * 2), 0, 0);
+}
+
 __device__ __forceinline__ bf8_t zero8() { return __builtin_bit_cast(bf8_t, make_uint4(0, 0, 0, 0)); }
 
 // exponentials of log-decay differences: G is kept in log2 units (g log2 e),
@@ -125,23 +138,42 @@ __device__ __forceinline__ int find_seq_m(const int32_t* chunk_off, int N, int c
 // prep: everything that does not depend on the state, chunk-parallel
 // ---------------------------------------------------------------------------
 // One workgroup (4 wavefronts) per (chunk, key head).  Wave w owns row block
-// w (tokens 16 w .. 16 w + 15) of K K^T.  Outputs per value head: T' as hi/lo
-// bf16 row-major 64 x 64 tiles (zeros above the diagonal and in rows /
-// columns past the sequence end) and G.
+// w (tokens 16 w .. 16 w + 15).  Per value head of the key head it produces
+//   G   in-chunk cumulative log-decay (log2 units)
+//   R   = P T'                          64 x 64, row t, column c   (hi / lo bf16)
+//   Z^T = K^T diag(e^{G_n - G}) T'      dk x 64, row j, column c   (hi / lo bf16)
+// with P = lower(Q K^T o Gamma) and T' = (I + A)^-1 diag(b), so that the scan
+// only needs O = scale (diag(gamma) Q S^T + R X) and S' = gamma_n S + Z^T X.
+// Rows and columns past the sequence end come out as exact zeros (K, Q and b
+// read as zero there, so T' vanishes outside the valid block).  R and Z^T are
+// stored in the scan's operand order: fragment f of a 64 x 64 (or dk x 64)
+// plane is 1 KiB, lane l of the consuming wavefront reads bytes 16 l .. 16 l + 15,
+// which hold row 16 (f / 2) + l % 16, columns 32 (f % 2) + 8 (l / 16) .. + 7.
+constexpr int kMaxRatio = 4;  // value heads per key head handled by this kernel
+
 template <int DK>
 __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
-    constexpr int KP = DK + 8;  // padded bf16 row
-    constexpr int AP = C + 4;   // padded fp32 row (16-byte aligned rows)
+    constexpr int KP = DK + 8;   // padded bf16 row of the K and Q tiles
+    constexpr int AP = C + 4;    // padded fp32 row (16-byte aligned rows)
+    constexpr int NKK = DK / 32;
+    constexpr int PPR = DK / 8;         // 16-byte pieces per row
+    constexpr int RPI = 64 / PPR;       // rows per coalesced 1 KiB load
+    constexpr int NLD = 16 / RPI;       // loads per wavefront per tile
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) float Am[C * AP];
-    __shared__ __attribute__((aligned(16))) float Tm[C * AP];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * KP];
+    __shared__ __attribute__((aligned(16))) float Am[C * AP];  // A, then T'^T
+    __shared__ __attribute__((aligned(16))) float Tm[C * AP];  // T = (I + A)^-1
     __shared__ __attribute__((aligned(16))) float Xm[32 * 36];
-    __shared__ float Gs[C], Bs[C];
+    __shared__ __attribute__((aligned(16))) float Gs[kMaxRatio][C];
+    __shared__ float Bs[kMaxRatio][C];
+    __shared__ __attribute__((aligned(16))) float Ds[kMaxRatio][C];
 
     const int H = A.H, HV = A.HV;
     const int c = blockIdx.x, hk = blockIdx.y, tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(w >= 0 && w < 4);
+    const int l = tid & 63, lr = l & 15, lg = l >> 4;
     const int total = min(A.chunk_off[A.N], A.max_chunks);
     if (c >= total) return;
     const int n = find_seq_m(A.chunk_off, A.N, c);
@@ -150,62 +182,98 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     const int t0 = s0 + (c - A.chunk_off[n]) * C;
     const int L = min(C, e0 - t0);
     const int ratio = HV / H;
-    const bf16_t* k = static_cast<const bf16_t*>(A.k);
+    const int hv0 = hk * ratio;
 
-    // K chunk -> LDS (rows past the sequence end are zero)
-    for (int idx = tid; idx < C * DK / 8; idx += 256) {
-        const int t = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-        const size_t off = ((size_t)(t0 + min(t, L - 1)) * H + hk) * DK + c8;
-        uint4 kv = *reinterpret_cast<const uint4*>(k + off);
-        if (t >= L) kv = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&Ks[t * KP + c8]) = kv;
+    // ---- every global load first: K and Q rows of this wave (coalesced), g and b ----
+    const uint32_t qk_row = (uint32_t)H * DK * 2;
+    const __amdgpu_buffer_rsrc_t rk =
+        in_rsrc(static_cast<const bf16_t*>(A.k) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
+    const __amdgpu_buffer_rsrc_t rq =
+        in_rsrc(static_cast<const bf16_t*>(A.q) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
+    bf8_t kst[NLD], qst[NLD];
+#pragma unroll
+    for (int p = 0; p < NLD; ++p) {
+        const int row = 16 * w + RPI * p + l / PPR;
+        const uint32_t off = ((uint32_t)row * H + hk) * DK * 2 + 16 * (l % PPR);
+        kst[p] = bload8(rk, off);
+        qst[p] = bload8(rq, off);
+    }
+    // wave w < ratio: g and b of value head hv0 + w for token l (zero past the end)
+    float gv = 0.f, bv = 0.f;
+    if (w < ratio) {
+        const __amdgpu_buffer_rsrc_t rg = in_rsrc(A.g + (size_t)t0 * HV, (uint32_t)L * HV * 4);
+        const __amdgpu_buffer_rsrc_t rb = in_rsrc(A.beta + (size_t)t0 * HV, (uint32_t)L * HV * 4);
+        gv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (int)((l * HV + hv0 + w) * 4), 0, 0));
+        bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)((l * HV + hv0 + w) * 4), 0, 0));
+    }
+#pragma unroll
+    for (int p = 0; p < NLD; ++p) {
+        const int at = (16 * w + RPI * p + l / PPR) * KP + 8 * (l % PPR);
+        *reinterpret_cast<bf8_t*>(&Ks[at]) = kst[p];
+        *reinterpret_cast<bf8_t*>(&Qs[at]) = qst[p];
+    }
+    // G (log2 units, inclusive in-chunk prefix sum), b and the end decays e^{G_n - G}
+    if (w < ratio) {
+        float gs = gv * kLog2e;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_up(gs, off, 64);
+            if (l >= off) gs += up;
+        }
+        const float gn = __shfl(gs, L - 1, 64);
+        Gs[w][l] = gs;
+        Bs[w][l] = bv;
+        Ds[w][l] = exp2f_(gn - gs);
+        A.ws_G[((size_t)c * HV + hv0 + w) * C + l] = gs;
     }
     __syncthreads();
 
-    // K K^T (row block w, column blocks sb <= w)
-    f4_t kk[4];
+    // K K^T (row block w against column blocks sb <= w) and the raw P^T tiles
+    //   kk[sb][r] = (K K^T)[t = 16 w + 4 lg + r][s = 16 sb + lr]
+    //   pq[sb][r] = (Q K^T)[t = 16 w + lr][s = 16 sb + 4 lg + r]
+    f4_t kk[4], pq[4];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) kk[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < 4; ++sb) {
+        kk[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+        pq[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
+    for (int ks = 0; ks < NKK; ++ks) {
         const int col = 32 * ks + 8 * lg;
+        bf8_t kb[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) kb[sb] = lds8(&Ks[(16 * sb + lr) * KP + col]);
         const bf8_t ka = lds8(&Ks[(16 * w + lr) * KP + col]);
+        const bf8_t qa = lds8(&Qs[(16 * w + lr) * KP + col]);
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             if (sb <= w) {
-                const bf8_t kb = lds8(&Ks[(16 * sb + lr) * KP + col]);
-                kk[sb] = mfma(ka, kb, kk[sb]);
+                kk[sb] = mfma(ka, kb[sb], kk[sb]);
+                pq[sb] = mfma(kb[sb], qa, pq[sb]);
             }
         }
     }
-    // kk[sb][r] = (K K^T)[t = 16 w + 4 lg + r][s = 16 sb + lr]
-
-    for (int hv = hk * ratio; hv < (hk + 1) * ratio; ++hv) {
-        const size_t tileoff = ((size_t)c * HV + hv) * C * C;
-        // G = in-chunk inclusive cumsum of g (wave 0), beta
-        if (w == 0) {
-            float gv = A.g[(size_t)(t0 + min(l, L - 1)) * HV + hv] * kLog2e;
-            float bv = A.beta[(size_t)(t0 + min(l, L - 1)) * HV + hv];
-            if (l >= L) gv = 0.f, bv = 0.f;
+    // selectors for K^T fragments: (K I)[s][j] picks column j of K exactly;
+    // sel[h] holds the 32 x 16 identity block for the column half h of a k-step
+    bf8_t sel[2];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(gv, off, 64);
-                if (l >= off) gv += up;
-            }
-            Gs[l] = gv;
-            Bs[l] = bv;
-            A.ws_G[((size_t)c * HV + hv) * C + l] = gv;
-        }
-        __syncthreads();
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int y = 0; y < 8; ++y)
+            sel[h][y] = static_cast<__bf16>((8 * lg + y == 16 * h + lr) ? 1.f : 0.f);
+
+    for (int i = 0; i < ratio; ++i) {
+        const int hv = hv0 + i;
+        const float* G = Gs[i];
         // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s})
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             if (sb <= w) {
-                const float Gsb = Gs[16 * sb + lr];
+                const float Gsb = G[16 * sb + lr];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * w + 4 * lg + r, s = 16 * sb + lr;
-                    Am[t * AP + s] = (s < t) ? Bs[t] * exp2f_(Gs[t] - Gsb) * kk[sb][r] : 0.f;
+                    Am[t * AP + s] = (s < t) ? Bs[i][t] * exp2f_(G[t] - Gsb) * kk[sb][r] : 0.f;
                 }
             }
         }
@@ -239,12 +307,12 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int e = tid + 256 * half;
-            const int j = (e >> 8) * 2, i = j + 1;  // (1,0) or (3,2)
+            const int j = (e >> 8) * 2, ii = j + 1;  // (1,0) or (3,2)
             const int rho = (e >> 4) & 15, kap = e & 15;
             float acc = 0.f;
 #pragma unroll
             for (int x = 0; x < 16; ++x)
-                acc += (x >= kap) ? Am[(16 * i + rho) * AP + 16 * j + x] *
+                acc += (x >= kap) ? Am[(16 * ii + rho) * AP + 16 * j + x] *
                                         Tm[(16 * j + x) * AP + 16 * j + kap]
                                   : 0.f;
             Xm[(16 * (e >> 8) + rho) * 36 + kap] = acc;
@@ -253,72 +321,175 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int e = tid + 256 * half;
-            const int j = (e >> 8) * 2, i = j + 1;
+            const int j = (e >> 8) * 2, ii = j + 1;
             const int rho = (e >> 4) & 15, kap = e & 15;
             float acc = 0.f;
 #pragma unroll
             for (int x = 0; x < 16; ++x)
-                acc += (x <= rho) ? Tm[(16 * i + rho) * AP + 16 * i + x] *
+                acc += (x <= rho) ? Tm[(16 * ii + rho) * AP + 16 * ii + x] *
                                         Xm[(16 * (e >> 8) + x) * 36 + kap]
                                   : 0.f;
-            Tm[(16 * i + rho) * AP + 16 * j + kap] = -acc;
+            Tm[(16 * ii + rho) * AP + 16 * j + kap] = -acc;
         }
         __syncthreads();
         // 32-block merge on MFMA: X = A[32:64, 0:32] T[0:32, 0:32]; T[32:64, 0:32] = -T_B X
         {
-            const int tb = w >> 1, jb = w & 1;
-            float av[8], bv[8];
+            const int tbm = w >> 1, jb = w & 1;
+            float av[8], bv8[8];
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
-                av[x] = Am[(32 + 16 * tb + lr) * AP + 8 * lg + x];
+                av[x] = Am[(32 + 16 * tbm + lr) * AP + 8 * lg + x];
                 const int xr = 8 * lg + x, cc = 16 * jb + lr;
-                bv[x] = (xr >= cc) ? Tm[xr * AP + cc] : 0.f;
+                bv8[x] = (xr >= cc) ? Tm[xr * AP + cc] : 0.f;
             }
             bf8_t ah, al, bh, bl;
             split8(av, ah, al);
-            split8(bv, bh, bl);
+            split8(bv8, bh, bl);
             f4_t xa = f4_t{0.f, 0.f, 0.f, 0.f};
             xa = mfma(ah, bh, xa);
             xa = mfma(ah, bl, xa);
             xa = mfma(al, bh, xa);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Xm[(16 * tb + 4 * lg + r) * 36 + 16 * jb + lr] = xa[r];
+            for (int r = 0; r < 4; ++r) Xm[(16 * tbm + 4 * lg + r) * 36 + 16 * jb + lr] = xa[r];
         }
         __syncthreads();
         {
-            const int tb = w >> 1, jb = w & 1;
-            float av[8], bv[8];
+            const int tbm = w >> 1, jb = w & 1;
+            float av[8], bv8[8];
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
-                const int rr = 16 * tb + lr, xc = 8 * lg + x;  // T_B row rr, column xc (lower)
+                const int rr = 16 * tbm + lr, xc = 8 * lg + x;  // T_B row rr, column xc (lower)
                 av[x] = (xc <= rr) ? Tm[(32 + rr) * AP + 32 + xc] : 0.f;
-                bv[x] = Xm[(8 * lg + x) * 36 + 16 * jb + lr];
+                bv8[x] = Xm[(8 * lg + x) * 36 + 16 * jb + lr];
             }
             bf8_t ah, al, bh, bl;
             split8(av, ah, al);
-            split8(bv, bh, bl);
+            split8(bv8, bh, bl);
             f4_t ta = f4_t{0.f, 0.f, 0.f, 0.f};
             ta = mfma(ah, bh, ta);
             ta = mfma(ah, bl, ta);
             ta = mfma(al, bh, ta);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Tm[(32 + 16 * tb + 4 * lg + r) * AP + 16 * jb + lr] = -ta[r];
+                Tm[(32 + 16 * tbm + 4 * lg + r) * AP + 16 * jb + lr] = -ta[r];
         }
         __syncthreads();
-        // T' = T diag(b) (lower triangle; zeros above) as hi / lo
+        // T'^T[c][s] = T[s][c] b_c (zero for s < c) into Am: thread row s, columns c4 .. c4 + 3
         for (int idx = tid; idx < C * C / 4; idx += 256) {
-            const int t = idx >> 4, s4 = 4 * (idx & 15);
-            float tv[4];
+            const int s_ = idx & 63, c4 = 4 * (idx >> 6);
+            const float4 t4 = *reinterpret_cast<const float4*>(&Tm[s_ * AP + c4]);
+            const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                tv[r] = (s4 + r <= t) ? Tm[t * AP + s4 + r] * Bs[s4 + r] : 0.f;
-            uint2 hi, lo;
-            split4(tv, hi, lo);
-            *reinterpret_cast<uint2*>(A.ws_Th + tileoff + t * C + s4) = hi;
-            *reinterpret_cast<uint2*>(A.ws_Tl + tileoff + t * C + s4) = lo;
+                Am[(c4 + r) * AP + s_] = (s_ >= c4 + r) ? tv[r] * Bs[i][c4 + r] : 0.f;
         }
         __syncthreads();
+
+        // R^T tiles (c block cb, t block w) = T'^T P^T: A = T'^T rows in the slot
+        // order of the P^T fragments, B = decayed and masked P^T (this wave's t)
+        {
+            const size_t rbase = ((size_t)c * HV + hv) * C * C;
+            const int t = 16 * w + lr;
+            const float Gt = G[t];
+            bf8_t ph[2], pl[2];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                float pv[8];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int sb = 2 * k2 + half;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int s_ = 16 * sb + 4 * lg + r;
+                        pv[4 * half + r] = (s_ <= t) ? pq[sb][r] * exp2f_(Gt - G[s_]) : 0.f;
+                    }
+                }
+                split8(pv, ph[k2], pl[k2]);
+            }
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                f4_t ra = f4_t{0.f, 0.f, 0.f, 0.f};
+                if (cb <= w) {
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2) {
+                        if (2 * k2 <= w) {
+                            const float* arow = &Am[(16 * cb + lr) * AP + 32 * k2 + 4 * lg];
+                            const float4 a0 = *reinterpret_cast<const float4*>(arow);
+                            const float4 a1 = *reinterpret_cast<const float4*>(arow + 16);
+                            const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                            bf8_t ah, al;
+                            split8(av, ah, al);
+                            ra = mfma(ah, ph[k2], ra);
+                            ra = mfma(ah, pl[k2], ra);
+                            ra = mfma(al, ph[k2], ra);
+                        }
+                    }
+                }
+                // ra[r] = R[t = 16 w + lr][c = 16 cb + 4 lg + r]: fragment (w, cb / 2),
+                // lane 16 (2 (cb & 1) + lg / 2) + lr, elements 4 (lg & 1) .. + 3
+                const float rv[4] = {ra[0], ra[1], ra[2], ra[3]};
+                uint2 hi, lo;
+                split4(rv, hi, lo);
+                const size_t off = rbase + (size_t)((2 * w + (cb >> 1)) * 64 +
+                                                    16 * (2 * (cb & 1) + (lg >> 1)) + lr) * 8 +
+                                   4 * (lg & 1);
+                *reinterpret_cast<uint2*>(A.ws_Rh + off) = hi;
+                *reinterpret_cast<uint2*>(A.ws_Rl + off) = lo;
+            }
+        }
+        // Z tiles (c block w, j block jb) = (T'^T diag(e^{G_n - G})) K with the
+        // contraction over s in the slot order s = 32 k2 + 4 lg + (0..3) and
+        // 32 k2 + 16 + 4 lg + (0..3); the K operand in that order comes from
+        // selection products (K I) of two K row blocks.  T'^T row 16 w + lr is zero
+        // before column 16 w, so k-steps start at w / 2.
+        {
+            const size_t zbase = ((size_t)c * HV + hv) * DK * C;
+            bf8_t ah[2], al[2];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const float* arow = &Am[(16 * w + lr) * AP + 32 * k2 + 4 * lg];
+                const float* drow = &Ds[i][32 * k2 + 4 * lg];
+                const float4 a0 = *reinterpret_cast<const float4*>(arow);
+                const float4 a1 = *reinterpret_cast<const float4*>(arow + 16);
+                const float4 d0 = *reinterpret_cast<const float4*>(drow);
+                const float4 d1 = *reinterpret_cast<const float4*>(drow + 16);
+                const float av[8] = {a0.x * d0.x, a0.y * d0.y, a0.z * d0.z, a0.w * d0.w,
+                                     a1.x * d1.x, a1.y * d1.y, a1.z * d1.z, a1.w * d1.w};
+                split8(av, ah[k2], al[k2]);
+            }
+#pragma unroll
+            for (int jb = 0; jb < DK / 16; ++jb) {
+                f4_t za = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    if (k2 >= (w >> 1)) {
+                        bf8_t kb;
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const int sb = 2 * k2 + half;
+                            const bf8_t krow = lds8(&Ks[(16 * sb + lr) * KP + 32 * (jb >> 1) + 8 * lg]);
+                            // tr[r] = K[16 sb + 4 lg + r][16 jb + lr] (exact)
+                            const f4_t tr = mfma(krow, sel[jb & 1], f4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) kb[4 * half + r] = static_cast<__bf16>(tr[r]);
+                        }
+                        za = mfma(ah[k2], kb, za);
+                        za = mfma(al[k2], kb, za);
+                    }
+                }
+                // za[r] = Z[c = 16 w + 4 lg + r][j = 16 jb + lr] = Z^T[j][c]: fragment
+                // (jb, w / 2), lane 16 (2 (w & 1) + lg / 2) + lr, elements 4 (lg & 1) .. + 3
+                const float zv[4] = {za[0], za[1], za[2], za[3]};
+                uint2 hi, lo;
+                split4(zv, hi, lo);
+                const size_t off = zbase + (size_t)((2 * jb + (w >> 1)) * 64 +
+                                                    16 * (2 * (w & 1) + (lg >> 1)) + lr) * 8 +
+                                   4 * (lg & 1);
+                *reinterpret_cast<uint2*>(A.ws_Zh + off) = hi;
+                *reinterpret_cast<uint2*>(A.ws_Zl + off) = lo;
+            }
+        }
+        __syncthreads();  // Am and Tm are rewritten for the next value head
     }
 }
 
@@ -326,32 +497,30 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
 // scan: sequential over chunks, state tile in MFMA accumulators
 // ---------------------------------------------------------------------------
 // 4 wavefronts, one per SIMD.  Wave w owns the chunk's row block tb = w
-// (tokens 16 w .. 16 w + 15) in K S^T, Q S^T, P, X, U and O for both 16-column
+// (tokens 16 w .. 16 w + 15) of K S^T, Q S^T, X and O for both 16-column
 // halves ib = 0, 1 of the state tile's 32 rows, and the state tiles
 // S^T[16 jb .. +15][16 ibS .. +15] for its DK/64 column blocks jb.
-// Per chunk:
-//   (A) K S^T, Q S^T, P^T = K Q^T (row block tb against column blocks <= tb);
-//       X = V - diag(gamma) K S^T -> LDS
-//   (B) U = T' X; U and U' -> LDS
-//   (C) O = gamma Q S^T + P U to memory, with P taken straight from the P^T
-//       accumulators (the contraction slots are ordered so that a lane's four
-//       accumulator values of two P^T tiles are its eight A-operand values,
-//       and U is read in the same order); S' = gamma_n S + K^T U' -> LDS;
-//       the next chunk's K rows and G go to the other half of a double buffer.
-// Operand fragments from memory (K, Q rows, G, V, T') are held in one register
-// set: each group is reloaded for the next chunk right after its last use, so
-// every load has about a chunk to arrive.  Loads go through buffer resources
+// Per chunk, one exchange through LDS:
+//   (A) K S^T, Q S^T from the state tile in LDS; X = V - diag(gamma) K S^T -> LDS
+//   (B) O = scale (diag(gamma) Q S^T + R X) to memory (computed transposed,
+//       so that each lane stores 16 contiguous bytes); S' = gamma_n S + Z^T X
+//       in the accumulators; S' -> LDS as hi / lo for the next chunk
+// Memory traffic is shaped for the vector-memory pipeline, which costs about
+// one cycle per touched 128-byte line and so dominates once the products are
+// cheap: R and Z^T arrive in operand order (one coalesced 1 KiB load per
+// fragment); K and Q rows of a wave's row block are loaded as whole lines into
+// that wave's own LDS area one chunk ahead and read back as fragments (only
+// the wave itself touches the area, so no barrier is involved).  Every group
+// is reloaded right after its last use.  Loads go through buffer resources
 // that end at the chunk's last valid row: rows past a sequence end read as
-// zero, which masks K, Q, V, X and U without selects, and output rows past
-// the end are dropped by the store's resource.  No branch surrounds a memory
-// operation whose count differs between paths, so the compiler waits for
-// exactly the group it needs.
+// zero, which masks K, Q, V and X without selects, and output rows past the
+// end are dropped by the store's resource.
 template <int DK, typename Tout>
 __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
     constexpr int BV = 32;
-    constexpr int KP = DK + 8;   // padded row of S and K (bf16)
-    constexpr int TP = C + 8;    // padded row of the [*, C] tiles (bf16)
+    constexpr int KP = DK + 8;   // padded row of the state tile (bf16)
+    constexpr int TP = C + 8;    // padded row of the X tile (bf16)
     constexpr int NKK = DK / 32;
     constexpr int NJB = DK / 64;  // state column blocks per wave
 
@@ -359,12 +528,11 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     __shared__ __attribute__((aligned(16))) __bf16 Sl[BV * KP];
     __shared__ __attribute__((aligned(16))) __bf16 Xh[BV * TP];
     __shared__ __attribute__((aligned(16))) __bf16 Xl[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Uh[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Ul[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Wh[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Wl[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C * KP];
-    __shared__ __attribute__((aligned(16))) float Gs[2][C];
+    __shared__ __attribute__((aligned(16))) __bf16 Kw[4][16 * KP];  // per-wave K rows
+    __shared__ __attribute__((aligned(16))) __bf16 Qw[4][16 * KP];  // per-wave Q rows
+    constexpr int PPR = DK / 8;    // 16-byte pieces per K / Q row
+    constexpr int RPI = 64 / PPR;  // rows per coalesced 1 KiB load
+    constexpr int NLD = 16 / RPI;  // loads per row block and tile
 
     const int H = A.H, HV = A.HV, dv = A.dv, N = A.N;
     const int tid = threadIdx.x;
@@ -435,37 +603,57 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
         return;
     }
 
-    // byte offsets of this lane's fragments inside a chunk (the same for every chunk)
+    // byte offsets of this lane's data inside a chunk (the same for every chunk)
     const uint32_t qk_row = (uint32_t)H * DK * 2;  // bytes per token of q, k
     const uint32_t v_row = (uint32_t)HV * dv * 2;  // bytes per token of v
-    const uint32_t kq_off = ((uint32_t)(16 * tb + lr) * H + hk) * DK * 2 + 16 * lg;
+    uint32_t kq_off[NLD];                          // coalesced rows of the row block
+#pragma unroll
+    for (int p = 0; p < NLD; ++p)
+        kq_off[p] = ((uint32_t)(16 * tb + RPI * p + l / PPR) * H + hk) * DK * 2 + 16 * (l % PPR);
     uint32_t v_off[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
         v_off[r] = ((uint32_t)(16 * tb + 4 * lg + r) * HV + h) * dv * 2 + (tile * BV + lr) * 2;
-    const uint32_t t_off = ((16 * tb + lr) * C + 8 * lg) * 2;
+    const uint32_t r_off = (2 * tb * 64 + l) * 16;  // fragment (tb, kk): + 1 KiB kk
+    uint32_t z_off[NJB];                             // fragment (jb, kk): + 1 KiB kk
+#pragma unroll
+    for (int x = 0; x < NJB; ++x) z_off[x] = (2 * (NJB * tb + x) * 64 + l) * 16;
 
-    // ---- operand fragments (one set; groups reloaded after their last use) ----
-    bf8_t kA[NKK], qA[NKK];      // K, Q row 16 tb + lr, k-step kk
-    bf8_t tH[2], tL[2];          // T' row 16 tb + lr, columns 32 kk + 8 lg ..
-    uint32_t vr[2][4];           // V[t = 16 tb + 4 lg + r][i = 16 ib + lr], raw bf16 bits
-    float4 gR;                   // G[16 tb + 4 lg + r]  (log2 units)
-    float gN;                    // G[L - 1]
+    // ---- operand data (one set; groups reloaded after their last use) ----
+    bf8_t kst[NLD], qst[NLD];      // K, Q rows of the next chunk, as loaded
+    bf8_t rH[2], rL[2];            // R fragments of row block tb
+    bf8_t zH[NJB][2], zL[NJB][2];  // Z^T fragments of column blocks NJB tb + x
+    uint32_t vr[2][4];             // V[t = 16 tb + 4 lg + r][i = 16 ib + lr], raw bf16 bits
+    float4 gR;                     // G[16 tb + 4 lg + r]  (log2 units)
+    float gT;                      // G[16 tb + lr]
+    float gN;                      // G[L - 1]
 
     auto chunk_t0 = [&](int jc) { return sq + jc * C; };
     auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
-    auto load_kq_g = [&](int jc) {
+    auto load_kq = [&](int jc) {
         const int t0 = chunk_t0(jc), L = chunk_L(jc);
         const __amdgpu_buffer_rsrc_t rk = in_rsrc(kp + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
         const __amdgpu_buffer_rsrc_t rq = in_rsrc(qp + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            kA[kk] = bload8(rk, kq_off + 64 * kk);
-            qA[kk] = bload8(rq, kq_off + 64 * kk);
+        for (int p = 0; p < NLD; ++p) {
+            kst[p] = bload8(rk, kq_off[p]);
+            qst[p] = bload8(rq, kq_off[p]);
         }
+    };
+    // loaded rows -> this wave's LDS area (after its fragment reads of the previous chunk)
+    auto stage_kq = [&]() {
+#pragma unroll
+        for (int p = 0; p < NLD; ++p) {
+            const int at = (RPI * p + l / PPR) * KP + 8 * (l % PPR);
+            *reinterpret_cast<bf8_t*>(&Kw[tb][at]) = kst[p];
+            *reinterpret_cast<bf8_t*>(&Qw[tb][at]) = qst[p];
+        }
+    };
+    auto load_g = [&](int jc) {
         const float* G = A.ws_G + ((size_t)(c_first + jc) * HV + h) * C;
         gR = *reinterpret_cast<const float4*>(G + 16 * tb + 4 * lg);
-        gN = G[L - 1];
+        gT = G[16 * tb + lr];
+        gN = G[chunk_L(jc) - 1];
     };
     auto load_v = [&](int jc) {
         const int t0 = chunk_t0(jc), L = chunk_L(jc);
@@ -476,71 +664,95 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
             for (int r = 0; r < 4; ++r)
                 vr[ib][r] = __builtin_amdgcn_raw_buffer_load_b16(rv, (int)(v_off[r] + 32 * ib), 0, 0);
     };
-    auto load_t = [&](int jc) {
-        const size_t tt = ((size_t)(c_first + jc) * HV + h) * C * C;
-        const __amdgpu_buffer_rsrc_t rh = in_rsrc(A.ws_Th + tt, C * C * 2);
-        const __amdgpu_buffer_rsrc_t rl = in_rsrc(A.ws_Tl + tt, C * C * 2);
+    auto load_rz = [&](int jc) {
+        const size_t cc = (size_t)(c_first + jc) * HV + h;
+        const __amdgpu_buffer_rsrc_t rh = in_rsrc(A.ws_Rh + cc * C * C, C * C * 2);
+        const __amdgpu_buffer_rsrc_t rl = in_rsrc(A.ws_Rl + cc * C * C, C * C * 2);
+        const __amdgpu_buffer_rsrc_t zh = in_rsrc(A.ws_Zh + cc * DK * C, DK * C * 2);
+        const __amdgpu_buffer_rsrc_t zl = in_rsrc(A.ws_Zl + cc * DK * C, DK * C * 2);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            tH[kk] = bload8(rh, t_off + 64 * kk);
-            tL[kk] = bload8(rl, t_off + 64 * kk);
+            rH[kk] = bload8(rh, r_off + 1024 * kk);
+            rL[kk] = bload8(rl, r_off + 1024 * kk);
+#pragma unroll
+            for (int x = 0; x < NJB; ++x) {
+                zH[x][kk] = bload8(zh, z_off[x] + 1024 * kk);
+                zL[x][kk] = bload8(zl, z_off[x] + 1024 * kk);
+            }
         }
     };
-    // K rows of row block tb and G of the chunk whose fragments are loaded -> LDS
-    auto stage_k_g = [&](int buf) {
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-            *reinterpret_cast<bf8_t*>(&Ks[buf][(16 * tb + lr) * KP + 32 * kk + 8 * lg]) = kA[kk];
-        if (lr == 0) *reinterpret_cast<float4*>(&Gs[buf][16 * tb + 4 * lg]) = gR;
-    };
 
-    load_kq_g(0);
+    load_kq(0);
+    stage_kq();
+    load_kq(min(1, nch - 1));
+    load_g(0);
     load_v(0);
-    load_t(0);
+    load_rz(0);
     store_state_lds();
-    stage_k_g(0);
     __syncthreads();
 
     for (int jc = 0; jc < nch; ++jc) {
-        const int nj = min(jc + 1, nch - 1);  // the last chunk re-reads itself
-        const int buf = jc & 1;
-        const __bf16* Kc = Ks[buf];
-        const float* Gc = Gs[buf];
+        const int nj = min(jc + 1, nch - 1);   // the last chunk re-reads itself
+        const int nj2 = min(jc + 2, nch - 1);
         const int t0 = chunk_t0(jc);
         const int L = chunk_L(jc);
+        // decays of this chunk, taken before the next chunk's G overwrites them
         const float gr[4] = {gR.x, gR.y, gR.z, gR.w};
-        const float gNc = gN;
+        float gn = exp2f_(gN);
+        float gt = exp2f_(gT);
         float gam[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) gam[r] = exp2f_(gr[r]);
+        // keep the exponentials here: computed at their use, they would hold
+        // the old G live across its reload and stall on the new load
+        asm volatile("" : "+v"(gn), "+v"(gt), "+v"(gam[0]), "+v"(gam[1]), "+v"(gam[2]),
+                     "+v"(gam[3]));
 
-        // (A) K S^T, Q S^T (row block tb, both column halves) and P^T tiles
-        f4_t ksa[2], qsa[2], pa[4];
+        // (A) K S^T, Q S^T for row block tb, both column halves; the state
+        // fragments of two k-steps are read before their products
+        bf8_t kA[NKK], qA[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            kA[kk] = lds8(&Kw[tb][lr * KP + 32 * kk + 8 * lg]);
+            qA[kk] = lds8(&Qw[tb][lr * KP + 32 * kk + 8 * lg]);
+        }
+        // the next chunk's rows replace them (same wavefront, after the reads)
+        stage_kq();
+        load_kq(nj2);
+        f4_t ksa[2], qsa[2];
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             ksa[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
             qsa[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) pa[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int k2 = 0; k2 < NKK; k2 += 2) {
+            bf8_t sh[2][2], sl[2][2];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const int col = 32 * kk + 8 * lg;
+            for (int u = 0; u < 2; ++u) {
+                const int col = 32 * (k2 + u) + 8 * lg;
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const bf8_t bh = lds8(&Sh[(16 * ib + lr) * KP + col]);
-                const bf8_t bl = lds8(&Sl[(16 * ib + lr) * KP + col]);
-                ksa[ib] = mfma(kA[kk], bh, ksa[ib]);
-                qsa[ib] = mfma(qA[kk], bh, qsa[ib]);
-                ksa[ib] = mfma(kA[kk], bl, ksa[ib]);
-                qsa[ib] = mfma(qA[kk], bl, qsa[ib]);
+                for (int ib = 0; ib < 2; ++ib) {
+                    sh[u][ib] = lds8(&Sh[(16 * ib + lr) * KP + col]);
+                    sl[u][ib] = lds8(&Sl[(16 * ib + lr) * KP + col]);
+                }
             }
-            // pa[sb][r] = (Q K^T)[t = 16 tb + lr][s = 16 sb + 4 lg + r]
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb)
-                if (sb <= tb) pa[sb] = mfma(lds8(&Kc[(16 * sb + lr) * KP + col]), qA[kk], pa[sb]);
+            for (int u = 0; u < 2; ++u) {
+                const int kk = k2 + u;
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    ksa[ib] = mfma(kA[kk], sh[u][ib], ksa[ib]);
+                    qsa[ib] = mfma(sh[u][ib], qA[kk], qsa[ib]);
+                }
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    ksa[ib] = mfma(kA[kk], sl[u][ib], ksa[ib]);
+                    qsa[ib] = mfma(sl[u][ib], qA[kk], qsa[ib]);
+                }
+            }
         }
-        load_kq_g(nj);
+        load_g(nj);
         float vf[2][4];
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
@@ -559,152 +771,66 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
             *reinterpret_cast<uint2*>(&Xh[off]) = hi;
             *reinterpret_cast<uint2*>(&Xl[off]) = lo;
         }
-        // P = P^T values masked to s <= t and decayed, split into hi / lo: the
-        // A operand of k-step kk holds s = 32 kk + 4 lg + (0..3) from tile 2 kk
-        // and s = 32 kk + 16 + 4 lg + (0..3) from tile 2 kk + 1.  Tiles below
-        // the diagonal block need no mask; tiles above it are zero.
-        uint4 pHw[2], pLw[2];
-        {
-            const int t = 16 * tb + lr;
-            const float Gt = Gc[t];
-            float pv[4][4];
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * sb + 4 * lg]);
-                const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
-                if (sb < tb) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) pv[sb][r] = pa[sb][r] * exp2f_(Gt - gs[r]);
-                } else if (sb == tb) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        pv[sb][r] = (4 * lg + r <= lr) ? pa[sb][r] * exp2f_(Gt - gs[r]) : 0.f;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) pv[sb][r] = 0.f;
-                }
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                split2(pv[2 * kk][0], pv[2 * kk][1], pHw[kk].x, pLw[kk].x);
-                split2(pv[2 * kk][2], pv[2 * kk][3], pHw[kk].y, pLw[kk].y);
-                split2(pv[2 * kk + 1][0], pv[2 * kk + 1][1], pHw[kk].z, pLw[kk].z);
-                split2(pv[2 * kk + 1][2], pv[2 * kk + 1][3], pHw[kk].w, pLw[kk].w);
-            }
-        }
         __syncthreads();
 
-        // (B) U = T' X for row block tb (T' is lower triangular: k-steps up to tb / 2)
-        f4_t ua[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
+        // (B) X fragments (token k-steps kk, state-row halves ib) serve both products
+        bf8_t xh[2][2], xl[2][2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (kk <= (tb >> 1)) {
-                const int col = 32 * kk + 8 * lg;
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const bf8_t bh = lds8(&Xh[(16 * ib + lr) * TP + col]);
-                    const bf8_t bl = lds8(&Xl[(16 * ib + lr) * TP + col]);
-                    ua[ib] = mfma(tH[kk], bh, ua[ib]);
-                    ua[ib] = mfma(tH[kk], bl, ua[ib]);
-                    ua[ib] = mfma(tL[kk], bh, ua[ib]);
-                }
-            }
-        }
-        load_t(nj);
-        {
-            float dec[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dec[r] = exp2f_(gNc - gr[r]);
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
-                float uv[4], wv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uv[r] = ua[ib][r];
-                    wv[r] = ua[ib][r] * dec[r];
-                }
-                uint2 hi, lo;
-                const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
-                split4(uv, hi, lo);
-                *reinterpret_cast<uint2*>(&Uh[off]) = hi;
-                *reinterpret_cast<uint2*>(&Ul[off]) = lo;
-                split4(wv, hi, lo);
-                *reinterpret_cast<uint2*>(&Wh[off]) = hi;
-                *reinterpret_cast<uint2*>(&Wl[off]) = lo;
+                xh[kk][ib] = lds8(&Xh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+                xl[kk][ib] = lds8(&Xl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
             }
-        }
-        __syncthreads();
-
-        // (C1) O = scale (diag(gamma) Q S^T + P U) for row block tb; U is read in
-        // the slot order of the P operand (two 8-byte pieces per k-step)
+        // O^T = scale (S Q^T diag(gamma) + X^T R^T), transposed so that a lane
+        // holds four consecutive outputs of one token; R is lower triangular,
+        // so row block tb needs the k-steps up to tb / 2
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) qsa[ib][r] *= gam[r];
+            for (int r = 0; r < 4; ++r) qsa[ib][r] *= gt;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             if (kk <= (tb >> 1)) {
-                const int col = 32 * kk + 4 * lg;
-                const bf8_t ph = __builtin_bit_cast(bf8_t, pHw[kk]);
-                const bf8_t pl = __builtin_bit_cast(bf8_t, pLw[kk]);
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
-                    const int row = (16 * ib + lr) * TP;
-                    const uint2 h0 = *reinterpret_cast<const uint2*>(&Uh[row + col]);
-                    const uint2 h1 = *reinterpret_cast<const uint2*>(&Uh[row + col + 16]);
-                    const uint2 l0 = *reinterpret_cast<const uint2*>(&Ul[row + col]);
-                    const uint2 l1 = *reinterpret_cast<const uint2*>(&Ul[row + col + 16]);
-                    const bf8_t bh = __builtin_bit_cast(bf8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
-                    const bf8_t bl = __builtin_bit_cast(bf8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
-                    qsa[ib] = mfma(ph, bh, qsa[ib]);
-                    qsa[ib] = mfma(ph, bl, qsa[ib]);
-                    qsa[ib] = mfma(pl, bh, qsa[ib]);
+                    qsa[ib] = mfma(xh[kk][ib], rH[kk], qsa[ib]);
+                    qsa[ib] = mfma(xl[kk][ib], rH[kk], qsa[ib]);
+                    qsa[ib] = mfma(xh[kk][ib], rL[kk], qsa[ib]);
                 }
             }
         }
-        {
-            // rows t >= L land at or past the resource end and are dropped
-            const __amdgpu_buffer_rsrc_t orsrc =
-                out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
+        // S'^T = gamma_n S^T + Z^T X for the wave's state tiles
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * tb + 4 * lg + r;
-                    out_store(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * ib + lr),
-                              A.scale * qsa[ib][r], op);
-                }
-        }
-        // (C2) S'^T = gamma_n S^T + K^T U' for the wave's state tiles; the K^T
-        // fragment (column j, tokens 32 kk + 8 lg .. +7) is gathered from the
-        // row-major K tile
-        const float gn = exp2f_(gNc);
-#pragma unroll
-        for (int x = 0; x < NJB; ++x) {
-            const int j = 16 * (NJB * tb + x) + lr;
-            bf8_t ka[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int y = 0; y < 8; ++y) ka[kk][y] = Kc[(32 * kk + 8 * lg + y) * KP + j];
+        for (int x = 0; x < NJB; ++x)
 #pragma unroll
             for (int ibS = 0; ibS < 2; ++ibS) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sacc[x][ibS][r] *= gn;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int col = 32 * kk + 8 * lg;
-                    const bf8_t bh = lds8(&Wh[(16 * ibS + lr) * TP + col]);
-                    const bf8_t bl = lds8(&Wl[(16 * ibS + lr) * TP + col]);
-                    sacc[x][ibS] = mfma(ka[kk], bh, sacc[x][ibS]);
-                    sacc[x][ibS] = mfma(ka[kk], bl, sacc[x][ibS]);
+                    sacc[x][ibS] = mfma(zH[x][kk], xh[kk][ibS], sacc[x][ibS]);
+                    sacc[x][ibS] = mfma(zH[x][kk], xl[kk][ibS], sacc[x][ibS]);
+                    sacc[x][ibS] = mfma(zL[x][kk], xh[kk][ibS], sacc[x][ibS]);
                 }
             }
+        load_rz(nj);
+        {
+            // qsa[ib][r] = O[t = 16 tb + lr][i = 16 ib + 4 lg + r]; rows t >= L land
+            // at or past the resource end and are dropped
+            const __amdgpu_buffer_rsrc_t orsrc =
+                out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
+            const int t = 16 * tb + lr;
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const float ov[4] = {A.scale * qsa[ib][0], A.scale * qsa[ib][1],
+                                     A.scale * qsa[ib][2], A.scale * qsa[ib][3]};
+                out_store4(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * ib + 4 * lg), ov,
+                           op);
+            }
         }
-        // Sh / Sl are read only in (A), and the other K / G buffer was last
-        // read in the previous chunk: both can be written before the barrier
+        // the state tile in LDS is read only in (A), which every wave has left
         store_state_lds();
-        stage_k_g(buf ^ 1);
         __syncthreads();
     }
 
@@ -725,7 +851,8 @@ static hipError_t launch_mfma_t(const PrefillArgs& A) {
 }
 
 bool prefill_mfma_eligible(const PrefillArgs& A) {
-    return A.in_bf16 && (A.dk == 64 || A.dk == 128) && (A.dv % 32 == 0);
+    return A.in_bf16 && (A.dk == 64 || A.dk == 128) && (A.dv % 32 == 0) &&
+           A.HV / A.H <= kMaxRatio;
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& A) {

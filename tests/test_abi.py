@@ -110,7 +110,7 @@ def test_prefill_workspace_bytes(L):
         maxc = (T + N * 63) // 64
         head = al(4 * (N + 1)) + al(maxc * HV * 64 * 4)
         valu = al(maxc * HV * 64 * 64 * 4)
-        mfma = 2 * al(maxc * HV * 64 * 64 * 2)
+        mfma = 2 * al(maxc * HV * 64 * 64 * 2) + 2 * al(maxc * HV * dk * 64 * 2)
         want = head + max(valu, mfma)
         assert f(N, T, H, HV, dk, 128) == want
         assert f(N, T, H, HV, dk, 128) % 256 == 0

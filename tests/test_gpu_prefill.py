@@ -180,3 +180,15 @@ def test_prefill_zero_tokens_copies_state():
     assert torch.equal(S, s0)
     o, S = gdn.prefill_chunked(e, e, ev, eg, eg, cu)
     assert torch.count_nonzero(S).item() == 0
+
+
+@pytest.mark.parametrize("ratio", [1, 4, 8])
+def test_prefill_value_heads_per_key_head(orc, ratio):
+    """GVA ratios up to 4 run the MFMA kernels (G, R and Z^T per value head of
+    a key head); 8 exercises the vector-unit path that larger ratios use."""
+    x = gi.make_prefill([130, 70, 1], 1, ratio, 128, 128, dtype="bf16", s0_std=0.05,
+                        seed=40 + ratio)
+    say(f"prefill value heads per key head = {ratio}")
+    o, S = gpu_prefill(x)
+    o_ref, S_ref = oracle_prefill(orc, x)
+    assert_parity(host(o), host(S), o_ref, S_ref, what=f"value heads per key head {ratio}")
