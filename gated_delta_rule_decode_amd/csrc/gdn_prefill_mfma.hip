@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     __shared__ __attribute__((aligned(16))) float Tm[C * AP];  // T = (I + A)^-1
     __shared__ __attribute__((aligned(16))) float Xm[32 * 36];
     __shared__ __attribute__((aligned(16))) float Gs[kMaxRatio][C];
-    __shared__ float Bs[kMaxRatio][C];
+    __shared__ __attribute__((aligned(16))) float Bs[kMaxRatio][C];
     __shared__ __attribute__((aligned(16))) float Ds[kMaxRatio][C];
 
     const int H = A.H, HV = A.HV;
@@ -265,15 +265,24 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     for (int i = 0; i < ratio; ++i) {
         const int hv = hv0 + i;
         const float* G = Gs[i];
-        // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s})
+        // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s}); branch-free: the
+        // exponent is clamped at 0 (only s < t is kept, where it is <= 0 anyway)
+        // and the mask multiplies
+        {
+            const float4 g4 = *reinterpret_cast<const float4*>(&G[16 * w + 4 * lg]);
+            const float4 b4 = *reinterpret_cast<const float4*>(&Bs[i][16 * w + 4 * lg]);
+            const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            if (sb <= w) {
-                const float Gsb = G[16 * sb + lr];
+            for (int sb = 0; sb < 4; ++sb) {
+                if (sb <= w) {
+                    const float Gsb = G[16 * sb + lr];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * w + 4 * lg + r, s = 16 * sb + lr;
-                    Am[t * AP + s] = (s < t) ? Bs[i][t] * exp2f_(G[t] - Gsb) * kk[sb][r] : 0.f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * w + 4 * lg + r, s = 16 * sb + lr;
+                        const float keep = (s < t) ? 1.f : 0.f;
+                        Am[t * AP + s] = keep * bt[r] * exp2f_(fminf(gt[r] - Gsb, 0.f)) * kk[sb][r];
+                    }
                 }
             }
         }
@@ -303,33 +312,36 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
             for (int t = 0; t < 16; ++t) Tm[(o + t) * AP + o + l] = col[t];
         }
         __syncthreads();
-        // 16-block merges: T_10 = -T_11 (A_10 T_00), T_32 = -T_33 (A_32 T_22)
+        // 16-block merges on MFMA, one per wavefront (0 and 1):
+        //   T_{ii,j} = -T_{ii,ii} (A_{ii,j} T_{jj}),  (ii, j) = (1, 0), (3, 2).
+        // The 16-long contraction fills slots 0..3 of each lane group (slots 4..7
+        // are zero), so the first product's accumulators (rows 4 lg + r, column
+        // lr) are exactly the second product's B operand.
+        if (w < 2) {
+            const int j = 2 * w, ii = j + 1;
+            const float4 a4 = *reinterpret_cast<const float4*>(&Am[(16 * ii + lr) * AP + 16 * j + 4 * lg]);
+            float av[8] = {a4.x, a4.y, a4.z, a4.w, 0.f, 0.f, 0.f, 0.f};
+            float bv8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int e = tid + 256 * half;
-            const int j = (e >> 8) * 2, ii = j + 1;  // (1,0) or (3,2)
-            const int rho = (e >> 4) & 15, kap = e & 15;
-            float acc = 0.f;
+            for (int y = 0; y < 4; ++y) bv8[y] = Tm[(16 * j + 4 * lg + y) * AP + 16 * j + lr];
+            bf8_t ah, al, bh, bl;
+            split8(av, ah, al);
+            split8(bv8, bh, bl);
+            f4_t xa = f4_t{0.f, 0.f, 0.f, 0.f};  // xa[r] = (A_{ii,j} T_{jj})[4 lg + r][lr]
+            xa = mfma(ah, bh, xa);
+            xa = mfma(ah, bl, xa);
+            xa = mfma(al, bh, xa);
+            const float4 t4 = *reinterpret_cast<const float4*>(&Tm[(16 * ii + lr) * AP + 16 * ii + 4 * lg]);
+            float tv[8] = {t4.x, t4.y, t4.z, t4.w, 0.f, 0.f, 0.f, 0.f};
+            float xv[8] = {xa[0], xa[1], xa[2], xa[3], 0.f, 0.f, 0.f, 0.f};
+            split8(tv, ah, al);
+            split8(xv, bh, bl);
+            f4_t ta = f4_t{0.f, 0.f, 0.f, 0.f};
+            ta = mfma(ah, bh, ta);
+            ta = mfma(ah, bl, ta);
+            ta = mfma(al, bh, ta);
 #pragma unroll
-            for (int x = 0; x < 16; ++x)
-                acc += (x >= kap) ? Am[(16 * ii + rho) * AP + 16 * j + x] *
-                                        Tm[(16 * j + x) * AP + 16 * j + kap]
-                                  : 0.f;
-            Xm[(16 * (e >> 8) + rho) * 36 + kap] = acc;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int e = tid + 256 * half;
-            const int j = (e >> 8) * 2, ii = j + 1;
-            const int rho = (e >> 4) & 15, kap = e & 15;
-            float acc = 0.f;
-#pragma unroll
-            for (int x = 0; x < 16; ++x)
-                acc += (x <= rho) ? Tm[(16 * ii + rho) * AP + 16 * ii + x] *
-                                        Xm[(16 * (e >> 8) + x) * 36 + kap]
-                                  : 0.f;
-            Tm[(16 * ii + rho) * AP + 16 * j + kap] = -acc;
+            for (int r = 0; r < 4; ++r) Tm[(16 * ii + 4 * lg + r) * AP + 16 * j + lr] = -ta[r];
         }
         __syncthreads();
         // 32-block merge on MFMA: X = A[32:64, 0:32] T[0:32, 0:32]; T[32:64, 0:32] = -T_B X
@@ -379,9 +391,11 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
             const int s_ = idx & 63, c4 = 4 * (idx >> 6);
             const float4 t4 = *reinterpret_cast<const float4*>(&Tm[s_ * AP + c4]);
             const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+            const float4 b4 = *reinterpret_cast<const float4*>(&Bs[i][c4]);
+            const float bc[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Am[(c4 + r) * AP + s_] = (s_ >= c4 + r) ? tv[r] * Bs[i][c4 + r] : 0.f;
+                Am[(c4 + r) * AP + s_] = ((s_ >= c4 + r) ? 1.f : 0.f) * tv[r] * bc[r];
         }
         __syncthreads();
 
@@ -398,10 +412,13 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int sb = 2 * k2 + half;
+                    const float4 g4 = *reinterpret_cast<const float4*>(&G[16 * sb + 4 * lg]);
+                    const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int s_ = 16 * sb + 4 * lg + r;
-                        pv[4 * half + r] = (s_ <= t) ? pq[sb][r] * exp2f_(Gt - G[s_]) : 0.f;
+                        const float keep = (s_ <= t) ? 1.f : 0.f;
+                        pv[4 * half + r] = keep * pq[sb][r] * exp2f_(fminf(Gt - gs[r], 0.f));
                     }
                 }
                 split8(pv, ph[k2], pl[k2]);
