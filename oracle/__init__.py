@@ -13,6 +13,10 @@ Functions
   recurrence(...)   the plain step-by-step gated delta rule over a packed batch
   decode(...)       one token per sequence: the same loop with T = N
   rmsnorm_gated(...) y = x / sqrt(mean(x^2) + eps) * w * silu(z)
+  gates(...)        g = -exp(A_log) softplus(a_raw + dt_bias), beta = sigmoid(b_raw)
+  l2norm(...)       x / sqrt(sum x^2 + eps) per row
+  decode_layer(...) one token per sequence against a slot-addressed state pool,
+                    optionally with q/k L2-normalised first
 
 Pinned by tests/test_oracle_pins.py (closed forms and invariants) and
 tests/test_oracle_mutations.py (planted mistakes fail a pin).
@@ -71,6 +75,17 @@ class Oracle:
         lib.gdn_oracle_rmsnorm_gated.argtypes = [
             _f64p, _f32p, _f32p, ctypes.c_long, ctypes.c_int, ctypes.c_double, _f64p]
         lib.gdn_oracle_max_threads.restype = ctypes.c_int
+        lib.gdn_oracle_gates.restype = ctypes.c_int
+        lib.gdn_oracle_gates.argtypes = [_f32p, _f32p, _f32p, _f32p, ctypes.c_long, ctypes.c_int,
+                                         _f64p, _f64p]
+        lib.gdn_oracle_l2norm.restype = ctypes.c_int
+        lib.gdn_oracle_l2norm.argtypes = [_f32p, ctypes.c_long, ctypes.c_int, ctypes.c_double,
+                                          _f64p]
+        lib.gdn_oracle_decode_layer.restype = ctypes.c_int
+        lib.gdn_oracle_decode_layer.argtypes = [
+            _f32p, _f32p, _f32p, _f64p, _f64p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+            ctypes.c_double, _f64p, _f64p, ctypes.c_int]
         self._lib = lib
 
     def max_threads(self) -> int:
@@ -130,17 +145,79 @@ class Oracle:
             raise RuntimeError("oracle rmsnorm failed")
         return y
 
+    def gates(self, a_raw, b_raw, A_log, dt_bias=None):
+        """a_raw, b_raw: [..., HV]; A_log, dt_bias: [HV].  Returns (g, beta) in
+        float64 with the shape of a_raw."""
+        a_raw, b_raw, A_log = _f32(a_raw), _f32(b_raw), _f32(A_log)
+        HV = A_log.shape[0]
+        if a_raw.shape != b_raw.shape or a_raw.shape[-1:] != (HV,):
+            raise ValueError("shapes")
+        dt = None if dt_bias is None else _f32(dt_bias)
+        if dt is not None and dt.shape != (HV,):
+            raise ValueError("dt_bias shape")
+        g = np.empty(a_raw.shape, dtype=np.float64)
+        beta = np.empty(a_raw.shape, dtype=np.float64)
+        rc = self._lib.gdn_oracle_gates(_ptr(a_raw, _f32p), _ptr(b_raw, _f32p),
+                                        _ptr(A_log, _f32p), _ptr(dt, _f32p), a_raw.size // HV,
+                                        HV, _ptr(g, _f64p), _ptr(beta, _f64p))
+        if rc != 0:
+            raise RuntimeError("oracle gates failed")
+        return g, beta
+
+    def l2norm(self, x, *, eps: float = 1e-6):
+        """Rows are the last axis of x; returns float64."""
+        x = _f32(x)
+        d = x.shape[-1]
+        y = np.empty(x.shape, dtype=np.float64)
+        rc = self._lib.gdn_oracle_l2norm(_ptr(x, _f32p), x.size // d, d, float(eps),
+                                         _ptr(y, _f64p))
+        if rc != 0:
+            raise RuntimeError("oracle l2norm failed")
+        return y
+
+    def decode_layer(self, q, k, v, g, beta, pool, *, slots=None, scale: float = 1.0,
+                     l2norm: bool = False, l2_eps: float = 1e-6, threads: int = 0):
+        """One token per sequence against a state pool.
+
+        q, k: [N, H, dk]; v: [N, HV, dv]; g, beta: [N, HV] (any float type,
+        used in float64); pool: [S, HV, dv, dk]; slots: [N] int32 or None
+        (sequence n -> slot n).  Returns (o [N, HV, dv], new_pool) in float64;
+        sequences whose slot lies outside [0, S) get o = 0 and touch no state."""
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        g = np.ascontiguousarray(g, dtype=np.float64)
+        beta = np.ascontiguousarray(beta, dtype=np.float64)
+        pool = np.array(pool, dtype=np.float64, copy=True, order="C")
+        N, H, dk = q.shape
+        HV, dv = v.shape[1], v.shape[2]
+        if k.shape != q.shape or v.shape[0] != N or g.shape != (N, HV) or beta.shape != (N, HV):
+            raise ValueError("inconsistent shapes")
+        if pool.ndim != 4 or pool.shape[1:] != (HV, dv, dk):
+            raise ValueError("pool shape")
+        sl = None if slots is None else np.ascontiguousarray(slots, dtype=np.int32)
+        if sl is not None and sl.shape != (N,):
+            raise ValueError("slots shape")
+        o = np.full((N, HV, dv), np.nan, dtype=np.float64)  # every element is written
+        rc = self._lib.gdn_oracle_decode_layer(
+            _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), _ptr(g, _f64p), _ptr(beta, _f64p),
+            _ptr(sl, _i32p), pool.shape[0], N, H, HV, dk, dv, float(scale), int(bool(l2norm)),
+            float(l2_eps), _ptr(pool, _f64p), _ptr(o, _f64p), int(threads))
+        if rc != 0:
+            raise RuntimeError("oracle decode_layer failed (sizes, or a slot used twice)")
+        return o, pool
+
 
 _DEFAULT: Optional[Oracle] = None
 
 
 def load(path: Optional[str] = None) -> Oracle:
-    """Load the oracle (building it first only if no library exists)."""
+    """Load the oracle (building it first if no library exists or the source
+    is newer than the library)."""
     global _DEFAULT
     if path is not None:
         return Oracle(path)
     if _DEFAULT is None:
-        if not os.path.exists(LIBRARY):
+        if (not os.path.exists(LIBRARY)
+                or os.path.getmtime(SOURCE) > os.path.getmtime(LIBRARY)):
             build()
         _DEFAULT = Oracle(LIBRARY)
     return _DEFAULT

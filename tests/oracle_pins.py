@@ -369,6 +369,142 @@ def pin_norm_closed_forms(orc):
     _close(y, want, 1e-14, "constant group")
 
 
+# ---------------------------------------------------------------------------
+# decode-layer pins: gate activations, q/k L2 norm, slot table
+# ---------------------------------------------------------------------------
+
+def pin_gate_closed_forms(orc):
+    """g = -exp(A_log) softplus(a_raw + dt_bias), beta = sigmoid(b_raw):
+    softplus(0) = ln 2, softplus(x) - softplus(-x) = x, softplus(40) = 40 to
+    1e-17, softplus(-40) = e^-40 to 1e-17; sigmoid(0) = 1/2,
+    sigmoid(+-ln 3) = 3/4, 1/4; the per-head scale multiplies by exp(A_log)."""
+    A = np.array([0.0, 0.6931471805599453, -1.25, 2.0], dtype=np.float32)
+    sc = np.exp(A.astype(np.float64))
+    dt = np.array([0.0, 0.25, -1.5, 3.0], dtype=np.float32)
+    # a_raw + dt_bias = 0, 40, -40 (all exact in float32)
+    a_raw = np.stack([-dt, 40.0 - dt, -40.0 - dt]).astype(np.float32)
+    b_raw = np.array([[0.0] * 4, [math.log(3.0)] * 4, [-math.log(3.0)] * 4], dtype=np.float32)
+    g, beta = orc.gates(a_raw, b_raw, A, dt)
+    _close(g[0] / sc, -math.log(2.0) * np.ones(4), 1e-15, "softplus(0) = ln 2")
+    _close(g[1] / sc, -40.0 * np.ones(4), 1e-15, "softplus(40)")
+    _close(g[2] / (sc * math.exp(-40.0)), -np.ones(4), 1e-12, "softplus(-40) / e^-40")
+    _close(beta[0], 0.5 * np.ones(4), 1e-15, "sigmoid(0)")
+    b3 = np.float64(np.float32(math.log(3.0)))
+    _close(beta[1], np.full(4, 1.0 / (1.0 + math.exp(-b3))), 1e-15, "sigmoid(ln 3)")
+    _close(beta[1], 0.75 * np.ones(4), 1e-7, "sigmoid(ln 3) = 3/4")
+    _close(beta[2], 0.25 * np.ones(4), 1e-7, "sigmoid(-ln 3) = 1/4")
+    # odd part of softplus and the complement of sigmoid on random inputs
+    r = _rng(30)
+    x = r.standard_normal((5, 4)).astype(np.float32) * 4
+    gp, bp = orc.gates(x, x, A, None)
+    gm, bm = orc.gates(-x, -x, A, None)
+    _close((gp - gm) / sc, -x.astype(np.float64), 1e-14, "softplus(x) - softplus(-x) = x")
+    _close(bp + bm, np.ones_like(bp), 1e-15, "sigmoid(x) + sigmoid(-x) = 1")
+
+
+def pin_gate_library(orc):
+    """Against torch's CPU softplus (threshold beyond the range) and sigmoid in fp64."""
+    import torch
+    r = _rng(31)
+    HV = 6
+    a_raw = (r.standard_normal((9, HV)) * 3).astype(np.float32)
+    b_raw = (r.standard_normal((9, HV)) * 3).astype(np.float32)
+    A = r.uniform(0, math.log(16), HV).astype(np.float32)
+    dt = r.standard_normal(HV).astype(np.float32)
+    g, beta = orc.gates(a_raw, b_raw, A, dt)
+    x = torch.from_numpy(a_raw.astype(np.float64)) + torch.from_numpy(dt.astype(np.float64))
+    want_g = -torch.exp(torch.from_numpy(A.astype(np.float64))) * \
+        torch.nn.functional.softplus(x, beta=1.0, threshold=1000.0)
+    want_b = torch.sigmoid(torch.from_numpy(b_raw.astype(np.float64)))
+    _close(g, want_g.numpy(), 1e-14, "g vs torch softplus")
+    _close(beta, want_b.numpy(), 1e-15, "beta vs torch sigmoid")
+
+
+def pin_l2norm(orc):
+    """x / sqrt(sum x^2 + eps): (3, 4) -> (0.6, 0.8) at eps = 0 and
+    (3, 4) / 6 at eps = 11; zero rows stay zero; torch's normalize at eps = 0."""
+    import torch
+    _close(orc.l2norm(np.array([[3.0, 4.0]]), eps=0.0), [[0.6, 0.8]], 1e-15, "3-4-5")
+    _close(orc.l2norm(np.array([[3.0, 4.0]]), eps=11.0), [[0.5, 4.0 / 6.0]], 1e-15, "eps inside")
+    _close(orc.l2norm(np.zeros((2, 5)), eps=1e-6), np.zeros((2, 5)), 0.0, "zero row")
+    r = _rng(32)
+    x = r.standard_normal((7, 16)).astype(np.float32)
+    want = torch.nn.functional.normalize(torch.from_numpy(x.astype(np.float64)), dim=-1)
+    _close(orc.l2norm(x, eps=0.0), want.numpy(), 1e-15, "vs torch normalize")
+
+
+def _layer_inputs(tag, N, H, HV, dk, dv):
+    r = _rng(tag)
+    q = r.standard_normal((N, H, dk)).astype(np.float32)
+    k = _unit(r.standard_normal((N, H, dk)))
+    v = r.standard_normal((N, HV, dv)).astype(np.float32)
+    g = (-r.random((N, HV)) * 0.5).astype(np.float32)
+    b = r.random((N, HV)).astype(np.float32)
+    return r, q, k, v, g, b
+
+
+def pin_decode_layer_reduces_to_step(orc):
+    """Without the slot table and the norm the layer step is the pinned
+    recurrence; with a slot table each sequence advances its own slot, slots no
+    sequence names keep their bits, and a skipped sequence reads 0."""
+    N, H, HV, dk, dv = 5, 2, 4, 8, 6
+    r, q, k, v, g, b = _layer_inputs(33, N, H, HV, dk, dv)
+    S = r.standard_normal((N, HV, dv, dk))
+    o_ref, s_ref = orc.decode(q, k, v, g, b, S, scale=0.7)
+    o, pool = orc.decode_layer(q, k, v, g, b, S, scale=0.7)
+    assert np.array_equal(o, o_ref) and np.array_equal(pool, s_ref), "identity slots"
+    # pool of 9 slots; sequences 1 and 3 skipped (-1 and 9 lie outside [0, 9))
+    slots = np.array([7, -1, 0, 9, 4], dtype=np.int32)
+    pool0 = r.standard_normal((9, HV, dv, dk))
+    o, pool = orc.decode_layer(q, k, v, g, b, pool0, slots=slots, scale=0.7)
+    live = [0, 2, 4]
+    o_ref, s_ref = orc.decode(q[live], k[live], v[live], g[live], b[live],
+                              pool0[slots[live]], scale=0.7)
+    assert np.array_equal(o[live], o_ref), "slot outputs"
+    assert np.array_equal(pool[slots[live]], s_ref), "slot states"
+    assert np.array_equal(o[[1, 3]], np.zeros((2, HV, dv))), "skipped outputs"
+    untouched = [s for s in range(9) if s not in (7, 0, 4)]
+    assert np.array_equal(pool[untouched], pool0[untouched]), "untouched slots"
+
+
+def pin_decode_layer_l2norm(orc):
+    """With the q/k norm the step equals the recurrence on normalised q and k
+    (to float32 rounding of the normalised inputs) and is unchanged by a
+    positive rescaling of q and k (eps = 0)."""
+    N, H, HV, dk, dv = 4, 2, 4, 8, 6
+    r, q, k, v, g, b = _layer_inputs(34, N, H, HV, dk, dv)
+    k = (r.standard_normal((N, H, dk)) * 3).astype(np.float32)
+    S = r.standard_normal((N, HV, dv, dk))
+    o, pool = orc.decode_layer(q, k, v, g, b, S, l2norm=True, l2_eps=1e-6)
+    o_ref, s_ref = orc.decode(orc.l2norm(q, eps=1e-6), orc.l2norm(k, eps=1e-6), v, g, b, S)
+    _close(o, o_ref, 1e-6, "l2 outputs")
+    _close(pool, s_ref, 1e-6, "l2 states")
+    o0, p0 = orc.decode_layer(q, k, v, g, b, S, l2norm=True, l2_eps=0.0)
+    o1, p1 = orc.decode_layer(q * 4, k * 0.5, v, g, b, S, l2norm=True, l2_eps=0.0)
+    _close(o1, o0, 1e-13, "rescaled q, k")
+    _close(p1, p0, 1e-13, "rescaled q, k (state)")
+    o2, _ = orc.decode_layer(q, k, v, g, b, S, l2norm=False)
+    assert np.max(np.abs(o2 - o0)) > 1e-3, "the norm changes the result"
+
+
+def pin_decode_layer_gates(orc):
+    """Layer step with activated gates: decay a = exp(g) in (0, 1) and, with
+    beta = sigmoid(b_raw) and an orthonormal key on a zero state, the stored
+    value is read back scaled by beta (the write strength)."""
+    N, H, HV, dk, dv = 3, 1, 2, 8, 4
+    r = _rng(35)
+    a_raw = r.standard_normal((N, HV)).astype(np.float32)
+    b_raw = r.standard_normal((N, HV)).astype(np.float32)
+    A = np.array([0.5, 1.5], dtype=np.float32)
+    g, beta = orc.gates(a_raw, b_raw, A, None)
+    assert np.all(g < 0) and np.all(np.exp(g) > 0), "decay in (0, 1)"
+    k = np.zeros((N, H, dk), np.float32)
+    k[np.arange(N), 0, np.arange(N)] = 1.0
+    v = r.standard_normal((N, HV, dv)).astype(np.float32)
+    o, _ = orc.decode_layer(k, k, v, g, beta, np.zeros((N, HV, dv, dk)))
+    _close(o, beta[:, :, None] * v.astype(np.float64), 1e-15, "read back b v")
+
+
 RECURRENCE_PINS = [
     pin_handworked_two_tokens, pin_single_token_closed_form, pin_decay_only,
     pin_exact_retrieval, pin_linear_readout, pin_delta_rule_invariants, pin_scale_linearity,
@@ -376,4 +512,6 @@ RECURRENCE_PINS = [
     pin_chunked_equals_step, pin_transition_product,
 ]
 NORM_PINS = [pin_norm_library, pin_norm_closed_forms]
-ALL_PINS = RECURRENCE_PINS + NORM_PINS
+LAYER_PINS = [pin_gate_closed_forms, pin_gate_library, pin_l2norm,
+              pin_decode_layer_reduces_to_step, pin_decode_layer_l2norm, pin_decode_layer_gates]
+ALL_PINS = RECURRENCE_PINS + NORM_PINS + LAYER_PINS

@@ -14,9 +14,9 @@ import pytest
 import oracle
 import oracle_pins
 
-UPDATE_BEGIN = "        /* S_t = a S_{t-1} - a b (S_{t-1} k_t) k_t^T + b v_t k_t^T */"
-READOUT_BEGIN = "        /* o_t = scale * S_t q_t */"
-READOUT_END = "            ot[i] = scale * acc;\n        }\n"
+UPDATE_BEGIN = "    /* S_t = a S_{t-1} - a b (S_{t-1} k_t) k_t^T + b v_t k_t^T */"
+READOUT_BEGIN = "    /* o_t = scale * S_t q_t */"
+READOUT_END = "        ot[i] = scale * acc;\n    }\n"
 
 
 def _swap_readout_before_update(src: str) -> str:
@@ -30,16 +30,16 @@ def _swap_readout_before_update(src: str) -> str:
 
 MUTATIONS = {
     "sign_of_delta_correction": [("upd -= a * b * sk[i]", "upd += a * b * sk[i]")],
-    "dropped_write_term": [("upd += b * (double)vt[i] * (double)kt[j];", "")],
+    "dropped_write_term": [("upd += b * (double)vt[i] * kt[j];", "")],
     "dropped_beta_in_correction": [("upd -= a * b * sk[i]", "upd -= a * sk[i]")],
     "no_decay_on_state": [("double upd = a * s;", "double upd = s;")],
     "decay_sign": [("exp((double)g[", "exp(-(double)g[")],
-    "readout_with_key": [("acc += S[(size_t)i * dk + j] * (double)qt[j];",
-                          "acc += S[(size_t)i * dk + j] * (double)kt[j];")],
-    "correction_uses_query": [("acc += S[(size_t)i * dk + j] * (double)kt[j];\n            sk[i]",
-                               "acc += S[(size_t)i * dk + j] * (double)qt[j];\n            sk[i]")],
-    "write_term_transposed_roles": [("upd += b * (double)vt[i] * (double)kt[j];",
-                                     "upd += b * (double)vt[j % dv] * (double)kt[i % dk];")],
+    "readout_with_key": [("acc += S[(size_t)i * dk + j] * qt[j];",
+                          "acc += S[(size_t)i * dk + j] * kt[j];")],
+    "correction_uses_query": [("acc += S[(size_t)i * dk + j] * kt[j];\n        sk[i]",
+                               "acc += S[(size_t)i * dk + j] * qt[j];\n        sk[i]")],
+    "write_term_transposed_roles": [("upd += b * (double)vt[i] * kt[j];",
+                                     "upd += b * (double)vt[j % dv] * kt[i % dk];")],
     "readout_unscaled": [("ot[i] = scale * acc;", "ot[i] = acc;")],
     "readout_before_update": "swap",
     "head_mapping_modulo": [("const int hk = h / (HV / H);", "const int hk = h % H;")],
@@ -47,6 +47,18 @@ MUTATIONS = {
     "norm_gate_sigmoid": [("const double gate = zi / (1.0 + exp(-zi));",
                            "const double gate = 1.0 / (1.0 + exp(-zi));")],
     "norm_weight_dropped": [("* (double)w[i] * gate", "* gate")],
+    "gate_sign": [("g[i] = -exp((double)A_log[h])", "g[i] = exp((double)A_log[h])")],
+    "gate_scale_not_exponentiated": [("g[i] = -exp((double)A_log[h])",
+                                      "g[i] = -(double)A_log[h]")],
+    "gate_dt_bias_dropped": [("(dt_bias ? (double)dt_bias[h] : 0.0)", "0.0")],
+    "softplus_as_relu": [(" + log1p(exp(-fabs(x)))", "")],
+    "beta_of_negated_input": [("1.0 / (1.0 + exp(-(double)b_raw[i]))",
+                               "1.0 / (1.0 + exp((double)b_raw[i]))")],
+    "l2_eps_outside_sqrt": [("1.0 / sqrt(ss + eps)", "1.0 / (sqrt(ss) + eps)")],
+    "l2_key_not_normalised": [("            l2norm_row(kd, dk, l2_eps);\n", "")],
+    "slot_table_ignored": [("pool + ((size_t)s * HV + h) * ssz", "pool + ((size_t)n * HV + h) * ssz")],
+    "skipped_sequence_output_unset": [("for (int i = 0; i < dv; ++i) ot[i] = 0.0;", "")],
+    "layer_decay_sign": [("exp(g[p]), beta[p]", "exp(-g[p]), beta[p]")],
 }
 
 
