@@ -7,6 +7,8 @@ raises (there is no fallback path).
 
     decode_step(q, k, v, g, beta, state, ...)          -> o
     decode_step_norm(q, k, v, g, beta, state, z, w)    -> y (and o on request)
+    decode_layer(q, k, v, state, ...)                  -> o and/or y (slot table,
+                                                          raw gates, q/k L2 norm)
     prefill_chunked(q, k, v, g, beta, cu_seqlens, ...) -> (o, final_state)
     rmsnorm_gated(x, z, w, ...)                        -> y
     prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk=64)
@@ -30,11 +32,12 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_version", "gdn_status_string", "gdn_last_hip_error", "gdn_decode_step",
-           "gdn_decode_step_norm", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
-           "gdn_rmsnorm_gated")
+           "gdn_decode_step_norm", "gdn_decode_layer_args_size", "gdn_decode_layer",
+           "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_rmsnorm_gated")
 
-__all__ = ["decode_step", "decode_step_norm", "prefill_chunked", "rmsnorm_gated", "prefill_workspace_bytes",
-           "GDNError", "lib", "LIBRARY", "EXPORTS", "version"]
+__all__ = ["decode_step", "decode_step_norm", "decode_layer", "prefill_chunked", "rmsnorm_gated",
+           "prefill_workspace_bytes", "DecodeLayerArgs", "GDNError", "lib", "LIBRARY", "EXPORTS",
+           "version"]
 
 
 class GDNError(RuntimeError):
@@ -46,6 +49,20 @@ class GDNError(RuntimeError):
 
 _LIB: Optional[ctypes.CDLL] = None
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class DecodeLayerArgs(ctypes.Structure):
+    """Mirror of gdn_decode_layer_args (field order and types as in gdn.h)."""
+    _fields_ = [
+        ("q", _vp), ("k", _vp), ("v", _vp), ("in_dtype", _i),
+        ("g", _vp), ("beta", _vp),
+        ("a_raw", _vp), ("b_raw", _vp), ("gate_dtype", _i), ("A_log", _vp), ("dt_bias", _vp),
+        ("qk_l2norm", _i), ("l2_eps", _f),
+        ("state", _vp), ("slots", _vp), ("num_slots", _i),
+        ("o", _vp), ("o_dtype", _i), ("z", _vp), ("z_dtype", _i), ("w", _vp), ("w_dtype", _i),
+        ("y", _vp), ("y_dtype", _i), ("eps", _f),
+        ("N", _i), ("H", _i), ("HV", _i), ("dk", _i), ("dv", _i), ("scale", _f),
+    ]
 
 
 def lib() -> ctypes.CDLL:
@@ -73,6 +90,12 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_step_norm.restype = _i
         L.gdn_decode_step_norm.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _i,
                                            _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _vp]
+        L.gdn_decode_layer_args_size.restype = _sz
+        L.gdn_decode_layer_args_size.argtypes = []
+        L.gdn_decode_layer.restype = _i
+        L.gdn_decode_layer.argtypes = [ctypes.POINTER(DecodeLayerArgs), _vp]
+        if L.gdn_decode_layer_args_size() != ctypes.sizeof(DecodeLayerArgs):
+            raise ImportError("gdn_decode_layer_args layout differs between gdn.h and the binding")
         L.gdn_prefill_workspace_bytes.restype = _sz
         L.gdn_prefill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
         L.gdn_prefill_chunked.restype = _i
@@ -197,6 +220,92 @@ def decode_step_norm(q, k, v, g, beta, state, z, w, *, y=None, o=None, scale: fl
         _dtype_code(o) if o is not None else GDN_F32, N, H, HV, dk, dv, float(scale),
         float(eps), _stream(q.device))
     _check("gdn_decode_step_norm", st)
+    return (y, o) if (return_o or o is not None) else y
+
+
+def decode_layer(q, k, v, state, *, g=None, beta=None, a_raw=None, b_raw=None, A_log=None,
+                 dt_bias=None, slots=None, qk_l2norm: bool = False, l2_eps: float = 1e-6,
+                 z=None, w=None, y=None, o=None, scale: float = 1.0, eps: float = 1e-6,
+                 out_dtype=None, return_o: bool = False):
+    """The serving form of the decode step (one launch).
+
+    state [S, HV, dv, dk] fp32 is a pool of S slots; ``slots`` [N] int32 names
+    the slot of each row (None: row n uses slot n, S >= N).  Rows whose slot is
+    outside [0, S) are skipped and read 0.  Gates: either ``g``/``beta`` [N, HV]
+    fp32, or raw ``a_raw``/``b_raw`` [N, HV] (fp32 or bf16) with ``A_log``
+    (and optionally ``dt_bias``) [HV] fp32, activated in the kernel as
+    g = -exp(A_log) softplus(a_raw + dt_bias), beta = sigmoid(b_raw).
+    ``qk_l2norm`` L2-normalises q and k first.  With ``z`` and ``w`` the
+    result is y = RMSNormGated(o) (and o as well with ``return_o``);
+    otherwise o."""
+    torch = _torch()
+    f32 = torch.float32
+    N, H, dk = q.shape
+    HV, dv = v.shape[1], v.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(state, "state", f32)
+    if k.shape != q.shape or v.shape[0] != N or state.dim() != 4 \
+            or tuple(state.shape[1:]) != (HV, dv, dk):
+        raise ValueError("inconsistent decode shapes")
+    a = DecodeLayerArgs()
+    a.q, a.k, a.v, a.in_dtype = _ptr(q), _ptr(k), _ptr(v), _dtype_code(q)
+    if a_raw is not None:
+        if b_raw is None or A_log is None or g is not None or beta is not None:
+            raise ValueError("raw gates need a_raw, b_raw and A_log (and no g / beta)")
+        _dev(a_raw, "a_raw")
+        _dev(b_raw, "b_raw", a_raw.dtype)
+        _dev(A_log, "A_log", f32)
+        if a_raw.shape != (N, HV) or b_raw.shape != (N, HV) or A_log.shape != (HV,):
+            raise ValueError("gate shapes")
+        if dt_bias is not None:
+            _dev(dt_bias, "dt_bias", f32)
+            if dt_bias.shape != (HV,):
+                raise ValueError("dt_bias shape")
+        a.a_raw, a.b_raw, a.gate_dtype = _ptr(a_raw), _ptr(b_raw), _dtype_code(a_raw)
+        a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    else:
+        if g is None or beta is None:
+            raise ValueError("give g and beta, or a_raw, b_raw and A_log")
+        _dev(g, "g", f32)
+        _dev(beta, "beta", f32)
+        if g.shape != (N, HV) or beta.shape != (N, HV):
+            raise ValueError("gate shapes")
+        a.g, a.beta = _ptr(g), _ptr(beta)
+    a.qk_l2norm, a.l2_eps = int(bool(qk_l2norm)), float(l2_eps)
+    a.state, a.num_slots = _ptr(state), int(state.shape[0])
+    if slots is not None:
+        _dev(slots, "slots", torch.int32)
+        if slots.shape != (N,):
+            raise ValueError("slots shape")
+        a.slots = _ptr(slots)
+    norm = z is not None or w is not None
+    if norm:
+        if z is None or w is None:
+            raise ValueError("RMSNormGated needs both z and w")
+        _dev(z, "z")
+        _dev(w, "w")
+        if z.shape != (N, HV, dv) or w.shape != (dv,):
+            raise ValueError("norm shapes")
+        if y is None:
+            y = torch.empty((N, HV, dv), dtype=out_dtype or f32, device=q.device)
+        _dev(y, "y")
+        a.z, a.z_dtype, a.w, a.w_dtype = _ptr(z), _dtype_code(z), _ptr(w), _dtype_code(w)
+        a.y, a.y_dtype, a.eps = _ptr(y), _dtype_code(y), float(eps)
+        if return_o and o is None:
+            o = torch.empty((N, HV, dv), dtype=f32, device=q.device)
+    elif o is None:
+        o = torch.empty((N, HV, dv), dtype=out_dtype or f32, device=q.device)
+    if o is not None:
+        _dev(o, "o")
+        if o.shape != (N, HV, dv):
+            raise ValueError("o shape")
+        a.o, a.o_dtype = _ptr(o), _dtype_code(o)
+    a.N, a.H, a.HV, a.dk, a.dv, a.scale = N, H, HV, dk, dv, float(scale)
+    st = lib().gdn_decode_layer(ctypes.byref(a), _stream(q.device))
+    _check("gdn_decode_layer", st)
+    if not norm:
+        return o
     return (y, o) if (return_o or o is not None) else y
 
 

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool valid_dtype(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
@@ -154,6 +154,57 @@ gdn_status gdn_decode_step_norm(const void* q, const void* k, const void* v, gdn
     a.z = z; a.w = w; a.y = y;
     a.z_bf16 = z_dtype == GDN_BF16; a.w_bf16 = w_dtype == GDN_BF16; a.y_bf16 = y_dtype == GDN_BF16;
     a.eps = eps;
+    a.stream = static_cast<hipStream_t>(stream);
+    return from_hip(gdn::launch_decode(a));
+}
+
+size_t gdn_decode_layer_args_size(void) { return sizeof(gdn_decode_layer_args); }
+
+gdn_status gdn_decode_layer(const gdn_decode_layer_args* p, void* stream) {
+    if (!p) return GDN_ERROR_INVALID_VALUE;
+    const gdn_decode_layer_args& x = *p;
+    if (x.N < 0 || x.num_slots < 0) return GDN_ERROR_INVALID_VALUE;
+    gdn_status st = heads_status(x.H, x.HV, x.dk, x.dv);
+    if (st != GDN_SUCCESS) return st;
+    const bool raw = x.a_raw != nullptr;
+    const bool norm = x.y != nullptr;
+    if (!valid_dtype(x.in_dtype) || (raw && !valid_dtype(x.gate_dtype)) ||
+        (x.o && !valid_dtype(x.o_dtype)) ||
+        (norm && (!valid_dtype(x.z_dtype) || !valid_dtype(x.w_dtype) || !valid_dtype(x.y_dtype))))
+        return GDN_ERROR_NOT_SUPPORTED;
+    if (!(x.l2_eps >= 0.f) || (norm && !(x.eps >= 0.f))) return GDN_ERROR_INVALID_VALUE;
+    if (!x.slots && x.num_slots < x.N) return GDN_ERROR_INVALID_VALUE;
+    if (x.N == 0) return GDN_SUCCESS;
+    if (!x.q || !x.k || !x.v || !x.state || !aligned16(x.q) || !aligned16(x.k) ||
+        !aligned16(x.v) || !aligned16(x.state))
+        return GDN_ERROR_INVALID_VALUE;
+    if (raw ? (!x.b_raw || !x.A_log) : (!x.g || !x.beta)) return GDN_ERROR_INVALID_VALUE;
+    if (!x.o && !norm) return GDN_ERROR_INVALID_VALUE;
+    if (x.o && !aligned16(x.o)) return GDN_ERROR_INVALID_VALUE;
+    if (norm && (!x.z || !x.w || !aligned16(x.z) || !aligned16(x.w) || !aligned16(x.y)))
+        return GDN_ERROR_INVALID_VALUE;
+    if ((size_t)x.N * x.HV > (size_t)(1u << 31) / (size_t)x.dv) return GDN_ERROR_NOT_SUPPORTED;
+    clear_pending();
+    gdn::DecodeArgs a{};
+    a.q = x.q; a.k = x.k; a.v = x.v; a.g = x.g; a.beta = x.beta; a.state = x.state; a.o = x.o;
+    a.in_bf16 = x.in_dtype == GDN_BF16; a.o_bf16 = x.o && x.o_dtype == GDN_BF16;
+    a.N = x.N; a.H = x.H; a.HV = x.HV; a.dk = x.dk; a.dv = x.dv; a.scale = x.scale;
+    a.fuse_norm = norm;
+    if (norm) {
+        a.z = x.z; a.w = x.w; a.y = x.y;
+        a.z_bf16 = x.z_dtype == GDN_BF16; a.w_bf16 = x.w_dtype == GDN_BF16;
+        a.y_bf16 = x.y_dtype == GDN_BF16;
+        a.eps = x.eps;
+    }
+    a.ext = true;
+    a.slots = x.slots;
+    a.num_slots = x.num_slots;
+    if (raw) {
+        a.a_raw = x.a_raw; a.b_raw = x.b_raw; a.gate_bf16 = x.gate_dtype == GDN_BF16;
+        a.A_log = x.A_log; a.dt_bias = x.dt_bias;
+    }
+    a.l2norm = x.qk_l2norm != 0;
+    a.l2_eps = x.l2_eps;
     a.stream = static_cast<hipStream_t>(stream);
     return from_hip(gdn::launch_decode(a));
 }

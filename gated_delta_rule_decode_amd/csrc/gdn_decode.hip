@@ -30,6 +30,15 @@
 // The fused variant owns a whole head (BV = dv) so that it can finish with
 // RMSNormGated (Qwen3.5-0.8B chat guide, section "Architektur") over the dv
 // outputs of the head: y = o / sqrt(mean(o^2) + eps) * w * silu(z).
+//
+// The layer variant (EXT) is the serving form of the same step: the state of
+// sequence n lives in slot slots[n] of a pool (a slot outside the pool skips
+// the sequence and writes zero outputs), the gates may arrive as raw
+// projections (g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b), the
+// Gated DeltaNet layer's parameterisation) and q, k may be L2-normalised in
+// the kernel: x / sqrt(sum x^2 + eps), one cross-lane sum per vector.  The
+// extras touch only per-head scalars and the q/k vectors, so the state sweep
+// is unchanged.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -55,7 +64,8 @@ __device__ __forceinline__ void st_any(void* p, size_t i, float v, bool bf16) {
 }
 
 // FUSE: finish with RMSNormGated over the head (requires BV == dv).
-template <int DK, int BV, int NT, typename Tin, bool FUSE>
+// EXT:  slot table, raw gates, q/k L2 norm.
+template <int DK, int BV, int NT, typename Tin, bool FUSE, bool EXT>
 __global__ __launch_bounds__(NT) void decode_kernel(const DecodeArgs A) {
     constexpr int LPR = DK / 4;       // lanes per state row
     constexpr int RPP = NT / LPR;     // rows per pass of the workgroup
@@ -76,16 +86,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecodeArgs A) {
     const int lc = threadIdx.x % LPR;  // column group: columns 4*lc .. 4*lc+3
     const int lr = threadIdx.x / LPR;  // row within a pass
 
-    float* S = A.state + ((size_t)nh * dv + (size_t)tile * BV) * DK + 4 * lc;
-
-    // the whole tile first: PASSES independent 16-byte loads in flight per lane
-    v4f s[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) s[p] = ld_state(S + (size_t)(p * RPP + lr) * DK);
-
-    const size_t qk = ((size_t)n * H + hk) * DK + 4 * lc;
-    const f4 k4 = io<Tin>::ld4(k + qk);
-    const f4 q4 = io<Tin>::ld4(q + qk);
     const size_t row0 = (size_t)nh * dv + (size_t)tile * BV + lr;  // this lane's first row
     // per-row inputs: lane lc < PASSES of a row group loads the values of its
     // row group's pass lc (one memory instruction for all passes); v is then
@@ -93,14 +93,50 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecodeArgs A) {
     // also finishes the row (o, y) for pass lc.
     const bool owner = lc < PASSES;
     const size_t myrow = row0 + (size_t)(owner ? lc : 0) * RPP;
+
+    int slot = n;
+    if constexpr (EXT) {
+        if (A.slots) slot = A.slots[n];
+        if ((unsigned)slot >= (unsigned)A.num_slots) {  // skipped sequence: zero outputs
+            if (owner) {
+                if (A.o) st_any<float>(A.o, myrow, 0.f, A.o_bf16);
+                if constexpr (FUSE) st_any<float>(A.y, myrow, 0.f, A.y_bf16);
+            }
+            return;  // uniform over the workgroup
+        }
+    }
+    float* S = A.state + (((size_t)slot * HV + h) * dv + (size_t)tile * BV) * DK + 4 * lc;
+
+    // the whole tile first: PASSES independent 16-byte loads in flight per lane
+    v4f s[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) s[p] = ld_state(S + (size_t)(p * RPP + lr) * DK);
+
+    const size_t qk = ((size_t)n * H + hk) * DK + 4 * lc;
+    f4 k4 = io<Tin>::ld4(k + qk);
+    f4 q4 = io<Tin>::ld4(q + qk);
     const float vmine = io<Tin>::ld(v + myrow);
     float zmine = 0.f, wmine = 0.f;
     if constexpr (FUSE) {
         zmine = ld_any<float>(A.z, myrow, A.z_bf16);
         wmine = ld_any<float>(A.w, (size_t)lr + (owner ? lc : 0) * RPP, A.w_bf16);
     }
-    const float a = expf(A.g[nh]);
-    const float b = A.beta[nh];
+    float a, b;
+    if (EXT && A.a_raw) {
+        const float x = ld_any<float>(A.a_raw, nh, A.gate_bf16) + (A.dt_bias ? A.dt_bias[h] : 0.f);
+        const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));  // softplus(x)
+        a = expf(-expf(A.A_log[h]) * sp);
+        b = 1.0f / (1.0f + expf(-ld_any<float>(A.b_raw, nh, A.gate_bf16)));
+    } else {
+        a = expf(A.g[nh]);
+        b = A.beta[nh];
+    }
+    if (EXT && A.l2norm) {
+        const float kn = 1.0f / sqrtf(group_sum<LPR>(dot4(k4, k4)) + A.l2_eps);
+        const float qn = 1.0f / sqrtf(group_sum<LPR>(dot4(q4, q4)) + A.l2_eps);
+        k4.x *= kn; k4.y *= kn; k4.z *= kn; k4.w *= kn;
+        q4.x *= qn; q4.y *= qn; q4.z *= qn; q4.w *= qn;
+    }
     const int gbase = (threadIdx.x & 63) & ~(LPR - 1);  // first lane of this row group in the wave
     float vv[PASSES];
 #pragma unroll
@@ -157,7 +193,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecodeArgs A) {
     }
 }
 
-template <int DK, int BV, typename Tin, bool FUSE>
+template <int DK, int BV, typename Tin, bool FUSE, bool EXT>
 static hipError_t launch_decode_t(const DecodeArgs& A) {
     constexpr int LPR = DK / 4;
     constexpr int LIMIT = FUSE ? 512 : 256;  // threads per workgroup
@@ -165,36 +201,38 @@ static hipError_t launch_decode_t(const DecodeArgs& A) {
     constexpr int NT = BV * LPR / PASSES;
     const int tiles = A.dv / BV;
     const size_t blocks = (size_t)A.N * A.HV * tiles;
-    hipLaunchKernelGGL((decode_kernel<DK, BV, NT, Tin, FUSE>), dim3((unsigned)blocks), dim3(NT),
+    hipLaunchKernelGGL((decode_kernel<DK, BV, NT, Tin, FUSE, EXT>), dim3((unsigned)blocks), dim3(NT),
                        0, A.stream, A);
     return hipGetLastError();
 }
 
-template <int DK, typename Tin>
+template <int DK, typename Tin, bool EXT>
 static hipError_t launch_decode_dk(const DecodeArgs& A) {
     if (A.fuse_norm) {
         switch (A.dv) {
-            case 16: return launch_decode_t<DK, 16, Tin, true>(A);
-            case 32: return launch_decode_t<DK, 32, Tin, true>(A);
-            case 64: return launch_decode_t<DK, 64, Tin, true>(A);
-            default: return launch_decode_t<DK, 128, Tin, true>(A);
+            case 16: return launch_decode_t<DK, 16, Tin, true, EXT>(A);
+            case 32: return launch_decode_t<DK, 32, Tin, true, EXT>(A);
+            case 64: return launch_decode_t<DK, 64, Tin, true, EXT>(A);
+            default: return launch_decode_t<DK, 128, Tin, true, EXT>(A);
         }
     }
-    return launch_decode_t<DK, 16, Tin, false>(A);
+    return launch_decode_t<DK, 16, Tin, false, EXT>(A);
 }
 
-template <typename Tin>
+template <typename Tin, bool EXT>
 static hipError_t launch_decode_in(const DecodeArgs& A) {
     switch (A.dk) {
-        case 16: return launch_decode_dk<16, Tin>(A);
-        case 32: return launch_decode_dk<32, Tin>(A);
-        case 64: return launch_decode_dk<64, Tin>(A);
-        default: return launch_decode_dk<128, Tin>(A);
+        case 16: return launch_decode_dk<16, Tin, EXT>(A);
+        case 32: return launch_decode_dk<32, Tin, EXT>(A);
+        case 64: return launch_decode_dk<64, Tin, EXT>(A);
+        default: return launch_decode_dk<128, Tin, EXT>(A);
     }
 }
 
 hipError_t launch_decode(const DecodeArgs& A) {
-    return A.in_bf16 ? launch_decode_in<bf16_t>(A) : launch_decode_in<float>(A);
+    if (A.ext)
+        return A.in_bf16 ? launch_decode_in<bf16_t, true>(A) : launch_decode_in<float, true>(A);
+    return A.in_bf16 ? launch_decode_in<bf16_t, false>(A) : launch_decode_in<float, false>(A);
 }
 
 }  // namespace gdn

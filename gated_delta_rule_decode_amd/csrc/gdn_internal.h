@@ -30,6 +30,17 @@ struct DecodeArgs {
     void* y;
     bool z_bf16, w_bf16, y_bf16;
     float eps;
+    // serving form (gdn_decode_layer): slot table, raw gates, q/k L2 norm
+    bool ext;
+    const int32_t* slots;  // may be null: sequence n -> slot n
+    int num_slots;         // state holds num_slots x HV heads
+    const void* a_raw;     // null: g and beta are used as given
+    const void* b_raw;
+    bool gate_bf16;
+    const float* A_log;
+    const float* dt_bias;  // may be null
+    bool l2norm;
+    float l2_eps;
     hipStream_t stream;
 };
 

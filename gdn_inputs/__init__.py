@@ -27,6 +27,12 @@ Recipe (the same for every workload unless stated):
   beta = sigmoid(x'), x' ~ N(0, 1), fp32.
   z ~ N(0, 1) rounded to bf16 (workload 0: fp32); the norm weight w = 1.
 
+Raw decode-layer inputs (``make_decode_raw``), for the serving form of the
+step that activates gates and normalises q, k itself: q, k ~ N(0, 1) NOT
+normalised; a_raw, b_raw ~ N(0, 1) (the draws behind g and beta above);
+A_log ~ U(0, ln 16) per value head (the same draw as A_h); dt_bias ~
+N(0, dt_bias_std^2) per value head; w ~ 1 + N(0, 0.1^2).
+
 Every tensor comes from its own numpy Generator keyed by (seed, workload,
 tensor tag), so a tensor does not depend on the order in which the others are
 drawn.  Values that are bf16 are returned as float32 arrays holding exactly
@@ -43,10 +49,12 @@ import numpy as np
 __all__ = [
     "round_bf16", "bf16_bits", "PrefillInputs", "DecodeInputs", "make_prefill",
     "make_decode", "config_lengths", "workload", "WORKLOADS", "decay_scale",
+    "DecodeRawInputs", "make_decode_raw",
 ]
 
 # tensor tags for the per-tensor generator streams
-_TAG = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "z": 6, "A": 7, "s0": 8, "len": 9}
+_TAG = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "z": 6, "A": 7, "s0": 8, "len": 9,
+        "dt": 10, "w": 11}
 
 
 def _rng(seed: int, stream: int, tag: str) -> np.random.Generator:
@@ -204,6 +212,60 @@ def make_decode(steps, N, H, HV, dk, dv, *, dtype="bf16", decay="qwen", seed: in
     beta = (1.0 / (1.0 + np.exp(-xb))).astype(np.float32)
     w = np.ones(dv, dtype=np.float32)
     return DecodeInputs(q, k, v, g, beta, z, w, dtype, H, HV, dk, dv)
+
+
+@dataclass
+class DecodeRawInputs:
+    """Per-step decode-layer inputs with raw gates: [steps, N, ...]."""
+    q: np.ndarray        # [steps, N, H, dk]  not normalised
+    k: np.ndarray        # [steps, N, H, dk]  not normalised
+    v: np.ndarray        # [steps, N, HV, dv]
+    a_raw: np.ndarray    # [steps, N, HV]
+    b_raw: np.ndarray    # [steps, N, HV]
+    A_log: np.ndarray    # [HV] float32
+    dt_bias: np.ndarray  # [HV] float32
+    z: np.ndarray        # [steps, N, HV, dv]
+    w: np.ndarray        # [dv]
+    dtype: str
+    gate_dtype: str
+    H: int
+    HV: int
+    dk: int
+    dv: int
+
+    @property
+    def steps(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def N(self) -> int:
+        return self.q.shape[1]
+
+
+def make_decode_raw(steps, N, H, HV, dk, dv, *, dtype="bf16", gate_dtype="f32", seed: int = 0,
+                    stream: int = 300, dt_bias_std: float = 0.5) -> DecodeRawInputs:
+    """Raw decode-layer inputs (q, k unnormalised; gates as projections)."""
+    lead = (steps, N)
+    q = _normal(_rng(seed, stream, "q"), lead + (H, dk))
+    k = _normal(_rng(seed, stream, "k"), lead + (H, dk))
+    v = _normal(_rng(seed, stream, "v"), lead + (HV, dv))
+    z = _normal(_rng(seed, stream, "z"), lead + (HV, dv))
+    a_raw = _normal(_rng(seed, stream, "g"), lead + (HV,))
+    b_raw = _normal(_rng(seed, stream, "beta"), lead + (HV,))
+    A_log = _rng(seed, stream, "A").uniform(0.0, math.log(16.0), size=HV).astype(np.float32)
+    dt_bias = (_normal(_rng(seed, stream, "dt"), (HV,)) * np.float32(dt_bias_std)).astype(
+        np.float32)
+    w = (1.0 + 0.1 * _normal(_rng(seed, stream, "w"), (dv,))).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v, z = round_bf16(q), round_bf16(k), round_bf16(v), round_bf16(z)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    if gate_dtype == "bf16":
+        a_raw, b_raw = round_bf16(a_raw), round_bf16(b_raw)
+    elif gate_dtype != "f32":
+        raise ValueError(gate_dtype)
+    return DecodeRawInputs(q, k, v, a_raw, b_raw, A_log, dt_bias, z, w, dtype, gate_dtype, H,
+                           HV, dk, dv)
 
 
 def config_lengths(seed: int = 0, stream: int = 400, n: int = 8, lo: int = 256,

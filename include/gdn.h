@@ -114,6 +114,73 @@ gdn_status gdn_decode_step_norm(const void* q, const void* k, const void* v, gdn
                                 int HV, int dk, int dv, float scale, float eps, void* stream);
 
 /*
+ * gdn_decode_layer -- the serving form of the decode step: the token mixer of
+ * one DeltaNet layer for one token per sequence, in one launch, with the
+ * steps on either side of the recurrence done in the kernel.
+ *
+ *  - State pool.  The decoder owns all recurrent state and is advanced one
+ *    token per call (Qwen3.5-0.8B Core ML card, section "Model"); a server
+ *    keeps the states of all live requests in one pool and names, per batch
+ *    row, the slot to advance.  A slot outside [0, num_slots) skips that row:
+ *    its o and y rows are written as 0 and no state is read or written.  Two
+ *    rows naming the same slot race (caller error; every access stays inside
+ *    the pool).
+ *  - Gate activations.  The pages name the decay and the write strength but
+ *    not how the layer produces them; given the raw per-(token, value head)
+ *    projections, the kernel applies the Gated DeltaNet layer's
+ *    parameterisation (Yang et al., ICLR 2025):
+ *        g = -exp(A_log[h]) * softplus(a_raw + dt_bias[h]),  beta = sigmoid(b_raw)
+ *  - q/k L2 norm.  Optionally q and k are divided by sqrt(sum of squares +
+ *    l2_eps) per (row, key head) before the step.
+ *  - RMSNormGated, as in gdn_decode_step_norm, when z, w and y are given.
+ *
+ * Zero-initialise the struct and fill in what is used; all pointers are
+ * device pointers, 16-byte aligned except slots, a_raw, b_raw, g, beta,
+ * A_log and dt_bias (element-aligned).
+ */
+typedef struct gdn_decode_layer_args {
+    const void* q;          /* [N, H, dk]   in_dtype                                      */
+    const void* k;          /* [N, H, dk]   in_dtype                                      */
+    const void* v;          /* [N, HV, dv]  in_dtype                                      */
+    gdn_dtype in_dtype;
+    /* gates, activated: used when a_raw is NULL                                          */
+    const float* g;         /* [N, HV] fp32 log-decay (a = exp(g))                        */
+    const float* beta;      /* [N, HV] fp32                                               */
+    /* gates, raw: used when a_raw is not NULL (then b_raw and A_log are required)        */
+    const void* a_raw;      /* [N, HV] gate_dtype                                         */
+    const void* b_raw;      /* [N, HV] gate_dtype                                         */
+    gdn_dtype gate_dtype;
+    const float* A_log;     /* [HV] fp32                                                  */
+    const float* dt_bias;   /* [HV] fp32, or NULL for zeros                               */
+    int qk_l2norm;          /* nonzero: L2-normalise q and k first                        */
+    float l2_eps;           /* >= 0; > 0 keeps an all-zero q or k finite                  */
+    float* state;           /* [num_slots, HV, dv, dk] fp32, advanced in place            */
+    const int32_t* slots;   /* [N] int32, or NULL: row n uses slot n (num_slots >= N)     */
+    int num_slots;          /* >= 0                                                       */
+    void* o;                /* [N, HV, dv] o_dtype: scale * S_t q_t, or NULL if y is set  */
+    gdn_dtype o_dtype;
+    const void* z;          /* [N, HV, dv] z_dtype  RMSNormGated gate input, or NULL      */
+    gdn_dtype z_dtype;
+    const void* w;          /* [dv] w_dtype         RMSNormGated weight, or NULL          */
+    gdn_dtype w_dtype;
+    void* y;                /* [N, HV, dv] y_dtype  normed output, or NULL                */
+    gdn_dtype y_dtype;
+    float eps;              /* RMSNormGated epsilon, >= 0                                 */
+    int N, H, HV, dk, dv;   /* N >= 0 rows (0 is a successful no-op)                      */
+    float scale;
+} gdn_decode_layer_args;
+
+/* sizeof(gdn_decode_layer_args) as compiled into the library (binding check). */
+size_t gdn_decode_layer_args_size(void);
+
+/*
+ * Returns GDN_ERROR_INVALID_VALUE for a NULL args, a missing or misaligned
+ * pointer, a negative size or epsilon, neither o nor y given, y given without
+ * z and w, or slots NULL with num_slots < N.
+ */
+gdn_status gdn_decode_layer(const gdn_decode_layer_args* args, void* stream);
+
+/*
  * gdn_prefill_workspace_bytes -- device workspace that gdn_prefill_chunked
  * needs for this problem (a multiple of 256 bytes; 0 when T_total == 0).
  * Returns 0 for sizes that gdn_prefill_chunked would reject.

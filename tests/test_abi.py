@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert gdn.version() == 100
+    assert gdn.version() == 200
     for code, name in gdn.STATUS.items():
         assert L.gdn_status_string(code).decode() == name
     assert L.gdn_status_string(99).decode() == "GDN_UNKNOWN_STATUS"
@@ -181,3 +181,55 @@ def test_decode_norm_validation(L):
     assert _decode_norm(L, dv=48) == 2
     assert _decode_norm(L, z_dt=9) == 2
     assert _decode_norm(L, HV=6, H=4) == 1
+
+
+def _layer(L, **kw):
+    a = gdn.DecodeLayerArgs()
+    base = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=1, g=FAKE, beta=FAKE, state=FAKE, num_slots=0,
+                o=FAKE, o_dtype=0, N=0, H=2, HV=4, dk=64, dv=64, scale=1.0, l2_eps=1e-6,
+                eps=1e-6)
+    base.update(kw)
+    for name, val in base.items():
+        setattr(a, name, val)
+    return L.gdn_decode_layer(ctypes.byref(a), None)
+
+
+def test_decode_layer_struct_layout(L):
+    """The binding's mirror of gdn_decode_layer_args has the library's size and
+    the header's field order."""
+    assert L.gdn_decode_layer_args_size() == ctypes.sizeof(gdn.DecodeLayerArgs)
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct gdn_decode_layer_args \{(.*?)\}", text, re.S).group(1)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        names = decl.split(None, 1)[1] if not decl.startswith("const") else decl.split(None, 2)[2]
+        fields += [n.strip().lstrip("*").strip() for n in names.split(",")]
+    assert fields == [f for f, _ in gdn.DecodeLayerArgs._fields_]
+
+
+def test_decode_layer_validation(L):
+    OK, INVALID, UNSUP = 0, 1, 2
+    assert L.gdn_decode_layer(None, None) == INVALID
+    assert _layer(L) == OK                                   # N == 0, num_slots 0 with slots
+    assert _layer(L, N=3, num_slots=2) == INVALID            # no slot table: num_slots < N
+    assert _layer(L, N=-1) == INVALID
+    assert _layer(L, num_slots=-1, slots=FAKE) == INVALID
+    assert _layer(L, dk=48) == UNSUP
+    assert _layer(L, HV=3) == INVALID
+    assert _layer(L, in_dtype=7) == UNSUP
+    assert _layer(L, l2_eps=-1.0) == INVALID
+    assert _layer(L, l2_eps=float("nan")) == INVALID
+    n1 = dict(N=1, num_slots=1)
+    assert _layer(L, q=0, **n1) == INVALID
+    assert _layer(L, state=MISALIGNED, **n1) == INVALID
+    assert _layer(L, g=0, **n1) == INVALID                   # activated gates missing
+    assert _layer(L, a_raw=FAKE, gate_dtype=1, **n1) == INVALID        # raw: b_raw, A_log missing
+    assert _layer(L, a_raw=FAKE, b_raw=FAKE, gate_dtype=5, A_log=FAKE, **n1) == UNSUP
+    assert _layer(L, o=0, **n1) == INVALID                   # neither o nor y
+    assert _layer(L, o=0, y=FAKE, y_dtype=0, z=FAKE, z_dtype=0, **n1) == INVALID  # no w
+    assert _layer(L, y=FAKE, y_dtype=0, z=FAKE, z_dtype=0, w=FAKE, w_dtype=0, eps=-1.0,
+                  **n1) == INVALID
+    assert _layer(L, o=MISALIGNED, **n1) == INVALID
