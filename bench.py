@@ -12,7 +12,12 @@ Infinity Cache) and its own inputs, all resident in HBM before timing starts.
 The decode step and its RMSNormGated run as one kernel (gdn_decode_step_norm).
 The launch sequence of a step is captured once in HIP graphs and replayed.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill2|prefill3|prefill4]
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill2|prefill3|prefill4|serve]
+
+``--workload serve`` times the serving form of the decode step
+(gdn_decode_layer) on the Qwen3.6-35B-A3B DeltaNet shape: 128 rows drawn from
+a pool of 256 state slots per layer, raw bf16 gates activated in the kernel,
+q/k L2-normalised in the kernel, RMSNormGated fused, over 30 DeltaNet layers.
 
 Prints one JSON line.  ``value`` = tokens per second per DeltaNet layer over
 the whole job: 32 x (512 + 256) tokens x 18 layers / job time.
@@ -87,6 +92,14 @@ def prefill_flops(T, H, HV, dk, dv, C=64):
     per_k = 2 * C * dk * 2
     per_v = C * C / 3 + (2 * dk * dv + 2 * C * dv) * 2 + 2 * dk * dv
     return T * (H * per_k + HV * per_v)
+
+
+def layer_bytes_per_row(H, HV, dk, dv, in_bytes=2, gate_bytes=2, z_bytes=2, y_bytes=4):
+    """HBM bytes per row of the serving decode step (gdn_decode_layer with raw
+    gates, q/k norm and RMSNormGated): the slot's fp32 state read and written,
+    q, k, v, the two raw gates, z in, y out, the slot index."""
+    return (HV * dk * dv * 4 * 2 + H * dk * in_bytes * 2 + HV * dv * in_bytes
+            + HV * 2 * gate_bytes + HV * dv * z_bytes + HV * dv * y_bytes + 4)
 
 
 def norm_bytes(rows, HV, dv, x_bytes=4, z_bytes=2, y_bytes=4):
@@ -344,13 +357,115 @@ def run_copy(args):
             "read_bytes_per_launch": n * 4, "write_bytes_per_launch": n * 4}
 
 
+def run_serve(args):
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    import gdn_inputs as gi
+
+    N, SLOTS, H, HV, d, L = 128, 256, 16, 32, 128, 30
+    steps = args.decode_steps or 16
+    dev = torch.device("cuda", 0)
+    bf = torch.bfloat16
+    log(f"serve: rows={N} slots={SLOTS} H={H} HV={HV} d={d} layers={L} steps={steps}")
+    rng = np.random.default_rng(7)
+    layers = []
+    for l in range(L):
+        r = gi.make_decode_raw(steps, N, H, HV, d, d, seed=7000 + l, gate_dtype="bf16")
+        pool = torch.empty(SLOTS, HV, d, d, device=dev)
+        pool.normal_(0.0, 0.02, generator=torch.Generator(device=dev).manual_seed(l))
+        layers.append(dict(
+            q=torch.from_numpy(r.q).to(dev, bf), k=torch.from_numpy(r.k).to(dev, bf),
+            v=torch.from_numpy(r.v).to(dev, bf), z=torch.from_numpy(r.z).to(dev, bf),
+            a=torch.from_numpy(r.a_raw).to(dev, bf), b=torch.from_numpy(r.b_raw).to(dev, bf),
+            A_log=torch.from_numpy(r.A_log).to(dev), dt=torch.from_numpy(r.dt_bias).to(dev),
+            w=torch.from_numpy(r.w).to(dev), pool=pool,
+            slots=torch.from_numpy(np.stack([rng.permutation(SLOTS)[:N] for _ in range(steps)])
+                                   .astype(np.int32)).to(dev),
+            y=torch.empty(N, HV, d, device=dev)))
+    scale = d ** -0.5
+    torch.cuda.synchronize()
+
+    def serve_phase():
+        for t in range(steps):
+            for Ly in layers:
+                gdn.decode_layer(Ly["q"][t], Ly["k"][t], Ly["v"][t], Ly["pool"], a_raw=Ly["a"][t],
+                                 b_raw=Ly["b"][t], A_log=Ly["A_log"], dt_bias=Ly["dt"],
+                                 slots=Ly["slots"][t], qk_l2norm=True, z=Ly["z"][t], w=Ly["w"],
+                                 y=Ly["y"], scale=scale)
+
+    g_sv, s = graph_capture(serve_phase)
+    for _ in range(args.warmup):
+        g_sv.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(args.steps):
+            g_sv.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+    launches = steps * L
+    launch_us = ms * 1e3 / launches
+    bytes_launch = layer_bytes_per_row(H, HV, d, d) * N
+    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
+
+    # cost of the serving extras: the same launch on one contiguous state set
+    # (rows 0..N-1 of layer 0's pool, no slot table) with and without them
+    Ly = layers[0]
+    st = Ly["pool"][:N]
+    g32 = torch.full((N, HV), -0.1, device=dev)
+    b32 = torch.full((N, HV), 0.5, device=dev)
+
+    def timed(fn, reps=50):
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                fn()
+            e0.record(s)
+            for _ in range(reps):
+                fn()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    plain_us = timed(lambda: gdn.decode_step_norm(Ly["q"][0], Ly["k"][0], Ly["v"][0], g32, b32,
+                                                  st, Ly["z"][0], Ly["w"], y=Ly["y"],
+                                                  scale=scale))
+    extras_us = timed(lambda: gdn.decode_layer(Ly["q"][0], Ly["k"][0], Ly["v"][0], st,
+                                               a_raw=Ly["a"][0], b_raw=Ly["b"][0],
+                                               A_log=Ly["A_log"], dt_bias=Ly["dt"],
+                                               qk_l2norm=True, z=Ly["z"][0], w=Ly["w"],
+                                               y=Ly["y"], scale=scale))
+
+    tokens = N * steps * L
+    return {
+        "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s per DeltaNet layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwen3.6-35b-a3b-deltanet-serving-decode", "rows": N,
+                   "state_slots": SLOTS, "qk_heads": H, "v_heads": HV, "d_k": d, "d_v": d,
+                   "layers": L, "decode_steps": steps, "gates": "raw bf16",
+                   "qk_l2norm": True, "norm": "RMSNormGated", "inputs": "bf16"},
+        "roofline": {"kernel": "decode_kernel (serving: slots, gates, q/k norm, RMSNormGated)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(launch_us, 3),
+                     "algorithmic_bytes_per_launch": bytes_launch},
+        "extras_cost": {"same_state_us_plain_decode_norm": round(plain_us, 3),
+                        "same_state_us_layer_with_gates_l2_norm": round(extras_us, 3)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill2", "prefill3", "prefill4", "copy"])
+                    choices=["decode", "prefill2", "prefill3", "prefill4", "copy", "serve"])
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--decode-steps", type=int, default=0)
     ap.add_argument("--cpu-layers", type=int, default=12)
@@ -369,6 +484,8 @@ def main():
         out = run_decode_job(args)
     elif args.workload == "copy":
         out = run_copy(args)
+    elif args.workload == "serve":
+        out = run_serve(args)
     else:
         out = run_prefill(args, int(args.workload[-1]))
     print(json.dumps(out), flush=True)
