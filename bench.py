@@ -12,7 +12,12 @@ Infinity Cache) and its own inputs, all resident in HBM before timing starts.
 The decode step and its RMSNormGated run as one kernel (gdn_decode_step_norm).
 The launch sequence of a step is captured once in HIP graphs and replayed.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill2|prefill3|prefill4|serve]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode|prefill2|prefill3|prefill4|prefill5|serve]
+
+``prefill5`` is one 32768-token prompt at the 0.8B shape (the case the
+segment-parallel scan is for); prefill lines also report the time with
+segmentation turned off.
 
 ``--workload serve`` times the serving form of the decode step
 (gdn_decode_layer) on the Qwen3.6-35B-A3B DeltaNet shape: 128 rows drawn from
@@ -281,12 +286,16 @@ def run_decode_job(args):
     return out
 
 
+LONG_PROMPT = {"name": "qwen3.5-0.8b-long-prompt-prefill", "N": 1, "T": 32768, "H": 16, "HV": 16,
+               "dk": 128}
+
+
 def run_prefill(args, cfg: int):
     import torch
     import gated_delta_rule_decode_amd as gdn
     import gdn_inputs as gi
 
-    w = gi.WORKLOADS[cfg]
+    w = LONG_PROMPT if cfg == 5 else gi.WORKLOADS[cfg]
     H, HV, d = w["H"], w["HV"], w["dk"]
     lengths = gi.config_lengths(0) if cfg == 4 else np.array([w["T"]] * w["N"])
     N, T = len(lengths), int(np.sum(lengths))
@@ -301,20 +310,24 @@ def run_prefill(args, cfg: int):
     o = torch.empty(T, HV, d, device=dev)
     sf = torch.empty(N, HV, d, d, device=dev)
     ws = torch.empty(gdn.prefill_workspace_bytes(N, T, H, HV, d, d), dtype=torch.uint8, device=dev)
-    call = lambda: gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf, o=o,
-                                       workspace=ws)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+    def timed(seg):
+        call = lambda: gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf,
+                                           o=o, workspace=ws, segment_chunks=seg)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+
+    ms = timed(0)               # the library's own choice of the segment-parallel scan
+    ms_whole = timed(-1)        # one chain per (sequence, head, tile), for comparison
     pb = prefill_bytes(T, N, H, HV, d, d, s0=s0 is not None)
     pfl = prefill_flops(T, H, HV, d, d)
     return {
@@ -330,6 +343,7 @@ def run_prefill(args, cfg: int):
                      "unit": "GB/s", "frac": round(pb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": None, "tflops": round(pfl / (ms * 1e-3) / 1e12, 2),
                      "mfma_bf16_frac": round(pfl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
+        "unsegmented_ms_per_step": round(ms_whole, 4),
     }
 
 
@@ -465,7 +479,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill2", "prefill3", "prefill4", "copy", "serve"])
+                    choices=["decode", "prefill2", "prefill3", "prefill4", "prefill5", "copy",
+                             "serve"])
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--decode-steps", type=int, default=0)
     ap.add_argument("--cpu-layers", type=int, default=12)

@@ -33,7 +33,8 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_version", "gdn_status_string", "gdn_last_hip_error", "gdn_decode_step",
            "gdn_decode_step_norm", "gdn_decode_layer_args_size", "gdn_decode_layer",
-           "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_rmsnorm_gated")
+           "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_prefill_chunked_seg",
+           "gdn_rmsnorm_gated")
 
 __all__ = ["decode_step", "decode_step_norm", "decode_layer", "prefill_chunked", "rmsnorm_gated",
            "prefill_workspace_bytes", "DecodeLayerArgs", "GDNError", "lib", "LIBRARY", "EXPORTS",
@@ -98,6 +99,9 @@ def lib() -> ctypes.CDLL:
             raise ImportError("gdn_decode_layer_args layout differs between gdn.h and the binding")
         L.gdn_prefill_workspace_bytes.restype = _sz
         L.gdn_prefill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+        L.gdn_prefill_chunked_seg.restype = _i
+        L.gdn_prefill_chunked_seg.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
+                                              _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
         L.gdn_prefill_chunked.restype = _i
         L.gdn_prefill_chunked.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
                                           _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]
@@ -316,11 +320,14 @@ def prefill_workspace_bytes(N: int, T_total: int, H: int, HV: int, dk: int, dv: 
 
 def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_state=None,
                     o=None, scale: float = 1.0, chunk: int = 64, workspace=None,
-                    out_dtype=None, return_final_state: bool = True) -> Tuple:
+                    out_dtype=None, return_final_state: bool = True,
+                    segment_chunks: int = 0) -> Tuple:
     """Chunked prefill of a packed batch.
 
     q, k [T, H, dk], v [T, HV, dv]; g, beta [T, HV] fp32; cu_seqlens [N+1]
     int32 on the device; initial_state [N, HV, dv, dk] fp32 or None (zeros).
+    ``segment_chunks``: 0 lets the library choose the segment-parallel scan,
+    -1 turns it off, >= 32 forces segments of that many chunks.
     Returns (o [T, HV, dv], final_state [N, HV, dv, dk] or None)."""
     torch = _torch()
     f32 = torch.float32
@@ -349,12 +356,16 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_s
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace")
-    st = lib().gdn_prefill_chunked(
-        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
-        _ptr(initial_state), _ptr(final_state), _ptr(o), _dtype_code(o), H, HV, dk, dv, chunk,
-        float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(q.device))
-    _check("gdn_prefill_chunked", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+            T, _ptr(initial_state), _ptr(final_state), _ptr(o), _dtype_code(o), H, HV, dk, dv,
+            chunk, float(scale))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+    if segment_chunks == 0:
+        st = lib().gdn_prefill_chunked(*args, *tail)
+        _check("gdn_prefill_chunked", st)
+    else:
+        st = lib().gdn_prefill_chunked_seg(*args, int(segment_chunks), *tail)
+        _check("gdn_prefill_chunked_seg", st)
     return o, final_state
 
 

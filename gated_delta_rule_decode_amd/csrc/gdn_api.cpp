@@ -42,7 +42,7 @@ void clear_pending() { (void)hipGetLastError(); }
 
 namespace gdn {
 
-PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk) {
+PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv) {
     (void)H;
     PrefillLayout L{};
     // upper bound on sum_n ceil(len_n / 64) given sum_n len_n = T
@@ -66,7 +66,32 @@ PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk) {
     L.ws_Zh = region + 2 * rplane;
     L.ws_Zl = region + 2 * rplane + zplane;
     const size_t mfma_end = region + 2 * rplane + 2 * zplane;
-    L.total = valu_end > mfma_end ? valu_end : mfma_end;
+    off = valu_end > mfma_end ? valu_end : mfma_end;
+    // segment-parallel scan: plan, tables and the per-segment states
+    const size_t segb = (size_t)N + (maxc + kSegMinChunks - 1) / kSegMinChunks;
+    const size_t corrb = segb + maxc / kCorrChunks + 1;
+    L.seg_bound = (int)segb;
+    L.corr_bound = (int)corrb;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    L.plan = take(kPlanInts * sizeof(int32_t));
+    L.seg_seq = take(segb * sizeof(int32_t));
+    L.seg_c0 = take(segb * sizeof(int32_t));
+    L.seg_nch = take(segb * sizeof(int32_t));
+    L.seg_idx = take(segb * sizeof(int32_t));
+    L.seq_seg0 = take((size_t)N * sizeof(int32_t));
+    L.seq_nseg = take((size_t)N * sizeof(int32_t));
+    L.multi_seq = take((size_t)N * sizeof(int32_t));
+    L.corr_seg = take(corrb * sizeof(int32_t));
+    L.corr_c0 = take(corrb * sizeof(int32_t));
+    L.ws_E = take(segb * HV * (size_t)dv * dk * sizeof(float));
+    L.ws_Phi = take(segb * HV * (size_t)dk * dk * sizeof(float));
+    L.ws_Sin = take(segb * HV * (size_t)dv * dk * sizeof(float));
+    L.ws_W = take((size_t)T * HV * dk * sizeof(float));
+    L.total = off;
     return L;
 }
 
@@ -213,16 +238,22 @@ size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, in
     if (N < 0 || T_total < 0) return 0;
     if (heads_status(H, HV, dk, dv) != GDN_SUCCESS || chunk != gdn::kChunk) return 0;
     if (N == 0 || T_total == 0) return 0;
-    return gdn::prefill_layout(N, T_total, H, HV, dk).total;
+    return gdn::prefill_layout(N, T_total, H, HV, dk, dv).total;
 }
 
-gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
-                               const float* g, const float* beta, const int32_t* cu_seqlens,
-                               int N, int T_total, const float* initial_state,
-                               float* final_state, void* o, gdn_dtype o_dtype, int H, int HV,
-                               int dk, int dv, int chunk, float scale, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                        const float* g, const float* beta, const int32_t* cu_seqlens, int N,
+                        int T_total, const float* initial_state, float* final_state, void* o,
+                        gdn_dtype o_dtype, int H, int HV, int dk, int dv, int chunk, float scale,
+                        int segment_chunks, void* workspace, size_t workspace_bytes,
+                        void* stream) {
     if (N < 0 || T_total < 0) return GDN_ERROR_INVALID_VALUE;
+    if (segment_chunks != 0 && segment_chunks != -1 && segment_chunks < gdn::kSegMinChunks)
+        return GDN_ERROR_INVALID_VALUE;
     gdn_status st = heads_status(H, HV, dk, dv);
     if (st != GDN_SUCCESS) return st;
     if (chunk != gdn::kChunk) return GDN_ERROR_NOT_SUPPORTED;
@@ -240,7 +271,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return GDN_ERROR_INVALID_VALUE;
-    const gdn::PrefillLayout L = gdn::prefill_layout(N, T_total, H, HV, dk);
+    const gdn::PrefillLayout L = gdn::prefill_layout(N, T_total, H, HV, dk, dv);
     if ((size_t)L.max_chunks * HV > (size_t)(1u << 31) / (gdn::kChunk * gdn::kChunk))
         return GDN_ERROR_NOT_SUPPORTED;
     if (!workspace || workspace_bytes < L.total) return GDN_ERROR_WORKSPACE;
@@ -259,9 +290,53 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
     a.ws_Zh = reinterpret_cast<uint16_t*>(ws + L.ws_Zh);
     a.ws_Zl = reinterpret_cast<uint16_t*>(ws + L.ws_Zl);
     a.max_chunks = L.max_chunks;
+    a.seg_req = segment_chunks;
+    a.seg_bound = L.seg_bound;
+    a.corr_bound = L.corr_bound;
+    a.plan = reinterpret_cast<int32_t*>(ws + L.plan);
+    a.seg_seq = reinterpret_cast<int32_t*>(ws + L.seg_seq);
+    a.seg_c0 = reinterpret_cast<int32_t*>(ws + L.seg_c0);
+    a.seg_nch = reinterpret_cast<int32_t*>(ws + L.seg_nch);
+    a.seg_idx = reinterpret_cast<int32_t*>(ws + L.seg_idx);
+    a.seq_seg0 = reinterpret_cast<int32_t*>(ws + L.seq_seg0);
+    a.seq_nseg = reinterpret_cast<int32_t*>(ws + L.seq_nseg);
+    a.multi_seq = reinterpret_cast<int32_t*>(ws + L.multi_seq);
+    a.corr_seg = reinterpret_cast<int32_t*>(ws + L.corr_seg);
+    a.corr_c0 = reinterpret_cast<int32_t*>(ws + L.corr_c0);
+    a.ws_E = reinterpret_cast<float*>(ws + L.ws_E);
+    a.ws_Phi = reinterpret_cast<float*>(ws + L.ws_Phi);
+    a.ws_Sin = reinterpret_cast<float*>(ws + L.ws_Sin);
+    a.ws_W = reinterpret_cast<float*>(ws + L.ws_W);
     a.stream = s;
     clear_pending();
     return from_hip(gdn::launch_prefill(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                               const float* g, const float* beta, const int32_t* cu_seqlens,
+                               int N, int T_total, const float* initial_state,
+                               float* final_state, void* o, gdn_dtype o_dtype, int H, int HV,
+                               int dk, int dv, int chunk, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, in_dtype, g, beta, cu_seqlens, N, T_total, initial_state,
+                        final_state, o, o_dtype, H, HV, dk, dv, chunk, scale, 0, workspace,
+                        workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_chunked_seg(const void* q, const void* k, const void* v,
+                                   gdn_dtype in_dtype, const float* g, const float* beta,
+                                   const int32_t* cu_seqlens, int N, int T_total,
+                                   const float* initial_state, float* final_state, void* o,
+                                   gdn_dtype o_dtype, int H, int HV, int dk, int dv, int chunk,
+                                   float scale, int segment_chunks, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, in_dtype, g, beta, cu_seqlens, N, T_total, initial_state,
+                        final_state, o, o_dtype, H, HV, dk, dv, chunk, scale, segment_chunks,
+                        workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_rmsnorm_gated(const void* x, gdn_dtype x_dtype, const void* z, gdn_dtype z_dtype,

@@ -71,8 +71,31 @@ struct PrefillArgs {
     uint16_t* ws_Zh;
     uint16_t* ws_Zl;
     int max_chunks;
+    // segment-parallel scan (MFMA path).  A sequence is cut into segments of
+    // whole chunks; the plan is made on the device from cu_seqlens.
+    int seg_req;         // 0: automatic; -1: never; >= kSegMinChunks: this segment length
+    int seg_bound;       // capacity of the segment tables
+    int corr_bound;      // capacity of the correction item table
+    int32_t* plan;       // [kPlanInts]: nseg, ncorr, segment length (0: none), nmulti
+    int32_t* seg_seq;    // [seg_bound] sequence of segment s
+    int32_t* seg_c0;     // [seg_bound] global index of its first chunk
+    int32_t* seg_nch;    // [seg_bound] its chunks
+    int32_t* seg_idx;    // [seg_bound] its position in the sequence (0: first)
+    int32_t* seq_seg0;   // [N] first segment of sequence n
+    int32_t* seq_nseg;   // [N] segments of sequence n
+    int32_t* multi_seq;  // [N] sequences with more than one segment
+    int32_t* corr_seg;   // [corr_bound] correction item: its segment
+    int32_t* corr_c0;    // [corr_bound] correction item: its first chunk (global index)
+    float* ws_E;         // [seg_bound, HV, dv, dk] end state of a segment's own pass
+    float* ws_Phi;       // [seg_bound, HV, dk, dk] transition of a segment
+    float* ws_Sin;       // [seg_bound, HV, dv, dk] state entering a segment
+    float* ws_W;         // [T, HV, dk] scale Phi_t q_t for tokens of later segments
     hipStream_t stream;
 };
+
+constexpr int kSegMinChunks = 32;  // shortest segment of the segment-parallel scan
+constexpr int kCorrChunks = 4;     // chunks per item of the correction pass
+constexpr int kPlanInts = 8;
 
 struct NormArgs {
     const void* x;
@@ -88,10 +111,13 @@ struct NormArgs {
 
 // Workspace layout of gdn_prefill_chunked (byte offsets, 256-aligned).
 struct PrefillLayout {
-    size_t chunk_off, ws_G, ws_T, ws_Rh, ws_Rl, ws_Zh, ws_Zl, total;
-    int max_chunks;
+    size_t chunk_off, ws_G, ws_T, ws_Rh, ws_Rl, ws_Zh, ws_Zl;
+    size_t plan, seg_seq, seg_c0, seg_nch, seg_idx, seq_seg0, seq_nseg, multi_seq, corr_seg,
+        corr_c0, ws_E, ws_Phi, ws_Sin, ws_W;
+    size_t total;
+    int max_chunks, seg_bound, corr_bound;
 };
-PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk);
+PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);

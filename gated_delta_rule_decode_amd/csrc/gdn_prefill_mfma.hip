@@ -29,6 +29,8 @@
 // of storing P), U = T' X, O and the state update.  It reads K, Q, V, G and T'
 // fragments straight from memory into registers one chunk ahead; LDS holds
 // the state tile, the X, U, U' exchange tiles and the chunk's K rows.
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -551,26 +553,56 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     constexpr int RPI = 64 / PPR;  // rows per coalesced 1 KiB load
     constexpr int NLD = 16 / RPI;  // loads per row block and tile
 
-    const int H = A.H, HV = A.HV, dv = A.dv, N = A.N;
+    const int H = A.H, HV = A.HV, dv = A.dv;
     const int tid = threadIdx.x;
     const int tb = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index = row block
     __builtin_assume(tb >= 0 && tb < 4);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int tiles = dv / BV;
+    // Work items.  The first part of the grid holds the value-state items
+    // (segment, value head, 32-row tile of S); the second the transition
+    // items of segments after a sequence's first (segment, value head, 32-row
+    // tile of Phi: the same scan from the identity with V = 0, writing
+    // w = scale Phi_t q_t instead of o).  Without segmentation a segment is a
+    // sequence and every transition item exits at once.
     // XCD-aware mapping: workgroup b runs on XCD b % 8; all tiles of a chain
-    // get the same b % 8 and neighbouring dispatch slots
+    // get the same b % 8 and neighbouring dispatch slots.
+    const int TV = dv / BV;
     const int b = blockIdx.x;
-    const int slot = b >> 3;
-    const int tile = slot % tiles;
-    const int chain = (slot / tiles) * 8 + (b & 7);
-    if (chain >= N * HV) return;
-    const int n = chain / HV, h = chain - n * HV;
+    const int nb1 = ((A.seg_bound * HV + 7) / 8) * 8 * TV;
+    const bool trans = b >= nb1;
+    const int bb = trans ? b - nb1 : b;
+    const int TT = trans ? DK / BV : TV;
+    const int slot = bb >> 3;
+    const int tile = slot % TT;
+    const int chain = (slot / TT) * 8 + (bb & 7);
+    const int nseg = __builtin_amdgcn_readfirstlane(A.plan[0]);
+    if (chain >= nseg * HV) return;
+    const int sg = chain / HV, h = chain - sg * HV;
+    const int n = __builtin_amdgcn_readfirstlane(A.seg_seq[sg]);
+    const int sidx = __builtin_amdgcn_readfirstlane(A.seg_idx[sg]);
+    if (trans && sidx == 0) return;
     const int hk = h / (HV / H);
-    const size_t sbase = ((size_t)chain * dv + (size_t)tile * BV) * DK;
     const bf16_t* kp = static_cast<const bf16_t*>(A.k);
     const bf16_t* qp = static_cast<const bf16_t*>(A.q);
     const bf16_t* vp = static_cast<const bf16_t*>(A.v);
     Tout* op = static_cast<Tout*>(A.o);
+    // where the item's state starts and ends (row-major, DK columns)
+    const float* init = nullptr;  // null: zero state (or the identity for a transition item)
+    float* fin;
+    size_t ibase = 0, fbase;
+    if (trans) {
+        fin = A.ws_Phi;
+        fbase = ((size_t)(sg * HV + h) * DK + (size_t)tile * BV) * DK;
+    } else if (sidx == 0) {
+        init = A.s0;
+        ibase = ((size_t)(n * HV + h) * dv + (size_t)tile * BV) * DK;
+        const bool whole = __builtin_amdgcn_readfirstlane(A.seq_nseg[n]) == 1;
+        fin = whole ? A.s_final : A.ws_E;
+        fbase = whole ? ibase : ((size_t)(sg * HV + h) * dv + (size_t)tile * BV) * DK;
+    } else {
+        fin = A.ws_E;
+        fbase = ((size_t)(sg * HV + h) * dv + (size_t)tile * BV) * DK;
+    }
 
     // state: sacc[x][ibS][r] = S[i = 16 ibS + lr][j = 16 (NJB tb + x) + 4 lg + r]
     f4_t sacc[NJB][2];
@@ -578,10 +610,14 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     for (int x = 0; x < NJB; ++x)
 #pragma unroll
         for (int ibS = 0; ibS < 2; ++ibS) {
-            const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * tb + x) + 4 * lg;
-            if (A.s0) {
-                const float4 v4 = *reinterpret_cast<const float4*>(A.s0 + off);
+            const int i = 16 * ibS + lr, j = 16 * (NJB * tb + x) + 4 * lg;
+            if (init) {
+                const float4 v4 = *reinterpret_cast<const float4*>(init + ibase + (size_t)i * DK + j);
                 sacc[x][ibS] = f4_t{v4.x, v4.y, v4.z, v4.w};
+            } else if (trans) {
+                const int d = tile * BV + i - j;  // identity: 1 where row == column
+                sacc[x][ibS] = f4_t{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f,
+                                    d == 3 ? 1.f : 0.f};
             } else {
                 sacc[x][ibS] = f4_t{0.f, 0.f, 0.f, 0.f};
             }
@@ -591,9 +627,18 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
         for (int x = 0; x < NJB; ++x)
 #pragma unroll
             for (int ibS = 0; ibS < 2; ++ibS) {
-                const size_t off = sbase + (size_t)(16 * ibS + lr) * DK + 16 * (NJB * tb + x) + 4 * lg;
-                *reinterpret_cast<float4*>(dst + off) =
-                    make_float4(sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]);
+                const int i = 16 * ibS + lr, j = 16 * (NJB * tb + x) + 4 * lg;
+                if (trans) {
+                    // Phi is stored transposed (Phi^T[j][i]): the combine pass
+                    // reads it as an MFMA B operand, 8 consecutive i per lane
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dst[(size_t)(sg * HV + h) * DK * DK + (size_t)(j + r) * DK + tile * BV + i] =
+                            sacc[x][ibS][r];
+                } else {
+                    *reinterpret_cast<float4*>(dst + fbase + (size_t)i * DK + j) =
+                        make_float4(sacc[x][ibS][0], sacc[x][ibS][1], sacc[x][ibS][2], sacc[x][ibS][3]);
+                }
             }
     };
     auto store_state_lds = [&]() {
@@ -612,11 +657,12 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
 
     int sq, eq;
     seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
-    const int c_first = A.chunk_off[n];
-    int nch = A.chunk_off[n + 1] - c_first;
+    const int c_first = __builtin_amdgcn_readfirstlane(A.seg_c0[sg]);
+    int nch = __builtin_amdgcn_readfirstlane(A.seg_nch[sg]);
+    sq += (c_first - min(A.chunk_off[n], A.max_chunks)) * C;  // the segment's first token
     if (c_first + nch > A.max_chunks) nch = max(0, A.max_chunks - c_first);
     if (nch <= 0) {
-        if (A.s_final) store_state(A.s_final);
+        if (fin) store_state(fin);
         return;
     }
 
@@ -631,6 +677,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
         v_off[r] = ((uint32_t)(16 * tb + 4 * lg + r) * HV + h) * dv * 2 + (tile * BV + lr) * 2;
+    const uint32_t v_on = trans ? 0u : 1u;  // a transition item reads V as zero
     const uint32_t r_off = (2 * tb * 64 + l) * 16;  // fragment (tb, kk): + 1 KiB kk
     uint32_t z_off[NJB];                             // fragment (jb, kk): + 1 KiB kk
 #pragma unroll
@@ -674,7 +721,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     };
     auto load_v = [&](int jc) {
         const int t0 = chunk_t0(jc), L = chunk_L(jc);
-        const __amdgpu_buffer_rsrc_t rv = in_rsrc(vp + (size_t)t0 * HV * dv, (uint32_t)L * v_row);
+        const __amdgpu_buffer_rsrc_t rv = in_rsrc(vp + (size_t)t0 * HV * dv, v_on * L * v_row);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -834,16 +881,29 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
         load_rz(nj);
         {
             // qsa[ib][r] = O[t = 16 tb + lr][i = 16 ib + 4 lg + r]; rows t >= L land
-            // at or past the resource end and are dropped
-            const __amdgpu_buffer_rsrc_t orsrc =
-                out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
+            // at or past the resource end and are dropped.  A transition item
+            // writes w (fp32, dk per token and head) instead of o.
             const int t = 16 * tb + lr;
+            if (trans) {
+                float* wp = A.ws_W + (size_t)t0 * HV * DK;
+                const __amdgpu_buffer_rsrc_t wr = out_rsrc(wp, (uint32_t)(L * HV * DK * 4));
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const float ov[4] = {A.scale * qsa[ib][0], A.scale * qsa[ib][1],
-                                     A.scale * qsa[ib][2], A.scale * qsa[ib][3]};
-                out_store4(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * ib + 4 * lg), ov,
-                           op);
+                for (int ib = 0; ib < 2; ++ib) {
+                    const float ov[4] = {A.scale * qsa[ib][0], A.scale * qsa[ib][1],
+                                         A.scale * qsa[ib][2], A.scale * qsa[ib][3]};
+                    out_store4(wr, (uint32_t)((t * HV + h) * DK + tile * BV + 16 * ib + 4 * lg), ov,
+                               wp);
+                }
+            } else {
+                const __amdgpu_buffer_rsrc_t orsrc =
+                    out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const float ov[4] = {A.scale * qsa[ib][0], A.scale * qsa[ib][1],
+                                         A.scale * qsa[ib][2], A.scale * qsa[ib][3]};
+                    out_store4(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * ib + 4 * lg),
+                               ov, op);
+                }
             }
         }
         // the state tile in LDS is read only in (A), which every wave has left
@@ -851,19 +911,414 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
         __syncthreads();
     }
 
-    if (A.s_final) store_state(A.s_final);
+    if (fin) store_state(fin);
 }
 
+// ---------------------------------------------------------------------------
+// segment-parallel scan: plan, combine, correction
+// ---------------------------------------------------------------------------
+// The chunk map of a segment is affine in the state entering it:
+//     S_end = S_in Phi + E,   o_t = scale S_t q_t = o0_t + S_in w_t,
+// with Phi the product of the segment's token transitions a (I - b k k^T),
+// E and o0 the end state and outputs of the segment's own pass from a zero
+// state, and w_t = scale Phi_t q_t.  So every segment after a sequence's first
+// runs twice in parallel with the other segments (the value pass from zero,
+// giving E and o0, and the transition pass from the identity with V = 0,
+// giving Phi and w), a short per-sequence pass chains
+// S_in(j+1) = S_in(j) Phi_j + E_j, and a parallel pass adds S_in w_t to o.
+
+// Exclusive prefix sum of count(i) over i < n; emit(i, position, count) is
+// called once for every i.  Returns the total.  All 256 threads take part.
+template <typename F, typename G>
+__device__ int block_exclusive_scan(int n, F count, G emit, int* buf) {
+    int carry = 0;
+    for (int base = 0; base < n; base += 256) {
+        const int i = base + (int)threadIdx.x;
+        const int c = i < n ? count(i) : 0;
+        buf[threadIdx.x] = c;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int add = (int)threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+            __syncthreads();
+            buf[threadIdx.x] += add;
+            __syncthreads();
+        }
+        if (i < n) emit(i, carry + buf[threadIdx.x] - c, c);
+        carry += buf[255];
+        __syncthreads();
+    }
+    return carry;
+}
+
+// Segment length candidates (chunks; 0: do not segment) and the cost model
+// that picks one, in microseconds, fitted to measurements of the scan on the
+// MI355X: a chain step takes about 2.2 us while at most 64 workgroups run,
+// 2.6 us up to 256 (one per CU) and 4.5 us where two share a CU, and the
+// whole launch sustains about 110 chain steps per us; a segmented run moves
+// about 8 (dk + dv) more bytes per token and head of every later segment (w
+// written and read, o read and written again) at about 5 TB/s, plus about
+// 3 us per segment of the combine pass.  A launch that already gives every
+// CU a chain is not segmented: segments add work and no idle CU takes it.
+constexpr int kSegCand[7] = {0, 1024, 512, 256, 128, 64, 32};
+constexpr int kNCand = 7;
+
+// One workgroup: choose the segment length, cut the sequences and list the
+// work of the combine and correction passes.  plan = {segments, correction
+// items, segment length (0: none), sequences with more than one segment}.
+__global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A, int TV, int TK) {
+    __shared__ int ibuf[256];
+    __shared__ float acc[3][kNCand];  // items, chain steps, tokens of later segments
+    __shared__ int s_cmax;
+    __shared__ int s_len;
+    const int N = A.N, HV = A.HV;
+    const int32_t* co = A.chunk_off;
+    auto nchunks = [&](int n) {
+        return max(0, min(co[n + 1], A.max_chunks) - min(co[n], A.max_chunks));
+    };
+
+    if (A.seg_req != 0) {
+        if (threadIdx.x == 0) s_len = A.seg_req < 0 ? 0 : A.seg_req;
+    } else {
+        if (threadIdx.x < 3 * kNCand) (&acc[0][0])[threadIdx.x] = 0.f;
+        if (threadIdx.x == 0) s_cmax = 0;
+        __syncthreads();
+        float items[kNCand] = {}, steps[kNCand] = {}, later[kNCand] = {};
+        int cmax = 0;
+        for (int n = threadIdx.x; n < N; n += 256) {
+            const int c = nchunks(n);
+            cmax = max(cmax, c);
+#pragma unroll
+            for (int k = 0; k < kNCand; ++k) {
+                const int L = kSegCand[k] ? kSegCand[k] : (1 << 30);
+                const int m = c > 0 ? (c + L - 1) / L : 1;
+                const int first = min(c, L);
+                items[k] += (float)HV * TV + (float)(m - 1) * HV * (TV + TK);
+                steps[k] += (float)first * HV * TV + (float)(c - first) * HV * (TV + TK);
+                later[k] += (float)(c - first) * kChunk;
+            }
+        }
+        // wavefront sums first, then one shared-memory atomic per wavefront
+        auto wsum = [](float x) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+            return x;
+        };
+#pragma unroll
+        for (int k = 0; k < kNCand; ++k) {
+            items[k] = wsum(items[k]);
+            steps[k] = wsum(steps[k]);
+            later[k] = wsum(later[k]);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) cmax = max(cmax, __shfl_xor(cmax, o, 64));
+        if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+            for (int k = 0; k < kNCand; ++k) {
+                atomicAdd(&acc[0][k], items[k]);
+                atomicAdd(&acc[1][k], steps[k]);
+                atomicAdd(&acc[2][k], later[k]);
+            }
+            atomicMax(&s_cmax, cmax);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int cm = s_cmax;
+            const float dk = 32.f * TK, dv = 32.f * TV;
+            float best = 0.f;
+            int bestL = 0;
+            for (int k = 0; k < (acc[0][0] < 256.f ? kNCand : 1); ++k) {
+                const int L = kSegCand[k] ? kSegCand[k] : (1 << 30);
+                const bool seg = cm > L;
+                const float step = acc[0][k] <= 64.f ? 2.2f : (acc[0][k] <= 256.f ? 2.6f : 4.5f);
+                float cost = fmaxf(acc[1][k] / 110.f, (float)min(cm, L) * step);
+                if (seg)
+                    cost += acc[2][k] * HV * 8.f * (dk + dv) / 5.0e6f + 3.f * ((cm + L - 1) / L) + 5.f;
+                if (k == 0 || cost < best) {
+                    best = cost;
+                    bestL = seg ? L : 0;
+                }
+            }
+            s_len = bestL;
+        }
+    }
+    __syncthreads();
+    const int Ls = s_len;
+    auto nseg_of = [&](int n) {
+        const int c = nchunks(n);
+        return (Ls > 0 && c > 0) ? (c + Ls - 1) / Ls : 1;
+    };
+    // segments of every sequence
+    const int nseg = block_exclusive_scan(
+        N, nseg_of,
+        [&](int n, int pos, int m) {
+            const int c = nchunks(n);
+            const int len = Ls > 0 ? Ls : c;
+            A.seq_seg0[n] = pos;
+            A.seq_nseg[n] = m;
+            for (int j = 0; j < m; ++j) {
+                A.seg_seq[pos + j] = n;
+                A.seg_c0[pos + j] = min(co[n], A.max_chunks) + j * len;
+                A.seg_nch[pos + j] = max(0, min(len, c - j * len));
+                A.seg_idx[pos + j] = j;
+            }
+        },
+        ibuf);
+    // sequences with more than one segment
+    const int nmulti = block_exclusive_scan(
+        N, [&](int n) { return nseg_of(n) > 1 ? 1 : 0; },
+        [&](int n, int pos, int c) {
+            if (c) A.multi_seq[pos] = n;
+        },
+        ibuf);
+    __syncthreads();  // the segment tables are complete
+    // correction items: groups of kCorrChunks chunks of every later segment
+    const int ncorr = block_exclusive_scan(
+        nseg,
+        [&](int sg) {
+            return A.seg_idx[sg] > 0 ? (A.seg_nch[sg] + kCorrChunks - 1) / kCorrChunks : 0;
+        },
+        [&](int sg, int pos, int c) {
+            for (int g = 0; g < c; ++g) {
+                A.corr_seg[pos + g] = sg;
+                A.corr_c0[pos + g] = A.seg_c0[sg] + g * kCorrChunks;
+            }
+        },
+        ibuf);
+    if (threadIdx.x == 0) {
+        A.plan[0] = nseg;
+        A.plan[1] = ncorr;
+        A.plan[2] = Ls;
+        A.plan[3] = nmulti;
+    }
+}
+
+// Combine: per (sequence with several segments, value head, 32-row tile of
+// S) walk the segments in order, S_in(j+1) = S_in(j) Phi_j + E_j; S_in of
+// every later segment is kept for the correction, and the last product is the
+// sequence's final state.  The product runs on MFMA with both operands split
+// into hi + lo bf16 (fp32 accumulation), S_in staying in LDS as fp32 between
+// steps; Phi^T and E of the next segment are loaded during the current step.
+// Wave w computes output column blocks NCB w .. NCB w + NCB - 1, both row
+// blocks.  Persistent over items.
+template <int DK>
+__global__ __launch_bounds__(256) void combine_kernel(const PrefillArgs A) {
+    constexpr int BV = 32;
+    constexpr int SP = DK + 4;        // padded fp32 row in LDS
+    constexpr int NKK = DK / 32;      // k-steps
+    constexpr int NCB = DK / 16 / 4;  // column blocks per wave
+    __shared__ __attribute__((aligned(16))) float Sc[BV * SP];
+    const int HV = A.HV, dv = A.dv, TV = dv / BV;
+    const int nmulti = A.plan[3];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, lr = l & 15, lg = l >> 4;
+    for (int item = blockIdx.x; item < nmulti * HV * TV; item += gridDim.x) {
+        const int m = item / (HV * TV);
+        const int h = (item / TV) % HV, tile = item % TV;
+        const int n = A.multi_seq[m];
+        const int s0 = A.seq_seg0[n], ns = A.seq_nseg[n];
+        auto rows = [&](float* base, int sgi) {  // this tile's 32 rows of a value state
+            return base + ((size_t)(sgi * HV + h) * dv + (size_t)tile * BV) * DK;
+        };
+        // B fragments (Phi^T rows = output columns) and E at the output positions
+        bf8_t bh[NCB][NKK], bl[NCB][NKK];
+        float ev[NCB][2][4];
+        auto load_next = [&](int sgi) {
+            const float* pt = A.ws_Phi + (size_t)(sgi * HV + h) * DK * DK;
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const float* p = pt + (size_t)(16 * (NCB * w + c) + lr) * DK + 32 * kk + 8 * lg;
+                    const float4 x0 = *reinterpret_cast<const float4*>(p);
+                    const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
+                    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    split8(x, bh[c][kk], bl[c][kk]);
+                }
+            const float* e = rows(A.ws_E, sgi);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ev[c][rb][r] = e[(size_t)(16 * rb + 4 * lg + r) * DK + 16 * (NCB * w + c) + lr];
+        };
+        __syncthreads();  // the previous item has finished with Sc
+        {
+            const float* e0 = rows(A.ws_E, s0);
+            for (int x = tid; x < BV * DK / 4; x += 256) {
+                const int r = x / (DK / 4), c = 4 * (x % (DK / 4));
+                *reinterpret_cast<float4*>(&Sc[r * SP + c]) = *reinterpret_cast<const float4*>(e0 + (size_t)r * DK + c);
+            }
+        }
+        if (ns > 1) load_next(s0 + 1);
+        __syncthreads();
+        for (int j = 1; j < ns; ++j) {
+            const int sgi = s0 + j;
+            // S_in of this segment, for the correction
+            {
+                float* dst = rows(A.ws_Sin, sgi);
+                for (int x = tid; x < BV * DK / 4; x += 256) {
+                    const int r = x / (DK / 4), c = 4 * (x % (DK / 4));
+                    *reinterpret_cast<float4*>(dst + (size_t)r * DK + c) = *reinterpret_cast<const float4*>(&Sc[r * SP + c]);
+                }
+            }
+            f4_t d[NCB][2];
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    d[c][rb] = f4_t{ev[c][rb][0], ev[c][rb][1], ev[c][rb][2], ev[c][rb][3]};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    const float* p = &Sc[(16 * rb + lr) * SP + 32 * kk + 8 * lg];
+                    const float4 x0 = *reinterpret_cast<const float4*>(p);
+                    const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
+                    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    bf8_t ah, al;
+                    split8(x, ah, al);
+#pragma unroll
+                    for (int c = 0; c < NCB; ++c) {
+                        d[c][rb] = mfma(ah, bh[c][kk], d[c][rb]);
+                        d[c][rb] = mfma(al, bh[c][kk], d[c][rb]);
+                        d[c][rb] = mfma(ah, bl[c][kk], d[c][rb]);
+                    }
+                }
+            if (j + 1 < ns) load_next(sgi + 1);
+            __syncthreads();  // every wave has read S_in
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Sc[(16 * rb + 4 * lg + r) * SP + 16 * (NCB * w + c) + lr] = d[c][rb][r];
+            __syncthreads();
+        }
+        if (A.s_final) {
+            float* dst = A.s_final + ((size_t)(n * HV + h) * dv + (size_t)tile * BV) * DK;
+            for (int x = tid; x < BV * DK / 4; x += 256) {
+                const int r = x / (DK / 4), c = 4 * (x % (DK / 4));
+                *reinterpret_cast<float4*>(dst + (size_t)r * DK + c) = *reinterpret_cast<const float4*>(&Sc[r * SP + c]);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float4 in_load4(__amdgpu_buffer_rsrc_t r, uint32_t off_elems) {
+    typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+    const u4_t u = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off_elems * 4), 0, 0));
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+__device__ __forceinline__ void load4_any(__amdgpu_buffer_rsrc_t r, uint32_t off, float* v, float*) {
+    const float4 x = in_load4(r, off);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+__device__ __forceinline__ void load4_any(__amdgpu_buffer_rsrc_t r, uint32_t off, float* v, bf16_t*) {
+    typedef unsigned u2_t __attribute__((ext_vector_type(2)));
+    const u2_t u = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off * 2), 0, 0));
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+
+// Correction: o_t += S_in w_t for the tokens of every later segment, as
+// O^T = S_in W^T on MFMA with both operands split into hi + lo bf16.  An item
+// is (group of kCorrChunks chunks of one segment, value head); S_in of the
+// item is staged in LDS once, wavefront w takes tokens 16 w .. 16 w + 15 of
+// each chunk.  Persistent over items.
+template <int DK, typename Tout>
+__global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
+    constexpr int C = kChunk;
+    constexpr int KP = DK + 8;
+    constexpr int NKK = DK / 32;
+    __shared__ __attribute__((aligned(16))) __bf16 Sh[128 * KP];
+    __shared__ __attribute__((aligned(16))) __bf16 Sl[128 * KP];
+    const int HV = A.HV, dv = A.dv;
+    const int ncorr = A.plan[1];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, lr = l & 15, lg = l >> 4;
+    Tout* op = static_cast<Tout*>(A.o);
+    for (int item = blockIdx.x; item < ncorr * HV; item += gridDim.x) {
+        const int ci = item / HV, h = item - ci * HV;
+        const int sg = A.corr_seg[ci];
+        const int cfirst = A.corr_c0[ci];
+        const int n = A.seg_seq[sg];
+        const int cend = min(A.seg_c0[sg] + A.seg_nch[sg], cfirst + kCorrChunks);
+        int sq, eq;
+        seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
+        const int cseq = min(A.chunk_off[n], A.max_chunks);
+        // S_in (dv x DK, fp32) -> hi / lo bf16 rows in LDS
+        const float* sin = A.ws_Sin + (size_t)(sg * HV + h) * dv * DK;
+        __syncthreads();  // the previous item has finished reading Sh, Sl
+        for (int e = tid; e < dv * DK / 8; e += 256) {
+            const int row = e / (DK / 8), col = 8 * (e % (DK / 8));
+            const float4 a = *reinterpret_cast<const float4*>(sin + (size_t)row * DK + col);
+            const float4 b = *reinterpret_cast<const float4*>(sin + (size_t)row * DK + col + 4);
+            const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            bf8_t hi, lo;
+            split8(x, hi, lo);
+            *reinterpret_cast<bf8_t*>(&Sh[row * KP + col]) = hi;
+            *reinterpret_cast<bf8_t*>(&Sl[row * KP + col]) = lo;
+        }
+        __syncthreads();
+        for (int c = cfirst; c < cend; ++c) {
+            const int t0 = sq + (c - cseq) * C;
+            const int L = min(C, eq - t0);
+            // W^T fragments: column = token 16 w + lr, k = 32 kk + 8 lg .. + 7
+            const __amdgpu_buffer_rsrc_t wr = in_rsrc(A.ws_W + (size_t)t0 * HV * DK, (uint32_t)(L * HV * DK * 4));
+            const uint32_t wrow = (uint32_t)((16 * w + lr) * HV + h) * DK;
+            bf8_t wh[NKK], wl[NKK];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const float4 a = in_load4(wr, wrow + 32 * kk + 8 * lg);
+                const float4 b = in_load4(wr, wrow + 32 * kk + 8 * lg + 4);
+                const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                split8(x, wh[kk], wl[kk]);
+            }
+            const __amdgpu_buffer_rsrc_t orr = out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
+            for (int nb = 0; nb < dv / 16; ++nb) {
+                f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const bf8_t ah = lds8(&Sh[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
+                    const bf8_t al = lds8(&Sl[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
+                    d = mfma(ah, wh[kk], d);
+                    d = mfma(al, wh[kk], d);
+                    d = mfma(ah, wl[kk], d);
+                }
+                // d[r] = (S_in W^T)[i = 16 nb + 4 lg + r][t = 16 w + lr]
+                const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * dv + 16 * nb + 4 * lg;
+                float ov[4];
+                load4_any(orr, off, ov, op);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ov[r] += d[r];
+                out_store4(orr, off, ov, op);
+            }
+        }
+    }
+}
+
+// plan -> prep -> scan (value and transition items) -> combine -> correction.
+// Without segmentation the last two find no work and exit.
 template <int DK, typename Tout>
 static hipError_t launch_mfma_t(const PrefillArgs& A) {
+    const int TV = A.dv / 32, TK = DK / 32;
+    hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK);
     hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.H), dim3(256), 0, A.stream, A);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int tiles = A.dv / 32;
-    const int chains = A.N * A.HV;
-    const size_t blocks = (size_t)((chains + 7) / 8) * 8 * tiles;
+    const size_t chains8 = (size_t)((A.seg_bound * A.HV + 7) / 8) * 8;
+    const size_t blocks = chains8 * (TV + TK);
     hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(256), 0,
                        A.stream, A);
+    const int cgrid = (int)std::min<size_t>((size_t)A.N * A.HV * TV, 1024);
+    hipLaunchKernelGGL((combine_kernel<DK>), dim3(cgrid), dim3(256), 0, A.stream, A);
+    const int rgrid = (int)std::min<size_t>((size_t)A.corr_bound * A.HV, 512);
+    hipLaunchKernelGGL((correct_kernel<DK, Tout>), dim3(rgrid), dim3(256), 0, A.stream, A);
     return hipGetLastError();
 }
 

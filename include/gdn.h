@@ -219,6 +219,33 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
                                size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_prefill_chunked_seg -- gdn_prefill_chunked with control over its
+ * segment-parallel scan.  The chunk map of the recurrence is affine in the
+ * state it starts from, so a long sequence can be cut into segments of whole
+ * chunks that run in parallel: each later segment runs once from a zero state
+ * and once for its transition (the product of its token maps), a short pass
+ * chains the segments' entry states, and a parallel pass adds each entry
+ * state's contribution to the segment's outputs.  It pays when few, long
+ * sequences leave most of the GPU idle (one long prompt), and costs extra
+ * work otherwise; gdn_prefill_chunked decides on the device from the lengths.
+ *
+ *   segment_chunks   0: decide automatically (as gdn_prefill_chunked)
+ *                   -1: never segment
+ *                  >= 32: segments of this many chunks (64 tokens each)
+ *   every other argument as gdn_prefill_chunked (same workspace size).
+ * Applies to the bf16-MFMA path (bf16 inputs, d_k in {64, 128}, d_v a
+ * multiple of 32); other shapes ignore it.  Other values of segment_chunks
+ * return GDN_ERROR_INVALID_VALUE.
+ */
+gdn_status gdn_prefill_chunked_seg(const void* q, const void* k, const void* v,
+                                   gdn_dtype in_dtype, const float* g, const float* beta,
+                                   const int32_t* cu_seqlens, int N, int T_total,
+                                   const float* initial_state, float* final_state, void* o,
+                                   gdn_dtype o_dtype, int H, int HV, int dk, int dv, int chunk,
+                                   float scale, int segment_chunks, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * gdn_rmsnorm_gated -- RMSNormGated, the norm that closes each DeltaNet layer
  * (Qwen3.5-0.8B chat guide, section "Architektur").  Per (row, head) group of
  * dv values:

@@ -57,7 +57,7 @@ def max_abs(a, ref) -> float:
     return float(np.max(np.abs(a - ref))) if a.size else 0.0
 
 
-def gpu_prefill(x, *, scale=1.0, s0=None, out_dtype=None, final=True):
+def gpu_prefill(x, *, scale=1.0, s0=None, out_dtype=None, final=True, segment_chunks=0):
     """Run gdn_prefill_chunked on PrefillInputs x; returns torch tensors."""
     import torch
     import gated_delta_rule_decode_amd as gdn
@@ -71,7 +71,8 @@ def gpu_prefill(x, *, scale=1.0, s0=None, out_dtype=None, final=True):
     elif x.s0 is not None:
         init = dev(x.s0)
     o, S = gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=init, scale=scale,
-                               out_dtype=out_dtype, return_final_state=final)
+                               out_dtype=out_dtype, return_final_state=final,
+                               segment_chunks=segment_chunks)
     return o, S
 
 

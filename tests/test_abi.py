@@ -96,6 +96,13 @@ def test_prefill_validation(L):
     assert _prefill(L, wsb=need - 1) == 3
     assert _prefill(L, ws=FAKE + 16) == 3            # workspace must be 256-aligned
     assert _prefill(L, o_dt=3) == 2
+    seg = lambda n: L.gdn_prefill_chunked_seg(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 2, 100, None,
+                                              FAKE, FAKE, 0, 2, 4, 128, 128, 64, 1.0, n, None,
+                                              0, None)
+    for bad in (1, 31, -2):
+        assert seg(bad) == 1                          # segment length below 32 chunks
+    for ok in (0, -1, 32, 1000):
+        assert seg(ok) == 3                           # passes that check, fails on the workspace
 
 
 def test_prefill_workspace_bytes(L):
@@ -111,7 +118,12 @@ def test_prefill_workspace_bytes(L):
         head = al(4 * (N + 1)) + al(maxc * HV * 64 * 4)
         valu = al(maxc * HV * 64 * 64 * 4)
         mfma = 2 * al(maxc * HV * 64 * 64 * 2) + 2 * al(maxc * HV * dk * 64 * 2)
-        want = head + max(valu, mfma)
+        segb = N + (maxc + 31) // 32
+        corrb = segb + maxc // 4 + 1
+        seg = (al(8 * 4) + 4 * al(segb * 4) + 3 * al(N * 4) + 2 * al(corrb * 4)
+               + 2 * al(segb * HV * 128 * dk * 4) + al(segb * HV * dk * dk * 4)
+               + al(T * HV * dk * 4))
+        want = head + max(valu, mfma) + seg
         assert f(N, T, H, HV, dk, 128) == want
         assert f(N, T, H, HV, dk, 128) % 256 == 0
 
