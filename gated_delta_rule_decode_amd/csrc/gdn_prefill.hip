@@ -322,15 +322,15 @@ static hipError_t launch_prefill_io(const PrefillArgs& A) {
     }
 }
 
-// Chunk table, then the bf16-MFMA kernels where they apply (bf16 inputs,
-// d_k in {64, 128}, d_v a multiple of 32) and the fp32 vector-unit kernels
-// above for every other supported shape and for fp32 inputs.
+// The bf16-MFMA kernels where they apply (bf16 inputs, d_k in {64, 128}, d_v
+// a multiple of 32); otherwise the chunk table and the fp32 vector-unit
+// kernels above (every other supported shape, fp32 inputs).
 hipError_t launch_prefill(const PrefillArgs& A) {
+    if (prefill_mfma_eligible(A)) return launch_prefill_mfma(A);  // builds its own chunk table
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, A.stream, A.cu_seqlens, A.N,
                        A.T, A.chunk_off);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (prefill_mfma_eligible(A)) return launch_prefill_mfma(A);
     if (A.in_bf16) {
         return A.o_bf16 ? launch_prefill_io<bf16_t, bf16_t>(A) : launch_prefill_io<bf16_t, float>(A);
     }

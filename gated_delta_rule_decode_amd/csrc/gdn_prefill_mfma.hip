@@ -962,18 +962,44 @@ __device__ int block_exclusive_scan(int n, F count, G emit, int* buf) {
 constexpr int kSegCand[7] = {0, 1024, 512, 256, 128, 64, 32};
 constexpr int kNCand = 7;
 
-// One workgroup: choose the segment length, cut the sequences and list the
-// work of the combine and correction passes.  plan = {segments, correction
-// items, segment length (0: none), sequences with more than one segment}.
+// One workgroup: the chunk table (chunk_off, the first global chunk of every
+// sequence), then the choice of the segment length, the segments of every
+// sequence and the work lists of the combine and correction passes.
+// plan = {segments, correction items, segment length (0: none), sequences
+// with more than one segment}.  Chunk counts of the first kPlanCache
+// sequences stay in LDS.
+constexpr int kPlanCache = 2048;
+
 __global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A, int TV, int TK) {
     __shared__ int ibuf[256];
+    __shared__ int cnt_sh[kPlanCache], off_sh[kPlanCache];
     __shared__ float acc[3][kNCand];  // items, chain steps, tokens of later segments
     __shared__ int s_cmax;
     __shared__ int s_len;
     const int N = A.N, HV = A.HV;
-    const int32_t* co = A.chunk_off;
+    int32_t* co = A.chunk_off;
+    auto count = [&](int n) {
+        int s, e;
+        seq_bounds_m(A.cu_seqlens, n, A.T, s, e);
+        return (e - s + kChunk - 1) / kChunk;
+    };
+    const int total = block_exclusive_scan(
+        N, count,
+        [&](int n, int pos, int c) {
+            co[n] = pos;
+            if (n < kPlanCache) {
+                cnt_sh[n] = c;
+                off_sh[n] = pos;
+            }
+        },
+        ibuf);
+    if (threadIdx.x == 0) co[N] = total;
+    __syncthreads();
+    auto first_chunk = [&](int n) { return min(n < kPlanCache ? off_sh[n] : co[n], A.max_chunks); };
     auto nchunks = [&](int n) {
-        return max(0, min(co[n + 1], A.max_chunks) - min(co[n], A.max_chunks));
+        const int o = n < kPlanCache ? off_sh[n] : co[n];
+        const int c = n < kPlanCache ? cnt_sh[n] : co[n + 1] - co[n];
+        return max(0, min(o + c, A.max_chunks) - min(o, A.max_chunks));
     };
 
     if (A.seg_req != 0) {
@@ -1057,7 +1083,7 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A,
             A.seq_nseg[n] = m;
             for (int j = 0; j < m; ++j) {
                 A.seg_seq[pos + j] = n;
-                A.seg_c0[pos + j] = min(co[n], A.max_chunks) + j * len;
+                A.seg_c0[pos + j] = first_chunk(n) + j * len;
                 A.seg_nch[pos + j] = max(0, min(len, c - j * len));
                 A.seg_idx[pos + j] = j;
             }
@@ -1305,20 +1331,33 @@ __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
 // plan -> prep -> scan (value and transition items) -> combine -> correction.
 // Without segmentation the last two find no work and exit.
 template <int DK, typename Tout>
-static hipError_t launch_mfma_t(const PrefillArgs& A) {
-    const int TV = A.dv / 32, TK = DK / 32;
+static hipError_t launch_mfma_t(const PrefillArgs& A0) {
+    const int TV = A0.dv / 32, TK = DK / 32;
+    // Segmentation is possible only when asked for, or, automatically, when
+    // the unsegmented scan leaves CUs idle (fewer than 256 workgroups) and
+    // some sequence may be longer than one segment; otherwise the plan is
+    // fixed to one segment per sequence and the later passes are not launched.
+    PrefillArgs A = A0;
+    const bool may = A.seg_req > 0 ||
+                     (A.seg_req == 0 && (size_t)A.N * A.HV * TV < 256 &&
+                      (A.T + kChunk - 1) / kChunk > kSegMinChunks);
+    if (!may) A.seg_req = -1;
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK);
     hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.H), dim3(256), 0, A.stream, A);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t chains8 = (size_t)((A.seg_bound * A.HV + 7) / 8) * 8;
-    const size_t blocks = chains8 * (TV + TK);
+    // value items of up to seg_bound segments (N without segmentation), then
+    // the transition items; the kernel splits the grid at seg_bound
+    const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * A.HV + 7) / 8) * 8;
+    const size_t blocks = may ? chains8 * (TV + TK) : chains8 * TV;
     hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(256), 0,
                        A.stream, A);
-    const int cgrid = (int)std::min<size_t>((size_t)A.N * A.HV * TV, 1024);
-    hipLaunchKernelGGL((combine_kernel<DK>), dim3(cgrid), dim3(256), 0, A.stream, A);
-    const int rgrid = (int)std::min<size_t>((size_t)A.corr_bound * A.HV, 512);
-    hipLaunchKernelGGL((correct_kernel<DK, Tout>), dim3(rgrid), dim3(256), 0, A.stream, A);
+    if (may) {
+        const int cgrid = (int)std::min<size_t>((size_t)A.N * A.HV * TV, 512);
+        hipLaunchKernelGGL((combine_kernel<DK>), dim3(cgrid), dim3(256), 0, A.stream, A);
+        const int rgrid = (int)std::min<size_t>((size_t)A.corr_bound * A.HV, 512);
+        hipLaunchKernelGGL((correct_kernel<DK, Tout>), dim3(rgrid), dim3(256), 0, A.stream, A);
+    }
     return hipGetLastError();
 }
 
