@@ -52,8 +52,8 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # counters read for a copy of known size; recorded in
 # profiles/decode_traffic_qwen35_08b.md together with the sha256 of the kernel
 # source it was measured on.  Reported only while that source is unchanged.
-DECODE_TRAFFIC = {"kernel_source_sha256": "368ed6c0e7a70c9134c2b00ee547d4ab39561258a86055a81f5ceff616e4eada",
-                  "bytes_per_launch": 68047522}
+DECODE_TRAFFIC = {"kernel_source_sha256": "84ac4e31a985811ba80f5d4b8970a5f867f15981be5e2c06c2eb6054861de803",
+                  "bytes_per_launch": 68047749}
 
 
 def measured_traffic():
