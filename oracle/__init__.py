@@ -17,6 +17,8 @@ Functions
   l2norm(...)       x / sqrt(sum x^2 + eps) per row
   decode_layer(...) one token per sequence against a slot-addressed state pool,
                     optionally with q/k L2-normalised first
+  rope(...)         rotary embedding on the first rd dimensions (rotate-half pairs)
+  attn_decode(...)  one decode step of gated full attention over a KV cache
 
 Pinned by tests/test_oracle_pins.py (closed forms and invariants) and
 tests/test_oracle_mutations.py (planted mistakes fail a pin).
@@ -86,6 +88,14 @@ class Oracle:
             _f32p, _f32p, _f32p, _f64p, _f64p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
             ctypes.c_double, _f64p, _f64p, ctypes.c_int]
+        lib.gdn_oracle_rope.restype = ctypes.c_int
+        lib.gdn_oracle_rope.argtypes = [_f32p, _i32p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_double, _f64p]
+        lib.gdn_oracle_attn_decode.restype = ctypes.c_int
+        lib.gdn_oracle_attn_decode.argtypes = [
+            _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _i32p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+            ctypes.c_double, _f64p, _f64p]
         self._lib = lib
 
     def max_threads(self) -> int:
@@ -204,6 +214,42 @@ class Oracle:
         if rc != 0:
             raise RuntimeError("oracle decode_layer failed (sizes, or a slot used twice)")
         return o, pool
+
+    def rope(self, x, pos, *, rd: int, theta: float):
+        """x: [..., d] float; pos: integer array with x's leading shape."""
+        x = _f32(x)
+        d = x.shape[-1]
+        p = np.ascontiguousarray(np.broadcast_to(pos, x.shape[:-1]), dtype=np.int32)
+        y = np.empty(x.shape, dtype=np.float64)
+        rc = self._lib.gdn_oracle_rope(_ptr(x, _f32p), _ptr(p, _i32p), x.size // d, d, int(rd),
+                                       float(theta), _ptr(y, _f64p))
+        if rc != 0:
+            raise RuntimeError("oracle rope failed")
+        return y
+
+    def attn_decode(self, q, knew, vnew, k_cache, v_cache, pos, *, gate=None, rd: int = 64,
+                    theta: float = 1e7, scale: float = 1.0):
+        """q (and gate): [N, Hq, d]; knew, vnew: [N, Hkv, d]; caches [N, Hkv, Lmax, d]
+        (rows t < pos[n] valid, keys rotated); pos: [N].  Returns (o [N, Hq, d],
+        rotated new key [N, Hkv, d]) in float64."""
+        q, knew, vnew = _f32(q), _f32(knew), _f32(vnew)
+        kc, vc = _f32(k_cache), _f32(v_cache)
+        g = None if gate is None else _f32(gate)
+        N, Hq, d = q.shape
+        Hkv, Lmax = kc.shape[1], kc.shape[2]
+        p = np.ascontiguousarray(pos, dtype=np.int32)
+        if knew.shape != (N, Hkv, d) or vnew.shape != knew.shape or kc.shape != (N, Hkv, Lmax, d) \
+                or vc.shape != kc.shape or p.shape != (N,) or (g is not None and g.shape != q.shape):
+            raise ValueError("shapes")
+        o = np.full((N, Hq, d), np.nan)
+        kr = np.full((N, Hkv, d), np.nan)
+        rc = self._lib.gdn_oracle_attn_decode(
+            _ptr(q, _f32p), _ptr(g, _f32p), _ptr(knew, _f32p), _ptr(vnew, _f32p), _ptr(kc, _f32p),
+            _ptr(vc, _f32p), _ptr(p, _i32p), N, Hq, Hkv, d, Lmax, int(rd), float(theta),
+            float(scale), _ptr(o, _f64p), _ptr(kr, _f64p))
+        if rc != 0:
+            raise RuntimeError("oracle attn_decode failed")
+        return o, kr
 
 
 _DEFAULT: Optional[Oracle] = None

@@ -26,7 +26,9 @@
  *
  * The serving form of the decode step (gdn_oracle_decode_layer) adds the
  * layer's gate activations, an optional L2 normalisation of q and k and a slot
- * table into a pool of states; see the comments at those functions.
+ * table into a pool of states; gdn_oracle_attn_decode is one decode step of
+ * the decoder's other token mixer, gated full attention; see the comments at
+ * those functions.
  *
  * Everything is computed in double from float32 inputs (bf16 inputs arrive as
  * exactly representable float32 values).  No chunking and no reordering beyond
@@ -41,7 +43,7 @@
 #include <omp.h>
 #endif
 
-int gdn_oracle_version(void) { return 2; }
+int gdn_oracle_version(void) { return 3; }
 
 int gdn_oracle_max_threads(void) {
 #ifdef _OPENMP
@@ -295,6 +297,115 @@ int gdn_oracle_decode_layer(const float* q, const float* k, const float* v, cons
         step_one(qd, kd, v + (size_t)p * dv, exp(g[p]), beta[p], dk, dv, scale,
                  pool + ((size_t)s * HV + h) * ssz, ot, wk);
         free(wk);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * Rotary position embedding on the first rd of d dimensions (the partial
+ * rotary embedding of the gated attention layers: Core AI card for
+ * Qwen3.6-35B-A3B, introduction, names partial mRoPE with theta = 1e7; for
+ * text every mRoPE section carries the same position, which is plain RoPE).
+ * Pairs (i, i + rd/2), i < rd/2, rotate by the angle p * theta^(-2i/rd):
+ *     y_i        = x_i cos - x_{i+rd/2} sin
+ *     y_{i+rd/2} = x_{i+rd/2} cos + x_i sin
+ * Dimensions rd .. d-1 pass unchanged.
+ *   x : [rows, d] float32    pos : [rows] int32    y : [rows, d] double
+ */
+static void rope_row(const double* x, int d, int rd, double theta, double p, double* y) {
+    for (int j = 0; j < d; ++j) y[j] = x[j];
+    const int half = rd / 2;
+    for (int i = 0; i < half; ++i) {
+        const double ang = p * pow(theta, -2.0 * i / rd);
+        const double c = cos(ang), s = sin(ang);
+        y[i] = x[i] * c - x[i + half] * s;
+        y[i + half] = x[i + half] * c + x[i] * s;
+    }
+}
+
+int gdn_oracle_rope(const float* x, const int32_t* pos, long rows, int d, int rd, double theta,
+                    double* y) {
+    if (rows < 0 || d <= 0 || rd < 0 || rd > d || rd % 2) return -1;
+    double* xd = (double*)malloc((size_t)d * sizeof(double));
+    if (!xd) return -1;
+    for (long r = 0; r < rows; ++r) {
+        for (int j = 0; j < d; ++j) xd[j] = (double)x[(size_t)r * d + j];
+        rope_row(xd, d, rd, theta, (double)pos[r], y + (size_t)r * d);
+    }
+    free(xd);
+    return 0;
+}
+
+/*
+ * One decode step of gated full attention (standard scaled dot-product
+ * attention: Qwen3.5-0.8B chat guide, section "Architektur"; GQA with query
+ * head h reading key/value head h / (Hq / Hkv)), written out:
+ *     qr = rope(q, pos), kr = rope(k_new, pos)
+ *     s_t = scale * qr . K_t   for t < pos (cached keys, stored rotated), and
+ *     s_pos = scale * qr . kr
+ *     o = sum_t softmax(s)_t V_t   (V_pos = v_new),   o *= sigmoid(gate) if given
+ *   q, gate : [N, Hq, d] float32 (gate may be NULL)
+ *   knew, vnew : [N, Hkv, d] float32
+ *   kc, vc  : [N, Hkv, Lmax, d] float32, rows t < pos[n] valid
+ *   pos     : [N] int32, 0 <= pos < Lmax
+ *   o       : [N, Hq, d] double
+ *   kr_out  : [N, Hkv, d] double, the rotated new key (what the step appends)
+ * Returns 0, or -1 on invalid sizes or a failed allocation.
+ */
+int gdn_oracle_attn_decode(const float* q, const float* gate, const float* knew,
+                           const float* vnew, const float* kc, const float* vc,
+                           const int32_t* pos, int N, int Hq, int Hkv, int d, int Lmax, int rd,
+                           double theta, double scale, double* o, double* kr_out) {
+    if (N < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 || rd < 0 || rd > d || rd % 2 ||
+        Lmax <= 0)
+        return -1;
+    for (int n = 0; n < N; ++n)
+        if (pos[n] < 0 || pos[n] >= Lmax) return -1;
+    int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (long p = 0; p < (long)N * Hq; ++p) {
+        const int n = (int)(p / Hq), h = (int)(p % Hq);
+        const int hk = h / (Hq / Hkv);
+        const int L = pos[n] + 1;
+        double* buf = (double*)malloc((size_t)(4 * d + L) * sizeof(double));
+        if (!buf) {
+            failed = 1;
+            continue;
+        }
+        double *xd = buf, *qr = buf + d, *kr = buf + 2 * d, *acc = buf + 3 * d, *sc = buf + 4 * d;
+        for (int j = 0; j < d; ++j) xd[j] = (double)q[(size_t)p * d + j];
+        rope_row(xd, d, rd, theta, (double)pos[n], qr);
+        const size_t kvh = (size_t)n * Hkv + hk;
+        for (int j = 0; j < d; ++j) xd[j] = (double)knew[kvh * d + j];
+        rope_row(xd, d, rd, theta, (double)pos[n], kr);
+        if (h % (Hq / Hkv) == 0)
+            for (int j = 0; j < d; ++j) kr_out[kvh * d + j] = kr[j];
+        double mx = -INFINITY;
+        for (int t = 0; t < L; ++t) {
+            const float* kt = kc + (kvh * Lmax + t) * d;
+            double s = 0.0;
+            for (int j = 0; j < d; ++j) s += qr[j] * (t < pos[n] ? (double)kt[j] : kr[j]);
+            sc[t] = scale * s;
+            if (sc[t] > mx) mx = sc[t];
+        }
+        double den = 0.0;
+        for (int t = 0; t < L; ++t) {
+            sc[t] = exp(sc[t] - mx);
+            den += sc[t];
+        }
+        for (int j = 0; j < d; ++j) acc[j] = 0.0;
+        for (int t = 0; t < L; ++t) {
+            const float* vt = t < pos[n] ? vc + (kvh * Lmax + t) * d : vnew + kvh * d;
+            for (int j = 0; j < d; ++j) acc[j] += sc[t] * (double)vt[j];
+        }
+        for (int j = 0; j < d; ++j) {
+            double v = acc[j] / den;
+            if (gate) v *= 1.0 / (1.0 + exp(-(double)gate[(size_t)p * d + j]));
+            o[(size_t)p * d + j] = v;
+        }
+        free(buf);
     }
     return failed ? -1 : 0;
 }

@@ -505,6 +505,116 @@ def pin_decode_layer_gates(orc):
     _close(o, beta[:, :, None] * v.astype(np.float64), 1e-15, "read back b v")
 
 
+# ---------------------------------------------------------------------------
+# gated full attention (decode step) and its rotary embedding
+# ---------------------------------------------------------------------------
+
+def pin_rope_closed_forms(orc):
+    """Position 0 is the identity; dimensions past rd pass unchanged; norms are
+    kept; a unit vector on pair i at position p lands on (cos a, sin a) in
+    dimensions (i, i + rd/2) with a = p theta^(-2i/rd)."""
+    r = _rng(40)
+    d, rd, th = 32, 16, 1e7
+    x = r.standard_normal((5, d)).astype(np.float32)
+    y0 = orc.rope(x, np.zeros(5, np.int32), rd=rd, theta=th)
+    _close(y0, x.astype(np.float64), 0.0, "position 0")
+    y = orc.rope(x, np.array([1, 7, 100, 4096, 65535]), rd=rd, theta=th)
+    _close(y[:, rd:], x[:, rd:].astype(np.float64), 0.0, "unrotated tail")
+    _close(np.linalg.norm(y, axis=1), np.linalg.norm(x.astype(np.float64), axis=1), 1e-14, "norm")
+    for i, p in ((0, 1), (1, 1), (3, 37), (7, 1000)):
+        e = np.zeros((1, d), np.float32)
+        e[0, i] = 1.0
+        a = p * th ** (-2.0 * i / rd)
+        want = np.zeros(d)
+        want[i], want[i + rd // 2] = math.cos(a), math.sin(a)
+        _close(orc.rope(e, np.array([p]), rd=rd, theta=th)[0], want, 1e-13, f"pair {i} at {p}")
+
+
+def pin_rope_relative(orc):
+    """Rotated dot products depend on the position difference only:
+    rope(q, p + s) . rope(k, t + s) = rope(q, p) . rope(k, t)."""
+    r = _rng(41)
+    d, rd = 64, 32
+    q = r.standard_normal((6, d)).astype(np.float32)
+    k = r.standard_normal((6, d)).astype(np.float32)
+    p = np.array([0, 3, 10, 200, 5000, 1])
+    t = np.array([0, 1, 17, 150, 4999, 30000])
+    base = np.sum(orc.rope(q, p, rd=rd, theta=1e4) * orc.rope(k, t, rd=rd, theta=1e4), axis=1)
+    for sft in (1, 123, 20000):
+        moved = np.sum(orc.rope(q, p + sft, rd=rd, theta=1e4) * orc.rope(k, t + sft, rd=rd, theta=1e4), axis=1)
+        _close(moved, base, 1e-9, f"shift {sft}")
+
+
+def _attn_case(tag, N=3, Hq=4, Hkv=2, d=32, Lmax=40):
+    r = _rng(tag)
+    q = r.standard_normal((N, Hq, d)).astype(np.float32)
+    gate = r.standard_normal((N, Hq, d)).astype(np.float32)
+    kn = r.standard_normal((N, Hkv, d)).astype(np.float32)
+    vn = r.standard_normal((N, Hkv, d)).astype(np.float32)
+    kc = r.standard_normal((N, Hkv, Lmax, d)).astype(np.float32)
+    vc = r.standard_normal((N, Hkv, Lmax, d)).astype(np.float32)
+    pos = r.integers(1, Lmax - 1, N).astype(np.int32)
+    return q, gate, kn, vn, kc, vc, pos
+
+
+def pin_attn_closed_forms(orc):
+    """Empty cache: o = v_new * sigmoid(gate) and the appended key is
+    rope(k_new, 0) = k_new; q = 0: uniform weights, o = the mean of the
+    cache's values and v_new; gate 0 halves o; a dominant score selects its
+    value."""
+    q, gate, kn, vn, kc, vc, pos = _attn_case(42)
+    N, Hq, d = q.shape
+    Hkv = kn.shape[1]
+    grp = Hq // Hkv
+    o, kr = orc.attn_decode(q, kn, vn, kc, vc, np.zeros(N, np.int32), gate=gate, rd=16)
+    want = np.repeat(vn, grp, axis=1).astype(np.float64) / (1 + np.exp(-gate.astype(np.float64)))
+    _close(o, want, 1e-15, "single position")
+    _close(kr, kn.astype(np.float64), 0.0, "appended key at position 0")
+    o, _ = orc.attn_decode(np.zeros_like(q), kn, vn, kc, vc, pos, rd=16)
+    for n in range(N):
+        vals = np.concatenate([vc[n, :, :pos[n]], vn[n, :, None]], axis=1).astype(np.float64)
+        _close(o[n], np.repeat(vals.mean(axis=1), grp, axis=0), 1e-14, "uniform weights")
+    o1, _ = orc.attn_decode(q, kn, vn, kc, vc, pos, rd=16, scale=0.3)
+    o2, _ = orc.attn_decode(q, kn, vn, kc, vc, pos, gate=np.zeros_like(gate), rd=16, scale=0.3)
+    _close(o2, 0.5 * o1, 1e-15, "gate 0")
+    # cached key t* = q (rd = 0: no rotation), huge scale: softmax picks t*
+    kc2 = kc.copy()
+    kc2[:, :, 0, :] = np.repeat(q[:, ::grp], 1, axis=1) * 4
+    o, _ = orc.attn_decode(q[:, ::grp], kn, vn, kc2, vc, pos, rd=0, scale=50.0)
+    _close(o, vc[:, :, 0, :].astype(np.float64), 1e-9, "dominant score")
+
+
+def pin_attn_library(orc):
+    """Against torch's CPU softmax and matmul in fp64 on rotated inputs
+    (the rotary embedding pinned above), with GQA by repeated heads."""
+    import torch
+    q, gate, kn, vn, kc, vc, pos = _attn_case(43, N=3, Hq=8, Hkv=2, d=32, Lmax=50)
+    rd, th, sc = 16, 1e7, 32 ** -0.5
+    o, kr = orc.attn_decode(q, kn, vn, kc, vc, pos, gate=gate, rd=rd, theta=th, scale=sc)
+    N, Hq, d = q.shape
+    grp = Hq // kn.shape[1]
+    qr = orc.rope(q, np.repeat(pos[:, None], Hq, axis=1), rd=rd, theta=th)
+    krw = orc.rope(kn, np.repeat(pos[:, None], kn.shape[1], axis=1), rd=rd, theta=th)
+    _close(kr, krw, 0.0, "appended key")
+    for n in range(N):
+        K = np.concatenate([kc[n, :, :pos[n]].astype(np.float64), krw[n][:, None]], axis=1)
+        V = np.concatenate([vc[n, :, :pos[n]], vn[n, :, None]], axis=1).astype(np.float64)
+        K, V = np.repeat(K, grp, axis=0), np.repeat(V, grp, axis=0)
+        s = torch.from_numpy(np.einsum("hd,htd->ht", qr[n], K) * sc)
+        w = torch.softmax(s, dim=-1).numpy()
+        want = np.einsum("ht,htd->hd", w, V) * torch.sigmoid(torch.from_numpy(gate[n].astype(np.float64))).numpy()
+        _close(o[n], want, 1e-13, f"sequence {n}")
+
+
+def pin_attn_gqa(orc):
+    """Query head h reads key/value head h / (Hq / Hkv): equal to repeated heads."""
+    q, gate, kn, vn, kc, vc, pos = _attn_case(44, N=2, Hq=6, Hkv=3, d=16, Lmax=20)
+    o1, _ = orc.attn_decode(q, kn, vn, kc, vc, pos, gate=gate, rd=8)
+    rep = lambda a: np.repeat(a, 2, axis=1)
+    o2, _ = orc.attn_decode(q, rep(kn), rep(vn), rep(kc), rep(vc), pos, gate=gate, rd=8)
+    assert np.array_equal(o1, o2), "GQA vs repeated heads"
+
+
 RECURRENCE_PINS = [
     pin_handworked_two_tokens, pin_single_token_closed_form, pin_decay_only,
     pin_exact_retrieval, pin_linear_readout, pin_delta_rule_invariants, pin_scale_linearity,
@@ -514,4 +624,6 @@ RECURRENCE_PINS = [
 NORM_PINS = [pin_norm_library, pin_norm_closed_forms]
 LAYER_PINS = [pin_gate_closed_forms, pin_gate_library, pin_l2norm,
               pin_decode_layer_reduces_to_step, pin_decode_layer_l2norm, pin_decode_layer_gates]
-ALL_PINS = RECURRENCE_PINS + NORM_PINS + LAYER_PINS
+ATTN_PINS = [pin_rope_closed_forms, pin_rope_relative, pin_attn_closed_forms, pin_attn_library,
+             pin_attn_gqa]
+ALL_PINS = RECURRENCE_PINS + NORM_PINS + LAYER_PINS + ATTN_PINS

@@ -59,6 +59,20 @@ MUTATIONS = {
     "slot_table_ignored": [("pool + ((size_t)s * HV + h) * ssz", "pool + ((size_t)n * HV + h) * ssz")],
     "skipped_sequence_output_unset": [("for (int i = 0; i < dv; ++i) ot[i] = 0.0;", "")],
     "layer_decay_sign": [("exp(g[p]), beta[p]", "exp(-g[p]), beta[p]")],
+    "rope_interleaved_pairs": [("        y[i] = x[i] * c - x[i + half] * s;\n        y[i + half] = x[i + half] * c + x[i] * s;",
+                                "        y[2 * i] = x[2 * i] * c - x[2 * i + 1] * s;\n        y[2 * i + 1] = x[2 * i + 1] * c + x[2 * i] * s;")],
+    "rope_rotation_sign": [("y[i] = x[i] * c - x[i + half] * s;", "y[i] = x[i] * c + x[i + half] * s;"),
+                           ("y[i + half] = x[i + half] * c + x[i] * s;", "y[i + half] = x[i + half] * c - x[i] * s;")],
+    "rope_frequency": [("pow(theta, -2.0 * i / rd)", "pow(theta, -1.0 * i / rd)")],
+    "attn_key_unrotated": [("rope_row(xd, d, rd, theta, (double)pos[n], kr);",
+                            "for (int j = 0; j < d; ++j) kr[j] = xd[j];")],
+    "attn_unscaled": [("sc[t] = scale * s;", "sc[t] = s;")],
+    "attn_new_token_dropped": [("const int L = pos[n] + 1;", "const int L = pos[n] > 0 ? pos[n] : 1;")],
+    "attn_gate_silu": [("v *= 1.0 / (1.0 + exp(-(double)gate[(size_t)p * d + j]));",
+                        "v *= (double)gate[(size_t)p * d + j] / (1.0 + exp(-(double)gate[(size_t)p * d + j]));")],
+    "attn_gqa_modulo": [("const int hk = h / (Hq / Hkv);", "const int hk = h % Hkv;")],
+    "attn_new_value_from_cache": [("t < pos[n] ? vc + (kvh * Lmax + t) * d : vnew + kvh * d",
+                                   "vc + (kvh * Lmax + t) * d")],
 }
 
 
