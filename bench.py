@@ -13,11 +13,16 @@ The decode step and its RMSNormGated run as one kernel (gdn_decode_step_norm).
 The launch sequence of a step is captured once in HIP graphs and replayed.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload decode|prefill2|prefill3|prefill4|prefill5|serve]
+                    [--workload decode|prefill2|prefill3|prefill4|prefill5|serve|attn]
 
 ``prefill5`` is one 32768-token prompt at the 0.8B shape (the case the
 segment-parallel scan is for); prefill lines also report the time with
 segmentation turned off.
+
+``--workload attn`` times one decode step of the gated full-attention layers
+of Qwen3.6-35B-A3B (16 query heads over 2 key/value heads, head_dim 256, a
+quarter rotated, theta 1e7; 10 of its 40 layers): 128 rows at position 8192
+of 8320-row bf16 caches per layer.
 
 ``--workload serve`` times the serving form of the decode step
 (gdn_decode_layer) on the Qwen3.6-35B-A3B DeltaNet shape: 128 rows drawn from
@@ -371,6 +376,77 @@ def run_copy(args):
             "read_bytes_per_launch": n * 4, "write_bytes_per_launch": n * 4}
 
 
+def attn_bytes(N, Hq, Hkv, D, ctx):
+    """HBM bytes of one attention decode step: the cached keys and values of
+    ctx positions read, q, gate, k_new, v_new in, o (fp32) out, the new key and
+    value written to the caches."""
+    return (N * Hkv * ctx * 2 * D * 2 + N * Hq * D * (2 + 2 + 4) + N * Hkv * D * 2 * 2
+            + N * Hkv * D * 2 * 2)
+
+
+def run_attn(args):
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+
+    N, Hq, Hkv, D, Lmax, P, L = 128, 16, 2, 256, 8320, 8192, 10
+    dev = torch.device("cuda", 0)
+    bf = torch.bfloat16
+    log(f"attn: rows={N} Hq={Hq} Hkv={Hkv} D={D} position={P} cache rows={Lmax} layers={L}")
+    gen = torch.Generator(device=dev).manual_seed(9)
+    layers = []
+    for _ in range(L):
+        layers.append(dict(
+            kc=torch.randn(N, Hkv, Lmax, D, device=dev, dtype=bf, generator=gen),
+            vc=torch.randn(N, Hkv, Lmax, D, device=dev, dtype=bf, generator=gen),
+            q=torch.randn(N, Hq, D, device=dev, dtype=bf, generator=gen),
+            g=torch.randn(N, Hq, D, device=dev, dtype=bf, generator=gen),
+            kn=torch.randn(N, Hkv, D, device=dev, dtype=bf, generator=gen),
+            vn=torch.randn(N, Hkv, D, device=dev, dtype=bf, generator=gen),
+            o=torch.empty(N, Hq, D, device=dev)))
+    pos = torch.full((N,), P, dtype=torch.int32, device=dev)
+    ws = torch.empty(gdn.attn_decode_workspace_bytes(N, Hq, Hkv, D, Lmax), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for Ly in layers:
+            gdn.attn_decode(Ly["q"], Ly["kn"], Ly["vn"], Ly["kc"], Ly["vc"], pos, gate=Ly["g"],
+                            o=Ly["o"], rotary_dim=64, rope_theta=1e7, workspace=ws)
+
+    g_at, s = graph_capture(step)
+    for _ in range(args.warmup):
+        g_at.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(args.steps):
+            g_at.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+    launch_us = ms * 1e3 / L
+    bytes_launch = attn_bytes(N, Hq, Hkv, D, P + 1)
+    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
+    return {
+        "metric": METRIC, "value": round(N * L / (ms * 1e-3), 1),
+        "unit": "tokens/s per attention layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwen3.6-35b-a3b-gated-attention-decode", "rows": N,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "position": P,
+                   "cache_rows": Lmax, "rotary_dim": 64, "rope_theta": 1e7, "layers": L,
+                   "cache": "bf16", "outputs": "f32"},
+        "roofline": {"kernel": "attn_split_kernel + attn_combine_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(launch_us, 3),
+                     "algorithmic_bytes_per_launch": bytes_launch},
+    }
+
+
 def run_serve(args):
     import torch
     import gated_delta_rule_decode_amd as gdn
@@ -480,7 +556,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill2", "prefill3", "prefill4", "prefill5", "copy",
-                             "serve"])
+                             "serve", "attn"])
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--decode-steps", type=int, default=0)
     ap.add_argument("--cpu-layers", type=int, default=12)
@@ -501,6 +577,8 @@ def main():
         out = run_copy(args)
     elif args.workload == "serve":
         out = run_serve(args)
+    elif args.workload == "attn":
+        out = run_attn(args)
     else:
         out = run_prefill(args, int(args.workload[-1]))
     print(json.dumps(out), flush=True)

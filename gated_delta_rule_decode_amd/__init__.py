@@ -11,6 +11,7 @@ raises (there is no fallback path).
                                                           raw gates, q/k L2 norm)
     prefill_chunked(q, k, v, g, beta, cu_seqlens, ...) -> (o, final_state)
     rmsnorm_gated(x, z, w, ...)                        -> y
+    attn_decode(q, k_new, v_new, k_cache, v_cache, pos, ...) -> o (gated full attention)
     prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk=64)
 
 Layouts (row-major, contiguous): q, k [tokens, H, dk]; v [tokens, HV, dv];
@@ -34,11 +35,12 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 EXPORTS = ("gdn_version", "gdn_status_string", "gdn_last_hip_error", "gdn_decode_step",
            "gdn_decode_step_norm", "gdn_decode_layer_args_size", "gdn_decode_layer",
            "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_prefill_chunked_seg",
+           "gdn_attn_decode_args_size", "gdn_attn_decode_workspace_bytes", "gdn_attn_decode",
            "gdn_rmsnorm_gated")
 
 __all__ = ["decode_step", "decode_step_norm", "decode_layer", "prefill_chunked", "rmsnorm_gated",
-           "prefill_workspace_bytes", "DecodeLayerArgs", "GDNError", "lib", "LIBRARY", "EXPORTS",
-           "version"]
+           "prefill_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
+           "DecodeLayerArgs", "AttnDecodeArgs", "GDNError", "lib", "LIBRARY", "EXPORTS", "version"]
 
 
 class GDNError(RuntimeError):
@@ -63,6 +65,16 @@ class DecodeLayerArgs(ctypes.Structure):
         ("o", _vp), ("o_dtype", _i), ("z", _vp), ("z_dtype", _i), ("w", _vp), ("w_dtype", _i),
         ("y", _vp), ("y_dtype", _i), ("eps", _f),
         ("N", _i), ("H", _i), ("HV", _i), ("dk", _i), ("dv", _i), ("scale", _f),
+    ]
+
+
+class AttnDecodeArgs(ctypes.Structure):
+    """Mirror of gdn_attn_decode_args (field order and types as in gdn.h)."""
+    _fields_ = [
+        ("q", _vp), ("gate", _vp), ("k_new", _vp), ("v_new", _vp), ("k_cache", _vp),
+        ("v_cache", _vp), ("pos", _vp), ("o", _vp), ("o_dtype", _i),
+        ("N", _i), ("Hq", _i), ("Hkv", _i), ("D", _i), ("Lmax", _i), ("rotary_dim", _i),
+        ("rope_theta", _f), ("scale", _f), ("workspace", _vp), ("workspace_bytes", _sz),
     ]
 
 
@@ -97,6 +109,14 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_layer.argtypes = [ctypes.POINTER(DecodeLayerArgs), _vp]
         if L.gdn_decode_layer_args_size() != ctypes.sizeof(DecodeLayerArgs):
             raise ImportError("gdn_decode_layer_args layout differs between gdn.h and the binding")
+        L.gdn_attn_decode_args_size.restype = _sz
+        L.gdn_attn_decode_args_size.argtypes = []
+        L.gdn_attn_decode_workspace_bytes.restype = _sz
+        L.gdn_attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+        L.gdn_attn_decode.restype = _i
+        L.gdn_attn_decode.argtypes = [ctypes.POINTER(AttnDecodeArgs), _vp]
+        if L.gdn_attn_decode_args_size() != ctypes.sizeof(AttnDecodeArgs):
+            raise ImportError("gdn_attn_decode_args layout differs between gdn.h and the binding")
         L.gdn_prefill_workspace_bytes.restype = _sz
         L.gdn_prefill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
         L.gdn_prefill_chunked_seg.restype = _i
@@ -367,6 +387,55 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_s
         st = lib().gdn_prefill_chunked_seg(*args, int(segment_chunks), *tail)
         _check("gdn_prefill_chunked_seg", st)
     return o, final_state
+
+
+def attn_decode_workspace_bytes(N: int, Hq: int, Hkv: int, D: int, Lmax: int) -> int:
+    return int(lib().gdn_attn_decode_workspace_bytes(N, Hq, Hkv, D, Lmax))
+
+
+def attn_decode(q, k_new, v_new, k_cache, v_cache, pos, *, gate=None, o=None,
+                rotary_dim: int = 64, rope_theta: float = 1e7, scale=None, out_dtype=None,
+                workspace=None):
+    """One decode step of gated full attention; appends the new key (rotated)
+    and value to the caches at row pos[n].
+
+    q (and gate) [N, Hq, D] bf16; k_new, v_new [N, Hkv, D] bf16; caches
+    [N, Hkv, Lmax, D] bf16 (keys stored rotated); pos [N] int32 on the device.
+    Returns o [N, Hq, D] (fp32 unless ``out_dtype`` or ``o`` says otherwise)."""
+    torch = _torch()
+    bf = torch.bfloat16
+    N, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _dev(t, name, bf)
+    _dev(pos, "pos", torch.int32)
+    if k_new.shape != (N, Hkv, D) or v_new.shape != k_new.shape \
+            or k_cache.shape != (N, Hkv, Lmax, D) or v_cache.shape != k_cache.shape \
+            or pos.shape != (N,):
+        raise ValueError("inconsistent attention shapes")
+    if gate is not None:
+        _dev(gate, "gate", bf)
+        if gate.shape != q.shape:
+            raise ValueError("gate shape")
+    if o is None:
+        o = torch.empty((N, Hq, D), dtype=out_dtype or torch.float32, device=q.device)
+    _dev(o, "o")
+    if workspace is None:
+        need = attn_decode_workspace_bytes(N, Hq, Hkv, D, Lmax)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    a = AttnDecodeArgs()
+    a.q, a.gate, a.k_new, a.v_new = _ptr(q), _ptr(gate), _ptr(k_new), _ptr(v_new)
+    a.k_cache, a.v_cache, a.pos, a.o, a.o_dtype = (_ptr(k_cache), _ptr(v_cache), _ptr(pos),
+                                                  _ptr(o), _dtype_code(o))
+    a.N, a.Hq, a.Hkv, a.D, a.Lmax, a.rotary_dim = N, Hq, Hkv, D, Lmax, int(rotary_dim)
+    a.rope_theta = float(rope_theta)
+    a.scale = float(D ** -0.5 if scale is None else scale)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib().gdn_attn_decode(ctypes.byref(a), _stream(q.device))
+    _check("gdn_attn_decode", st)
+    return o
 
 
 def rmsnorm_gated(x, z, w, *, y=None, eps: float = 1e-6, out_dtype=None):

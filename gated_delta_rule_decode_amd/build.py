@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip", "gdn_prefill_mfma.hip",
+SOURCES = ["gdn_api.cpp", "gdn_attn.hip", "gdn_decode.hip", "gdn_prefill.hip", "gdn_prefill_mfma.hip",
            "gdn_rmsnorm.hip"]
 ARCH = "gfx950"
 

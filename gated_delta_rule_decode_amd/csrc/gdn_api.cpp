@@ -234,6 +234,71 @@ gdn_status gdn_decode_layer(const gdn_decode_layer_args* p, void* stream) {
     return from_hip(gdn::launch_decode(a));
 }
 
+size_t gdn_attn_decode_args_size(void) { return sizeof(gdn_attn_decode_args); }
+
+}  // extern "C"
+
+namespace {
+
+gdn_status attn_shape_status(int N, int Hq, int Hkv, int D, int Lmax) {
+    if (N < 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || Hq % Hkv) return GDN_ERROR_INVALID_VALUE;
+    const int G = Hq / Hkv;
+    if (D != 64 && D != 128 && D != 256) return GDN_ERROR_NOT_SUPPORTED;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return GDN_ERROR_NOT_SUPPORTED;
+    if ((size_t)N * Hkv > 65535 || (size_t)Lmax * D * 2 > (size_t)INT32_MAX)
+        return GDN_ERROR_NOT_SUPPORTED;
+    return GDN_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_attn_decode_workspace_bytes(int N, int Hq, int Hkv, int D, int Lmax) {
+    if (attn_shape_status(N, Hq, Hkv, D, Lmax) != GDN_SUCCESS || N == 0) return 0;
+    int split, nsplit;
+    size_t bytes;
+    gdn::attn_plan(N, Hq, Hkv, D, Lmax, split, nsplit, bytes);
+    return align256(bytes);
+}
+
+gdn_status gdn_attn_decode(const gdn_attn_decode_args* p, void* stream) {
+    if (!p) return GDN_ERROR_INVALID_VALUE;
+    const gdn_attn_decode_args& x = *p;
+    gdn_status st = attn_shape_status(x.N, x.Hq, x.Hkv, x.D, x.Lmax);
+    if (st != GDN_SUCCESS) return st;
+    if (!valid_dtype(x.o_dtype)) return GDN_ERROR_NOT_SUPPORTED;
+    if (x.rotary_dim < 0 || x.rotary_dim > x.D || (x.rotary_dim & 1) || !(x.rope_theta > 0.f))
+        return GDN_ERROR_INVALID_VALUE;
+    if (x.N == 0) return GDN_SUCCESS;
+    if (!x.q || !x.k_new || !x.v_new || !x.k_cache || !x.v_cache || !x.pos || !x.o)
+        return GDN_ERROR_INVALID_VALUE;
+    if (!aligned16(x.q) || !aligned16(x.k_new) || !aligned16(x.v_new) || !aligned16(x.k_cache) ||
+        !aligned16(x.v_cache) || !aligned16(x.o) || (x.gate && !aligned16(x.gate)))
+        return GDN_ERROR_INVALID_VALUE;
+    gdn::AttnArgs a{};
+    size_t need;
+    gdn::attn_plan(x.N, x.Hq, x.Hkv, x.D, x.Lmax, a.split, a.nsplit, need);
+    if (!x.workspace || x.workspace_bytes < need) return GDN_ERROR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(x.workspace) & 255u) != 0) return GDN_ERROR_WORKSPACE;
+    a.q = static_cast<const uint16_t*>(x.q);
+    a.gate = static_cast<const uint16_t*>(x.gate);
+    a.k_new = static_cast<const uint16_t*>(x.k_new);
+    a.v_new = static_cast<const uint16_t*>(x.v_new);
+    a.k_cache = static_cast<uint16_t*>(x.k_cache);
+    a.v_cache = static_cast<uint16_t*>(x.v_cache);
+    a.pos = x.pos;
+    a.o = x.o;
+    a.o_bf16 = x.o_dtype == GDN_BF16;
+    a.N = x.N; a.Hq = x.Hq; a.Hkv = x.Hkv; a.D = x.D; a.Lmax = x.Lmax; a.rd = x.rotary_dim;
+    a.theta = x.rope_theta;
+    a.scale = x.scale;
+    a.part = static_cast<float*>(x.workspace);
+    a.stream = static_cast<hipStream_t>(stream);
+    clear_pending();
+    return from_hip(gdn::launch_attn_decode(a));
+}
+
 size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv, int chunk) {
     if (N < 0 || T_total < 0) return 0;
     if (heads_status(H, HV, dk, dv) != GDN_SUCCESS || chunk != gdn::kChunk) return 0;

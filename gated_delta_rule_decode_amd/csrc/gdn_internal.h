@@ -119,6 +119,27 @@ struct PrefillLayout {
 };
 PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv);
 
+// One decode step of gated full attention (gdn_attn_decode).
+struct AttnArgs {
+    const uint16_t* q;       // [N, Hq, D] bf16, before the rotary embedding
+    const uint16_t* gate;    // [N, Hq, D] bf16 or null
+    const uint16_t* k_new;   // [N, Hkv, D] bf16, before the rotary embedding
+    const uint16_t* v_new;   // [N, Hkv, D] bf16
+    uint16_t* k_cache;       // [N, Hkv, Lmax, D] bf16 (rotated keys)
+    uint16_t* v_cache;       // [N, Hkv, Lmax, D] bf16
+    const int32_t* pos;      // [N] position of the new token
+    void* o;                 // [N, Hq, D]
+    bool o_bf16;
+    int N, Hq, Hkv, D, Lmax, rd;
+    float theta, scale;
+    int split;               // positions per split workgroup (multiple of 16)
+    int nsplit;              // splits per (row, key/value head) in the grid
+    float* part;             // [N, Hkv, nsplit, G, D + 2] fp32 partial results
+    hipStream_t stream;
+};
+void attn_plan(int N, int Hq, int Hkv, int D, int Lmax, int& split, int& nsplit, size_t& bytes);
+hipError_t launch_attn_decode(const AttnArgs& a);
+
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 bool prefill_mfma_eligible(const PrefillArgs& a);

@@ -33,15 +33,10 @@
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_mfma.h"
 
 namespace gdn {
 
-typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f4_t mfma(bf8_t a, bf8_t b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ bf8_t lds8(const __bf16* p) {
     return *reinterpret_cast<const bf8_t*>(p);
@@ -84,39 +79,6 @@ __device__ __forceinline__ bf8_t zero8() { return __builtin_bit_cast(bf8_t, make
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-typedef float f2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
-
-// two floats -> packed hi and lo bf16 words (one conversion per word)
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{x0, x1}, bf2_t));
-    const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
-    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{x0 - h0, x1 - h1}, bf2_t));
-}
-// fp32 x -> (hi, lo) with hi = bf16(x), lo = bf16(x - hi): 4 or 8 values
-__device__ __forceinline__ void split4(const float* x, uint2& hi, uint2& lo) {
-    split2(x[0], x[1], hi.x, lo.x);
-    split2(x[2], x[3], hi.y, lo.y);
-}
-__device__ __forceinline__ void split8(const float* x, bf8_t& hi, bf8_t& lo) {
-    uint4 h, o;
-    split2(x[0], x[1], h.x, o.x);
-    split2(x[2], x[3], h.y, o.y);
-    split2(x[4], x[5], h.z, o.z);
-    split2(x[6], x[7], h.w, o.w);
-    hi = __builtin_bit_cast(bf8_t, h);
-    lo = __builtin_bit_cast(bf8_t, o);
-}
-
-// Raw buffer loads: the resource covers exactly the valid rows of a chunk, so
-// rows past a sequence end read as zero without a clamp or a select.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t in_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-__device__ __forceinline__ bf8_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(bf8_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
 
 __device__ __forceinline__ void seq_bounds_m(const int32_t* cu, int n, int T, int& s, int& e) {
     int a = cu[n], b = cu[n + 1];

@@ -33,6 +33,10 @@ normalised; a_raw, b_raw ~ N(0, 1) (the draws behind g and beta above);
 A_log ~ U(0, ln 16) per value head (the same draw as A_h); dt_bias ~
 N(0, dt_bias_std^2) per value head; w ~ 1 + N(0, 0.1^2).
 
+Attention decode inputs (``make_attn``): q, gate, k_new, v_new and both
+caches ~ N(0, 1) rounded to bf16; the cached keys are arbitrary values (they
+stand for keys stored after their rotation); pos[n] ~ U[0, Lmax) unless given.
+
 Every tensor comes from its own numpy Generator keyed by (seed, workload,
 tensor tag), so a tensor does not depend on the order in which the others are
 drawn.  Values that are bf16 are returned as float32 arrays holding exactly
@@ -49,12 +53,12 @@ import numpy as np
 __all__ = [
     "round_bf16", "bf16_bits", "PrefillInputs", "DecodeInputs", "make_prefill",
     "make_decode", "config_lengths", "workload", "WORKLOADS", "decay_scale",
-    "DecodeRawInputs", "make_decode_raw",
+    "DecodeRawInputs", "make_decode_raw", "AttnInputs", "make_attn",
 ]
 
 # tensor tags for the per-tensor generator streams
 _TAG = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "z": 6, "A": 7, "s0": 8, "len": 9,
-        "dt": 10, "w": 11}
+        "dt": 10, "w": 11, "kc": 12, "vc": 13, "pos": 14}
 
 
 def _rng(seed: int, stream: int, tag: str) -> np.random.Generator:
@@ -266,6 +270,33 @@ def make_decode_raw(steps, N, H, HV, dk, dv, *, dtype="bf16", gate_dtype="f32", 
         raise ValueError(gate_dtype)
     return DecodeRawInputs(q, k, v, a_raw, b_raw, A_log, dt_bias, z, w, dtype, gate_dtype, H,
                            HV, dk, dv)
+
+
+@dataclass
+class AttnInputs:
+    """One attention decode step: [N, heads, D] tokens and [N, Hkv, Lmax, D] caches."""
+    q: np.ndarray        # [N, Hq, D]
+    gate: np.ndarray     # [N, Hq, D]
+    k_new: np.ndarray    # [N, Hkv, D]
+    v_new: np.ndarray    # [N, Hkv, D]
+    k_cache: np.ndarray  # [N, Hkv, Lmax, D]
+    v_cache: np.ndarray  # [N, Hkv, Lmax, D]
+    pos: np.ndarray      # [N] int32
+
+
+def make_attn(N, Hq, Hkv, D, Lmax, *, pos=None, seed: int = 0, stream: int = 500) -> AttnInputs:
+    """bf16-exact attention decode inputs (float32 arrays)."""
+    f = lambda tag, shape: round_bf16(_normal(_rng(seed, stream, tag), shape))
+    q = f("q", (N, Hq, D))
+    gate = f("z", (N, Hq, D))
+    kn = f("k", (N, Hkv, D))
+    vn = f("v", (N, Hkv, D))
+    kc = f("kc", (N, Hkv, Lmax, D))
+    vc = f("vc", (N, Hkv, Lmax, D))
+    if pos is None:
+        pos = _rng(seed, stream, "pos").integers(0, Lmax, size=N)
+    pos = np.asarray(pos, dtype=np.int32)
+    return AttnInputs(q, gate, kn, vn, kc, vc, pos)
 
 
 def config_lengths(seed: int = 0, stream: int = 400, n: int = 8, lo: int = 256,

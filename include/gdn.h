@@ -246,6 +246,61 @@ gdn_status gdn_prefill_chunked_seg(const void* q, const void* k, const void* v,
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_attn_decode -- one decode step of gated full attention, the hybrid
+ * decoder's other token mixer (standard scaled dot-product attention: chat
+ * guide (de), section "Architektur"; head_dim 256, 16 query heads over 2
+ * key/value heads, partial mRoPE with theta = 1e7: Core AI card for
+ * Qwen3.6-35B-A3B, introduction).  Per row n, query head h, key/value head
+ * h / (Hq / Hkv), p = pos[n]:
+ *
+ *     qr = rope(q, p), kr = rope(k_new, p)
+ *     o  = sigmoid(gate) * softmax_t(scale qr . K_t) V_t,   t = 0 .. p
+ *
+ * with K_t, V_t the cached rows for t < p and (kr, v_new) for t = p; the call
+ * also writes kr (rounded to bf16) and v_new into the caches at row p.  rope
+ * rotates the pairs (i, i + rotary_dim/2), i < rotary_dim/2, by the angle
+ * p * rope_theta^(-2i/rotary_dim) and leaves the other dimensions as they
+ * are (text tokens carry the same position on every mRoPE section).  The
+ * pages give only the names of these parts; the rotate-half pairing, keys
+ * cached after rotation and the sigmoid output gate are this library's
+ * readings.
+ */
+typedef struct gdn_attn_decode_args {
+    const void* q;          /* [N, Hq, D] bf16, before the rotary embedding           */
+    const void* gate;       /* [N, Hq, D] bf16 output gate, or NULL for none          */
+    const void* k_new;      /* [N, Hkv, D] bf16, before the rotary embedding          */
+    const void* v_new;      /* [N, Hkv, D] bf16                                       */
+    void* k_cache;          /* [N, Hkv, Lmax, D] bf16: rows t < pos[n] are read (keys  */
+                            /* stored rotated), row pos[n] is written                  */
+    void* v_cache;          /* [N, Hkv, Lmax, D] bf16, the same rows                   */
+    const int32_t* pos;     /* [N] int32: 0 <= pos[n] < Lmax (not checked on the host) */
+    void* o;                /* [N, Hq, D] o_dtype                                      */
+    gdn_dtype o_dtype;
+    int N, Hq, Hkv, D, Lmax;  /* D in {64, 128, 256}; Hq / Hkv in {1, 2, 4, 8, 16}     */
+    int rotary_dim;         /* even, <= D (64 for head_dim 256 with a quarter rotated) */
+    float rope_theta;       /* > 0 (1e7)                                               */
+    float scale;            /* usually D^-1/2                                          */
+    void* workspace;        /* device memory, 256-byte aligned, at least              */
+    size_t workspace_bytes; /* gdn_attn_decode_workspace_bytes(N, Hq, Hkv, D, Lmax)    */
+} gdn_attn_decode_args;
+
+/* sizeof(gdn_attn_decode_args) as compiled into the library (binding check). */
+size_t gdn_attn_decode_args_size(void);
+
+/* Workspace gdn_attn_decode needs (partial results of its position splits). */
+size_t gdn_attn_decode_workspace_bytes(int N, int Hq, int Hkv, int D, int Lmax);
+
+/*
+ * Returns GDN_ERROR_INVALID_VALUE for a NULL args, a missing or misaligned
+ * pointer, non-positive sizes, an odd or too large rotary_dim, or
+ * rope_theta <= 0; GDN_ERROR_NOT_SUPPORTED for other D, head ratios or
+ * dtypes; GDN_ERROR_WORKSPACE for a missing or short workspace.  pos lives on
+ * the device and is not checked on the host: a row with pos[n] outside
+ * [0, Lmax) touches no cache and gets NaN outputs.
+ */
+gdn_status gdn_attn_decode(const gdn_attn_decode_args* args, void* stream);
+
+/*
  * gdn_rmsnorm_gated -- RMSNormGated, the norm that closes each DeltaNet layer
  * (Qwen3.5-0.8B chat guide, section "Architektur").  Per (row, head) group of
  * dv values:

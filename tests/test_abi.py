@@ -245,3 +245,37 @@ def test_decode_layer_validation(L):
     assert _layer(L, y=FAKE, y_dtype=0, z=FAKE, z_dtype=0, w=FAKE, w_dtype=0, eps=-1.0,
                   **n1) == INVALID
     assert _layer(L, o=MISALIGNED, **n1) == INVALID
+
+
+def _attn(L, **kw):
+    a = gdn.AttnDecodeArgs()
+    base = dict(q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, pos=FAKE, o=FAKE,
+                o_dtype=0, N=2, Hq=16, Hkv=2, D=256, Lmax=100, rotary_dim=64, rope_theta=1e7,
+                scale=0.0625, workspace=FAKE, workspace_bytes=1 << 30)
+    base.update(kw)
+    for name, val in base.items():
+        setattr(a, name, val)
+    return L.gdn_attn_decode(ctypes.byref(a), None)
+
+
+def test_attn_decode_validation(L):
+    OK, INVALID, UNSUP, WS = 0, 1, 2, 3
+    assert L.gdn_attn_decode_args_size() == ctypes.sizeof(gdn.AttnDecodeArgs)
+    assert L.gdn_attn_decode(None, None) == INVALID
+    assert _attn(L, N=0) == OK
+    assert _attn(L, N=-1) == INVALID
+    assert _attn(L, Hq=15) == INVALID
+    assert _attn(L, Hq=12, Hkv=2) == UNSUP          # group of 6
+    assert _attn(L, D=96) == UNSUP
+    assert _attn(L, o_dtype=4) == UNSUP
+    assert _attn(L, rotary_dim=63) == INVALID
+    assert _attn(L, rotary_dim=512) == INVALID
+    assert _attn(L, rope_theta=0.0) == INVALID
+    assert _attn(L, q=0) == INVALID
+    assert _attn(L, k_cache=MISALIGNED) == INVALID
+    assert _attn(L, workspace=0) == WS
+    need = L.gdn_attn_decode_workspace_bytes(2, 16, 2, 256, 100)
+    assert need > 0 and need % 256 == 0
+    assert _attn(L, workspace_bytes=need - 1) == WS
+    assert _attn(L, workspace=FAKE + 16) == WS
+    assert L.gdn_attn_decode_workspace_bytes(2, 16, 2, 96, 100) == 0

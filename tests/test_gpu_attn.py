@@ -1,0 +1,173 @@
+"""gdn_attn_decode (one decode step of gated full attention) on the GPU
+against the fp64 oracle: outputs, the rows appended to the caches, chains of
+steps, grouped heads, the 35B-A3B shape at full size and graph replays.
+
+The oracle keeps its own caches in chains: it appends its own rotated key,
+rounded to bf16 (the cache format), and v_new.
+"""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+from gpu_helpers import dev, host, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-3      # rel-L2 of o (bf16 inputs, fp32 arithmetic; measured ~1e-6)
+O_TOL_BF16 = 4e-3  # with o rounded to bf16
+
+
+def _gpu(x, *, rd, theta, scale, gate=True, out_dtype=None):
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    bf = torch.bfloat16
+    kc, vc = dev(x.k_cache, bf), dev(x.v_cache, bf)
+    o = gdn.attn_decode(dev(x.q, bf), dev(x.k_new, bf), dev(x.v_new, bf), kc, vc, dev(x.pos),
+                        gate=dev(x.gate, bf) if gate else None, rotary_dim=rd, rope_theta=theta,
+                        scale=scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o, kc, vc
+
+
+def _check_cache(kc, vc, x, kr_ref):
+    """Row pos holds bf16(rope(k_new)) and v_new; every other row is untouched."""
+    k, v = host(kc), host(vc)
+    N = x.pos.shape[0]
+    for n in range(N):
+        p = x.pos[n]
+        want = gi.round_bf16(kr_ref[n].astype(np.float32)).astype(np.float64)
+        err = np.abs(k[n, :, p] - want)
+        assert np.all(err <= np.abs(want) * 2.0 ** -7 + 1e-30), "appended key"
+        assert np.array_equal(v[n, :, p], x.v_new[n].astype(np.float64)), "appended value"
+        keep = np.ones(k.shape[2], bool)
+        keep[p] = False
+        assert np.array_equal(k[n][:, keep], x.k_cache[n][:, keep].astype(np.float64))
+        assert np.array_equal(v[n][:, keep], x.v_cache[n][:, keep].astype(np.float64))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,rd", [(16, 2, 256, 64), (8, 8, 128, 128), (4, 1, 64, 32),
+                                         (32, 2, 128, 0), (2, 1, 256, 256)])
+def test_attn_matches_oracle(orc, Hq, Hkv, D, rd):
+    N, Lmax = 4, 300
+    x = gi.make_attn(N, Hq, Hkv, D, Lmax, pos=[0, 17, 298, 150], seed=Hq + D + rd)
+    sc = D ** -0.5
+    say(f"attn decode Hq={Hq} Hkv={Hkv} D={D} rd={rd}")
+    o, kc, vc = _gpu(x, rd=rd, theta=1e7, scale=sc)
+    o_ref, kr = orc.attn_decode(x.q, x.k_new, x.v_new, x.k_cache, x.v_cache, x.pos, gate=x.gate,
+                                rd=rd, theta=1e7, scale=sc)
+    err = rel_l2(host(o), o_ref)
+    print(f"[parity] attn Hq={Hq} Hkv={Hkv} D={D} rd={rd}: o rel-L2 {err:.3e}")
+    assert err <= O_TOL
+    _check_cache(kc, vc, x, kr)
+
+
+def test_attn_without_gate_and_bf16_output(orc):
+    import torch
+    x = gi.make_attn(3, 16, 2, 256, 200, seed=81)
+    o, _, _ = _gpu(x, rd=64, theta=1e7, scale=1 / 16, gate=False, out_dtype=torch.bfloat16)
+    o_ref, _ = orc.attn_decode(x.q, x.k_new, x.v_new, x.k_cache, x.v_cache, x.pos, rd=64,
+                               theta=1e7, scale=1 / 16)
+    err = rel_l2(host(o), o_ref)
+    print(f"[parity] attn no gate, bf16 o: rel-L2 {err:.3e}")
+    assert o.dtype == torch.bfloat16 and err <= O_TOL_BF16
+
+
+def test_attn_chain_of_steps(orc):
+    """Six steps appending to the caches; each side keeps its own caches."""
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    N, Hq, Hkv, D, Lmax, rd = 3, 16, 2, 256, 96, 64
+    x = gi.make_attn(N, Hq, Hkv, D, Lmax, pos=[0, 40, 89], seed=82)
+    bf = torch.bfloat16
+    kc_g, vc_g = dev(x.k_cache, bf), dev(x.v_cache, bf)
+    kc_o, vc_o = x.k_cache.copy(), x.v_cache.copy()
+    r = np.random.default_rng(82)
+    say("attn chain of six steps")
+    for step in range(6):
+        pos = (x.pos + step).astype(np.int32)
+        q = gi.round_bf16(r.standard_normal((N, Hq, D)).astype(np.float32))
+        kn = gi.round_bf16(r.standard_normal((N, Hkv, D)).astype(np.float32))
+        vn = gi.round_bf16(r.standard_normal((N, Hkv, D)).astype(np.float32))
+        gt = gi.round_bf16(r.standard_normal((N, Hq, D)).astype(np.float32))
+        o = gdn.attn_decode(dev(q, bf), dev(kn, bf), dev(vn, bf), kc_g, vc_g, dev(pos),
+                            gate=dev(gt, bf), rotary_dim=rd, rope_theta=1e7)
+        o_ref, kr = orc.attn_decode(q, kn, vn, kc_o, vc_o, pos, gate=gt, rd=rd, theta=1e7,
+                                    scale=D ** -0.5)
+        for n in range(N):
+            kc_o[n, :, pos[n]] = gi.round_bf16(kr[n].astype(np.float32))
+            vc_o[n, :, pos[n]] = vn[n]
+        err = rel_l2(host(o), o_ref)
+        print(f"[parity] attn chain step {step}: o rel-L2 {err:.3e}")
+        assert err <= O_TOL
+
+
+def test_attn_full_size_35b(orc):
+    """The 35B-A3B attention shape in the benchmark's launch configuration:
+    128 rows, 16 query heads over 2 key/value heads, D = 256, a quarter of it
+    rotated, theta 1e7, positions around 8192 in caches of 8320 rows."""
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    N, Hq, Hkv, D, Lmax, rd = 128, 16, 2, 256, 8320, 64
+    g = torch.Generator(device="cuda").manual_seed(83)
+    bf = torch.bfloat16
+    kc = torch.randn(N, Hkv, Lmax, D, device="cuda", generator=g).to(bf)
+    vc = torch.randn(N, Hkv, Lmax, D, device="cuda", generator=g).to(bf)
+    q = torch.randn(N, Hq, D, device="cuda", generator=g).to(bf)
+    gt = torch.randn(N, Hq, D, device="cuda", generator=g).to(bf)
+    kn = torch.randn(N, Hkv, D, device="cuda", generator=g).to(bf)
+    vn = torch.randn(N, Hkv, D, device="cuda", generator=g).to(bf)
+    pos = torch.randint(8000, 8300, (N,), device="cuda", generator=g, dtype=torch.int32)
+    h = lambda t: t.float().cpu().numpy()
+    kc_h, vc_h = h(kc), h(vc)
+    say("attn full size 35B-A3B: 128 rows, 8320-row caches")
+    o = gdn.attn_decode(q, kn, vn, kc, vc, pos, gate=gt, rotary_dim=rd, rope_theta=1e7)
+    torch.cuda.synchronize()
+    o_ref, _ = orc.attn_decode(h(q), h(kn), h(vn), kc_h, vc_h, pos.cpu().numpy(), gate=h(gt),
+                               rd=rd, theta=1e7, scale=D ** -0.5)
+    err = rel_l2(host(o), o_ref)
+    print(f"[parity] attn full size: o rel-L2 {err:.3e}")
+    assert err <= O_TOL
+
+
+def test_attn_long_single_row(orc):
+    """One row at position 32767 of a 32768-row cache (many splits)."""
+    x = gi.make_attn(1, 16, 2, 256, 32768, pos=[32767], seed=84)
+    say("attn one row at position 32767")
+    o, kc, vc = _gpu(x, rd=64, theta=1e7, scale=1 / 16)
+    o_ref, kr = orc.attn_decode(x.q, x.k_new, x.v_new, x.k_cache, x.v_cache, x.pos, gate=x.gate,
+                                rd=64, theta=1e7, scale=1 / 16)
+    err = rel_l2(host(o), o_ref)
+    print(f"[parity] attn position 32767: o rel-L2 {err:.3e}")
+    assert err <= O_TOL
+
+
+def test_attn_graph_replay_matches_eager():
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    x = gi.make_attn(8, 16, 2, 256, 512, seed=85)
+    bf = torch.bfloat16
+    q, kn, vn, gt = dev(x.q, bf), dev(x.k_new, bf), dev(x.v_new, bf), dev(x.gate, bf)
+    pos = dev(x.pos)
+    kc_e, vc_e = dev(x.k_cache, bf), dev(x.v_cache, bf)
+    kc_g, vc_g = dev(x.k_cache, bf), dev(x.v_cache, bf)
+    o_g = torch.empty(8, 16, 256, device="cuda")
+    ws = torch.empty(gdn.attn_decode_workspace_bytes(8, 16, 2, 256, 512), dtype=torch.uint8,
+                     device="cuda")
+    say("attn graph capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        gdn.attn_decode(q, kn, vn, kc_g, vc_g, pos, gate=gt, o=o_g, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            gdn.attn_decode(q, kn, vn, kc_g, vc_g, pos, gate=gt, o=o_g, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o_e = gdn.attn_decode(q, kn, vn, kc_e, vc_e, pos, gate=gt)
+        o_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_e, o_g), rep
+        assert torch.equal(kc_e, kc_g) and torch.equal(vc_e, vc_g), rep
+        _ = (o_e * 2).sum().item()
