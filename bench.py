@@ -61,12 +61,22 @@ DECODE_TRAFFIC = {"kernel_source_sha256": "84ac4e31a985811ba80f5d4b8970a5f867f15
                   "bytes_per_launch": 68047749}
 
 
-def measured_traffic():
+# The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
+# profiles/serving_decode_traffic.md) and the attention decode step
+# (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
+SERVE_TRAFFIC = {"kernel_source_sha256": "84ac4e31a985811ba80f5d4b8970a5f867f15981be5e2c06c2eb6054861de803",
+                 "bytes_per_launch": 543601426}
+ATTN_TRAFFIC = {"kernel_source_sha256": "968b682904fb9e7fb717268ae63aa6069e46d659e75ac20c59cb29387abe4316",
+                "bytes_per_launch": 2185151813}
+
+
+def measured_traffic(record=None, source="gdn_decode.hip"):
     import hashlib
-    path = os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc", "gdn_decode.hip")
+    record = record or DECODE_TRAFFIC
+    path = os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc", source)
     with open(path, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    return DECODE_TRAFFIC["bytes_per_launch"] if sha == DECODE_TRAFFIC["kernel_source_sha256"] else None
+    return record["bytes_per_launch"] if sha == record["kernel_source_sha256"] else None
 
 
 def log(msg):
@@ -441,7 +451,8 @@ def run_attn(args):
                    "cache": "bf16", "outputs": "f32"},
         "roofline": {"kernel": "attn_split_kernel + attn_combine_kernel", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(ATTN_TRAFFIC, "gdn_attn.hip"),
                      "avg_launch_us": round(launch_us, 3),
                      "algorithmic_bytes_per_launch": bytes_launch},
     }
@@ -541,7 +552,8 @@ def run_serve(args):
                    "qk_l2norm": True, "norm": "RMSNormGated", "inputs": "bf16"},
         "roofline": {"kernel": "decode_kernel (serving: slots, gates, q/k norm, RMSNormGated)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(SERVE_TRAFFIC),
                      "avg_launch_us": round(launch_us, 3),
                      "algorithmic_bytes_per_launch": bytes_launch},
         "extras_cost": {"same_state_us_plain_decode_norm": round(plain_us, 3),
