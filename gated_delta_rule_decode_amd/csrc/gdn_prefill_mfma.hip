@@ -113,8 +113,12 @@ __device__ __forceinline__ int find_seq_m(const int32_t* chunk_off, int N, int c
 // stored in the scan's operand order: fragment f of a 64 x 64 (or dk x 64)
 // plane is 1 KiB, lane l of the consuming wavefront reads bytes 16 l .. 16 l + 15,
 // which hold row 16 (f / 2) + l % 16, columns 32 (f % 2) + 8 (l / 16) .. + 7.
-constexpr int kMaxRatio = 4;  // value heads per key head handled by this kernel
 
+// One workgroup per (chunk, value head): K K^T and Q K^T are computed again for
+// every value head of a key head.  That costs a few MFMAs and an L2 re-read of
+// K and Q, and nothing lives across value heads, so the kernel needs 70 VGPRs
+// (196 when a workgroup looped over the value heads of its key head) and LDS
+// alone sets the occupancy at three workgroups per CU.
 template <int DK>
 __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
@@ -124,17 +128,25 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     constexpr int PPR = DK / 8;         // 16-byte pieces per row
     constexpr int RPI = 64 / PPR;       // rows per coalesced 1 KiB load
     constexpr int NLD = 16 / RPI;       // loads per wavefront per tile
+    // LDS, 52,992 bytes at d_k = 128 (three workgroups per CU): Q is needed
+    // only for the first products, so T = (I + A)^-1 takes its place; the
+    // 32-block merge's X lives in T's upper-right block, which T (lower
+    // triangular) never uses; G, b and e^{G_n - G} are held for one value head
+    // at a time.
+    static_assert(C * KP * 2 <= C * AP * 4, "Q fits in the buffer of T");
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * KP];
+    __shared__ __attribute__((aligned(16))) float QT[C * AP];
     __shared__ __attribute__((aligned(16))) float Am[C * AP];  // A, then T'^T
-    __shared__ __attribute__((aligned(16))) float Tm[C * AP];  // T = (I + A)^-1
-    __shared__ __attribute__((aligned(16))) float Xm[32 * 36];
-    __shared__ __attribute__((aligned(16))) float Gs[kMaxRatio][C];
-    __shared__ __attribute__((aligned(16))) float Bs[kMaxRatio][C];
-    __shared__ __attribute__((aligned(16))) float Ds[kMaxRatio][C];
+    __shared__ __attribute__((aligned(16))) float Gs[C];
+    __shared__ __attribute__((aligned(16))) float Bs[C];
+    __shared__ __attribute__((aligned(16))) float Ds[C];
+    __bf16* const Qs = reinterpret_cast<__bf16*>(QT);
+    float* const Tm = QT;        // T, rows 0 .. 63, lower triangle
+    float* const Xm = QT + 32;   // X [32 x 32], rows 0 .. 31 of T's columns 32 .. 63
 
     const int H = A.H, HV = A.HV;
-    const int c = blockIdx.x, hk = blockIdx.y, tid = threadIdx.x;
+    const int c = blockIdx.x, tid = threadIdx.x;
+    const int hv = blockIdx.y, hk = hv / (A.HV / A.H);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     __builtin_assume(w >= 0 && w < 4);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
@@ -145,8 +157,6 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     seq_bounds_m(A.cu_seqlens, n, A.T, s0, e0);
     const int t0 = s0 + (c - A.chunk_off[n]) * C;
     const int L = min(C, e0 - t0);
-    const int ratio = HV / H;
-    const int hv0 = hk * ratio;
 
     // ---- every global load first: K and Q rows of this wave (coalesced), g and b ----
     const uint32_t qk_row = (uint32_t)H * DK * 2;
@@ -162,13 +172,13 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
         kst[p] = bload8(rk, off);
         qst[p] = bload8(rq, off);
     }
-    // wave w < ratio: g and b of value head hv0 + w for token l (zero past the end)
+    // wave 0: g and b of the value head for token l (zero past the end)
     float gv = 0.f, bv = 0.f;
-    if (w < ratio) {
+    if (w == 0) {
         const __amdgpu_buffer_rsrc_t rg = in_rsrc(A.g + (size_t)t0 * HV, (uint32_t)L * HV * 4);
         const __amdgpu_buffer_rsrc_t rb = in_rsrc(A.beta + (size_t)t0 * HV, (uint32_t)L * HV * 4);
-        gv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (int)((l * HV + hv0 + w) * 4), 0, 0));
-        bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)((l * HV + hv0 + w) * 4), 0, 0));
+        gv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (int)((l * HV + hv) * 4), 0, 0));
+        bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)((l * HV + hv) * 4), 0, 0));
     }
 #pragma unroll
     for (int p = 0; p < NLD; ++p) {
@@ -176,8 +186,8 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
         *reinterpret_cast<bf8_t*>(&Ks[at]) = kst[p];
         *reinterpret_cast<bf8_t*>(&Qs[at]) = qst[p];
     }
-    // G (log2 units, inclusive in-chunk prefix sum), b and the end decays e^{G_n - G}
-    if (w < ratio) {
+    // G (log2 units, inclusive in-chunk prefix sum) and the end decays e^{G_n - G}
+    if (w == 0) {
         float gs = gv * kLog2e;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -185,10 +195,10 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
             if (l >= off) gs += up;
         }
         const float gn = __shfl(gs, L - 1, 64);
-        Gs[w][l] = gs;
-        Bs[w][l] = bv;
-        Ds[w][l] = exp2f_(gn - gs);
-        A.ws_G[((size_t)c * HV + hv0 + w) * C + l] = gs;
+        Gs[l] = gs;
+        Bs[l] = bv;
+        Ds[l] = exp2f_(gn - gs);
+        A.ws_G[((size_t)c * HV + hv) * C + l] = gs;
     }
     __syncthreads();
 
@@ -226,15 +236,14 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
         for (int y = 0; y < 8; ++y)
             sel[h][y] = static_cast<__bf16>((8 * lg + y == 16 * h + lr) ? 1.f : 0.f);
 
-    for (int i = 0; i < ratio; ++i) {
-        const int hv = hv0 + i;
-        const float* G = Gs[i];
+    {
+        const float* G = Gs;
         // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s}); branch-free: the
         // exponent is clamped at 0 (only s < t is kept, where it is <= 0 anyway)
         // and the mask multiplies
         {
             const float4 g4 = *reinterpret_cast<const float4*>(&G[16 * w + 4 * lg]);
-            const float4 b4 = *reinterpret_cast<const float4*>(&Bs[i][16 * w + 4 * lg]);
+            const float4 b4 = *reinterpret_cast<const float4*>(&Bs[16 * w + 4 * lg]);
             const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
             const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
@@ -326,7 +335,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
             xa = mfma(ah, bl, xa);
             xa = mfma(al, bh, xa);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Xm[(16 * tbm + 4 * lg + r) * 36 + 16 * jb + lr] = xa[r];
+            for (int r = 0; r < 4; ++r) Xm[(16 * tbm + 4 * lg + r) * AP + 16 * jb + lr] = xa[r];
         }
         __syncthreads();
         {
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
             for (int x = 0; x < 8; ++x) {
                 const int rr = 16 * tbm + lr, xc = 8 * lg + x;  // T_B row rr, column xc (lower)
                 av[x] = (xc <= rr) ? Tm[(32 + rr) * AP + 32 + xc] : 0.f;
-                bv8[x] = Xm[(8 * lg + x) * 36 + 16 * jb + lr];
+                bv8[x] = Xm[(8 * lg + x) * AP + 16 * jb + lr];
             }
             bf8_t ah, al, bh, bl;
             split8(av, ah, al);
@@ -355,11 +364,11 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
             const int s_ = idx & 63, c4 = 4 * (idx >> 6);
             const float4 t4 = *reinterpret_cast<const float4*>(&Tm[s_ * AP + c4]);
             const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
-            const float4 b4 = *reinterpret_cast<const float4*>(&Bs[i][c4]);
+            const float4 b4 = *reinterpret_cast<const float4*>(&Bs[c4]);
             const float bc[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Am[(c4 + r) * AP + s_] = ((s_ >= c4 + r) ? 1.f : 0.f) * tv[r] * bc[r];
+            for (int r = 0; r < 4; ++r)  // a select, not a 0/1 factor: T's upper blocks are never written
+                Am[(c4 + r) * AP + s_] = (s_ >= c4 + r) ? tv[r] * bc[r] : 0.f;
         }
         __syncthreads();
 
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const float* arow = &Am[(16 * w + lr) * AP + 32 * k2 + 4 * lg];
-                const float* drow = &Ds[i][32 * k2 + 4 * lg];
+                const float* drow = &Ds[32 * k2 + 4 * lg];
                 const float4 a0 = *reinterpret_cast<const float4*>(arow);
                 const float4 a1 = *reinterpret_cast<const float4*>(arow + 16);
                 const float4 d0 = *reinterpret_cast<const float4*>(drow);
@@ -1305,7 +1314,8 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
                       (A.T + kChunk - 1) / kChunk > kSegMinChunks);
     if (!may) A.seg_req = -1;
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK);
-    hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.H), dim3(256), 0, A.stream, A);
+    hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.HV), dim3(256), 0,
+                       A.stream, A);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // value items of up to seg_bound segments (N without segmentation), then
@@ -1324,8 +1334,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
 }
 
 bool prefill_mfma_eligible(const PrefillArgs& A) {
-    return A.in_bf16 && (A.dk == 64 || A.dk == 128) && (A.dv % 32 == 0) &&
-           A.HV / A.H <= kMaxRatio;
+    return A.in_bf16 && (A.dk == 64 || A.dk == 128) && (A.dv % 32 == 0);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& A) {
