@@ -64,8 +64,10 @@ template <> struct io<bf16_t> {
     }
 };
 
+// explicit fused multiply-adds: every kernel that uses it rounds the same way,
+// whatever the compiler would contract in its context
 __device__ __forceinline__ float dot4(f4 a, f4 b) {
-    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+    return __builtin_fmaf(a.w, b.w, __builtin_fmaf(a.z, b.z, __builtin_fmaf(a.y, b.y, a.x * b.x)));
 }
 
 // ---- cross-lane sums -------------------------------------------------------

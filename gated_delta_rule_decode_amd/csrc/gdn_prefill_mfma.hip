@@ -22,13 +22,12 @@
 // accumulators of the update product.
 //
 // Work split.  What does not depend on the state runs chunk-parallel in
-// prep_mfma: per (chunk, key head) K K^T, and per value head of that key head
-// G, the triangular inverse and T', stored pre-split as hi/lo bf16 row-major
-// tiles.  The sequential scan_mfma runs the rest: K S^T, Q S^T, the causal
-// Q K^T (computed again per chunk: it costs less MFMA time than the HBM bytes
-// of storing P), U = T' X, O and the state update.  It reads K, Q, V, G and T'
-// fragments straight from memory into registers one chunk ahead; LDS holds
-// the state tile, the X, U, U' exchange tiles and the chunk's K rows.
+// prep_mfma, one workgroup per (chunk, value head): G, K K^T, Q K^T, the
+// triangular inverse T' and the two state-free products R = P T' and
+// Z^T = K^T diag(e^{G_n - G}) T', stored pre-split as hi/lo bf16 in the
+// scan's operand order.  The sequential scan_mfma runs the rest:
+// K S^T, Q S^T, X = V - diag(gamma) K S^T, O = scale (diag(gamma) Q S^T + R X)
+// and S' = gamma_n S + Z^T X, with the state in MFMA accumulators.
 #include <algorithm>
 
 #include "gdn_device.h"
@@ -101,8 +100,8 @@ __device__ __forceinline__ int find_seq_m(const int32_t* chunk_off, int N, int c
 // ---------------------------------------------------------------------------
 // prep: everything that does not depend on the state, chunk-parallel
 // ---------------------------------------------------------------------------
-// One workgroup (4 wavefronts) per (chunk, key head).  Wave w owns row block
-// w (tokens 16 w .. 16 w + 15).  Per value head of the key head it produces
+// One workgroup (4 wavefronts) per (chunk, value head).  Wave w owns row block
+// w (tokens 16 w .. 16 w + 15).  It produces
 //   G   in-chunk cumulative log-decay (log2 units)
 //   R   = P T'                          64 x 64, row t, column c   (hi / lo bf16)
 //   Z^T = K^T diag(e^{G_n - G}) T'      dk x 64, row j, column c   (hi / lo bf16)
