@@ -56,27 +56,79 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # job shape) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by the same
 # counters read for a copy of known size; recorded in
 # profiles/decode_traffic_qwen35_08b.md together with the sha256 of the kernel
-# source it was measured on.  Reported only while that source is unchanged.
-DECODE_TRAFFIC = {"kernel_source_sha256": "84ac4e31a985811ba80f5d4b8970a5f867f15981be5e2c06c2eb6054861de803",
-                  "bytes_per_launch": 68047749}
+# source (and the local headers it includes) it was measured on.  Reported only
+# while those sources are unchanged.
+DECODE_TRAFFIC = {"kernel_source_sha256": "c991137cdce08f1e395c42ab8b486626df2dcc866379eaa7eb5e9f9f38c6b0ef",
+                  "bytes_per_launch": 68046813}
 
 
 # The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
 # profiles/serving_decode_traffic.md) and the attention decode step
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
-SERVE_TRAFFIC = {"kernel_source_sha256": "84ac4e31a985811ba80f5d4b8970a5f867f15981be5e2c06c2eb6054861de803",
-                 "bytes_per_launch": 543601426}
-ATTN_TRAFFIC = {"kernel_source_sha256": "968b682904fb9e7fb717268ae63aa6069e46d659e75ac20c59cb29387abe4316",
-                "bytes_per_launch": 2185151813}
+SERVE_TRAFFIC = {"kernel_source_sha256": "c991137cdce08f1e395c42ab8b486626df2dcc866379eaa7eb5e9f9f38c6b0ef",
+                 "bytes_per_launch": 543602051}
+ATTN_TRAFFIC = {"kernel_source_sha256": "f0e5c6a0864c66fb225a6b0a5128a06596eff634201784893bddddcdd8b9267c",
+                "bytes_per_launch": 2185161095}
+
+
+def kernel_sources_sha256(source):
+    """sha256 over a kernel source and the local headers it includes (and
+    theirs), in include order."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc")
+    h, seen = hashlib.sha256(), []
+
+    def visit(name):
+        if name in seen or not os.path.exists(os.path.join(csrc, name)):
+            return
+        seen.append(name)
+        with open(os.path.join(csrc, name), "rb") as f:
+            data = f.read()
+        h.update(data)
+        for inc in re.findall(rb'#include "([^"]+)"', data):
+            visit(inc.decode())
+
+    visit(source)
+    return h.hexdigest()
 
 
 def measured_traffic(record=None, source="gdn_decode.hip"):
-    import hashlib
     record = record or DECODE_TRAFFIC
-    path = os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc", source)
-    with open(path, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    return record["bytes_per_launch"] if sha == record["kernel_source_sha256"] else None
+    ok = kernel_sources_sha256(source) == record["kernel_source_sha256"]
+    return record["bytes_per_launch"] if ok else None
+
+
+def copy_same_bytes(nbytes, copies=18, reps=16):
+    """A plain device copy (torch's copy_) moving the same bytes as one launch:
+    nbytes read and nbytes written, over `copies` rotating buffer pairs, captured
+    in a HIP graph and timed like the launches it is compared with."""
+    import torch
+    n = nbytes // 4
+    src = [torch.randn(n, device="cuda") for _ in range(copies)]
+    dst = [torch.empty(n, device="cuda") for _ in range(copies)]
+
+    def run():
+        for _ in range(reps):
+            for a, b in zip(src, dst):
+                b.copy_(a)
+
+    g, s = graph_capture(run)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(3):
+            g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (3 * reps * copies)
+    del g, src, dst
+    torch.cuda.empty_cache()
+    return {"kind": "torch copy_", "read_bytes": n * 4, "written_bytes": n * 4,
+            "us": round(us, 3), "GBs": round(2 * n * 4 / (us * 1e-6) / 1e9, 1)}
 
 
 def log(msg):
@@ -263,6 +315,8 @@ def run_decode_job(args):
     pf_call_us = pe0.elapsed_time(pe1) * 1e3 / 5
     pf_b = prefill_bytes(N * T, N, H, HV, d, d)
     pf_f = prefill_flops(N * T, H, HV, d, d)
+    # a plain copy of the launch's state bytes, for the achievable bandwidth
+    copy_ref = copy_same_bytes(N * HV * d * d * 4)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s per DeltaNet layer",
@@ -282,6 +336,7 @@ def run_decode_job(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "avg_launch_us": round(dec_launch_us, 3),
                      "algorithmic_bytes_per_launch": bytes_launch},
+        "copy_same_bytes": copy_ref,
         "roofline_prefill": {"call_us": round(pf_call_us, 2),
                              "hbm_achieved_GBs": round(pf_b / (pf_call_us * 1e-6) / 1e9, 1),
                              "hbm_frac": round(pf_b / (pf_call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -325,24 +380,39 @@ def run_prefill(args, cfg: int):
     o = torch.empty(T, HV, d, device=dev)
     sf = torch.empty(N, HV, d, d, device=dev)
     ws = torch.empty(gdn.prefill_workspace_bytes(N, T, H, HV, d, d), dtype=torch.uint8, device=dev)
+    def call(seg):
+        gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf, o=o,
+                            workspace=ws, segment_chunks=seg)
+
     def timed(seg):
-        call = lambda: gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf,
-                                           o=o, workspace=ws, segment_chunks=seg)
-        for _ in range(args.warmup):
-            call()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record()
         for _ in range(args.steps):
-            call()
+            call(seg)
         e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return max(e0.elapsed_time(e1), wall * 1e3) / args.steps
 
-    ms = timed(0)               # the library's own choice of the segment-parallel scan
-    ms_whole = timed(-1)        # one chain per (sequence, head, tile), for comparison
+    # warm-up: the requested calls, and at least a quarter second of calls so
+    # that the clocks have settled; then the library's own choice of the
+    # segment-parallel scan (0) and one chain per (sequence, head, tile) (-1),
+    # alternately, three times each (medians)
+    t_end = time.perf_counter() + 0.25
+    n_w = 0
+    while n_w < args.warmup or time.perf_counter() < t_end:
+        call(0)
+        call(-1)
+        torch.cuda.synchronize()
+        n_w += 1
+    runs = {0: [], -1: []}
+    for _ in range(3):
+        for seg in (0, -1):
+            runs[seg].append(timed(seg))
+    ms = float(np.median(runs[0]))
+    ms_whole = float(np.median(runs[-1]))
     pb = prefill_bytes(T, N, H, HV, d, d, s0=s0 is not None)
     pfl = prefill_flops(T, H, HV, d, d)
     return {
@@ -539,6 +609,7 @@ def run_serve(args):
                                                A_log=Ly["A_log"], dt_bias=Ly["dt"],
                                                qk_l2norm=True, z=Ly["z"][0], w=Ly["w"],
                                                y=Ly["y"], scale=scale))
+    copy_ref = copy_same_bytes(N * HV * d * d * 4, copies=4, reps=8)
 
     tokens = N * steps * L
     return {
@@ -556,6 +627,7 @@ def run_serve(args):
                      "traffic": measured_traffic(SERVE_TRAFFIC),
                      "avg_launch_us": round(launch_us, 3),
                      "algorithmic_bytes_per_launch": bytes_launch},
+        "copy_same_bytes": copy_ref,
         "extras_cost": {"same_state_us_plain_decode_norm": round(plain_us, 3),
                         "same_state_us_layer_with_gates_l2_norm": round(extras_us, 3)},
     }
