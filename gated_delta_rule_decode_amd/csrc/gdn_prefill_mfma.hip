@@ -885,6 +885,380 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
 }
 
 // ---------------------------------------------------------------------------
+// scan by rows: one workgroup per chain, a wavefront per 32 state rows
+// ---------------------------------------------------------------------------
+// The same chunk step as scan_mfma (same products, same rounding), arranged
+// so that the workgroup owns a whole head (d_k = d_v = 128: four wavefronts of
+// 32 state rows) and every wavefront runs the full chunk for its rows:
+//   (A) K S^T and S Q^T for all 64 tokens of the chunk and its 32 rows,
+//   X = V - diag(gamma) K S^T, kept in the wavefront's own LDS area,
+//   (B) O^T = scale (S Q^T diag(gamma) + X^T R^T), S'^T = gamma_n S^T + Z^T X.
+// Rows never interact, so the wavefronts need each other only for the
+// chunk's shared operands: K, Q, V rows and the Z^T fragments are loaded once
+// per workgroup (a chunk ahead, into registers) and staged in LDS between two
+// barriers; the R fragments come straight from memory into registers, a chunk
+// ahead.  The state of the wavefront's rows lives in MFMA accumulators
+// (S'^T tiles) and in its LDS area as hi / lo bf16 for the next chunk's (A);
+// X takes the same area while the state is in the accumulators.
+template <typename Tout>
+__global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
+    constexpr int DK = 128, DV = 128, C = kChunk;
+    constexpr int KP = DK + 8;  // padded bf16 row of K, Q and the state
+    constexpr int VP = DV + 8;  // padded bf16 row of the V tile
+    constexpr int TP = C + 8;   // padded bf16 row of X (tokens)
+    constexpr int NJB = DK / 16;
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * KP];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[C * VP];
+    __shared__ __attribute__((aligned(16))) bf8_t Zf[2][2 * NJB][64];  // Z^T fragments hi, lo
+    __shared__ __attribute__((aligned(16))) float Gs[C];
+    __shared__ __attribute__((aligned(16))) __bf16 Sp[4][2][32 * KP];  // per wavefront: S hi, lo / X
+
+    const int H = A.H, HV = A.HV;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // rows 32 w .. 32 w + 31
+    __builtin_assume(w >= 0 && w < 4);
+    const int l = tid & 63, lr = l & 15, lg = l >> 4;
+    // value items (segment, head) first, then the transition items of later segments
+    const int b = blockIdx.x;
+    const int nb1 = A.seg_bound * HV;
+    const bool trans = b >= nb1;
+    const int chain = trans ? b - nb1 : b;
+    const int nseg = __builtin_amdgcn_readfirstlane(A.plan[0]);
+    if (chain >= nseg * HV) return;
+    const int sg = chain / HV, h = chain - sg * HV;
+    const int n = __builtin_amdgcn_readfirstlane(A.seg_seq[sg]);
+    const int sidx = __builtin_amdgcn_readfirstlane(A.seg_idx[sg]);
+    if (trans && sidx == 0) return;
+    const int hk = h / (HV / H);
+    Tout* op = static_cast<Tout*>(A.o);
+    const float* init = nullptr;  // null: zero state (or the identity for a transition item)
+    float* fin;
+    size_t ibase = 0, fbase;
+    if (trans) {
+        fin = A.ws_Phi;
+        fbase = (size_t)(sg * HV + h) * DK * DK;
+    } else if (sidx == 0) {
+        init = A.s0;
+        ibase = (size_t)(n * HV + h) * DV * DK;
+        const bool whole = __builtin_amdgcn_readfirstlane(A.seq_nseg[n]) == 1;
+        fin = whole ? A.s_final : A.ws_E;
+        fbase = whole ? ibase : (size_t)(sg * HV + h) * DV * DK;
+    } else {
+        fin = A.ws_E;
+        fbase = (size_t)(sg * HV + h) * DV * DK;
+    }
+
+    // state: sacc[jb][ib][r] = S[i = 32 w + 16 ib + lr][j = 16 jb + 4 lg + r]
+    f4_t sacc[NJB][2];
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const int i = 32 * w + 16 * ib + lr, j = 16 * jb + 4 * lg;
+            if (init) {
+                const float4 v4 = *reinterpret_cast<const float4*>(init + ibase + (size_t)i * DK + j);
+                sacc[jb][ib] = f4_t{v4.x, v4.y, v4.z, v4.w};
+            } else if (trans) {
+                const int d = i - j;  // identity
+                sacc[jb][ib] = f4_t{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f,
+                                    d == 3 ? 1.f : 0.f};
+            } else {
+                sacc[jb][ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    auto store_state = [&]() {
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const int i = 32 * w + 16 * ib + lr, j = 16 * jb + 4 * lg;
+                if (trans) {
+                    // Phi stored transposed (Phi^T[j][i]), as the combine pass reads it
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) fin[fbase + (size_t)(j + r) * DK + i] = sacc[jb][ib][r];
+                } else {
+                    *reinterpret_cast<float4*>(fin + fbase + (size_t)i * DK + j) =
+                        make_float4(sacc[jb][ib][0], sacc[jb][ib][1], sacc[jb][ib][2], sacc[jb][ib][3]);
+                }
+            }
+    };
+    __bf16* const Sh = Sp[w][0];
+    __bf16* const Sl = Sp[w][1];
+    __bf16* const Xh = Sp[w][0];           // X [32 rows][64 tokens] hi, in the state's place
+    __bf16* const Xl = Sp[w][0] + 32 * TP;  // and lo (both inside the hi plane)
+    auto state_to_lds = [&]() {
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const int off = (16 * ib + lr) * KP + 16 * jb + 4 * lg;
+                float sv[4] = {sacc[jb][ib][0], sacc[jb][ib][1], sacc[jb][ib][2], sacc[jb][ib][3]};
+                uint2 hi, lo;
+                split4(sv, hi, lo);
+                *reinterpret_cast<uint2*>(&Sh[off]) = hi;
+                *reinterpret_cast<uint2*>(&Sl[off]) = lo;
+            }
+    };
+
+    int sq, eq;
+    seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
+    const int c_first = __builtin_amdgcn_readfirstlane(A.seg_c0[sg]);
+    int nch = __builtin_amdgcn_readfirstlane(A.seg_nch[sg]);
+    sq += (c_first - min(A.chunk_off[n], A.max_chunks)) * C;  // the segment's first token
+    if (c_first + nch > A.max_chunks) nch = max(0, A.max_chunks - c_first);
+    if (nch <= 0) {
+        store_state();
+        return;
+    }
+
+    // ---- loads of a chunk (issued a chunk ahead) ----
+    const uint32_t qk_row = (uint32_t)H * DK * 2;       // bytes per token of q, k
+    const uint32_t v_row = (uint32_t)HV * DV * 2;       // bytes per token of v
+    const uint32_t v_on = trans ? 0u : 1u;              // a transition item reads V as zero
+    // cooperative pieces: 16 bytes, piece p = tid + 256 q of a 64 x 256-byte tile
+    uint32_t kq_off[4], v_off[4];
+    int st_off[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int p = tid + 256 * q, row = p >> 4, c16 = p & 15;
+        kq_off[q] = ((uint32_t)row * H + hk) * DK * 2 + 16 * c16;
+        v_off[q] = ((uint32_t)row * HV + h) * DV * 2 + 16 * c16;
+        st_off[q] = row * KP + 8 * c16;  // KP == VP
+    }
+    bf8_t kst[4], qst[4], vst[4], zst[2][4];
+    float gst = 0.f;
+    struct RF {
+        bf8_t h[4][2], lo[4][2];  // R fragments (row block tb, k-step kk), hi / lo
+    };
+    RF rn, rc;  // next chunk's, this chunk's
+    auto chunk_t0 = [&](int jc) { return sq + jc * C; };
+    auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
+    auto load_chunk = [&](int jc) {
+        const int t0 = chunk_t0(jc), L = chunk_L(jc);
+        const __amdgpu_buffer_rsrc_t rk =
+            in_rsrc(static_cast<const bf16_t*>(A.k) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
+        const __amdgpu_buffer_rsrc_t rq =
+            in_rsrc(static_cast<const bf16_t*>(A.q) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
+        const __amdgpu_buffer_rsrc_t rv =
+            in_rsrc(static_cast<const bf16_t*>(A.v) + (size_t)t0 * HV * DV, v_on * L * v_row);
+        const size_t cc = (size_t)(c_first + jc) * HV + h;
+        const __amdgpu_buffer_rsrc_t zh = in_rsrc(A.ws_Zh + cc * DK * C, DK * C * 2);
+        const __amdgpu_buffer_rsrc_t zl = in_rsrc(A.ws_Zl + cc * DK * C, DK * C * 2);
+        const __amdgpu_buffer_rsrc_t rh = in_rsrc(A.ws_Rh + cc * C * C, C * C * 2);
+        const __amdgpu_buffer_rsrc_t rl = in_rsrc(A.ws_Rl + cc * C * C, C * C * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            kst[q] = bload8(rk, kq_off[q]);
+            qst[q] = bload8(rq, kq_off[q]);
+            vst[q] = bload8(rv, v_off[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            zst[0][q] = bload8(zh, (uint32_t)(tid + 256 * q) * 16);
+            zst[1][q] = bload8(zl, (uint32_t)(tid + 256 * q) * 16);
+        }
+        if (tid < C) gst = A.ws_G[cc * C + tid];
+        // R: fragment (tb, kk) is 1 KiB at 1024 (2 tb + kk); row blocks 0, 1 need k-step 0 only
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk <= (tb >> 1)) {
+                    rn.h[tb][kk] = bload8(rh, (uint32_t)(1024 * (2 * tb + kk) + 16 * l));
+                    rn.lo[tb][kk] = bload8(rl, (uint32_t)(1024 * (2 * tb + kk) + 16 * l));
+                } else {
+                    rn.h[tb][kk] = zero8();
+                    rn.lo[tb][kk] = zero8();
+                }
+            }
+    };
+    auto stage_chunk = [&]() {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<bf8_t*>(&Ks[st_off[q]]) = kst[q];
+            *reinterpret_cast<bf8_t*>(&Qs[st_off[q]]) = qst[q];
+            *reinterpret_cast<bf8_t*>(&Vs[st_off[q]]) = vst[q];
+            const int p = tid + 256 * q;
+            Zf[0][p >> 6][p & 63] = zst[0][q];
+            Zf[1][p >> 6][p & 63] = zst[1][q];
+        }
+        if (tid < C) Gs[tid] = gst;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                rc.h[tb][kk] = rn.h[tb][kk];
+                rc.lo[tb][kk] = rn.lo[tb][kk];
+            }
+    };
+
+    load_chunk(0);
+    state_to_lds();
+    for (int jc = 0; jc < nch; ++jc) {
+        const int t0 = chunk_t0(jc), L = chunk_L(jc);
+        __syncthreads();  // every wavefront is done with the previous chunk's shared operands
+        stage_chunk();
+        __syncthreads();
+        load_chunk(min(jc + 1, nch - 1));  // the last chunk loads itself again
+
+        // decays of this chunk (G in log2 units)
+        float gt[4], gam[4][4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            gt[tb] = exp2f_(Gs[16 * tb + lr]);
+            const float4 g4 = *reinterpret_cast<const float4*>(&Gs[16 * tb + 4 * lg]);
+            gam[tb][0] = exp2f_(g4.x);
+            gam[tb][1] = exp2f_(g4.y);
+            gam[tb][2] = exp2f_(g4.z);
+            gam[tb][3] = exp2f_(g4.w);
+        }
+        const float gn = exp2f_(Gs[L - 1]);
+
+        // (A) ksa[tb][ib][r] = (K S^T)[t = 16 tb + 4 lg + r][i = 16 ib + lr]
+        //     qsa[tb][ib][r] = (S Q^T)[i = 16 ib + 4 lg + r][t = 16 tb + lr]
+        f4_t ksa[4][2], qsa[4][2];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                ksa[tb][ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+                qsa[tb][ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            const int col = 32 * kk + 8 * lg;
+            bf8_t sh[2], sl[2], ka[4], qa[4];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                sh[ib] = lds8(&Sh[(16 * ib + lr) * KP + col]);
+                sl[ib] = lds8(&Sl[(16 * ib + lr) * KP + col]);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                ka[tb] = lds8(&Ks[(16 * tb + lr) * KP + col]);
+                qa[tb] = lds8(&Qs[(16 * tb + lr) * KP + col]);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    ksa[tb][ib] = mfma(ka[tb], sh[ib], ksa[tb][ib]);
+                    qsa[tb][ib] = mfma(sh[ib], qa[tb], qsa[tb][ib]);
+                    ksa[tb][ib] = mfma(ka[tb], sl[ib], ksa[tb][ib]);
+                    qsa[tb][ib] = mfma(sl[ib], qa[tb], qsa[tb][ib]);
+                }
+        }
+        // X = V - diag(gamma) K S^T (zero in rows past the end: V and K read as zero),
+        // into the wavefront's area as X[i][t] hi / lo
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                float xv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float vv = static_cast<float>(Vs[(16 * tb + 4 * lg + r) * VP + 32 * w + 16 * ib + lr]);
+                    xv[r] = vv - gam[tb][r] * ksa[tb][ib][r];
+                }
+                uint2 hi, lo;
+                split4(xv, hi, lo);
+                const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
+                *reinterpret_cast<uint2*>(&Xh[off]) = hi;
+                *reinterpret_cast<uint2*>(&Xl[off]) = lo;
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // (B) X fragments: k-step kk (tokens 32 kk + 8 lg ..), rows 16 ib + lr
+        bf8_t xh[2][2], xl[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                xh[kk][ib] = lds8(&Xh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+                xl[kk][ib] = lds8(&Xl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+            }
+        // O^T = scale (S Q^T diag(gamma) + X^T R^T); R is lower triangular, so
+        // row block tb needs the k-steps up to tb / 2
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) qsa[tb][ib][r] *= gt[tb];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (kk <= (tb >> 1)) {
+                        qsa[tb][ib] = mfma(xh[kk][ib], rc.h[tb][kk], qsa[tb][ib]);
+                        qsa[tb][ib] = mfma(xl[kk][ib], rc.h[tb][kk], qsa[tb][ib]);
+                        qsa[tb][ib] = mfma(xh[kk][ib], rc.lo[tb][kk], qsa[tb][ib]);
+                    }
+                }
+            }
+        // S'^T = gamma_n S^T + Z^T X
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            bf8_t zh[2], zl[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                zh[kk] = Zf[0][2 * jb + kk][l];
+                zl[kk] = Zf[1][2 * jb + kk][l];
+            }
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[jb][ib][r] *= gn;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    sacc[jb][ib] = mfma(zh[kk], xh[kk][ib], sacc[jb][ib]);
+                    sacc[jb][ib] = mfma(zh[kk], xl[kk][ib], sacc[jb][ib]);
+                    sacc[jb][ib] = mfma(zl[kk], xh[kk][ib], sacc[jb][ib]);
+                }
+            }
+        }
+        // outputs: qsa[tb][ib][r] = O[t = 16 tb + lr][i = 32 w + 16 ib + 4 lg + r]
+        // (w for a transition item); rows t >= L land past the resource end
+        {
+            const int trow = lr;
+            if (trans) {
+                float* wp = A.ws_W + (size_t)t0 * HV * DK;
+                const __amdgpu_buffer_rsrc_t wr = out_rsrc(wp, (uint32_t)(L * HV * DK * 4));
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        const float ov[4] = {A.scale * qsa[tb][ib][0], A.scale * qsa[tb][ib][1],
+                                             A.scale * qsa[tb][ib][2], A.scale * qsa[tb][ib][3]};
+                        out_store4(wr, (uint32_t)(((16 * tb + trow) * HV + h) * DK + 32 * w + 16 * ib + 4 * lg),
+                                   ov, wp);
+                    }
+            } else {
+                const __amdgpu_buffer_rsrc_t orsrc =
+                    out_rsrc(op + (size_t)t0 * HV * DV, (uint32_t)(L * HV * DV * sizeof(Tout)));
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        const float ov[4] = {A.scale * qsa[tb][ib][0], A.scale * qsa[tb][ib][1],
+                                             A.scale * qsa[tb][ib][2], A.scale * qsa[tb][ib][3]};
+                        out_store4(orsrc,
+                                   (uint32_t)(((16 * tb + trow) * HV + h) * DV + 32 * w + 16 * ib + 4 * lg),
+                                   ov, op);
+                    }
+            }
+        }
+        // the next chunk's state (X is no longer read: same wavefront, in order)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        state_to_lds();
+    }
+    store_state();
+}
+
+// ---------------------------------------------------------------------------
 // segment-parallel scan: plan, combine, correction
 // ---------------------------------------------------------------------------
 // The chunk map of a segment is affine in the state entering it:
@@ -1298,11 +1672,17 @@ __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
     }
 }
 
+constexpr size_t kRowsMinChains = 512;
+
 // plan -> prep -> scan (value and transition items) -> combine -> correction.
 // Without segmentation the last two find no work and exit.
 template <int DK, typename Tout>
 static hipError_t launch_mfma_t(const PrefillArgs& A0) {
-    const int TV = A0.dv / 32, TK = DK / 32;
+    // Many chains at d_k = d_v = 128: one workgroup per chain (scan_rows_kernel,
+    // more work per CU and chunk step); otherwise one per 32 state rows of a
+    // chain (scan_mfma_kernel, the shorter chunk step)
+    const bool rows = DK == 128 && A0.dv == 128 && (size_t)A0.N * A0.HV >= kRowsMinChains;
+    const int TV = rows ? 1 : A0.dv / 32, TK = rows ? 1 : DK / 32;
     // Segmentation is possible only when asked for, or, automatically, when
     // the unsegmented scan leaves CUs idle (fewer than 256 workgroups) and
     // some sequence may be longer than one segment; otherwise the plan is
@@ -1319,10 +1699,16 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
     if (err != hipSuccess) return err;
     // value items of up to seg_bound segments (N without segmentation), then
     // the transition items; the kernel splits the grid at seg_bound
-    const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * A.HV + 7) / 8) * 8;
-    const size_t blocks = may ? chains8 * (TV + TK) : chains8 * TV;
-    hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(256), 0,
-                       A.stream, A);
+    if (rows) {
+        const size_t blocks = may ? (size_t)2 * A.seg_bound * A.HV : (size_t)A.N * A.HV;
+        hipLaunchKernelGGL((scan_rows_kernel<Tout>), dim3((unsigned)blocks), dim3(256), 0,
+                           A.stream, A);
+    } else {
+        const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * A.HV + 7) / 8) * 8;
+        const size_t blocks = may ? chains8 * (TV + TK) : chains8 * TV;
+        hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(256), 0,
+                           A.stream, A);
+    }
     if (may) {
         const int cgrid = (int)std::min<size_t>((size_t)A.N * A.HV * TV, 512);
         hipLaunchKernelGGL((combine_kernel<DK>), dim3(cgrid), dim3(256), 0, A.stream, A);

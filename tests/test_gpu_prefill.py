@@ -192,3 +192,53 @@ def test_prefill_value_heads_per_key_head(orc, ratio):
     o, S = gpu_prefill(x)
     o_ref, S_ref = oracle_prefill(orc, x)
     assert_parity(host(o), host(S), o_ref, S_ref, what=f"value heads per key head {ratio}")
+
+
+def _lengths_many(seed, n, hi):
+    rng = np.random.default_rng(seed)
+    out = [int(x) for x in rng.integers(0, hi, size=n)]
+    out[0], out[1], out[2], out[3] = 0, 1, 64, 65  # empty, one token, whole and ragged chunks
+    return out
+
+
+@pytest.mark.parametrize("H,HV,N", [(16, 16, 32), (8, 16, 32), (16, 32, 16)])
+def test_prefill_many_chains_matches_oracle(orc, H, HV, N):
+    """At least 512 (sequence, value head) chains at d = 128: the scan runs one
+    workgroup per chain (a wavefront per 32 state rows)."""
+    lengths = _lengths_many(100 + HV + N, N, 300)
+    x = gi.make_prefill(lengths, H, HV, 128, 128, s0_std=0.02, seed=101 + H)
+    say(f"prefill many chains: N={N} H={H} HV={HV} T={sum(lengths)}")
+    o, S = gpu_prefill(x, scale=128 ** -0.5)
+    o_ref, S_ref = oracle_prefill(orc, x, scale=128 ** -0.5)
+    assert_parity(host(o), host(S), o_ref, S_ref, what=f"many chains H={H} HV={HV}")
+
+
+def test_prefill_many_chains_equals_per_tile_form():
+    """The per-chain scan (N HV >= 512) and the per-32-row scan (the same
+    sequences in two calls of fewer chains) perform the same products in the
+    same order: outputs and final states agree bit for bit."""
+    lengths = _lengths_many(7, 32, 400)
+    x = gi.make_prefill(lengths, 16, 16, 128, 128, s0_std=0.02, decay="mild", seed=102)
+    say("prefill per-chain form vs per-tile form")
+    o, S = gpu_prefill(x, scale=128 ** -0.5)
+    o, S = host(o), host(S)
+    cu = x.cu_seqlens
+    for half in (slice(0, 16), slice(16, 32)):
+        a, e = cu[half.start], cu[half.stop]
+        y = gi.PrefillInputs(x.q[a:e], x.k[a:e], x.v[a:e], x.g[a:e], x.beta[a:e], x.z[a:e], x.w,
+                             (cu[half.start:half.stop + 1] - a).astype(np.int32), x.s0[half],
+                             x.dtype, 16, 16, 128, 128)
+        oh, Sh = gpu_prefill(y, scale=128 ** -0.5)
+        assert np.array_equal(o[a:e], host(oh))
+        assert np.array_equal(S[half], host(Sh))
+
+
+def test_prefill_many_chains_forced_segments(orc):
+    """Forced segments with the per-chain scan: transition items (from the
+    identity, V = 0), the combine and the correction passes."""
+    lengths = [2100] * 8 + [0, 70] + [1500] * 22
+    x = gi.make_prefill(lengths, 16, 16, 128, 128, s0_std=0.02, decay="mild", seed=103)
+    say(f"prefill many chains, segments of 32 chunks: T={sum(lengths)}")
+    o, S = gpu_prefill(x, scale=128 ** -0.5, segment_chunks=32)
+    o_ref, S_ref = oracle_prefill(orc, x, scale=128 ** -0.5)
+    assert_parity(host(o), host(S), o_ref, S_ref, what="many chains, segmented")
