@@ -1296,9 +1296,11 @@ __device__ int block_exclusive_scan(int n, F count, G emit, int* buf) {
 
 // Segment length candidates (chunks; 0: do not segment) and the cost model
 // that picks one, in microseconds, fitted to measurements of the scan on the
-// MI355X: a chain step takes about 2.2 us while at most 64 workgroups run,
-// 2.6 us up to 256 (one per CU) and 4.5 us where two share a CU, and the
-// whole launch sustains about 110 chain steps per us; a segmented run moves
+// MI355X: with a workgroup per 32 state rows, a chain step takes about 2.2 us
+// while at most 64 workgroups run, 2.6 us up to 256 (one per CU) and 4.5 us
+// where two share a CU, and the whole launch sustains about 110 chain steps
+// per us; with a workgroup per chain, a step takes about 5.6 us (one per CU)
+// and the launch sustains about 46 steps per us; a segmented run moves
 // about 8 (dk + dv) more bytes per token and head of every later segment (w
 // written and read, o read and written again) at about 5 TB/s, plus about
 // 3 us per segment of the combine pass.  A launch that already gives every
@@ -1314,7 +1316,8 @@ constexpr int kNCand = 7;
 // sequences stay in LDS.
 constexpr int kPlanCache = 2048;
 
-__global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A, int TV, int TK) {
+__global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A, int TV, int TK,
+                                                            int rows) {
     __shared__ int ibuf[256];
     __shared__ int cnt_sh[kPlanCache], off_sh[kPlanCache];
     __shared__ float acc[3][kNCand];  // items, chain steps, tokens of later segments
@@ -1393,14 +1396,15 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A,
         __syncthreads();
         if (threadIdx.x == 0) {
             const int cm = s_cmax;
-            const float dk = 32.f * TK, dv = 32.f * TV;
+            const float dk = (float)A.dk, dv = (float)A.dv;
             float best = 0.f;
             int bestL = 0;
             for (int k = 0; k < (acc[0][0] < 256.f ? kNCand : 1); ++k) {
                 const int L = kSegCand[k] ? kSegCand[k] : (1 << 30);
                 const bool seg = cm > L;
-                const float step = acc[0][k] <= 64.f ? 2.2f : (acc[0][k] <= 256.f ? 2.6f : 4.5f);
-                float cost = fmaxf(acc[1][k] / 110.f, (float)min(cm, L) * step);
+                const float step = rows ? 5.6f
+                                        : (acc[0][k] <= 64.f ? 2.2f : (acc[0][k] <= 256.f ? 2.6f : 4.5f));
+                float cost = fmaxf(acc[1][k] / (rows ? 46.f : 110.f), (float)min(cm, L) * step);
                 if (seg)
                     cost += acc[2][k] * HV * 8.f * (dk + dv) / 5.0e6f + 3.f * ((cm + L - 1) / L) + 5.f;
                 if (k == 0 || cost < best) {
@@ -1673,15 +1677,20 @@ __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
 }
 
 constexpr size_t kRowsMinChains = 512;
+constexpr size_t kRowsMinTokensPerSeq = 16384;
 
 // plan -> prep -> scan (value and transition items) -> combine -> correction.
 // Without segmentation the last two find no work and exit.
 template <int DK, typename Tout>
 static hipError_t launch_mfma_t(const PrefillArgs& A0) {
-    // Many chains at d_k = d_v = 128: one workgroup per chain (scan_rows_kernel,
-    // more work per CU and chunk step); otherwise one per 32 state rows of a
-    // chain (scan_mfma_kernel, the shorter chunk step)
-    const bool rows = DK == 128 && A0.dv == 128 && (size_t)A0.N * A0.HV >= kRowsMinChains;
+    // At d_k = d_v = 128, one workgroup per chain (scan_rows_kernel: more work
+    // per CU and chunk step) when there are many chains, or when long
+    // sequences may be segmented (the segments then fill the CUs); otherwise
+    // one workgroup per 32 state rows of a chain (scan_mfma_kernel, the
+    // shorter chunk step)
+    const bool rows = DK == 128 && A0.dv == 128 &&
+                      ((size_t)A0.N * A0.HV >= kRowsMinChains ||
+                       (A0.seg_req >= 0 && (size_t)A0.T >= kRowsMinTokensPerSeq * (size_t)A0.N));
     const int TV = rows ? 1 : A0.dv / 32, TK = rows ? 1 : DK / 32;
     // Segmentation is possible only when asked for, or, automatically, when
     // the unsegmented scan leaves CUs idle (fewer than 256 workgroups) and
@@ -1692,7 +1701,8 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
                      (A.seg_req == 0 && (size_t)A.N * A.HV * TV < 256 &&
                       (A.T + kChunk - 1) / kChunk > kSegMinChunks);
     if (!may) A.seg_req = -1;
-    hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK);
+    hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK,
+                       rows ? 1 : 0);
     hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.HV), dim3(256), 0,
                        A.stream, A);
     hipError_t err = hipGetLastError();
