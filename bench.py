@@ -4,9 +4,10 @@ Default workload (one "step"): the Qwen3.5-0.8B DeltaNet decode job over the
 18 DeltaNet layers of the model (18 of 24 layers; Qwen3.5-0.8B chat guide,
 section "Architektur").  32 sequences, 16 key/query heads, 16 value heads,
 d_k = d_v = 128, bf16 q/k/v, fp32 state.  Per layer: a 512-token chunked
-prefill of every sequence from a zero state (gdn_prefill_chunked) followed by
-RMSNormGated of its outputs; then 256 decode steps, each advancing all 18
-layer-states by one token (decode + RMSNormGated per layer).
+prefill of every sequence from a zero state followed by RMSNormGated of its
+outputs, in one call (gdn_prefill_chunked_norm: the norm runs inside the
+scan); then 256 decode steps, each advancing all 18 layer-states by one token
+(decode + RMSNormGated per layer).
 Every layer has its own state (18 x 32 MiB = 576 MiB, more than the 256 MB
 Infinity Cache) and its own inputs, all resident in HBM before timing starts.
 The decode step and its RMSNormGated run as one kernel (gdn_decode_step_norm).
@@ -245,15 +246,14 @@ def run_decode_job(args):
                            yd=torch.empty(N, HV, d, device=dev)))
     w = torch.ones(d, device=dev)
     cu = torch.arange(0, N * T + 1, T, dtype=torch.int32, device=dev)
-    ws = torch.empty(gdn.prefill_workspace_bytes(N, N * T, H, HV, d, d), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(gdn.prefill_norm_workspace_bytes(N, N * T, H, HV, d, d),
+                     dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def prefill_phase():
         for Ly in layers:
-            gdn.prefill_chunked(Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu,
-                                final_state=Ly["state"], o=Ly["o"], workspace=ws)
-            gdn.rmsnorm_gated(Ly["o"], Ly["z"], w, y=Ly["y"])
+            gdn.prefill_chunked_norm(Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu, Ly["z"], w,
+                                     final_state=Ly["state"], y=Ly["y"], workspace=ws)
 
     def decode_phase():
         for t in range(steps):
@@ -302,17 +302,23 @@ def run_decode_job(args):
     bytes_launch = decode_bytes_per_token(H, HV, d, d) * N
     achieved = bytes_launch / (dec_launch_us * 1e-6) / 1e9
 
-    # prefill kernels: one layer's call timed alone
-    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # prefill kernels: one layer's call timed alone, the prefill by itself
+    # (gdn_prefill_chunked) and with the norm (the job's call)
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     Ly = layers[0]
     with torch.cuda.stream(s):
-        pe0.record(s)
+        pe[0].record(s)
         for _ in range(5):
             gdn.prefill_chunked(Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu,
                                 final_state=Ly["state"], o=Ly["o"], workspace=ws)
-        pe1.record(s)
+        pe[1].record(s)
+        for _ in range(5):
+            gdn.prefill_chunked_norm(Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu, Ly["z"], w,
+                                     final_state=Ly["state"], y=Ly["y"], workspace=ws)
+        pe[2].record(s)
     torch.cuda.synchronize()
-    pf_call_us = pe0.elapsed_time(pe1) * 1e3 / 5
+    pf_call_us = pe[0].elapsed_time(pe[1]) * 1e3 / 5
+    pf_norm_call_us = pe[1].elapsed_time(pe[2]) * 1e3 / 5
     pf_b = prefill_bytes(N * T, N, H, HV, d, d)
     pf_f = prefill_flops(N * T, H, HV, d, d)
     # a plain copy of the launch's state bytes, for the achievable bandwidth
@@ -338,6 +344,7 @@ def run_decode_job(args):
                      "algorithmic_bytes_per_launch": bytes_launch},
         "copy_same_bytes": copy_ref,
         "roofline_prefill": {"call_us": round(pf_call_us, 2),
+                             "with_norm_call_us": round(pf_norm_call_us, 2),
                              "hbm_achieved_GBs": round(pf_b / (pf_call_us * 1e-6) / 1e9, 1),
                              "hbm_frac": round(pf_b / (pf_call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                              "tflops": round(pf_f / (pf_call_us * 1e-6) / 1e12, 2),

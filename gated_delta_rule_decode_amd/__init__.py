@@ -35,11 +35,13 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 EXPORTS = ("gdn_version", "gdn_status_string", "gdn_last_hip_error", "gdn_decode_step",
            "gdn_decode_step_norm", "gdn_decode_layer_args_size", "gdn_decode_layer",
            "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_prefill_chunked_seg",
+           "gdn_prefill_norm_workspace_bytes", "gdn_prefill_chunked_norm",
            "gdn_attn_decode_args_size", "gdn_attn_decode_workspace_bytes", "gdn_attn_decode",
            "gdn_rmsnorm_gated")
 
-__all__ = ["decode_step", "decode_step_norm", "decode_layer", "prefill_chunked", "rmsnorm_gated",
-           "prefill_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
+__all__ = ["decode_step", "decode_step_norm", "decode_layer", "prefill_chunked",
+           "prefill_chunked_norm", "rmsnorm_gated", "prefill_workspace_bytes",
+           "prefill_norm_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
            "DecodeLayerArgs", "AttnDecodeArgs", "GDNError", "lib", "LIBRARY", "EXPORTS", "version"]
 
 
@@ -125,6 +127,12 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill_chunked.restype = _i
         L.gdn_prefill_chunked.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
                                           _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]
+        L.gdn_prefill_norm_workspace_bytes.restype = _sz
+        L.gdn_prefill_norm_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+        L.gdn_prefill_chunked_norm.restype = _i
+        L.gdn_prefill_chunked_norm.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp,
+                                               _vp, _vp, _i, _vp, _i, _vp, _i, _vp, _i, _i, _i,
+                                               _i, _i, _i, _f, _f, _vp, _sz, _vp]
         L.gdn_rmsnorm_gated.restype = _i
         L.gdn_rmsnorm_gated.argtypes = [_vp, _i, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp]
         _LIB = L
@@ -387,6 +395,63 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_s
         st = lib().gdn_prefill_chunked_seg(*args, int(segment_chunks), *tail)
         _check("gdn_prefill_chunked_seg", st)
     return o, final_state
+
+
+def prefill_norm_workspace_bytes(N: int, T_total: int, H: int, HV: int, dk: int, dv: int,
+                                 chunk: int = 64) -> int:
+    return int(lib().gdn_prefill_norm_workspace_bytes(N, T_total, H, HV, dk, dv, chunk))
+
+
+def prefill_chunked_norm(q, k, v, g, beta, cu_seqlens, z, w, *, initial_state=None,
+                         final_state=None, y=None, o=None, scale: float = 1.0, eps: float = 1e-6,
+                         chunk: int = 64, workspace=None, out_dtype=None,
+                         return_final_state: bool = True, return_o: bool = False) -> Tuple:
+    """prefill_chunked followed by RMSNormGated of every (token, value head).
+
+    z [T, HV, dv] (fp32 or bf16), w [dv].  Returns (y, final_state), or
+    (y, final_state, o) with ``return_o`` (o is then written as well)."""
+    torch = _torch()
+    f32 = torch.float32
+    T, H, dk = q.shape
+    HV, dv = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(g, "g", f32)
+    _dev(beta, "beta", f32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(z, "z")
+    _dev(w, "w")
+    if k.shape != q.shape or v.shape[0] != T or g.shape != (T, HV) or beta.shape != (T, HV) \
+            or z.shape != (T, HV, dv) or w.shape != (dv,):
+        raise ValueError("inconsistent prefill shapes")
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", f32)
+        if initial_state.shape != (N, HV, dv, dk):
+            raise ValueError("initial_state shape")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((N, HV, dv, dk), dtype=f32, device=q.device)
+    if final_state is not None:
+        _dev(final_state, "final_state", f32)
+    if y is None:
+        y = torch.empty((T, HV, dv), dtype=out_dtype or f32, device=q.device)
+    _dev(y, "y")
+    if return_o and o is None:
+        o = torch.empty((T, HV, dv), dtype=f32, device=q.device)
+    if o is not None:
+        _dev(o, "o")
+    need = prefill_norm_workspace_bytes(N, T, H, HV, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    st = lib().gdn_prefill_chunked_norm(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+        _ptr(initial_state), _ptr(final_state), _ptr(z), _dtype_code(z), _ptr(w), _dtype_code(w),
+        _ptr(y), _dtype_code(y), _ptr(o), _dtype_code(o) if o is not None else GDN_F32, H, HV, dk,
+        dv, chunk, float(scale), float(eps), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check("gdn_prefill_chunked_norm", st)
+    return (y, final_state, o) if (return_o or o is not None) else (y, final_state)
 
 
 def attn_decode_workspace_bytes(N: int, Hq: int, Hkv: int, D: int, Lmax: int) -> int:

@@ -310,12 +310,16 @@ size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, in
 
 namespace {
 
-gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
-                        const float* g, const float* beta, const int32_t* cu_seqlens, int N,
-                        int T_total, const float* initial_state, float* final_state, void* o,
-                        gdn_dtype o_dtype, int H, int HV, int dk, int dv, int chunk, float scale,
-                        int segment_chunks, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+// Validates a prefill call and fills a.  Returns GDN_SUCCESS with *done set
+// when nothing is left to launch (N == 0, or T_total == 0 after the state
+// copy); workspace_need is the size the workspace must have.
+gdn_status prefill_setup(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                         const float* g, const float* beta, const int32_t* cu_seqlens, int N,
+                         int T_total, const float* initial_state, float* final_state, void* o,
+                         gdn_dtype o_dtype, int H, int HV, int dk, int dv, int chunk, float scale,
+                         int segment_chunks, void* workspace, size_t workspace_bytes,
+                         size_t workspace_need, void* stream, gdn::PrefillArgs& a, bool* done) {
+    *done = true;
     if (N < 0 || T_total < 0) return GDN_ERROR_INVALID_VALUE;
     if (segment_chunks != 0 && segment_chunks != -1 && segment_chunks < gdn::kSegMinChunks)
         return GDN_ERROR_INVALID_VALUE;
@@ -333,16 +337,17 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
         clear_pending();
         return from_hip(gdn::launch_state_copy(initial_state, final_state, state_elems, s));
     }
+    if (workspace_need == 0) workspace_need = gdn::prefill_layout(N, T_total, H, HV, dk, dv).total;
     if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return GDN_ERROR_INVALID_VALUE;
     const gdn::PrefillLayout L = gdn::prefill_layout(N, T_total, H, HV, dk, dv);
     if ((size_t)L.max_chunks * HV > (size_t)(1u << 31) / (gdn::kChunk * gdn::kChunk))
         return GDN_ERROR_NOT_SUPPORTED;
-    if (!workspace || workspace_bytes < L.total) return GDN_ERROR_WORKSPACE;
+    if (!workspace || workspace_bytes < workspace_need) return GDN_ERROR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN_ERROR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
-    gdn::PrefillArgs a{};
+    a = gdn::PrefillArgs{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
     a.s0 = initial_state; a.s_final = final_state; a.o = o;
     a.in_bf16 = in_dtype == GDN_BF16; a.o_bf16 = o_dtype == GDN_BF16;
@@ -373,8 +378,31 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype i
     a.ws_Sin = reinterpret_cast<float*>(ws + L.ws_Sin);
     a.ws_W = reinterpret_cast<float*>(ws + L.ws_W);
     a.stream = s;
+    *done = false;
+    return GDN_SUCCESS;
+}
+
+gdn_status prefill_impl(const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                        const float* g, const float* beta, const int32_t* cu_seqlens, int N,
+                        int T_total, const float* initial_state, float* final_state, void* o,
+                        gdn_dtype o_dtype, int H, int HV, int dk, int dv, int chunk, float scale,
+                        int segment_chunks, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    gdn::PrefillArgs a;
+    bool done;
+    const gdn_status st = prefill_setup(q, k, v, in_dtype, g, beta, cu_seqlens, N, T_total,
+                                        initial_state, final_state, o, o_dtype, H, HV, dk, dv,
+                                        chunk, scale, segment_chunks, workspace, workspace_bytes,
+                                        0, stream, a, &done);
+    if (st != GDN_SUCCESS || done) return st;
     clear_pending();
     return from_hip(gdn::launch_prefill(a));
+}
+
+// bytes of the fp32 outputs that gdn_prefill_chunked_norm keeps in its
+// workspace, past the prefill's own part, when the norm is a launch of its own
+size_t norm_o_bytes(int T_total, int HV, int dv) {
+    return align256((size_t)T_total * HV * dv * sizeof(float));
 }
 
 }  // namespace
@@ -402,6 +430,63 @@ gdn_status gdn_prefill_chunked_seg(const void* q, const void* k, const void* v,
     return prefill_impl(q, k, v, in_dtype, g, beta, cu_seqlens, N, T_total, initial_state,
                         final_state, o, o_dtype, H, HV, dk, dv, chunk, scale, segment_chunks,
                         workspace, workspace_bytes, stream);
+}
+
+size_t gdn_prefill_norm_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv,
+                                        int chunk) {
+    const size_t base = gdn_prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk);
+    return base == 0 ? 0 : base + norm_o_bytes(T_total, HV, dv);
+}
+
+gdn_status gdn_prefill_chunked_norm(const void* q, const void* k, const void* v,
+                                    gdn_dtype in_dtype, const float* g, const float* beta,
+                                    const int32_t* cu_seqlens, int N, int T_total,
+                                    const float* initial_state, float* final_state,
+                                    const void* z, gdn_dtype z_dtype, const void* w,
+                                    gdn_dtype w_dtype, void* y, gdn_dtype y_dtype, void* o,
+                                    gdn_dtype o_dtype, int H, int HV, int dk, int dv, int chunk,
+                                    float scale, float eps, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(z_dtype) || !valid_dtype(w_dtype) || !valid_dtype(y_dtype))
+        return GDN_ERROR_NOT_SUPPORTED;
+    if (!(eps >= 0.f)) return GDN_ERROR_INVALID_VALUE;
+    if (N > 0 && T_total > 0) {
+        if (!z || !w || !y || !aligned16(z) || !aligned16(w) || !aligned16(y))
+            return GDN_ERROR_INVALID_VALUE;
+        if (o && o == y) return GDN_ERROR_INVALID_VALUE;
+    }
+    // the prefill writes o when it is given, else the workspace's fp32 outputs
+    // (or, fused, y itself); the check of o is the prefill's own
+    const size_t base = gdn_prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk);
+    const size_t need = base + (base ? norm_o_bytes(T_total, HV, dv) : 0);
+    if (base && N > 0 && !o &&
+        (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+        return GDN_ERROR_WORKSPACE;
+    void* o_fp32 = (base && workspace) ? static_cast<char*>(workspace) + base : nullptr;
+    gdn::PrefillArgs a;
+    bool done;
+    gdn_status st = prefill_setup(q, k, v, in_dtype, g, beta, cu_seqlens, N, T_total,
+                                  initial_state, final_state, o ? o : o_fp32,
+                                  o ? o_dtype : GDN_F32, H, HV, dk, dv, chunk, scale, 0, workspace,
+                                  workspace_bytes, need, stream, a, &done);
+    if (st != GDN_SUCCESS || done) return st;
+    clear_pending();
+    if (!o && gdn::prefill_fuses_norm(a)) {
+        a.o = y;
+        a.o_bf16 = y_dtype == GDN_BF16;
+        a.nz = z;
+        a.nw = w;
+        a.nz_bf16 = z_dtype == GDN_BF16;
+        a.nw_bf16 = w_dtype == GDN_BF16;
+        a.eps = eps;
+        return from_hip(gdn::launch_prefill(a));
+    }
+    st = from_hip(gdn::launch_prefill(a));
+    if (st != GDN_SUCCESS) return st;
+    const long groups = (long)T_total * HV;
+    gdn::NormArgs na{a.o, z, w, y, a.o_bf16, z_dtype == GDN_BF16, w_dtype == GDN_BF16,
+                     y_dtype == GDN_BF16, groups, dv, eps, a.stream};
+    return from_hip(gdn::launch_rmsnorm_gated(na));
 }
 
 gdn_status gdn_rmsnorm_gated(const void* x, gdn_dtype x_dtype, const void* z, gdn_dtype z_dtype,

@@ -90,6 +90,12 @@ struct PrefillArgs {
     float* ws_Phi;       // [seg_bound, HV, dk, dk] transition of a segment
     float* ws_Sin;       // [seg_bound, HV, dv, dk] state entering a segment
     float* ws_W;         // [T, HV, dk] scale Phi_t q_t for tokens of later segments
+    // RMSNormGated fused into the scan (gdn_prefill_chunked_norm): with nz set,
+    // o receives y = o / sqrt(mean(o^2) + eps) * w * silu(z) instead of o
+    const void* nz;      // [T, HV, dv] gate input, or null for no norm
+    const void* nw;      // [dv] weight
+    bool nz_bf16, nw_bf16;
+    float eps;
     hipStream_t stream;
 };
 
@@ -118,6 +124,10 @@ struct PrefillLayout {
     int max_chunks, seg_bound, corr_bound;
 };
 PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv);
+// true when launch_prefill, given nz, writes the normed outputs itself (the
+// per-chain scan without segmentation); otherwise nz must be null and the
+// norm runs as its own launch
+bool prefill_fuses_norm(const PrefillArgs& A);
 
 // One decode step of gated full attention (gdn_attn_decode).
 struct AttnArgs {

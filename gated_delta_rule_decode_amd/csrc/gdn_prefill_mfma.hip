@@ -29,6 +29,7 @@
 // K S^T, Q S^T, X = V - diag(gamma) K S^T, O = scale (diag(gamma) Q S^T + R X)
 // and S' = gamma_n S + Z^T X, with the state in MFMA accumulators.
 #include <algorithm>
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -77,6 +78,13 @@ __device__ __forceinline__ bf8_t zero8() { return __builtin_bit_cast(bf8_t, make
 // so e^{G_t - G_s} is one hardware exp2
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// silu(z) = z / (1 + e^-z) from the hardware exp2 and reciprocal (about 1 ulp
+// each): a few instructions where the library forms take tens, which the
+// per-chain scan, with one wavefront per SIMD, would wait for
+__device__ __forceinline__ float silu_hw(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + exp2f_(-kLog2e * z));
+}
 
 
 __device__ __forceinline__ void seq_bounds_m(const int32_t* cu, int n, int T, int& s, int& e) {
@@ -900,8 +908,15 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
 // ahead.  The state of the wavefront's rows lives in MFMA accumulators
 // (S'^T tiles) and in its LDS area as hi / lo bf16 for the next chunk's (A);
 // X takes the same area while the state is in the accumulators.
-template <typename Tout>
+//
+// With a gate type Tz (bf16_t or float; void for none) the workgroup, which
+// holds all d_v outputs of its head, also applies RMSNormGated to them
+// (Qwen3.5-0.8B chat guide, section "Architektur"): per token,
+// y = o / sqrt(mean(o^2) + eps) * w * silu(z), the sum of squares taken over
+// the four wavefronts' rows through LDS, and y is written in place of o.
+template <typename Tout, typename Tz>
 __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
+    constexpr bool NORM = !std::is_void_v<Tz>;
     constexpr int DK = 128, DV = 128, C = kChunk;
     constexpr int KP = DK + 8;  // padded bf16 row of K, Q and the state
     constexpr int VP = DV + 8;  // padded bf16 row of the V tile
@@ -913,6 +928,8 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
     __shared__ __attribute__((aligned(16))) bf8_t Zf[2][2 * NJB][64];  // Z^T fragments hi, lo
     __shared__ __attribute__((aligned(16))) float Gs[C];
     __shared__ __attribute__((aligned(16))) __bf16 Sp[4][2][32 * KP];  // per wavefront: S hi, lo / X
+    __shared__ __attribute__((aligned(16))) float Wn[NORM ? DV : 1];      // norm weight
+    __shared__ __attribute__((aligned(16))) float Nss[NORM ? C * 4 : 1];  // [token][wavefront] sums of o^2
 
     const int H = A.H, HV = A.HV;
     const int tid = threadIdx.x;
@@ -932,6 +949,11 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
     if (trans && sidx == 0) return;
     const int hk = h / (HV / H);
     Tout* op = static_cast<Tout*>(A.o);
+    if constexpr (NORM) {
+        if (tid < DV)  // read after the first barrier of the chunk loop
+            Wn[tid] = A.nw_bf16 ? bf16_to_f32(static_cast<const bf16_t*>(A.nw)[tid])
+                                : static_cast<const float*>(A.nw)[tid];
+    }
     const float* init = nullptr;  // null: zero state (or the identity for a transition item)
     float* fin;
     size_t ibase = 0, fbase;
@@ -1171,6 +1193,24 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+        // the norm's gate inputs for this lane's outputs (zero past the end),
+        // in flight during (B)
+        typedef std::conditional_t<std::is_same_v<Tz, float>, float4, uint2> zraw_t;
+        zraw_t zr[4][2];
+        if constexpr (NORM) {
+            const __amdgpu_buffer_rsrc_t zrs = in_rsrc(static_cast<const Tz*>(A.nz) + (size_t)t0 * HV * DV,
+                                                       (uint32_t)(L * HV * DV * sizeof(Tz)));
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const int off = (int)((((16 * tb + lr) * HV + h) * DV + 32 * w + 16 * ib + 4 * lg) * sizeof(Tz));
+                    if constexpr (std::is_same_v<Tz, float>)
+                        zr[tb][ib] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(zrs, off, 0, 0));
+                    else
+                        zr[tb][ib] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zrs, off, 0, 0));
+                }
+        }
         // (B) X fragments: k-step kk (tokens 32 kk + 8 lg ..), rows 16 ib + lr
         bf8_t xh[2][2], xl[2][2];
 #pragma unroll
@@ -1237,12 +1277,54 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
             } else {
                 const __amdgpu_buffer_rsrc_t orsrc =
                     out_rsrc(op + (size_t)t0 * HV * DV, (uint32_t)(L * HV * DV * sizeof(Tout)));
+                float inv[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (NORM) {
+                    // sum of o^2 over this wavefront's 32 rows of token 16 tb + lr
+                    // (the four lane groups lg), then over the wavefronts
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        float ss = 0.f;
+#pragma unroll
+                        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float o = A.scale * qsa[tb][ib][r];
+                                ss = __builtin_fmaf(o, o, ss);
+                            }
+                        ss += swz_xor16(ss);
+                        ss += xor32(ss);
+                        if (lg == 0) Nss[(16 * tb + lr) * 4 + w] = ss;
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        const float4 p = *reinterpret_cast<const float4*>(&Nss[(16 * tb + lr) * 4]);
+                        inv[tb] = 1.0f / sqrtf((((p.x + p.y) + p.z) + p.w) * (1.0f / DV) + A.eps);
+                    }
+                }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib) {
-                        const float ov[4] = {A.scale * qsa[tb][ib][0], A.scale * qsa[tb][ib][1],
-                                             A.scale * qsa[tb][ib][2], A.scale * qsa[tb][ib][3]};
+                        float ov[4] = {A.scale * qsa[tb][ib][0], A.scale * qsa[tb][ib][1],
+                                       A.scale * qsa[tb][ib][2], A.scale * qsa[tb][ib][3]};
+                        if constexpr (NORM) {
+                            float zv[4];
+                            if constexpr (std::is_same_v<Tz, float>) {
+                                zv[0] = zr[tb][ib].x; zv[1] = zr[tb][ib].y;
+                                zv[2] = zr[tb][ib].z; zv[3] = zr[tb][ib].w;
+                            } else {
+                                zv[0] = __uint_as_float(zr[tb][ib].x << 16);
+                                zv[1] = __uint_as_float(zr[tb][ib].x & 0xffff0000u);
+                                zv[2] = __uint_as_float(zr[tb][ib].y << 16);
+                                zv[3] = __uint_as_float(zr[tb][ib].y & 0xffff0000u);
+                            }
+                            const float4 wv = *reinterpret_cast<const float4*>(&Wn[32 * w + 16 * ib + 4 * lg]);
+                            const float wr[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                ov[r] = ov[r] * inv[tb] * wr[r] * silu_hw(zv[r]);
+                        }
                         out_store4(orsrc,
                                    (uint32_t)(((16 * tb + trow) * HV + h) * DV + 32 * w + 16 * ib + 4 * lg),
                                    ov, op);
@@ -1679,27 +1761,34 @@ __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
 constexpr size_t kRowsMinChains = 512;
 constexpr size_t kRowsMinTokensPerSeq = 16384;
 
+// At d_k = d_v = 128, one workgroup per chain (scan_rows_kernel: more work
+// per CU and chunk step) when there are many chains, or when long sequences
+// may be segmented (the segments then fill the CUs); otherwise one workgroup
+// per 32 state rows of a chain (scan_mfma_kernel, the shorter chunk step)
+static bool use_rows(const PrefillArgs& A, int dk) {
+    return dk == 128 && A.dv == 128 &&
+           ((size_t)A.N * A.HV >= kRowsMinChains ||
+            (A.seg_req >= 0 && (size_t)A.T >= kRowsMinTokensPerSeq * (size_t)A.N));
+}
+
+// Segmentation is possible only when asked for, or, automatically, when the
+// unsegmented scan leaves CUs idle (fewer than 256 workgroups) and some
+// sequence may be longer than one segment; otherwise the plan is fixed to one
+// segment per sequence and the later passes are not launched.
+static bool may_segment(const PrefillArgs& A, int dk) {
+    const size_t TV = use_rows(A, dk) ? 1 : (size_t)A.dv / 32;
+    return A.seg_req > 0 || (A.seg_req == 0 && (size_t)A.N * A.HV * TV < 256 &&
+                             (A.T + kChunk - 1) / kChunk > kSegMinChunks);
+}
+
 // plan -> prep -> scan (value and transition items) -> combine -> correction.
 // Without segmentation the last two find no work and exit.
 template <int DK, typename Tout>
 static hipError_t launch_mfma_t(const PrefillArgs& A0) {
-    // At d_k = d_v = 128, one workgroup per chain (scan_rows_kernel: more work
-    // per CU and chunk step) when there are many chains, or when long
-    // sequences may be segmented (the segments then fill the CUs); otherwise
-    // one workgroup per 32 state rows of a chain (scan_mfma_kernel, the
-    // shorter chunk step)
-    const bool rows = DK == 128 && A0.dv == 128 &&
-                      ((size_t)A0.N * A0.HV >= kRowsMinChains ||
-                       (A0.seg_req >= 0 && (size_t)A0.T >= kRowsMinTokensPerSeq * (size_t)A0.N));
+    const bool rows = use_rows(A0, DK);
     const int TV = rows ? 1 : A0.dv / 32, TK = rows ? 1 : DK / 32;
-    // Segmentation is possible only when asked for, or, automatically, when
-    // the unsegmented scan leaves CUs idle (fewer than 256 workgroups) and
-    // some sequence may be longer than one segment; otherwise the plan is
-    // fixed to one segment per sequence and the later passes are not launched.
     PrefillArgs A = A0;
-    const bool may = A.seg_req > 0 ||
-                     (A.seg_req == 0 && (size_t)A.N * A.HV * TV < 256 &&
-                      (A.T + kChunk - 1) / kChunk > kSegMinChunks);
+    const bool may = may_segment(A0, DK);
     if (!may) A.seg_req = -1;
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK,
                        rows ? 1 : 0);
@@ -1711,8 +1800,15 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
     // the transition items; the kernel splits the grid at seg_bound
     if (rows) {
         const size_t blocks = may ? (size_t)2 * A.seg_bound * A.HV : (size_t)A.N * A.HV;
-        hipLaunchKernelGGL((scan_rows_kernel<Tout>), dim3((unsigned)blocks), dim3(256), 0,
-                           A.stream, A);
+        if (A.nz && A.nz_bf16)
+            hipLaunchKernelGGL((scan_rows_kernel<Tout, bf16_t>), dim3((unsigned)blocks), dim3(256), 0,
+                               A.stream, A);
+        else if (A.nz)
+            hipLaunchKernelGGL((scan_rows_kernel<Tout, float>), dim3((unsigned)blocks), dim3(256), 0,
+                               A.stream, A);
+        else
+            hipLaunchKernelGGL((scan_rows_kernel<Tout, void>), dim3((unsigned)blocks), dim3(256), 0,
+                               A.stream, A);
     } else {
         const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * A.HV + 7) / 8) * 8;
         const size_t blocks = may ? chains8 * (TV + TK) : chains8 * TV;
@@ -1730,6 +1826,10 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
 
 bool prefill_mfma_eligible(const PrefillArgs& A) {
     return A.in_bf16 && (A.dk == 64 || A.dk == 128) && (A.dv % 32 == 0);
+}
+
+bool prefill_fuses_norm(const PrefillArgs& A) {
+    return prefill_mfma_eligible(A) && use_rows(A, A.dk) && !may_segment(A, A.dk);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& A) {

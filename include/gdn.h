@@ -246,6 +246,43 @@ gdn_status gdn_prefill_chunked_seg(const void* q, const void* k, const void* v,
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_prefill_chunked_norm -- gdn_prefill_chunked followed by RMSNormGated of
+ * each (token, value head)'s outputs: the prompt pass of the token mixer up to
+ * the norm that closes the DeltaNet layer (Qwen3.5-0.8B chat guide, section
+ * "Architektur").  Per (token, value head) group of dv outputs o:
+ *
+ *     y = o / sqrt(mean(o^2) + eps) * w * silu(z)
+ *
+ *   q .. final_state   as gdn_prefill_chunked
+ *   z        [T_total, HV, dv]  z_dtype   gate input of the norm
+ *   w        [dv]               w_dtype   norm weight shared by heads
+ *   y        [T_total, HV, dv]  y_dtype   the normed outputs
+ *   o        [T_total, HV, dv]  o_dtype   the raw outputs too, or NULL
+ *   eps >= 0; chunk must be 64
+ *   workspace device memory of workspace_bytes >=
+ *             gdn_prefill_norm_workspace_bytes(...) (256-byte aligned)
+ * Where the scan runs one workgroup per head (d_k = d_v = 128 with at least
+ * 512 (sequence, value head) chains, no segmentation) and o is NULL, the norm
+ * is applied inside the scan and o never reaches memory; otherwise the raw
+ * outputs go to o (or, in fp32, to the workspace) and a second launch applies
+ * the norm.  y may not be o.  Errors as gdn_prefill_chunked, plus
+ * GDN_ERROR_INVALID_VALUE for a missing or misaligned z, w or y, y == o or a
+ * negative eps.
+ */
+size_t gdn_prefill_norm_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv,
+                                        int chunk);
+
+gdn_status gdn_prefill_chunked_norm(const void* q, const void* k, const void* v,
+                                    gdn_dtype in_dtype, const float* g, const float* beta,
+                                    const int32_t* cu_seqlens, int N, int T_total,
+                                    const float* initial_state, float* final_state,
+                                    const void* z, gdn_dtype z_dtype, const void* w,
+                                    gdn_dtype w_dtype, void* y, gdn_dtype y_dtype, void* o,
+                                    gdn_dtype o_dtype, int H, int HV, int dk, int dv, int chunk,
+                                    float scale, float eps, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * gdn_attn_decode -- one decode step of gated full attention, the hybrid
  * decoder's other token mixer (standard scaled dot-product attention: chat
  * guide (de), section "Architektur"; head_dim 256, 16 query heads over 2

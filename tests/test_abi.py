@@ -128,6 +128,43 @@ def test_prefill_workspace_bytes(L):
         assert f(N, T, H, HV, dk, 128) % 256 == 0
 
 
+def _prefill_norm(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=1, g=FAKE, beta=FAKE, cu=FAKE, N=2, T=100, s0=None,
+             sf=FAKE, z=FAKE, zd=1, w=FAKE, wd=0, y=FAKE, yd=0, o=None, o_dt=0, H=2, HV=4,
+             dk=128, dv=128, chunk=64, scale=1.0, eps=1e-6, ws=None, wsb=0)
+    a.update(kw)
+    return L.gdn_prefill_chunked_norm(
+        a["q"], a["k"], a["v"], a["in_dt"], a["g"], a["beta"], a["cu"], a["N"], a["T"], a["s0"],
+        a["sf"], a["z"], a["zd"], a["w"], a["wd"], a["y"], a["yd"], a["o"], a["o_dt"], a["H"],
+        a["HV"], a["dk"], a["dv"], a["chunk"], a["scale"], a["eps"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_norm_validation(L):
+    need = gdn.prefill_norm_workspace_bytes(2, 100, 2, 4, 128, 128)
+    # the prefill's workspace plus fp32 outputs for the norm's own launch
+    assert need == gdn.prefill_workspace_bytes(2, 100, 2, 4, 128, 128) + (100 * 4 * 128 * 4 + 255) // 256 * 256
+    assert gdn.prefill_norm_workspace_bytes(0, 100, 2, 4, 128, 128) == 0
+    assert gdn.prefill_norm_workspace_bytes(2, 100, 2, 4, 96, 128) == 0
+    assert _prefill_norm(L, N=0) == 0
+    assert _prefill_norm(L, N=-1) == 1
+    assert _prefill_norm(L, eps=-1.0) == 1
+    assert _prefill_norm(L, zd=3) == 2
+    assert _prefill_norm(L, yd=3) == 2
+    for arg in ("z", "w", "y"):
+        assert _prefill_norm(L, **{arg: None}) == 1
+        assert _prefill_norm(L, **{arg: MISALIGNED}) == 1
+    assert _prefill_norm(L, o=FAKE + 256, y=FAKE + 256, ws=FAKE, wsb=need) == 1  # y == o
+    assert _prefill_norm(L, chunk=32) == 2
+    assert _prefill_norm(L, dk=48) == 2
+    assert _prefill_norm(L, HV=5) == 1
+    assert _prefill_norm(L) == 3                     # no workspace
+    assert _prefill_norm(L, ws=FAKE, wsb=need - 1) == 3
+    assert _prefill_norm(L, ws=FAKE + 16, wsb=need) == 3
+    # the documented size holds whether or not o is given
+    ws_prefill = gdn.prefill_workspace_bytes(2, 100, 2, 4, 128, 128)
+    assert _prefill_norm(L, o=FAKE + 256, ws=FAKE, wsb=ws_prefill) == 3
+
+
 def _norm(L, **kw):
     a = dict(x=FAKE, xd=0, z=FAKE, zd=1, w=FAKE, wd=0, y=FAKE, yd=0, rows=4, HV=2, dv=128,
              eps=1e-6)
