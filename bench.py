@@ -59,17 +59,17 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # profiles/decode_traffic_qwen35_08b.md together with the sha256 of the kernel
 # source (and the local headers it includes) it was measured on.  Reported only
 # while those sources are unchanged.
-DECODE_TRAFFIC = {"kernel_source_sha256": "c991137cdce08f1e395c42ab8b486626df2dcc866379eaa7eb5e9f9f38c6b0ef",
-                  "bytes_per_launch": 68046813}
+DECODE_TRAFFIC = {"kernel_source_sha256": "ff5870fb86b5843f8041a9ed5fd045a678f2170baacbcb8ac0e92ab8c18504a9",
+                  "bytes_per_launch": 68046771}
 
 
 # The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
 # profiles/serving_decode_traffic.md) and the attention decode step
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
-SERVE_TRAFFIC = {"kernel_source_sha256": "c991137cdce08f1e395c42ab8b486626df2dcc866379eaa7eb5e9f9f38c6b0ef",
-                 "bytes_per_launch": 543602051}
-ATTN_TRAFFIC = {"kernel_source_sha256": "f0e5c6a0864c66fb225a6b0a5128a06596eff634201784893bddddcdd8b9267c",
-                "bytes_per_launch": 2185161095}
+SERVE_TRAFFIC = {"kernel_source_sha256": "ff5870fb86b5843f8041a9ed5fd045a678f2170baacbcb8ac0e92ab8c18504a9",
+                 "bytes_per_launch": 543601972}
+ATTN_TRAFFIC = {"kernel_source_sha256": "9b70f194d33e83c72c177f4bb393b13a06bff68cce1d04c3e64b98773ad67b13",
+                "bytes_per_launch": 2185173300}
 
 
 def kernel_sources_sha256(source):
