@@ -25,6 +25,9 @@ of Qwen3.6-35B-A3B (16 query heads over 2 key/value heads, head_dim 256, a
 quarter rotated, theta 1e7; 10 of its 40 layers): 128 rows at position 8192
 of 8320-row bf16 caches per layer.
 
+``--workload norm`` times RMSNormGated on its own (gdn_rmsnorm_gated) at the
+job's prefill output shape (32 x 512 tokens, 16 value heads, d_v = 128).
+
 ``--workload serve`` times the serving form of the decode step
 (gdn_decode_layer) on the Qwen3.6-35B-A3B DeltaNet shape: 128 rows drawn from
 a pool of 256 state slots per layer, raw bf16 gates activated in the kernel,
@@ -70,6 +73,10 @@ SERVE_TRAFFIC = {"kernel_source_sha256": "ff5870fb86b5843f8041a9ed5fd045a678f217
                  "bytes_per_launch": 543601972}
 ATTN_TRAFFIC = {"kernel_source_sha256": "9b70f194d33e83c72c177f4bb393b13a06bff68cce1d04c3e64b98773ad67b13",
                 "bytes_per_launch": 2185173300}
+# RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
+# profiles/rmsnorm_gated_traffic.md)
+NORM_TRAFFIC = {"kernel_source_sha256": "9241f48c4927a381f3dbcd29f95477690ab668304fc708a2988ec09b54079396",
+                "bytes_per_launch": 335597881}
 
 
 def kernel_sources_sha256(source):
@@ -535,6 +542,66 @@ def run_attn(args):
     }
 
 
+def norm_bytes(rows, HV, dv, x_bytes=4, z_bytes=2, y_bytes=4, w_bytes=4):
+    """HBM bytes of one RMSNormGated launch: x and z read, y written, the
+    weight read once."""
+    return rows * HV * dv * (x_bytes + z_bytes + y_bytes) + dv * w_bytes
+
+
+def run_norm(args):
+    """RMSNormGated on its own (gdn_rmsnorm_gated) at the 0.8B job's prefill
+    output shape: 32 x 512 tokens, 16 value heads, d_v = 128, fp32 x, bf16 z,
+    fp32 y; 18 layers, each with its own tensors, in a HIP graph."""
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+
+    rows, HV, dv, L = 32 * 512, 16, 128, args.layers
+    dev = torch.device("cuda", 0)
+    log(f"norm: rows={rows} HV={HV} dv={dv} layers={L}")
+    gen = torch.Generator(device=dev).manual_seed(11)
+    layers = [dict(x=torch.randn(rows, HV, dv, device=dev, generator=gen),
+                   z=torch.randn(rows, HV, dv, device=dev, generator=gen).to(torch.bfloat16),
+                   y=torch.empty(rows, HV, dv, device=dev)) for _ in range(L)]
+    w = torch.ones(dv, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for Ly in layers:
+            gdn.rmsnorm_gated(Ly["x"], Ly["z"], w, y=Ly["y"])
+
+    g_n, s = graph_capture(step)
+    for _ in range(args.warmup):
+        g_n.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(args.steps):
+            g_n.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+    launch_us = ms * 1e3 / L
+    bytes_launch = norm_bytes(rows, HV, dv)
+    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
+    return {
+        "metric": METRIC, "value": round(rows * L / (ms * 1e-3), 1),
+        "unit": "tokens/s per DeltaNet layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwen3.5-0.8b-rmsnormgated", "rows": rows, "v_heads": HV,
+                   "d_v": dv, "layers": L, "x": "f32", "z": "bf16", "y": "f32"},
+        "roofline": {"kernel": "rmsnorm_gated_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(NORM_TRAFFIC, "gdn_rmsnorm.hip"),
+                     "avg_launch_us": round(launch_us, 3),
+                     "algorithmic_bytes_per_launch": bytes_launch},
+    }
+
+
 def run_serve(args):
     import torch
     import gated_delta_rule_decode_amd as gdn
@@ -647,7 +714,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill2", "prefill3", "prefill4", "prefill5", "copy",
-                             "serve", "attn"])
+                             "serve", "attn", "norm"])
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--decode-steps", type=int, default=0)
     ap.add_argument("--cpu-layers", type=int, default=12)
@@ -670,6 +737,8 @@ def main():
         out = run_serve(args)
     elif args.workload == "attn":
         out = run_attn(args)
+    elif args.workload == "norm":
+        out = run_norm(args)
     else:
         out = run_prefill(args, int(args.workload[-1]))
     print(json.dumps(out), flush=True)

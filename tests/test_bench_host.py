@@ -68,3 +68,9 @@ def test_kernel_hash_covers_included_headers(tmp_path, monkeypatch):
     first = bench.kernel_sources_sha256("k.hip")
     (csrc / "h.h").write_text("// header two\n")
     assert bench.kernel_sources_sha256("k.hip") != first
+
+
+def test_norm_bytes_job_prefill_shape():
+    # fp32 x read, bf16 z read, fp32 y written per element; the weight once
+    rows, HV, dv = 32 * 512, 16, 128
+    assert bench.norm_bytes(rows, HV, dv) == rows * HV * dv * 10 + dv * 4 == 335_544_832
