@@ -354,8 +354,10 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_s
 
     q, k [T, H, dk], v [T, HV, dv]; g, beta [T, HV] fp32; cu_seqlens [N+1]
     int32 on the device; initial_state [N, HV, dv, dk] fp32 or None (zeros).
-    ``segment_chunks``: 0 lets the library choose the segment-parallel scan,
-    -1 turns it off, >= 32 forces segments of that many chunks.
+    ``segment_chunks``: 0 lets the library choose the segment-parallel scan
+    (when the chains leave CUs idle), -2 also lets it segment one long prompt
+    among short ones, -1 turns it off, >= 32 forces segments of that many
+    chunks.
     Returns (o [T, HV, dv], final_state [N, HV, dv, dk] or None)."""
     torch = _torch()
     f32 = torch.float32

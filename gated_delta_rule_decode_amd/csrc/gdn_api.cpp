@@ -321,7 +321,8 @@ gdn_status prefill_setup(const void* q, const void* k, const void* v, gdn_dtype 
                          size_t workspace_need, void* stream, gdn::PrefillArgs& a, bool* done) {
     *done = true;
     if (N < 0 || T_total < 0) return GDN_ERROR_INVALID_VALUE;
-    if (segment_chunks != 0 && segment_chunks != -1 && segment_chunks < gdn::kSegMinChunks)
+    if (segment_chunks != 0 && segment_chunks != -1 && segment_chunks != gdn::kSegAutoSkewed &&
+        segment_chunks < gdn::kSegMinChunks)
         return GDN_ERROR_INVALID_VALUE;
     gdn_status st = heads_status(H, HV, dk, dv);
     if (st != GDN_SUCCESS) return st;
@@ -471,16 +472,16 @@ gdn_status gdn_prefill_chunked_norm(const void* q, const void* k, const void* v,
                                   workspace_bytes, need, stream, a, &done);
     if (st != GDN_SUCCESS || done) return st;
     clear_pending();
-    if (!o && gdn::prefill_fuses_norm(a)) {
-        a.o = y;
-        a.o_bf16 = y_dtype == GDN_BF16;
-        a.nz = z;
-        a.nw = w;
-        a.nz_bf16 = z_dtype == GDN_BF16;
-        a.nw_bf16 = w_dtype == GDN_BF16;
-        a.eps = eps;
-        return from_hip(gdn::launch_prefill(a));
-    }
+    gdn::PrefillArgs f = a;  // the fused form: y in place of o
+    f.o = y;
+    f.o_bf16 = y_dtype == GDN_BF16;
+    f.nz = z;
+    f.nw = w;
+    f.nz_bf16 = z_dtype == GDN_BF16;
+    f.nw_bf16 = w_dtype == GDN_BF16;
+    f.eps = eps;
+    f.ws_o = static_cast<float*>(o_fp32);  // raw outputs of later segments
+    if (!o && gdn::prefill_fuses_norm(f)) return from_hip(gdn::launch_prefill(f));
     st = from_hip(gdn::launch_prefill(a));
     if (st != GDN_SUCCESS) return st;
     const long groups = (long)T_total * HV;

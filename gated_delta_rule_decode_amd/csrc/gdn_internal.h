@@ -73,7 +73,8 @@ struct PrefillArgs {
     int max_chunks;
     // segment-parallel scan (MFMA path).  A sequence is cut into segments of
     // whole chunks; the plan is made on the device from cu_seqlens.
-    int seg_req;         // 0: automatic; -1: never; >= kSegMinChunks: this segment length
+    int seg_req;         // 0: automatic; kSegAutoSkewed: automatic for skewed lengths;
+                         // -1: never; >= kSegMinChunks: this segment length
     int seg_bound;       // capacity of the segment tables
     int corr_bound;      // capacity of the correction item table
     int32_t* plan;       // [kPlanInts]: nseg, ncorr, segment length (0: none), nmulti
@@ -96,10 +97,13 @@ struct PrefillArgs {
     const void* nw;      // [dv] weight
     bool nz_bf16, nw_bf16;
     float eps;
+    float* ws_o;         // [T, HV, dv] fp32: with the norm and segments, the raw
+                         // outputs of later segments until the correction pass
     hipStream_t stream;
 };
 
 constexpr int kSegMinChunks = 32;  // shortest segment of the segment-parallel scan
+constexpr int kSegAutoSkewed = -2; // segment_chunks: automatic, also when the chains fill the CUs
 constexpr int kCorrChunks = 4;     // chunks per item of the correction pass
 constexpr int kPlanInts = 8;
 
@@ -124,9 +128,9 @@ struct PrefillLayout {
     int max_chunks, seg_bound, corr_bound;
 };
 PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv);
-// true when launch_prefill, given nz, writes the normed outputs itself (the
-// per-chain scan without segmentation); otherwise nz must be null and the
-// norm runs as its own launch
+// true when launch_prefill, given nz (and ws_o), writes the normed outputs
+// itself (the per-chain scan, and with segments the correction pass);
+// otherwise nz must be null and the norm runs as its own launch
 bool prefill_fuses_norm(const PrefillArgs& A);
 
 // One decode step of gated full attention (gdn_attn_decode).

@@ -513,7 +513,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
 // zero, which masks K, Q, V and X without selects, and output rows past the
 // end are dropped by the store's resource.
 template <int DK, typename Tout>
-__global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
+__device__ __forceinline__ void scan_mfma_item(const PrefillArgs& A, const int b) {
     constexpr int C = kChunk;
     constexpr int BV = 32;
     constexpr int KP = DK + 8;   // padded row of the state tile (bf16)
@@ -545,7 +545,6 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     // XCD-aware mapping: workgroup b runs on XCD b % 8; all tiles of a chain
     // get the same b % 8 and neighbouring dispatch slots.
     const int TV = dv / BV;
-    const int b = blockIdx.x;
     const int nb1 = ((A.seg_bound * HV + 7) / 8) * 8 * TV;
     const bool trans = b >= nb1;
     const int bb = trans ? b - nb1 : b;
@@ -892,6 +891,15 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
     if (fin) store_state(fin);
 }
 
+// Persistent over work items: workgroup blockIdx.x takes items blockIdx.x,
+// blockIdx.x + gridDim.x, ...  (the grid is a multiple of 8, so an item keeps
+// its XCD).  The host sizes the grid to the work it can see: the unsegmented
+// items when they already fill the CUs, otherwise every possible item.
+template <int DK, typename Tout>
+__global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A, int items) {
+    for (int b = blockIdx.x; b < items; b += gridDim.x) scan_mfma_item<DK, Tout>(A, b);
+}
+
 // ---------------------------------------------------------------------------
 // scan by rows: one workgroup per chain, a wavefront per 32 state rows
 // ---------------------------------------------------------------------------
@@ -914,8 +922,11 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A) {
 // (Qwen3.5-0.8B chat guide, section "Architektur"): per token,
 // y = o / sqrt(mean(o^2) + eps) * w * silu(z), the sum of squares taken over
 // the four wavefronts' rows through LDS, and y is written in place of o.
+// That holds for a sequence's first segment, whose outputs are final; a later
+// segment writes its raw fp32 outputs to ws_o, and the correction pass adds
+// the entering state's part and applies the norm.
 template <typename Tout, typename Tz>
-__global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
+__device__ __forceinline__ void scan_rows_item(const PrefillArgs& A, const int b) {
     constexpr bool NORM = !std::is_void_v<Tz>;
     constexpr int DK = 128, DV = 128, C = kChunk;
     constexpr int KP = DK + 8;  // padded bf16 row of K, Q and the state
@@ -937,7 +948,6 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
     __builtin_assume(w >= 0 && w < 4);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
     // value items (segment, head) first, then the transition items of later segments
-    const int b = blockIdx.x;
     const int nb1 = A.seg_bound * HV;
     const bool trans = b >= nb1;
     const int chain = trans ? b - nb1 : b;
@@ -1275,10 +1285,15 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
                                    ov, wp);
                     }
             } else {
+                // with the norm, a later segment's raw outputs go to ws_o for the
+                // correction pass (fp32 outputs only: the host fuses the norm
+                // into segmented runs only then)
+                const bool normed = NORM && sidx == 0;
+                Tout* const dst = (NORM && !normed) ? reinterpret_cast<Tout*>(A.ws_o) : op;
                 const __amdgpu_buffer_rsrc_t orsrc =
-                    out_rsrc(op + (size_t)t0 * HV * DV, (uint32_t)(L * HV * DV * sizeof(Tout)));
+                    out_rsrc(dst + (size_t)t0 * HV * DV, (uint32_t)(L * HV * DV * sizeof(Tout)));
                 float inv[4] = {1.f, 1.f, 1.f, 1.f};
-                if constexpr (NORM) {
+                if (normed) {
                     // sum of o^2 over this wavefront's 32 rows of token 16 tb + lr
                     // (the four lane groups lg), then over the wavefronts
 #pragma unroll
@@ -1308,7 +1323,7 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
                     for (int ib = 0; ib < 2; ++ib) {
                         float ov[4] = {A.scale * qsa[tb][ib][0], A.scale * qsa[tb][ib][1],
                                        A.scale * qsa[tb][ib][2], A.scale * qsa[tb][ib][3]};
-                        if constexpr (NORM) {
+                        if (normed) {
                             float zv[4];
                             if constexpr (std::is_same_v<Tz, float>) {
                                 zv[0] = zr[tb][ib].x; zv[1] = zr[tb][ib].y;
@@ -1327,7 +1342,7 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
                         }
                         out_store4(orsrc,
                                    (uint32_t)(((16 * tb + trow) * HV + h) * DV + 32 * w + 16 * ib + 4 * lg),
-                                   ov, op);
+                                   ov, dst);
                     }
             }
         }
@@ -1338,6 +1353,14 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
         state_to_lds();
     }
     store_state();
+}
+
+// One item per workgroup (a loop over items, as in scan_mfma_kernel, costs
+// this kernel registers it does not have: values hoisted out of the loop
+// spill at 512 VGPRs).
+template <typename Tout, typename Tz>
+__global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
+    scan_rows_item<Tout, Tz>(A, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1386,7 +1409,9 @@ __device__ int block_exclusive_scan(int n, F count, G emit, int* buf) {
 // about 8 (dk + dv) more bytes per token and head of every later segment (w
 // written and read, o read and written again) at about 5 TB/s, plus about
 // 3 us per segment of the combine pass.  A launch that already gives every
-// CU a chain is not segmented: segments add work and no idle CU takes it.
+// CU a workgroup is segmented only when its longest chain takes more than
+// twice as long as the launch's throughput allows (one long prompt among
+// short ones): then the segments of that chain run beside the other work.
 constexpr int kSegCand[7] = {0, 1024, 512, 256, 128, 64, 32};
 constexpr int kNCand = 7;
 
@@ -1431,7 +1456,7 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A,
         return max(0, min(o + c, A.max_chunks) - min(o, A.max_chunks));
     };
 
-    if (A.seg_req != 0) {
+    if (A.seg_req != 0 && A.seg_req != kSegAutoSkewed) {
         if (threadIdx.x == 0) s_len = A.seg_req < 0 ? 0 : A.seg_req;
     } else {
         if (threadIdx.x < 3 * kNCand) (&acc[0][0])[threadIdx.x] = 0.f;
@@ -1481,12 +1506,16 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A,
             const float dk = (float)A.dk, dv = (float)A.dv;
             float best = 0.f;
             int bestL = 0;
-            for (int k = 0; k < (acc[0][0] < 256.f ? kNCand : 1); ++k) {
+            const float thr = rows ? 46.f : 110.f;
+            auto step_of = [&](float items) {
+                return rows ? 5.6f : (items <= 64.f ? 2.2f : (items <= 256.f ? 2.6f : 4.5f));
+            };
+            const bool skewed = (float)cm * step_of(acc[0][0]) > 2.f * acc[1][0] / thr;
+            for (int k = 0; k < (acc[0][0] < 256.f || skewed ? kNCand : 1); ++k) {
                 const int L = kSegCand[k] ? kSegCand[k] : (1 << 30);
                 const bool seg = cm > L;
-                const float step = rows ? 5.6f
-                                        : (acc[0][k] <= 64.f ? 2.2f : (acc[0][k] <= 256.f ? 2.6f : 4.5f));
-                float cost = fmaxf(acc[1][k] / (rows ? 46.f : 110.f), (float)min(cm, L) * step);
+                const float step = step_of(acc[0][k]);
+                float cost = fmaxf(acc[1][k] / thr, (float)min(cm, L) * step);
                 if (seg)
                     cost += acc[2][k] * HV * 8.f * (dk + dv) / 5.0e6f + 3.f * ((cm + L - 1) / L) + 5.f;
                 if (k == 0 || cost < best) {
@@ -1685,8 +1714,13 @@ __device__ __forceinline__ void load4_any(__amdgpu_buffer_rsrc_t r, uint32_t off
 // is (group of kCorrChunks chunks of one segment, value head); S_in of the
 // item is staged in LDS once, wavefront w takes tokens 16 w .. 16 w + 15 of
 // each chunk.  Persistent over items.
-template <int DK, typename Tout>
+// With a gate type Tz (d_v = 128; void for none) the raw outputs come from
+// ws_o and leave as RMSNormGated's y: a wavefront holds every output of its
+// 16 tokens (the 4 lane groups lg times the 8 blocks nb), so the sum of
+// squares is a sum over lg and needs no LDS.
+template <int DK, typename Tout, typename Tz>
 __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
+    constexpr bool NORM = !std::is_void_v<Tz>;
     constexpr int C = kChunk;
     constexpr int KP = DK + 8;
     constexpr int NKK = DK / 32;
@@ -1736,23 +1770,70 @@ __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
                 split8(x, wh[kk], wl[kk]);
             }
             const __amdgpu_buffer_rsrc_t orr = out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
-            for (int nb = 0; nb < dv / 16; ++nb) {
-                f4_t d = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (NORM) {
+                constexpr int NB = 128 / 16;  // d_v = 128
+                float* rp = A.ws_o + (size_t)t0 * HV * 128;
+                const __amdgpu_buffer_rsrc_t rr = out_rsrc(rp, (uint32_t)(L * HV * 128 * 4));
+                const __amdgpu_buffer_rsrc_t zrs = in_rsrc(static_cast<const Tz*>(A.nz) + (size_t)t0 * HV * 128,
+                                                           (uint32_t)(L * HV * 128 * sizeof(Tz)));
+                float ov[NB][4];
+                float ss = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const bf8_t ah = lds8(&Sh[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
-                    const bf8_t al = lds8(&Sl[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
-                    d = mfma(ah, wh[kk], d);
-                    d = mfma(al, wh[kk], d);
-                    d = mfma(ah, wl[kk], d);
+                for (int nb = 0; nb < NB; ++nb) {
+                    f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        const bf8_t ah = lds8(&Sh[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
+                        const bf8_t al = lds8(&Sl[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
+                        d = mfma(ah, wh[kk], d);
+                        d = mfma(al, wh[kk], d);
+                        d = mfma(ah, wl[kk], d);
+                    }
+                    const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * 128 + 16 * nb + 4 * lg;
+                    load4_any(rr, off, ov[nb], rp);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ov[nb][r] += d[r];
+                        ss = __builtin_fmaf(ov[nb][r], ov[nb][r], ss);
+                    }
                 }
-                // d[r] = (S_in W^T)[i = 16 nb + 4 lg + r][t = 16 w + lr]
-                const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * dv + 16 * nb + 4 * lg;
-                float ov[4];
-                load4_any(orr, off, ov, op);
+                ss += swz_xor16(ss);
+                ss += xor32(ss);
+                const float inv = 1.0f / sqrtf(ss * (1.0f / 128) + A.eps);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ov[r] += d[r];
-                out_store4(orr, off, ov, op);
+                for (int nb = 0; nb < NB; ++nb) {
+                    const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * 128 + 16 * nb + 4 * lg;
+                    float zv[4];
+                    load4_any(zrs, off, zv, static_cast<Tz*>(nullptr));
+                    float y[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * nb + 4 * lg + r;
+                        const float wi = A.nw_bf16 ? bf16_to_f32(static_cast<const bf16_t*>(A.nw)[i])
+                                                   : static_cast<const float*>(A.nw)[i];
+                        y[r] = ov[nb][r] * inv * wi * silu_hw(zv[r]);
+                    }
+                    out_store4(orr, off, y, op);
+                }
+            } else {
+                for (int nb = 0; nb < dv / 16; ++nb) {
+                    f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        const bf8_t ah = lds8(&Sh[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
+                        const bf8_t al = lds8(&Sl[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
+                        d = mfma(ah, wh[kk], d);
+                        d = mfma(al, wh[kk], d);
+                        d = mfma(ah, wl[kk], d);
+                    }
+                    // d[r] = (S_in W^T)[i = 16 nb + 4 lg + r][t = 16 w + lr]
+                    const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * dv + 16 * nb + 4 * lg;
+                    float ov[4];
+                    load4_any(orr, off, ov, op);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ov[r] += d[r];
+                    out_store4(orr, off, ov, op);
+                }
             }
         }
     }
@@ -1763,22 +1844,29 @@ constexpr size_t kRowsMinTokensPerSeq = 16384;
 
 // At d_k = d_v = 128, one workgroup per chain (scan_rows_kernel: more work
 // per CU and chunk step) when there are many chains, or when long sequences
-// may be segmented (the segments then fill the CUs); otherwise one workgroup
-// per 32 state rows of a chain (scan_mfma_kernel, the shorter chunk step)
+// on fewer chains than CUs may be segmented (the segments then fill the CUs);
+// otherwise one workgroup per 32 state rows of a chain (scan_mfma_kernel, the
+// shorter chunk step)
 static bool use_rows(const PrefillArgs& A, int dk) {
     return dk == 128 && A.dv == 128 &&
            ((size_t)A.N * A.HV >= kRowsMinChains ||
-            (A.seg_req >= 0 && (size_t)A.T >= kRowsMinTokensPerSeq * (size_t)A.N));
+            (A.seg_req != -1 && (size_t)A.N * A.HV < 256 &&
+             (size_t)A.T >= kRowsMinTokensPerSeq * (size_t)A.N));
 }
 
-// Segmentation is possible only when asked for, or, automatically, when the
-// unsegmented scan leaves CUs idle (fewer than 256 workgroups) and some
-// sequence may be longer than one segment; otherwise the plan is fixed to one
-// segment per sequence and the later passes are not launched.
+// Segmentation is possible when asked for; automatically (seg_req 0) when
+// the unsegmented scan leaves CUs idle (fewer than 256 workgroups) and some
+// sequence may be longer than one segment; and with kSegAutoSkewed whenever
+// some sequence may be longer than one segment (one long prompt among short
+// ones, whose chains already fill the CUs: the planner decides from the
+// lengths).  Otherwise the plan is fixed to one segment per sequence and the
+// later passes are not launched: a possible plan costs their two launches
+// even when it turns out to be unsegmented.
 static bool may_segment(const PrefillArgs& A, int dk) {
     const size_t TV = use_rows(A, dk) ? 1 : (size_t)A.dv / 32;
-    return A.seg_req > 0 || (A.seg_req == 0 && (size_t)A.N * A.HV * TV < 256 &&
-                             (A.T + kChunk - 1) / kChunk > kSegMinChunks);
+    const bool longer = (A.T + kChunk - 1) / kChunk > kSegMinChunks;
+    return A.seg_req > 0 || (A.seg_req == kSegAutoSkewed && longer) ||
+           (A.seg_req == 0 && longer && (size_t)A.N * A.HV * TV < 256);
 }
 
 // plan -> prep -> scan (value and transition items) -> combine -> correction.
@@ -1798,28 +1886,41 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
     if (err != hipSuccess) return err;
     // value items of up to seg_bound segments (N without segmentation), then
     // the transition items; the kernel splits the grid at seg_bound
+    // the grid of the per-tile scan: every possible item when the
+    // unsegmented items leave CUs idle, otherwise just the unsegmented items
+    // (any segments' items are then taken by the same workgroups in turn, and
+    // when there are none no workgroup is launched only to exit)
     if (rows) {
-        const size_t blocks = may ? (size_t)2 * A.seg_bound * A.HV : (size_t)A.N * A.HV;
+        const size_t items = may ? (size_t)2 * A.seg_bound * A.HV : (size_t)A.N * A.HV;
+        const dim3 grid((unsigned)items);
         if (A.nz && A.nz_bf16)
-            hipLaunchKernelGGL((scan_rows_kernel<Tout, bf16_t>), dim3((unsigned)blocks), dim3(256), 0,
-                               A.stream, A);
+            hipLaunchKernelGGL((scan_rows_kernel<Tout, bf16_t>), grid, dim3(256), 0, A.stream, A);
         else if (A.nz)
-            hipLaunchKernelGGL((scan_rows_kernel<Tout, float>), dim3((unsigned)blocks), dim3(256), 0,
-                               A.stream, A);
+            hipLaunchKernelGGL((scan_rows_kernel<Tout, float>), grid, dim3(256), 0, A.stream, A);
         else
-            hipLaunchKernelGGL((scan_rows_kernel<Tout, void>), dim3((unsigned)blocks), dim3(256), 0,
-                               A.stream, A);
+            hipLaunchKernelGGL((scan_rows_kernel<Tout, void>), grid, dim3(256), 0, A.stream, A);
     } else {
         const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * A.HV + 7) / 8) * 8;
-        const size_t blocks = may ? chains8 * (TV + TK) : chains8 * TV;
-        hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)blocks), dim3(256), 0,
-                           A.stream, A);
+        const size_t items = may ? chains8 * (TV + TK) : chains8 * TV;
+        const size_t unseg = (size_t)((A.N * A.HV + 7) / 8) * 8 * TV;
+        const size_t grid = (may && (size_t)A.N * A.HV * TV < 256) ? items : unseg;
+        hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)grid), dim3(256), 0,
+                           A.stream, A, (int)items);
     }
     if (may) {
         const int cgrid = (int)std::min<size_t>((size_t)A.N * A.HV * TV, 512);
         hipLaunchKernelGGL((combine_kernel<DK>), dim3(cgrid), dim3(256), 0, A.stream, A);
         const int rgrid = (int)std::min<size_t>((size_t)A.corr_bound * A.HV, 512);
-        hipLaunchKernelGGL((correct_kernel<DK, Tout>), dim3(rgrid), dim3(256), 0, A.stream, A);
+        if constexpr (DK == 128) {
+            if (A.nz && A.nz_bf16)
+                hipLaunchKernelGGL((correct_kernel<DK, Tout, bf16_t>), dim3(rgrid), dim3(256), 0, A.stream, A);
+            else if (A.nz)
+                hipLaunchKernelGGL((correct_kernel<DK, Tout, float>), dim3(rgrid), dim3(256), 0, A.stream, A);
+            else
+                hipLaunchKernelGGL((correct_kernel<DK, Tout, void>), dim3(rgrid), dim3(256), 0, A.stream, A);
+        } else {
+            hipLaunchKernelGGL((correct_kernel<DK, Tout, void>), dim3(rgrid), dim3(256), 0, A.stream, A);
+        }
     }
     return hipGetLastError();
 }
@@ -1829,7 +1930,9 @@ bool prefill_mfma_eligible(const PrefillArgs& A) {
 }
 
 bool prefill_fuses_norm(const PrefillArgs& A) {
-    return prefill_mfma_eligible(A) && use_rows(A, A.dk) && !may_segment(A, A.dk);
+    // with segments the later segments' raw outputs pass through the output
+    // type: fused then only for fp32 outputs
+    return prefill_mfma_eligible(A) && use_rows(A, A.dk) && (!A.o_bf16 || !may_segment(A, A.dk));
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& A) {

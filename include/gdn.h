@@ -229,7 +229,12 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
  * sequences leave most of the GPU idle (one long prompt), and costs extra
  * work otherwise; gdn_prefill_chunked decides on the device from the lengths.
  *
- *   segment_chunks   0: decide automatically (as gdn_prefill_chunked)
+ *   segment_chunks   0: decide automatically (as gdn_prefill_chunked): only when
+ *                      the (sequence, value head) chains leave CUs idle
+ *                   -2: decide automatically from the lengths also when the
+ *                      chains fill the GPU: for batches with one prompt far
+ *                      longer than the rest (costs two near-empty launches
+ *                      when it decides against segments)
  *                   -1: never segment
  *                  >= 32: segments of this many chunks (64 tokens each)
  *   every other argument as gdn_prefill_chunked (same workspace size).

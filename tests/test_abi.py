@@ -99,9 +99,9 @@ def test_prefill_validation(L):
     seg = lambda n: L.gdn_prefill_chunked_seg(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 2, 100, None,
                                               FAKE, FAKE, 0, 2, 4, 128, 128, 64, 1.0, n, None,
                                               0, None)
-    for bad in (1, 31, -2):
+    for bad in (1, 31, -3):
         assert seg(bad) == 1                          # segment length below 32 chunks
-    for ok in (0, -1, 32, 1000):
+    for ok in (0, -1, -2, 32, 1000):
         assert seg(ok) == 3                           # passes that check, fails on the workspace
 
 

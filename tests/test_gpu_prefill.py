@@ -14,6 +14,36 @@ from gpu_helpers import (assert_parity, dev, gpu_prefill, host, oracle_prefill, 
 pytestmark = pytest.mark.gpu
 
 
+def test_prefill_varlen_at_the_token_cap(orc):
+    """The long-context varlen prefill at its largest size: 8 packed sequences
+    of 131,072 tokens in all, the longest at the 65,536-token maximum and the
+    shortest at the 256-token minimum, 16 key / 32 value heads, S0 ~ N(0, 0.02);
+    the library's own choice of scan.  Compared sequence by sequence, so the
+    fp64 outputs are never held whole."""
+    from gpu_helpers import O_REL_L2, S_MAX_ABS
+    lengths = [65536, 256, 30000, 12000, 9000, 8000, 5000, 1280]
+    assert sum(lengths) == 131072
+    x = gi.make_prefill(lengths, 16, 32, 128, 128, s0_std=0.02, seed=131)
+    say(f"prefill varlen at the token cap: lengths={lengths}")
+    o, S = gpu_prefill(x)
+    Sh = host(S)
+    num = den = 0.0
+    worst = 0.0
+    cu = x.cu_seqlens
+    for n in range(x.N):
+        a, e = int(cu[n]), int(cu[n + 1])
+        o_ref, S_ref = orc.recurrence(x.q[a:e], x.k[a:e], x.v[a:e], x.g[a:e], x.beta[a:e],
+                                      np.array([0, e - a], np.int32), s0=x.s0[n:n + 1])
+        og = host(o[a:e])
+        num += float(np.sum((og - o_ref) ** 2))
+        den += float(np.sum(o_ref ** 2))
+        worst = max(worst, float(np.max(np.abs(Sh[n] - S_ref[0]))))
+        del o_ref, og
+    ro = (num / den) ** 0.5
+    print(f"[parity] token cap: o rel-L2 {ro:.3e}, state max-abs {worst:.3e}", flush=True)
+    assert ro <= O_REL_L2 and worst <= S_MAX_ABS
+
+
 def test_prefill_tiny_d16_fp32(orc):
     x = gi.workload(0)
     say("prefill tiny d=16 fp32")

@@ -1,9 +1,11 @@
 """gdn_prefill_chunked_norm on the GPU: the chunked prefill followed by
 RMSNormGated of every (token, value head).  Where the scan runs one workgroup
-per chain (d = 128, at least 512 chains, no segmentation) the norm is applied
-inside the scan; elsewhere the library runs the norm as a second launch on
-fp32 outputs kept in the workspace.  Checked against the fp64 oracle (the
-norm of the oracle's outputs) and against the two separate calls.
+per chain (d = 128: at least 512 chains, or long prompts on fewer) the norm
+is applied inside the scan, and for the later segments of a segmented
+sequence inside the correction pass; elsewhere the library runs the norm as a
+second launch on fp32 outputs kept in the workspace.  Checked against the
+fp64 oracle (the norm of the oracle's outputs) and against the two separate
+calls.
 """
 import dataclasses
 
@@ -46,16 +48,29 @@ def _two_calls(x, *, scale, zd="bf16", wd="f32", yd="f32"):
     return y, S, o
 
 
-@pytest.mark.parametrize("H,HV,N,zd,wd,yd", [(16, 16, 32, "bf16", "f32", "f32"),
-                                             (8, 16, 32, "f32", "bf16", "f32"),
-                                             (16, 32, 16, "bf16", "bf16", "bf16")])
-def test_prefill_norm_fused_matches_oracle(orc, H, HV, N, zd, wd, yd):
-    lengths = _lengths_many(300 + HV + N, N, 300)
-    x = gi.make_prefill(lengths, H, HV, 128, 128, s0_std=0.02, seed=301 + H)
+def _fused_lengths(kind, HV, N):
+    if kind == "many":      # >= 512 chains, short sequences: one segment each
+        return _lengths_many(300 + HV + N, N, 300)
+    if kind == "long":      # one long prompt on few chains: segmented
+        return [20000]
+    return [32768] + [1024] * 15  # "skewed": 512 chains, unsegmented
+
+
+@pytest.mark.parametrize("kind,H,HV,N,zd,wd,yd", [("many", 16, 16, 32, "bf16", "f32", "f32"),
+                                                  ("many", 8, 16, 32, "f32", "bf16", "f32"),
+                                                  ("many", 16, 32, 16, "bf16", "bf16", "bf16"),
+                                                  ("long", 4, 4, 1, "bf16", "f32", "f32"),
+                                                  ("long", 2, 4, 1, "f32", "f32", "bf16"),
+                                                  ("skewed", 16, 32, 16, "bf16", "f32", "f32")])
+def test_prefill_norm_fused_matches_oracle(orc, kind, H, HV, N, zd, wd, yd):
+    lengths = _fused_lengths(kind, HV, N)
+    x = gi.make_prefill(lengths, H, HV, 128, 128, s0_std=0.02,
+                        decay="mild" if kind != "many" else "qwen", seed=301 + H)
     # a weight that is not all ones (bf16-exact when passed as bf16)
     wv = (1.0 + 0.5 * np.random.default_rng(HV + N).standard_normal(128)).astype(np.float32)
     x = dataclasses.replace(x, w=gi.round_bf16(wv) if wd == "bf16" else wv)
-    say(f"prefill+norm fused: N={N} H={H} HV={HV} z={zd} w={wd} y={yd} T={sum(lengths)}")
+    say(f"prefill+norm fused ({kind}): N={len(lengths)} H={H} HV={HV} z={zd} w={wd} y={yd} "
+        f"T={sum(lengths)}")
     y, S = _norm_call(x, scale=128 ** -0.5, zd=zd, wd=wd, yd=yd)
     o_ref, S_ref = oracle_prefill(orc, x, scale=128 ** -0.5)
     y_ref = orc.rmsnorm_gated(o_ref, x.z, x.w, eps=1e-6)
@@ -66,13 +81,18 @@ def test_prefill_norm_fused_matches_oracle(orc, H, HV, N, zd, wd, yd):
     assert ry <= tol_y and ms <= S_MAX_ABS
 
 
-def test_prefill_norm_fused_agrees_with_two_calls():
+@pytest.mark.parametrize("kind", ["many", "long"])
+def test_prefill_norm_fused_agrees_with_two_calls(kind):
     """Same scan: the final states agree bit for bit; the fused norm sums the
     squares in another order and takes SiLU from the hardware exp2 and
-    reciprocal, so y agrees to fp32 rounding."""
-    x = gi.make_prefill(_lengths_many(7, 32, 400), 16, 16, 128, 128, s0_std=0.02,
-                        decay="mild", seed=302)
-    say("prefill+norm fused vs two calls")
+    reciprocal, so y agrees to fp32 rounding (with segments too: the later
+    segments' raw outputs go through fp32 as in the plain call)."""
+    if kind == "many":
+        x = gi.make_prefill(_lengths_many(7, 32, 400), 16, 16, 128, 128, s0_std=0.02,
+                            decay="mild", seed=302)
+    else:
+        x = gi.make_prefill([30000, 3000], 4, 4, 128, 128, s0_std=0.02, decay="mild", seed=307)
+    say(f"prefill+norm fused vs two calls ({kind})")
     y, S = _norm_call(x, scale=128 ** -0.5)
     y2, S2, _ = _two_calls(x, scale=128 ** -0.5)
     assert np.array_equal(host(S), host(S2))
@@ -80,15 +100,15 @@ def test_prefill_norm_fused_agrees_with_two_calls():
     assert max_abs(host(y), host(y2)) <= 1e-5 * max(1.0, float(np.abs(host(y2)).max()))
 
 
-@pytest.mark.parametrize("case", ["per-tile", "segmented", "with-o"])
+@pytest.mark.parametrize("case", ["per-tile", "per-tile-segmented", "with-o"])
 def test_prefill_norm_other_paths_equal_two_calls(case):
     """Where the norm is its own launch, the call is exactly the two calls:
-    few chains (per-32-row scan), a long prompt cut into segments, and any call
-    that also asks for the raw outputs."""
+    few chains (per-32-row scan, unsegmented or segmented: d_v = 64 here) and
+    any call that also asks for the raw outputs."""
     if case == "per-tile":
         x = gi.make_prefill([200, 0, 129, 64], 2, 4, 128, 128, s0_std=0.02, seed=303)
-    elif case == "segmented":
-        x = gi.make_prefill([20000], 4, 4, 128, 128, s0_std=0.02, decay="mild", seed=304)
+    elif case == "per-tile-segmented":
+        x = gi.make_prefill([20000], 4, 4, 128, 64, s0_std=0.02, decay="mild", seed=304)
     else:
         x = gi.make_prefill(_lengths_many(9, 32, 200), 16, 16, 128, 128, s0_std=0.02, seed=305)
     say(f"prefill+norm {case}: lengths={list(x.lengths)[:6]} HV={x.HV}")

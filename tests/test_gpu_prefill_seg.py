@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 
 import gdn_inputs as gi
-from gpu_helpers import assert_parity, gpu_prefill, host, oracle_prefill, rel_l2, say
+from gpu_helpers import (O_REL_L2, S_MAX_ABS, assert_parity, gpu_prefill, host, oracle_prefill,
+                         rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -160,3 +161,30 @@ def test_prefill_graph_replay_matches_eager(segment_chunks):
         assert torch.equal(o, o_eager), f"replay {rep}: outputs differ"
         assert torch.equal(sf, s_eager), f"replay {rep}: final states differ"
         _ = (o * 2).sum().item()  # eager work between replays
+
+
+@pytest.mark.parametrize("mode", [-2, 0])
+def test_skewed_batch_automatic(orc, mode):
+    """A batch whose chains already fill the CUs (16 x 32 = 512) but whose
+    longest sequence is 32 times the rest: with segment_chunks = -2 the
+    planner cuts that sequence into segments, which run beside the short ones;
+    with 0 it runs unsegmented.  Compared with the oracle sequence by
+    sequence."""
+    lengths, H, HV = [32768] + [1024] * 15, 16, 32
+    x = gi.make_prefill(lengths, H, HV, 128, 128, s0_std=0.02, seed=95 + len(lengths))
+    say(f"prefill skewed batch, mode {mode}: lengths={lengths[:4]}.. N={len(lengths)} HV={HV}")
+    o, S = gpu_prefill(x, segment_chunks=mode)
+    Sh = host(S)
+    num = den = worst = 0.0
+    cu = x.cu_seqlens
+    for n in range(x.N):
+        a, e = int(cu[n]), int(cu[n + 1])
+        o_ref, S_ref = orc.recurrence(x.q[a:e], x.k[a:e], x.v[a:e], x.g[a:e], x.beta[a:e],
+                                      np.array([0, e - a], np.int32), s0=x.s0[n:n + 1])
+        og = host(o[a:e])
+        num += float(np.sum((og - o_ref) ** 2))
+        den += float(np.sum(o_ref ** 2))
+        worst = max(worst, float(np.max(np.abs(Sh[n] - S_ref[0]))))
+    ro = (num / den) ** 0.5
+    print(f"[parity] skewed batch: o rel-L2 {ro:.3e}, state max-abs {worst:.3e}", flush=True)
+    assert ro <= O_REL_L2 and worst <= S_MAX_ABS
