@@ -62,21 +62,21 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # profiles/decode_traffic_qwen35_08b.md together with the sha256 of the kernel
 # source (and the local headers it includes) it was measured on.  Reported only
 # while those sources are unchanged.
-DECODE_TRAFFIC = {"kernel_source_sha256": "ff5870fb86b5843f8041a9ed5fd045a678f2170baacbcb8ac0e92ab8c18504a9",
-                  "bytes_per_launch": 68046771}
+DECODE_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
+                  "bytes_per_launch": 68046132}
 
 
 # The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
 # profiles/serving_decode_traffic.md) and the attention decode step
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
-SERVE_TRAFFIC = {"kernel_source_sha256": "ff5870fb86b5843f8041a9ed5fd045a678f2170baacbcb8ac0e92ab8c18504a9",
-                 "bytes_per_launch": 543601972}
-ATTN_TRAFFIC = {"kernel_source_sha256": "9b70f194d33e83c72c177f4bb393b13a06bff68cce1d04c3e64b98773ad67b13",
-                "bytes_per_launch": 2185173300}
+SERVE_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
+                 "bytes_per_launch": 543595770}
+ATTN_TRAFFIC = {"kernel_source_sha256": "307e9311a1db99216f64ad4f2a186d5037925cb4b7bb87d0d6756a8c362ee5c5",
+                "bytes_per_launch": 2185070580}
 # RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
 # profiles/rmsnorm_gated_traffic.md)
-NORM_TRAFFIC = {"kernel_source_sha256": "9241f48c4927a381f3dbcd29f95477690ab668304fc708a2988ec09b54079396",
-                "bytes_per_launch": 335597881}
+NORM_TRAFFIC = {"kernel_source_sha256": "8014073d5bbde2fe478883ec30d9322ab0c7f7757ad23136244750031bf4a1ce",
+                "bytes_per_launch": 335584886}
 
 
 def kernel_sources_sha256(source):
