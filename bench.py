@@ -25,6 +25,10 @@ of Qwen3.6-35B-A3B (16 query heads over 2 key/value heads, head_dim 256, a
 quarter rotated, theta 1e7; 10 of its 40 layers): 128 rows at position 8192
 of 8320-row bf16 caches per layer.
 
+``--workload decode3`` times the decode step at the 35B-A3B DeltaNet shape
+(16 key / 32 value heads): batch 128 seeded from a 2 x 8192-token prefill, 4
+layer-states rotated.
+
 ``--workload norm`` times RMSNormGated on its own (gdn_rmsnorm_gated) at the
 job's prefill output shape (32 x 512 tokens, 16 value heads, d_v = 128).
 
@@ -542,6 +546,77 @@ def run_attn(args):
     }
 
 
+def run_decode3(args):
+    """The 35B-A3B-shaped decode (16 key / 32 value heads, d = 128): batch 128,
+    slot n starting from the final state n mod 2 of a 2 x 8192-token prefill,
+    then ``steps`` decode steps (decode + RMSNormGated in one kernel) over 4
+    layer-states (4 x 256 MiB, beyond the 256 MB Infinity Cache), each with
+    its own inputs; the decode phase is captured in a HIP graph."""
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    import gdn_inputs as gi
+
+    N, H, HV, d, T, L = 128, 16, 32, 128, 8192, 4
+    steps = args.decode_steps or 128
+    dev = torch.device("cuda", 0)
+    log(f"decode3: N={N} H={H} HV={HV} d={d} prefill 2 x {T} steps={steps} layer-states={L}")
+    head_scale = gi.decay_scale(0, 1003, HV, "qwen")
+    cu = torch.tensor([0, T, 2 * T], dtype=torch.int32, device=dev)
+    w = torch.ones(d, device=dev)
+    layers = []
+    for l in range(L):
+        q, k, v, g, b, _ = gi.device_tokens((2 * T,), H, HV, d, d, seed=3000 + l,
+                                            head_scale=head_scale, device=dev, with_z=False)
+        _, S2 = gdn.prefill_chunked(q, k, v, g, b, cu)
+        del q, k, v, g, b
+        state = S2[torch.arange(N, device=dev) % 2].contiguous()
+        dq, dk_, dv_, dg, db, dz = gi.device_tokens((steps, N), H, HV, d, d, seed=6000 + l,
+                                                    head_scale=head_scale, device=dev)
+        layers.append(dict(dq=dq, dk=dk_, dv=dv_, dg=dg, db=db, dz=dz, state=state,
+                           yd=torch.empty(N, HV, d, device=dev)))
+    torch.cuda.synchronize()
+
+    def decode_phase():
+        for t in range(steps):
+            for Ly in layers:
+                gdn.decode_step_norm(Ly["dq"][t], Ly["dk"][t], Ly["dv"][t], Ly["dg"][t],
+                                     Ly["db"][t], Ly["state"], Ly["dz"][t], w, y=Ly["yd"])
+
+    g_dec, s = graph_capture(decode_phase)
+    for _ in range(args.warmup):
+        g_dec.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(args.steps):
+            g_dec.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+    launch_us = ms * 1e3 / (steps * L)
+    bytes_launch = decode_bytes_per_token(H, HV, d, d) * N
+    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
+    return {
+        "metric": METRIC, "value": round(N * steps * L / (ms * 1e-3), 1),
+        "unit": "tokens/s per DeltaNet layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwen3.6-35b-a3b-deltanet-decode", "sequences": N,
+                   "qk_heads": H, "v_heads": HV, "d_k": d, "d_v": d,
+                   "seeded_from": "2 x 8192-token prefill (slot n from state n mod 2)",
+                   "decode_steps": steps, "layer_states": L, "inputs": "bf16",
+                   "state": "f32", "outputs": "f32"},
+        "roofline": {"kernel": "decode_kernel (decode + RMSNormGated)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(launch_us, 3),
+                     "algorithmic_bytes_per_launch": bytes_launch},
+    }
+
+
 def norm_bytes(rows, HV, dv, x_bytes=4, z_bytes=2, y_bytes=4, w_bytes=4):
     """HBM bytes of one RMSNormGated launch: x and z read, y written, the
     weight read once."""
@@ -714,7 +789,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill2", "prefill3", "prefill4", "prefill5", "copy",
-                             "serve", "attn", "norm"])
+                             "serve", "attn", "norm", "decode3"])
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--decode-steps", type=int, default=0)
     ap.add_argument("--cpu-layers", type=int, default=12)
@@ -739,6 +814,8 @@ def main():
         out = run_attn(args)
     elif args.workload == "norm":
         out = run_norm(args)
+    elif args.workload == "decode3":
+        out = run_decode3(args)
     else:
         out = run_prefill(args, int(args.workload[-1]))
     print(json.dumps(out), flush=True)
