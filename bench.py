@@ -77,6 +77,10 @@ SERVE_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd35
                  "bytes_per_launch": 543595770}
 ATTN_TRAFFIC = {"kernel_source_sha256": "307e9311a1db99216f64ad4f2a186d5037925cb4b7bb87d0d6756a8c362ee5c5",
                 "bytes_per_launch": 2185070580}
+# The fused decode at the 35B-A3B shape, batch 128 (gdn_decode.hip;
+# profiles/decode_traffic_35b.md)
+DECODE3_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
+                   "bytes_per_launch": 543840264}
 # RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
 # profiles/rmsnorm_gated_traffic.md)
 NORM_TRAFFIC = {"kernel_source_sha256": "8014073d5bbde2fe478883ec30d9322ab0c7f7757ad23136244750031bf4a1ce",
@@ -611,7 +615,8 @@ def run_decode3(args):
                    "state": "f32", "outputs": "f32"},
         "roofline": {"kernel": "decode_kernel (decode + RMSNormGated)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(DECODE3_TRAFFIC),
                      "avg_launch_us": round(launch_us, 3),
                      "algorithmic_bytes_per_launch": bytes_launch},
     }
