@@ -135,21 +135,23 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
     constexpr int PPR = DK / 8;         // 16-byte pieces per row
     constexpr int RPI = 64 / PPR;       // rows per coalesced 1 KiB load
     constexpr int NLD = 16 / RPI;       // loads per wavefront per tile
-    // LDS, 52,992 bytes at d_k = 128 (three workgroups per CU): Q is needed
-    // only for the first products, so T = (I + A)^-1 takes its place; the
-    // 32-block merge's X lives in T's upper-right block, which T (lower
-    // triangular) never uses; G, b and e^{G_n - G} are held for one value head
-    // at a time.
-    static_assert(C * KP * 2 <= C * AP * 4, "Q fits in the buffer of T");
+    // LDS, 35,584 bytes at d_k = 128 (four workgroups per CU).  Beside K, one
+    // 64 x 64 fp32 buffer holds in turn Q (needed only for the first
+    // products), A, T = (I + A)^-1 written over A block by block (every block
+    // of A is read before its place is written), and T'^T (T staged through
+    // registers first).  The 32-block merge's X lives in the upper-right block,
+    // which neither A nor T (lower triangular) uses.  G, b and e^{G_n - G}
+    // are held for the value head.
+    static_assert(C * KP * 2 <= C * AP * 4, "Q fits in the buffer of A and T");
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) float QT[C * AP];
-    __shared__ __attribute__((aligned(16))) float Am[C * AP];  // A, then T'^T
+    __shared__ __attribute__((aligned(16))) float Bf[C * AP];  // Q, A, T, then T'^T
     __shared__ __attribute__((aligned(16))) float Gs[C];
     __shared__ __attribute__((aligned(16))) float Bs[C];
     __shared__ __attribute__((aligned(16))) float Ds[C];
-    __bf16* const Qs = reinterpret_cast<__bf16*>(QT);
-    float* const Tm = QT;        // T, rows 0 .. 63, lower triangle
-    float* const Xm = QT + 32;   // X [32 x 32], rows 0 .. 31 of T's columns 32 .. 63
+    __bf16* const Qs = reinterpret_cast<__bf16*>(Bf);
+    float* const Am = Bf;        // A (lower blocks), later T'^T
+    float* const Tm = Bf;        // T, rows 0 .. 63, lower triangle
+    float* const Xm = Bf + 32;   // X [32 x 32], rows 0 .. 31, columns 32 .. 63
 
     const int H = A.H, HV = A.HV;
     const int c = blockIdx.x, tid = threadIdx.x;
@@ -243,6 +245,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
         for (int y = 0; y < 8; ++y)
             sel[h][y] = static_cast<__bf16>((8 * lg + y == 16 * h + lr) ? 1.f : 0.f);
 
+    __syncthreads();  // every wavefront has read Q: A takes its place
     {
         const float* G = Gs;
         // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s}); branch-free: the
@@ -366,15 +369,25 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillArgs A) {
                 Tm[(32 + 16 * tbm + 4 * lg + r) * AP + 16 * jb + lr] = -ta[r];
         }
         __syncthreads();
-        // T'^T[c][s] = T[s][c] b_c (zero for s < c) into Am: thread row s, columns c4 .. c4 + 3
-        for (int idx = tid; idx < C * C / 4; idx += 256) {
-            const int s_ = idx & 63, c4 = 4 * (idx >> 6);
-            const float4 t4 = *reinterpret_cast<const float4*>(&Tm[s_ * AP + c4]);
-            const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+        // T'^T[c][s] = T[s][c] b_c (zero for s < c) in T's place: each thread
+        // reads its pieces of T (row s, columns c4 .. c4 + 3), then, after a
+        // barrier, writes their transposes
+        constexpr int NTP = C * C / 4 / 256;
+        float4 tq[NTP];
+#pragma unroll
+        for (int it = 0; it < NTP; ++it) {
+            const int idx = tid + 256 * it, s_ = idx & 63, c4 = 4 * (idx >> 6);
+            tq[it] = *reinterpret_cast<const float4*>(&Tm[s_ * AP + c4]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < NTP; ++it) {
+            const int idx = tid + 256 * it, s_ = idx & 63, c4 = 4 * (idx >> 6);
+            const float tv[4] = {tq[it].x, tq[it].y, tq[it].z, tq[it].w};
             const float4 b4 = *reinterpret_cast<const float4*>(&Bs[c4]);
             const float bc[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)  // a select, not a 0/1 factor: T's upper blocks are never written
+            for (int r = 0; r < 4; ++r)  // a select, not a 0/1 factor: T's upper blocks hold other data
                 Am[(c4 + r) * AP + s_] = (s_ >= c4 + r) ? tv[r] * bc[r] : 0.f;
         }
         __syncthreads();
