@@ -67,16 +67,16 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # source (and the local headers it includes) it was measured on.  Reported only
 # while those sources are unchanged.
 DECODE_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
-                  "bytes_per_launch": 68046132}
+                  "bytes_per_launch": 68046342}
 
 
 # The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
 # profiles/serving_decode_traffic.md) and the attention decode step
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
 SERVE_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
-                 "bytes_per_launch": 543595770}
+                 "bytes_per_launch": 543594255}
 ATTN_TRAFFIC = {"kernel_source_sha256": "307e9311a1db99216f64ad4f2a186d5037925cb4b7bb87d0d6756a8c362ee5c5",
-                "bytes_per_launch": 2185070580}
+                "bytes_per_launch": 2185084533}
 # The fused decode at the 35B-A3B shape, batch 128 (gdn_decode.hip;
 # profiles/decode_traffic_35b.md)
 DECODE3_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
@@ -84,7 +84,7 @@ DECODE3_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd
 # RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
 # profiles/rmsnorm_gated_traffic.md)
 NORM_TRAFFIC = {"kernel_source_sha256": "8014073d5bbde2fe478883ec30d9322ab0c7f7757ad23136244750031bf4a1ce",
-                "bytes_per_launch": 335584886}
+                "bytes_per_launch": 335592899}
 
 
 def kernel_sources_sha256(source):
