@@ -1,44 +1,51 @@
 """Benchmark of the Gated DeltaNet token mixer (libgdn) on one MI355X.
 
-Default workload (one "step"): the Qwen3.5-0.8B DeltaNet decode job over the
-18 DeltaNet layers of the model (18 of 24 layers; Qwen3.5-0.8B chat guide,
-section "Architektur").  32 sequences, 16 key/query heads, 16 value heads,
-d_k = d_v = 128, bf16 q/k/v, fp32 state.  Per layer: a 512-token chunked
-prefill of every sequence from a zero state followed by RMSNormGated of its
-outputs, in one call (gdn_prefill_chunked_norm: the norm runs inside the
-scan); then 256 decode steps, each advancing all 18 layer-states by one token
-(decode + RMSNormGated per layer).
-Every layer has its own state (18 x 32 MiB = 576 MiB, more than the 256 MB
-Infinity Cache) and its own inputs, all resident in HBM before timing starts.
-The decode step and its RMSNormGated run as one kernel (gdn_decode_step_norm).
-The launch sequence of a step is captured once in HIP graphs and replayed.
+Default workload (one "step"): the Qwen3.6-35B-A3B DeltaNet job, 16 key/query
+heads shared by 32 value heads (two value heads per key head: the Core AI
+card for Qwen3.6-35B-A3B, introduction), d_k = d_v = 128, bf16 q/k/v, fp32
+state, over 4 layer-states (4 x 256 MiB of decode state, beyond the 256 MB
+Infinity Cache).  Per layer-state:
+
+  * prefill: a packed batch of 2 x 8192-token prompts from zero states,
+    followed by RMSNormGated of every output (gdn_prefill_chunked_norm);
+  * seeding: decode row n starts from the prefill's final state n mod 2
+    (a device gather of the two states into the 128-row decode batch);
+  * decode: 128 steps at batch 128, decode + RMSNormGated in one kernel
+    (gdn_decode_step_norm), each step advancing all 4 layer-states.
+
+Every layer-state has its own inputs, all resident in HBM before timing
+starts; each phase's launches are captured once in a HIP graph and replayed.
+``value`` = tokens per second per DeltaNet layer over the whole job:
+4 x (2 x 8192 + 128 x 128) tokens / job time.  The line also carries the
+decode kernel's HBM roofline, the prefill call's HBM and MFMA fractions, the
+long-context varlen prefill at its 131,072-token cap (8 packed sequences,
+32 value heads, nonzero initial states) as a phase, and the fp64 oracle timed
+on the host cores on a sample of the job.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload decode|prefill2|prefill3|prefill4|prefill5|serve|attn]
+                    [--workload job35b|job08b|prefill2|prefill3|prefill4|prefill4cap|prefill5|
+                                decode3|serve|attn|norm|copy]
 
-``prefill5`` is one 32768-token prompt at the 0.8B shape (the case the
-segment-parallel scan is for); prefill lines also report the time with
-segmentation turned off.
+``job08b`` is the Qwen3.5-0.8B DeltaNet job over its 18 DeltaNet layers (18 of
+24 layers; Qwen3.5-0.8B chat guide, section "Architektur"): 32 sequences,
+16 key/query and 16 value heads, a 512-token prefill + RMSNormGated per
+sequence, then 256 decode + RMSNormGated steps.
 
-``--workload attn`` times one decode step of the gated full-attention layers
-of Qwen3.6-35B-A3B (16 query heads over 2 key/value heads, head_dim 256, a
-quarter rotated, theta 1e7; 10 of its 40 layers): 128 rows at position 8192
-of 8320-row bf16 caches per layer.
+``prefill2|3|4|4cap|5`` time one prefill call per workload (4 x 4096 tokens at
+the 0.8B shape; 2 x 8192 at the 35B-A3B shape; the long-context varlen draw;
+the same at its 131,072-token cap; one 32768-token prompt) with the library's
+own choice of scan and with segmentation off.
 
-``--workload decode3`` times the decode step at the 35B-A3B DeltaNet shape
-(16 key / 32 value heads): batch 128 seeded from a 2 x 8192-token prefill, 4
-layer-states rotated.
+``decode3`` times the decode step alone at the 35B-A3B shape (batch 128, 4
+layer-states).  ``serve`` times the serving form (gdn_decode_layer: 128 rows
+from a pool of 256 slots, raw bf16 gates, q/k L2 norm, RMSNormGated; 30
+DeltaNet layers).  ``attn`` times one decode step of the gated full-attention
+layers of Qwen3.6-35B-A3B (16 query over 2 key/value heads, head_dim 256, a
+quarter rotated, theta 1e7; 128 rows at position 8192).  ``norm`` times
+RMSNormGated on its own.  ``copy`` is the calibration copy for the traffic
+counters.
 
-``--workload norm`` times RMSNormGated on its own (gdn_rmsnorm_gated) at the
-job's prefill output shape (32 x 512 tokens, 16 value heads, d_v = 128).
-
-``--workload serve`` times the serving form of the decode step
-(gdn_decode_layer) on the Qwen3.6-35B-A3B DeltaNet shape: 128 rows drawn from
-a pool of 256 state slots per layer, raw bf16 gates activated in the kernel,
-q/k L2-normalised in the kernel, RMSNormGated fused, over 30 DeltaNet layers.
-
-Prints one JSON line.  ``value`` = tokens per second per DeltaNet layer over
-the whole job: 32 x (512 + 256) tokens x 18 layers / job time.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -85,6 +92,19 @@ DECODE3_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd
 # profiles/rmsnorm_gated_traffic.md)
 NORM_TRAFFIC = {"kernel_source_sha256": "8014073d5bbde2fe478883ec30d9322ab0c7f7757ad23136244750031bf4a1ce",
                 "bytes_per_launch": 335592899}
+
+
+# Prefill counters from rocprofv3 runs of the bench lines (per call: issued
+# bf16 MFMA flops from SQ_INSTS_VALU_MFMA_MOPS_BF16, and HBM bytes from
+# FETCH_SIZE / WRITE_SIZE scaled by the copy calibration), keyed on the
+# prefill kernel sources they were measured on; profiles/ holds the runs.
+PREFILL_COUNTERS = {"kernel_source_sha256": None, "issued_mfma_flops": {}, "traffic_bytes": {}}
+
+
+def recorded(record, source):
+    """A counter record when its kernel sources are unchanged, else None."""
+    ok = record.get("kernel_source_sha256") == kernel_sources_sha256(source)
+    return record if ok else None
 
 
 def kernel_sources_sha256(source):
@@ -235,6 +255,283 @@ def cpu_baseline_decode_job(layers_sample: int, N, T, H, HV, d, steps, seed=0):
     return N * (T + steps) * layers_sample / dt, dt, orc.max_threads()
 
 
+JOB35 = dict(name="qwen3.6-35b-a3b-deltanet-job", N=2, T=8192, H=16, HV=32, d=128,
+             decode_N=128, decode_steps=128)
+
+
+def cpu_baseline_job35b(samples: int, N, T, H, HV, d, dec_N, steps, seed=0):
+    """The fp64 oracle on ``samples`` layer-states of the 35B-A3B job: the
+    N x T-token prefill + RMSNormGated, then ``steps`` decode steps of dec_N
+    rows (row n from the prefill's final state n mod N) + RMSNormGated.  Input
+    generation is not timed.  Returns (tokens/s per layer, seconds, threads)."""
+    import gdn_inputs as gi
+    import oracle
+    orc = oracle.load()
+    secs = 0.0
+    for l in range(samples):
+        x = gi.make_prefill([T] * N, H, HV, d, d, seed=seed + l, stream=1003)
+        dd = gi.make_decode(steps, dec_N, H, HV, d, d, seed=seed + l, stream=2003,
+                            decay_stream=1003)
+        t0 = time.perf_counter()
+        o, S = orc.recurrence(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens)
+        orc.rmsnorm_gated(o, x.z, x.w)
+        del o
+        S = S[np.arange(dec_N) % N]
+        for t in range(steps):
+            od, S = orc.decode(dd.q[t], dd.k[t], dd.v[t], dd.g[t], dd.beta[t], S)
+            orc.rmsnorm_gated(od, dd.z[t], dd.w)
+        secs += time.perf_counter() - t0
+        del x, dd, S
+    return (N * T + dec_N * steps) * samples / secs, secs, orc.max_threads()
+
+
+def cpu_baseline_prefill(lengths, H, HV, d, s0_std=0.0, seed=0):
+    """The fp64 oracle on a packed prefill of the given lengths + RMSNormGated
+    (generation not timed).  Returns (tokens/s, seconds, threads)."""
+    import gdn_inputs as gi
+    import oracle
+    orc = oracle.load()
+    x = gi.make_prefill(list(lengths), H, HV, d, d, s0_std=s0_std, seed=seed, stream=1004)
+    t0 = time.perf_counter()
+    o, _ = orc.recurrence(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, s0=x.s0)
+    orc.rmsnorm_gated(o, x.z, x.w)
+    secs = time.perf_counter() - t0
+    return int(np.sum(lengths)) / secs, secs, orc.max_threads()
+
+
+def timed_calls(fn, reps, stream):
+    """Average time of ``reps`` back-to-back calls of fn on ``stream``
+    (HIP events on that stream), in microseconds."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def prefill_roofline(us, T, N, H, HV, d, *, s0=False, o_bytes=4, issued=None, traffic=None):
+    """HBM and bf16-MFMA fractions of one prefill call of ``us`` microseconds
+    (algorithmic bytes and flops; issued MFMA flops and counted HBM bytes per
+    call from the recorded rocprofv3 counters when they match the sources)."""
+    b = prefill_bytes(T, N, H, HV, d, d, o_bytes=o_bytes, s0=s0)
+    f = prefill_flops(T, H, HV, d, d)
+    sec = us * 1e-6
+    out = {"call_us": round(us, 2), "tokens_per_s": round(T / sec, 1),
+           "hbm_achieved_GBs": round(b / sec / 1e9, 1),
+           "hbm_frac": round(b / sec / 1e9 / HBM_PEAK_GBS, 4),
+           "tflops": round(f / sec / 1e12, 2),
+           "mfma_bf16_frac": round(f / sec / 1e12 / BF16_PEAK_TFLOPS, 5),
+           "algorithmic_bytes": b, "algorithmic_flops": f,
+           "bound": "hbm" if b / (HBM_PEAK_GBS * 1e9) >= f / (BF16_PEAK_TFLOPS * 1e12) else "mfma"}
+    if issued is not None:
+        out["issued_mfma_flops"] = issued
+        out["issued_mfma_bf16_frac"] = round(issued / sec / 1e12 / BF16_PEAK_TFLOPS, 5)
+    out["traffic"] = traffic
+    return out
+
+
+def run_job35b(args):
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    import gdn_inputs as gi
+
+    J = JOB35
+    N, T, H, HV, d, Nd = J["N"], J["T"], J["H"], J["HV"], J["d"], J["decode_N"]
+    steps = args.decode_steps or J["decode_steps"]
+    L = args.layer_states
+    dev = torch.device("cuda", 0)
+    log(f"35B-A3B job: prefill {N} x {T} H={H} HV={HV} d={d}, then decode batch {Nd} x "
+        f"{steps} steps, {L} layer-states")
+    head_scale = gi.decay_scale(0, 1003, HV, "qwen")
+    cu = torch.tensor([0, T, 2 * T], dtype=torch.int32, device=dev)
+    w = torch.ones(d, device=dev)
+    seed_rows = torch.arange(Nd, device=dev) % N
+    layers = []
+    for l in range(L):
+        q, k, v, g, b, z = gi.device_tokens((N * T,), H, HV, d, d, seed=3000 + l,
+                                            head_scale=head_scale, device=dev)
+        dq, dk_, dv_, dg, db, dz = gi.device_tokens((steps, Nd), H, HV, d, d, seed=6000 + l,
+                                                    head_scale=head_scale, device=dev)
+        layers.append(dict(q=q, k=k, v=v, g=g, b=b, z=z, dq=dq, dk=dk_, dv=dv_, dg=dg, db=db,
+                           dz=dz, pf_state=torch.empty(N, HV, d, d, device=dev),
+                           pool=torch.empty(Nd, HV, d, d, device=dev),
+                           y=torch.empty(N * T, HV, d, device=dev),
+                           yd=torch.empty(Nd, HV, d, device=dev)))
+    ws = torch.empty(gdn.prefill_norm_workspace_bytes(N, N * T, H, HV, d, d),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill_phase():
+        for Ly in layers:
+            gdn.prefill_chunked_norm(Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu, Ly["z"], w,
+                                     final_state=Ly["pf_state"], y=Ly["y"], workspace=ws)
+            torch.index_select(Ly["pf_state"], 0, seed_rows, out=Ly["pool"])
+
+    def decode_phase():
+        for t in range(steps):
+            for Ly in layers:
+                gdn.decode_step_norm(Ly["dq"][t], Ly["dk"][t], Ly["dv"][t], Ly["dg"][t],
+                                     Ly["db"][t], Ly["pool"], Ly["dz"][t], w, y=Ly["yd"])
+
+    t0 = time.perf_counter()
+    g_pf, s = graph_capture(prefill_phase)
+    g_dec, _ = graph_capture(decode_phase)
+    log(f"graphs captured in {time.perf_counter() - t0:.1f}s")
+    for _ in range(args.warmup):
+        g_pf.replay()
+        g_dec.replay()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    with torch.cuda.stream(s):
+        for i in range(args.steps):
+            ev[i][0].record(s)
+            g_pf.replay()
+            ev[i][1].record(s)
+            g_dec.replay()
+            ev[i][2].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    pf_ms = sum(a.elapsed_time(b_) for a, b_, _ in ev)
+    dec_ms = sum(b_.elapsed_time(c) for _, b_, c in ev)
+    job_ms = (pf_ms + dec_ms) / args.steps
+    ms_per_step = max(job_ms, wall * 1e3 / args.steps)
+    pf_tokens, dec_tokens = N * T * L, Nd * steps * L
+    value = (pf_tokens + dec_tokens) / (ms_per_step * 1e-3)
+
+    # dominant kernel: decode + RMSNormGated, steps x layer-states launches on s
+    launches = steps * L
+    dec_launch_us = dec_ms / args.steps * 1e3 / launches
+    bytes_launch = decode_bytes_per_token(H, HV, d, d) * Nd
+    achieved = bytes_launch / (dec_launch_us * 1e-6) / 1e9
+
+    # one prefill call timed alone (layer-state 0): the job's call (prefill +
+    # RMSNormGated), the bare prefill with fp32 o, and with bf16 o
+    Ly = layers[0]
+    o32 = torch.empty(N * T, HV, d, device=dev)
+    o16 = torch.empty(N * T, HV, d, device=dev, dtype=torch.bfloat16)
+    ws_p = torch.empty(gdn.prefill_workspace_bytes(N, N * T, H, HV, d, d), dtype=torch.uint8,
+                       device=dev)
+    us_norm = timed_calls(lambda: gdn.prefill_chunked_norm(
+        Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu, Ly["z"], w, final_state=Ly["pf_state"],
+        y=Ly["y"], workspace=ws), 5, s)
+    us_f32 = timed_calls(lambda: gdn.prefill_chunked(
+        Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu, final_state=Ly["pf_state"], o=o32,
+        workspace=ws_p), 5, s)
+    us_b16 = timed_calls(lambda: gdn.prefill_chunked(
+        Ly["q"], Ly["k"], Ly["v"], Ly["g"], Ly["b"], cu, final_state=Ly["pf_state"], o=o16,
+        workspace=ws_p), 5, s)
+    del o32, o16, ws_p
+    copy_ref = copy_same_bytes(Nd * HV * d * d * 4, copies=L, reps=8)
+    rec = recorded(PREFILL_COUNTERS, "gdn_prefill_mfma.hip")
+    pf_line = prefill_roofline(us_f32, N * T, N, H, HV, d,
+                               issued=rec and rec["issued_mfma_flops"].get("job35b"),
+                               traffic=rec and rec["traffic_bytes"].get("job35b"))
+    pf_line["with_norm_call_us"] = round(us_norm, 2)
+    pf_line["bf16_o"] = {k_: v_ for k_, v_ in prefill_roofline(us_b16, N * T, N, H, HV, d,
+                                                               o_bytes=2).items()
+                         if k_ in ("call_us", "tokens_per_s", "hbm_frac", "mfma_bf16_frac")}
+    del layers, ws
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s per DeltaNet layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": J["name"], "prefill_sequences": N, "prefill_tokens_per_seq": T,
+                   "qk_heads": H, "v_heads": HV, "d_k": d, "d_v": d, "decode_batch": Nd,
+                   "decode_steps": steps, "layer_states": L,
+                   "decode_seeding": "row n from prefill final state n mod 2",
+                   "inputs": "bf16", "state": "f32", "outputs": "f32 (RMSNormGated y)"},
+        "phases": {"prefill_tokens_per_s_per_layer": round(pf_tokens / (pf_ms / args.steps * 1e-3), 1),
+                   "decode_tokens_per_s_per_layer": round(dec_tokens / (dec_ms / args.steps * 1e-3), 1),
+                   "prefill_ms_per_step": round(pf_ms / args.steps, 4),
+                   "decode_ms_per_step": round(dec_ms / args.steps, 4),
+                   "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+        "roofline": {"kernel": "decode_kernel (decode + RMSNormGated)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(DECODE3_TRAFFIC),
+                     "avg_launch_us": round(dec_launch_us, 3),
+                     "algorithmic_bytes_per_launch": bytes_launch},
+        "copy_same_bytes": copy_ref,
+        "roofline_prefill": pf_line,
+    }
+    if not args.no_cap:
+        out["phases"]["long_context_varlen_cap"] = prefill_cap_phase(args)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a sample of the job")
+        v_cpu, secs, thr = cpu_baseline_job35b(args.cpu_layers, N, T, H, HV, d, Nd, steps)
+        out["cpu_baseline"] = {"value": round(v_cpu, 1), "unit": "tokens/s per DeltaNet layer",
+                               "cores": thr, "kind": "oracle",
+                               "sample": f"{args.cpu_layers} layer-state(s) of the job: "
+                                         f"{N} x {T}-token prefill + RMSNormGated, then {Nd} "
+                                         f"rows x {steps} decode steps + RMSNormGated, fp64, "
+                                         f"{secs:.1f} s"}
+    return out
+
+
+def prefill_cap_phase(args):
+    """The long-context varlen prefill at its 131,072-token cap (8 packed
+    sequences, 16 key / 32 value heads, S0 ~ N(0, 0.02)): one call timed with
+    the library's own choice of scan, fp32 and bf16 outputs, with its HBM and
+    MFMA fractions and the oracle on a bounded sample of it."""
+    import torch
+    import gated_delta_rule_decode_amd as gdn
+    import gdn_inputs as gi
+    w4 = gi.WORKLOADS[4]
+    H, HV, d = w4["H"], w4["HV"], w4["dk"]
+    lengths = np.array(gi.CAP_LENGTHS)
+    N, T = len(lengths), int(lengths.sum())
+    dev = torch.device("cuda", 0)
+    log(f"varlen prefill at the cap: {T} tokens in {N} sequences")
+    head_scale = gi.decay_scale(0, 1004, HV, "qwen")
+    q, k, v, g, b, _ = gi.device_tokens((T,), H, HV, d, d, seed=4, head_scale=head_scale,
+                                        device=dev, with_z=False)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).to(dev)
+    s0 = torch.randn(N, HV, d, d, device=dev) * w4["s0_std"]
+    sf = torch.empty(N, HV, d, d, device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(N, T, H, HV, d, d), dtype=torch.uint8,
+                     device=dev)
+    s = torch.cuda.Stream()
+    res = {}
+    for name, dt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        o = torch.empty(T, HV, d, device=dev, dtype=dt)
+        us = timed_calls(lambda: gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0,
+                                                     final_state=sf, o=o, workspace=ws), 3, s)
+        res[name] = us
+        del o
+    rec = recorded(PREFILL_COUNTERS, "gdn_prefill_mfma.hip")
+    out = {"workload": "long-context-varlen-prefill at the 131,072-token cap",
+           "lengths": [int(x) for x in lengths], "qk_heads": H, "v_heads": HV,
+           "roofline": prefill_roofline(res["f32"], T, N, H, HV, d, s0=True,
+                                        issued=rec and rec["issued_mfma_flops"].get("cap"),
+                                        traffic=rec and rec["traffic_bytes"].get("cap")),
+           "bf16_o": {k_: v_ for k_, v_ in prefill_roofline(res["bf16"], T, N, H, HV, d, s0=True,
+                                                            o_bytes=2).items()
+                      if k_ in ("call_us", "tokens_per_s", "hbm_frac", "mfma_bf16_frac")}}
+    del q, k, v, g, b, s0, sf, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        sample = [5000, 1280]  # two of the cap's sequences
+        v_cpu, secs, thr = cpu_baseline_prefill(sample, H, HV, d, s0_std=w4["s0_std"])
+        out["cpu_baseline"] = {"value": round(v_cpu, 1), "unit": "tokens/s (one layer)",
+                               "cores": thr, "kind": "oracle",
+                               "sample": f"sequences of {sample} tokens of the cap batch, "
+                                         f"32 value heads, prefill + RMSNormGated, fp64, "
+                                         f"{secs:.1f} s"}
+    return out
+
+
 def run_decode_job(args):
     import torch
     import gated_delta_rule_decode_amd as gdn
@@ -344,7 +641,7 @@ def run_decode_job(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "qwen3.5-0.8b-deltanet-decode-job", "sequences": N,
+        "config": {"workload": "qwen3.5-0.8b-deltanet-job", "sequences": N,
                    "qk_heads": H, "v_heads": HV, "d_k": d, "d_v": d,
                    "prefill_tokens_per_seq": T, "decode_steps": steps, "layers": L,
                    "inputs": "bf16", "state": "f32", "outputs": "f32"},
@@ -382,18 +679,25 @@ LONG_PROMPT = {"name": "qwen3.5-0.8b-long-prompt-prefill", "N": 1, "T": 32768, "
                "dk": 128}
 
 
-def run_prefill(args, cfg: int):
+def run_prefill(args, cfg: str):
     import torch
     import gated_delta_rule_decode_amd as gdn
     import gdn_inputs as gi
 
-    w = LONG_PROMPT if cfg == 5 else gi.WORKLOADS[cfg]
+    cap = cfg == "4cap"
+    cfg_n = 4 if cap else int(cfg)
+    w = LONG_PROMPT if cfg_n == 5 else gi.WORKLOADS[cfg_n]
     H, HV, d = w["H"], w["HV"], w["dk"]
-    lengths = gi.config_lengths(0) if cfg == 4 else np.array([w["T"]] * w["N"])
+    if cap:
+        lengths = np.array(gi.CAP_LENGTHS)
+    elif cfg_n == 4:
+        lengths = gi.config_lengths(0)
+    else:
+        lengths = np.array([w["T"]] * w["N"])
     N, T = len(lengths), int(np.sum(lengths))
     dev = torch.device("cuda", 0)
-    head_scale = gi.decay_scale(0, 1000 + cfg, HV, "qwen")
-    q, k, v, g, b, _ = gi.device_tokens((T,), H, HV, d, d, seed=cfg, head_scale=head_scale,
+    head_scale = gi.decay_scale(0, 1000 + cfg_n, HV, "qwen")
+    q, k, v, g, b, _ = gi.device_tokens((T,), H, HV, d, d, seed=cfg_n, head_scale=head_scale,
                                         device=dev, with_z=False)
     cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).to(dev)
     s0 = None
@@ -437,21 +741,47 @@ def run_prefill(args, cfg: int):
     ms_whole = float(np.median(runs[-1]))
     pb = prefill_bytes(T, N, H, HV, d, d, s0=s0 is not None)
     pfl = prefill_flops(T, H, HV, d, d)
-    return {
+    key = f"prefill{cfg}"
+    rec = recorded(PREFILL_COUNTERS, "gdn_prefill_mfma.hip")
+    issued = rec and rec["issued_mfma_flops"].get(key)
+    out = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s (one layer)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w["name"], "sequences": N, "tokens": T,
+        "config": {"workload": w["name"] + ("-at-the-cap" if cap else ""), "sequences": N,
+                   "tokens": T,
                    "lengths": [int(x) for x in lengths], "qk_heads": H, "v_heads": HV,
                    "d_k": d, "d_v": d, "chunk": 64},
-        "roofline": {"kernel": "prefill (chunk_table + prep + scan)", "bound": "hbm",
+        "roofline": {"kernel": "prefill (all kernels of one call)", "bound": "hbm",
                      "achieved": round(pb / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(pb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "tflops": round(pfl / (ms * 1e-3) / 1e12, 2),
-                     "mfma_bf16_frac": round(pfl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
+                     "traffic": rec and rec["traffic_bytes"].get(key),
+                     "algorithmic_bytes": pb, "algorithmic_flops": pfl,
+                     "tflops": round(pfl / (ms * 1e-3) / 1e12, 2),
+                     "mfma_bf16_frac": round(pfl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+                     "issued_mfma_flops": issued,
+                     "issued_mfma_bf16_frac": issued and round(issued / (ms * 1e-3) / 1e12 /
+                                                               BF16_PEAK_TFLOPS, 5)},
         "unsegmented_ms_per_step": round(ms_whole, 4),
     }
+    del q, k, v, g, b, o, sf, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        # a bounded sample of the same workload: its first 4096 tokens (of the
+        # first sequences), all heads, prefill + RMSNormGated
+        sample, left = [], 4096
+        for x in lengths:
+            if left <= 0:
+                break
+            sample.append(int(min(x, left)))
+            left -= sample[-1]
+        v_cpu, secs, thr = cpu_baseline_prefill(sample, H, HV, d, s0_std=w.get("s0_std", 0.0))
+        out["cpu_baseline"] = {"value": round(v_cpu, 1), "unit": "tokens/s (one layer)",
+                               "cores": thr, "kind": "oracle",
+                               "sample": f"sequences of {sample} tokens of the workload, "
+                                         f"prefill + RMSNormGated, fp64, {secs:.1f} s"}
+    return out
 
 
 def run_copy(args):
@@ -792,13 +1122,21 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill2", "prefill3", "prefill4", "prefill5", "copy",
-                             "serve", "attn", "norm", "decode3"])
-    ap.add_argument("--layers", type=int, default=18)
+    ap.add_argument("--workload", default="job35b",
+                    choices=["job35b", "job08b", "decode", "prefill2", "prefill3", "prefill4",
+                             "prefill4cap", "prefill5", "copy", "serve", "attn", "norm",
+                             "decode3"])
+    ap.add_argument("--layers", type=int, default=18,
+                    help="DeltaNet layers of the 0.8B job (and the norm workload)")
+    ap.add_argument("--layer-states", type=int, default=4,
+                    help="layer-states of the 35B-A3B job")
     ap.add_argument("--decode-steps", type=int, default=0)
-    ap.add_argument("--cpu-layers", type=int, default=12)
+    ap.add_argument("--cpu-layers", type=int, default=0,
+                    help="layer-states in the oracle's sample (default: 4 for the 35B-A3B "
+                         "job, 12 for the 0.8B job)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cap", action="store_true",
+                    help="35B-A3B job: skip the varlen-prefill-at-the-cap phase")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -809,7 +1147,11 @@ def main():
         sys.exit(2)
     import gated_delta_rule_decode_amd as gdn
     gdn.lib()  # loud failure without the HIP library
-    if args.workload == "decode":
+    if args.workload == "job35b":
+        args.cpu_layers = args.cpu_layers or 4
+        out = run_job35b(args)
+    elif args.workload in ("job08b", "decode"):
+        args.cpu_layers = args.cpu_layers or 12
         out = run_decode_job(args)
     elif args.workload == "copy":
         out = run_copy(args)
@@ -822,7 +1164,7 @@ def main():
     elif args.workload == "decode3":
         out = run_decode3(args)
     else:
-        out = run_prefill(args, int(args.workload[-1]))
+        out = run_prefill(args, args.workload[len("prefill"):])
     print(json.dumps(out), flush=True)
 
 

@@ -34,7 +34,8 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_version", "gdn_status_string", "gdn_last_hip_error", "gdn_decode_step",
            "gdn_decode_step_norm", "gdn_decode_layer_args_size", "gdn_decode_layer",
-           "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_prefill_chunked_seg",
+           "gdn_prefill_workspace_bytes", "gdn_prefill_workspace_bytes_seg",
+           "gdn_prefill_chunked", "gdn_prefill_chunked_seg",
            "gdn_prefill_norm_workspace_bytes", "gdn_prefill_chunked_norm",
            "gdn_attn_decode_args_size", "gdn_attn_decode_workspace_bytes", "gdn_attn_decode",
            "gdn_rmsnorm_gated")
@@ -121,6 +122,8 @@ def lib() -> ctypes.CDLL:
             raise ImportError("gdn_attn_decode_args layout differs between gdn.h and the binding")
         L.gdn_prefill_workspace_bytes.restype = _sz
         L.gdn_prefill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+        L.gdn_prefill_workspace_bytes_seg.restype = _sz
+        L.gdn_prefill_workspace_bytes_seg.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
         L.gdn_prefill_chunked_seg.restype = _i
         L.gdn_prefill_chunked_seg.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
                                               _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
@@ -342,8 +345,10 @@ def decode_layer(q, k, v, state, *, g=None, beta=None, a_raw=None, b_raw=None, A
 
 
 def prefill_workspace_bytes(N: int, T_total: int, H: int, HV: int, dk: int, dv: int,
-                            chunk: int = 64) -> int:
-    return int(lib().gdn_prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk))
+                            chunk: int = 64, segment_chunks: int = 0) -> int:
+    """Workspace bytes of prefill_chunked with this ``segment_chunks``."""
+    return int(lib().gdn_prefill_workspace_bytes_seg(N, T_total, H, HV, dk, dv, chunk,
+                                                     int(segment_chunks)))
 
 
 def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_state=None,
@@ -382,7 +387,7 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_s
     if o is None:
         o = torch.empty((T, HV, dv), dtype=out_dtype or f32, device=q.device)
     _dev(o, "o")
-    need = prefill_workspace_bytes(N, T, H, HV, dk, dv, chunk)
+    need = prefill_workspace_bytes(N, T, H, HV, dk, dv, chunk, segment_chunks)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace")

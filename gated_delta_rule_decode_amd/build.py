@@ -36,7 +36,7 @@ def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
             "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-munsafe-fp-atomics", "-ffp-contract=fast",
+            "-ffp-contract=fast",
             # MFMA accumulators in ordinary VGPRs: results feed vector code
             # directly, without accumulator-register copies
             "-mllvm", "-amdgpu-mfma-vgpr-form=1"]

@@ -20,6 +20,10 @@ bool valid_dtype(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+bool valid_seg_req(int r) {
+    return r == 0 || r == -1 || r == gdn::kSegAutoSkewed || r >= gdn::kSegMinChunks;
+}
+
 gdn_status heads_status(int H, int HV, int dk, int dv) {
     if (H <= 0 || HV <= 0 || dk <= 0 || dv <= 0) return GDN_ERROR_INVALID_VALUE;
     if (HV % H != 0) return GDN_ERROR_INVALID_VALUE;
@@ -42,7 +46,7 @@ void clear_pending() { (void)hipGetLastError(); }
 
 namespace gdn {
 
-PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv) {
+PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv, bool seg) {
     (void)H;
     PrefillLayout L{};
     // upper bound on sum_n ceil(len_n / 64) given sum_n len_n = T
@@ -67,9 +71,11 @@ PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv) {
     L.ws_Zl = region + 2 * rplane + zplane;
     const size_t mfma_end = region + 2 * rplane + 2 * zplane;
     off = valu_end > mfma_end ? valu_end : mfma_end;
-    // segment-parallel scan: plan, tables and the per-segment states
-    const size_t segb = (size_t)N + (maxc + kSegMinChunks - 1) / kSegMinChunks;
-    const size_t corrb = segb + maxc / kCorrChunks + 1;
+    // segment-parallel scan: plan, tables and the per-segment states.  A call
+    // that cannot segment has one segment per sequence and no correction
+    // items, and never touches E, Phi, S_in or w: they take no space then.
+    const size_t segb = seg ? (size_t)N + (maxc + kSegMinChunks - 1) / kSegMinChunks : (size_t)N;
+    const size_t corrb = seg ? segb + maxc / kCorrChunks + 1 : 1;
     L.seg_bound = (int)segb;
     L.corr_bound = (int)corrb;
     auto take = [&](size_t bytes) {
@@ -87,10 +93,11 @@ PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv) {
     L.multi_seq = take((size_t)N * sizeof(int32_t));
     L.corr_seg = take(corrb * sizeof(int32_t));
     L.corr_c0 = take(corrb * sizeof(int32_t));
-    L.ws_E = take(segb * HV * (size_t)dv * dk * sizeof(float));
-    L.ws_Phi = take(segb * HV * (size_t)dk * dk * sizeof(float));
-    L.ws_Sin = take(segb * HV * (size_t)dv * dk * sizeof(float));
-    L.ws_W = take((size_t)T * HV * dk * sizeof(float));
+    const size_t segs = seg ? segb : 0;
+    L.ws_E = take(segs * HV * (size_t)dv * dk * sizeof(float));
+    L.ws_Phi = take(segs * HV * (size_t)dk * dk * sizeof(float));
+    L.ws_Sin = take(segs * HV * (size_t)dv * dk * sizeof(float));
+    L.ws_W = take(seg ? (size_t)T * HV * dk * sizeof(float) : 0);
     L.total = off;
     return L;
 }
@@ -299,11 +306,19 @@ gdn_status gdn_attn_decode(const gdn_attn_decode_args* p, void* stream) {
     return from_hip(gdn::launch_attn_decode(a));
 }
 
-size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv, int chunk) {
+size_t gdn_prefill_workspace_bytes_seg(int N, int T_total, int H, int HV, int dk, int dv,
+                                       int chunk, int segment_chunks) {
     if (N < 0 || T_total < 0) return 0;
     if (heads_status(H, HV, dk, dv) != GDN_SUCCESS || chunk != gdn::kChunk) return 0;
+    if (!valid_seg_req(segment_chunks)) return 0;
     if (N == 0 || T_total == 0) return 0;
-    return gdn::prefill_layout(N, T_total, H, HV, dk, dv).total;
+    // the size covers bf16 inputs, the only ones that can segment
+    const bool seg = gdn::prefill_may_segment(N, T_total, HV, dk, dv, true, segment_chunks);
+    return gdn::prefill_layout(N, T_total, H, HV, dk, dv, seg).total;
+}
+
+size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv, int chunk) {
+    return gdn_prefill_workspace_bytes_seg(N, T_total, H, HV, dk, dv, chunk, 0);
 }
 
 }  // extern "C"
@@ -321,9 +336,7 @@ gdn_status prefill_setup(const void* q, const void* k, const void* v, gdn_dtype 
                          size_t workspace_need, void* stream, gdn::PrefillArgs& a, bool* done) {
     *done = true;
     if (N < 0 || T_total < 0) return GDN_ERROR_INVALID_VALUE;
-    if (segment_chunks != 0 && segment_chunks != -1 && segment_chunks != gdn::kSegAutoSkewed &&
-        segment_chunks < gdn::kSegMinChunks)
-        return GDN_ERROR_INVALID_VALUE;
+    if (!valid_seg_req(segment_chunks)) return GDN_ERROR_INVALID_VALUE;
     gdn_status st = heads_status(H, HV, dk, dv);
     if (st != GDN_SUCCESS) return st;
     if (chunk != gdn::kChunk) return GDN_ERROR_NOT_SUPPORTED;
@@ -338,11 +351,14 @@ gdn_status prefill_setup(const void* q, const void* k, const void* v, gdn_dtype 
         clear_pending();
         return from_hip(gdn::launch_state_copy(initial_state, final_state, state_elems, s));
     }
-    if (workspace_need == 0) workspace_need = gdn::prefill_layout(N, T_total, H, HV, dk, dv).total;
+    // the layout the query gives for this segment_chunks (the size covers
+    // bf16 inputs; fp32 inputs never segment and use a prefix of it)
+    const bool seg = gdn::prefill_may_segment(N, T_total, HV, dk, dv, true, segment_chunks);
+    const gdn::PrefillLayout L = gdn::prefill_layout(N, T_total, H, HV, dk, dv, seg);
+    if (workspace_need == 0) workspace_need = L.total;
     if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return GDN_ERROR_INVALID_VALUE;
-    const gdn::PrefillLayout L = gdn::prefill_layout(N, T_total, H, HV, dk, dv);
     if ((size_t)L.max_chunks * HV > (size_t)(1u << 31) / (gdn::kChunk * gdn::kChunk))
         return GDN_ERROR_NOT_SUPPORTED;
     if (!workspace || workspace_bytes < workspace_need) return GDN_ERROR_WORKSPACE;

@@ -77,7 +77,8 @@ __device__ __forceinline__ float ld_any(const void* p, size_t i, bool bf16) {
 }
 
 // Element i of an fp32 or bf16 array with one 4-byte load and no branch: the
-// aligned dword that holds the element (in bounds for arrays of even length).
+// aligned dword that holds the element (in bounds for arrays of even length;
+// z and w have dv, an even count, per row).
 __device__ __forceinline__ float ld_any_nb(const void* p, size_t i, bool bf16) {
     const size_t byte = bf16 ? i * 2 : i * 4;
     const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(p) + (byte & ~size_t(3)));
@@ -87,7 +88,9 @@ __device__ __forceinline__ float ld_any_nb(const void* p, size_t i, bool bf16) {
 
 // Per-head scalars (uniform over the workgroup, never written by the kernel):
 // read through the constant address space so they come in by scalar loads,
-// which the vector-memory counter does not wait for.
+// which the vector-memory counter does not wait for.  ld_uniform_any reads the
+// aligned dword holding the element, like ld_any_nb: callers keep the last
+// element of an odd-length bf16 array off it.
 typedef const __attribute__((address_space(4))) float cfloat_t;
 typedef const __attribute__((address_space(4))) uint32_t cu32_t;
 __device__ __forceinline__ float ld_uniform(const float* p, size_t i) {
@@ -175,9 +178,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecodeArgs A) {
             wmine = ld_any_nb(A.w, (size_t)lr + (owner ? lc : 0) * RPP, A.w_bf16);
         }
         if (EXT && A.a_raw) {
-            graw = ld_uniform_any(A.a_raw, nh, A.gate_bf16) +
-                   (A.dt_bias ? ld_uniform(A.dt_bias, h) : 0.f);
-            braw = ld_uniform_any(A.b_raw, nh, A.gate_bf16);
+            // the dword holding a bf16 gate reaches past an array of odd length
+            // at its last element: that element takes a 16-bit load instead
+            const size_t ngate = (size_t)A.N * HV;
+            if (A.gate_bf16 && (ngate & 1) && (size_t)nh + 1 == ngate) {
+                graw = ld_any<float>(A.a_raw, nh, true);
+                braw = ld_any<float>(A.b_raw, nh, true);
+            } else {
+                graw = ld_uniform_any(A.a_raw, nh, A.gate_bf16);
+                braw = ld_uniform_any(A.b_raw, nh, A.gate_bf16);
+            }
+            graw += A.dt_bias ? ld_uniform(A.dt_bias, h) : 0.f;
         } else {
             graw = ld_uniform(A.g, nh);
             braw = ld_uniform(A.beta, nh);

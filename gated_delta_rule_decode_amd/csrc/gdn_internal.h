@@ -127,7 +127,13 @@ struct PrefillLayout {
     size_t total;
     int max_chunks, seg_bound, corr_bound;
 };
-PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv);
+// seg: reserve the segment-parallel scan's tables and buffers (only when
+// prefill_may_segment says the call can segment)
+PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv, bool seg);
+// Whether a prefill call of this shape can take the segment-parallel scan
+// (the bf16 MFMA path with segments forced, or allowed and useful by the
+// host's rule); the device plan then decides from the lengths.
+bool prefill_may_segment(int N, int T, int HV, int dk, int dv, bool in_bf16, int seg_req);
 // true when launch_prefill, given nz (and ws_o), writes the normed outputs
 // itself (the per-chain scan, and with segments the correction pass);
 // otherwise nz must be null and the norm runs as its own launch

@@ -1942,6 +1942,12 @@ bool prefill_mfma_eligible(const PrefillArgs& A) {
     return A.in_bf16 && (A.dk == 64 || A.dk == 128) && (A.dv % 32 == 0);
 }
 
+bool prefill_may_segment(int N, int T, int HV, int dk, int dv, bool in_bf16, int seg_req) {
+    PrefillArgs A{};
+    A.N = N; A.T = T; A.HV = HV; A.dk = dk; A.dv = dv; A.in_bf16 = in_bf16; A.seg_req = seg_req;
+    return prefill_mfma_eligible(A) && may_segment(A, dk);
+}
+
 bool prefill_fuses_norm(const PrefillArgs& A) {
     // with segments the later segments' raw outputs pass through the output
     // type: fused then only for fp32 outputs

@@ -311,6 +311,12 @@ def config_lengths(seed: int = 0, stream: int = 400, n: int = 8, lo: int = 256,
             return L
 
 
+# Workload 4 at its largest size: 131,072 tokens in 8 sequences, the longest at
+# the 65,536-token maximum and the shortest at the 256-token minimum of the
+# length draw (a packing the draw allows at its cap).
+CAP_LENGTHS = (65536, 256, 30000, 12000, 9000, 8000, 5000, 1280)
+
+
 # workload table: shapes only; the tests and the benchmark build the tensors
 WORKLOADS = {
     0: dict(name="tiny-step-d16", N=1, T=64, H=1, HV=1, dk=16, dv=16, dtype="f32",

@@ -183,10 +183,25 @@ gdn_status gdn_decode_layer(const gdn_decode_layer_args* args, void* stream);
 /*
  * gdn_prefill_workspace_bytes -- device workspace that gdn_prefill_chunked
  * needs for this problem (a multiple of 256 bytes; 0 when T_total == 0).
- * Returns 0 for sizes that gdn_prefill_chunked would reject.
+ * Returns 0 for sizes that gdn_prefill_chunked would reject.  The size holds
+ * the segment-parallel scan's buffers (per segment two d_v x d_k and one
+ * d_k x d_k fp32 matrix per value head, and d_k fp32 per token and value
+ * head) only when the call can segment: bf16 inputs with d_k in {64, 128},
+ * sequences longer than 32 chunks, and (sequence, value head) chains that
+ * leave the GPU's compute units idle.
  */
 size_t gdn_prefill_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv,
                                    int chunk);
+
+/*
+ * gdn_prefill_workspace_bytes_seg -- the workspace of gdn_prefill_chunked_seg
+ * with this segment_chunks (0: the same as gdn_prefill_workspace_bytes; -1:
+ * no segment buffers; -2 or a forced length: the buffers whenever a sequence
+ * may be longer than one segment).  Returns 0 for sizes or a segment_chunks
+ * the call would reject.
+ */
+size_t gdn_prefill_workspace_bytes_seg(int N, int T_total, int H, int HV, int dk, int dv,
+                                       int chunk, int segment_chunks);
 
 /*
  * gdn_prefill_chunked -- a whole packed batch of prompts in the chunked
@@ -237,7 +252,9 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, gdn_
  *                      when it decides against segments)
  *                   -1: never segment
  *                  >= 32: segments of this many chunks (64 tokens each)
- *   every other argument as gdn_prefill_chunked (same workspace size).
+ *   workspace      at least gdn_prefill_workspace_bytes_seg(..., segment_chunks)
+ *                  bytes, 256-byte aligned
+ *   every other argument as gdn_prefill_chunked.
  * Applies to the bf16-MFMA path (bf16 inputs, d_k in {64, 128}, d_v a
  * multiple of 32); other shapes ignore it.  Other values of segment_chunks
  * return GDN_ERROR_INVALID_VALUE.

@@ -105,27 +105,70 @@ def test_prefill_validation(L):
         assert seg(ok) == 3                           # passes that check, fails on the workspace
 
 
+def _may_segment(N, T, HV, dk, dv, seg_req):
+    """The host's rule for whether a bf16 call can take the segment-parallel
+    scan (the per-chain scan at d = 128 with many chains or long prompts on
+    few; segments when forced, or when the chains leave CUs idle)."""
+    if dk not in (64, 128) or dv % 32:
+        return False
+    rows = dk == 128 and dv == 128 and (N * HV >= 512 or (seg_req != -1 and N * HV < 256
+                                                           and T >= 16384 * N))
+    TV = 1 if rows else dv // 32
+    longer = (T + 63) // 64 > 32
+    return seg_req > 0 or (seg_req == -2 and longer) or (seg_req == 0 and longer
+                                                          and N * HV * TV < 256)
+
+
+def _want_bytes(N, T, HV, dk, dv, seg):
+    al = lambda x: (x + 255) // 256 * 256
+    maxc = (T + N * 63) // 64
+    head = al(4 * (N + 1)) + al(maxc * HV * 64 * 4)
+    valu = al(maxc * HV * 64 * 64 * 4)
+    mfma = 2 * al(maxc * HV * 64 * 64 * 2) + 2 * al(maxc * HV * dk * 64 * 2)
+    segb = N + (maxc + 31) // 32 if seg else N
+    corrb = segb + maxc // 4 + 1 if seg else 1
+    segs = segb if seg else 0
+    tail = (al(8 * 4) + 4 * al(segb * 4) + 3 * al(N * 4) + 2 * al(corrb * 4)
+            + 2 * al(segs * HV * dv * dk * 4) + al(segs * HV * dk * dk * 4)
+            + al((T if seg else 0) * HV * dk * 4))
+    return head + max(valu, mfma) + tail
+
+
 def test_prefill_workspace_bytes(L):
     f = gdn.prefill_workspace_bytes
     assert f(0, 100, 2, 4, 128, 128) == 0
     assert f(2, 0, 2, 4, 128, 128) == 0
     assert f(2, 100, 2, 4, 128, 128, 32) == 0
     assert f(2, 100, 2, 4, 96, 128) == 0
-    al = lambda x: (x + 255) // 256 * 256
-    for N, T, H, HV, dk in ((1, 1, 1, 1, 16), (4, 16384, 16, 16, 128), (8, 131072, 16, 32, 128),
-                            (3, 65, 2, 2, 64)):
-        maxc = (T + N * 63) // 64
-        head = al(4 * (N + 1)) + al(maxc * HV * 64 * 4)
-        valu = al(maxc * HV * 64 * 64 * 4)
-        mfma = 2 * al(maxc * HV * 64 * 64 * 2) + 2 * al(maxc * HV * dk * 64 * 2)
-        segb = N + (maxc + 31) // 32
-        corrb = segb + maxc // 4 + 1
-        seg = (al(8 * 4) + 4 * al(segb * 4) + 3 * al(N * 4) + 2 * al(corrb * 4)
-               + 2 * al(segb * HV * 128 * dk * 4) + al(segb * HV * dk * dk * 4)
-               + al(T * HV * dk * 4))
-        want = head + max(valu, mfma) + seg
-        assert f(N, T, H, HV, dk, 128) == want
-        assert f(N, T, H, HV, dk, 128) % 256 == 0
+    assert f(2, 100, 2, 4, 128, 128, segment_chunks=5) == 0   # a length the call rejects
+    for N, T, H, HV, dk, dv in ((1, 1, 1, 1, 16, 16), (4, 16384, 16, 16, 128, 128),
+                                (8, 131072, 16, 32, 128, 128), (3, 65, 2, 2, 64, 128),
+                                (1, 32768, 16, 16, 128, 128), (2, 8192, 16, 32, 128, 128),
+                                (1, 6000, 1, 2, 128, 64)):
+        for req in (0, -1, -2, 32):
+            seg = _may_segment(N, T, HV, dk, dv, req)
+            got = f(N, T, H, HV, dk, dv, segment_chunks=req)
+            assert got == _want_bytes(N, T, HV, dk, dv, seg), (N, T, HV, dk, dv, req)
+            assert got % 256 == 0
+        assert f(N, T, H, HV, dk, dv) == L.gdn_prefill_workspace_bytes(N, T, H, HV, dk, dv, 64)
+    # one long prompt on few chains segments by default; a batch that fills the GPU does not
+    assert _may_segment(1, 32768, 16, 128, 128, 0)
+    assert not _may_segment(8, 131072, 32, 128, 128, 0)
+
+
+def test_prefill_workspace_without_segments_at_the_token_cap():
+    """At the long-context varlen cap (8 sequences, 131,072 tokens, 32 value
+    heads) the default call cannot segment (its 1024 per-tile chains fill the
+    GPU): its workspace holds no segment buffers and is over 2 GB smaller than
+    a call with forced segments."""
+    args = (8, 131072, 16, 32, 128, 128)
+    auto = gdn.prefill_workspace_bytes(*args)
+    forced = gdn.prefill_workspace_bytes(*args, segment_chunks=32)
+    off = gdn.prefill_workspace_bytes(*args, segment_chunks=-1)
+    print(f"workspace at the cap: default {auto / 2**30:.2f} GiB, forced segments "
+          f"{forced / 2**30:.2f} GiB")
+    assert auto == off
+    assert forced - auto >= 2 * 10 ** 9
 
 
 def _prefill_norm(L, **kw):

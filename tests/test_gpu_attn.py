@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import gdn_inputs as gi
-from gpu_helpers import dev, host, rel_l2, say
+from gpu_helpers import dev, head_errors, host, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -127,6 +127,8 @@ def test_attn_full_size_35b(orc):
     err = rel_l2(host(o), o_ref)
     print(f"[parity] attn full size: o rel-L2 {err:.3e}")
     assert err <= O_TOL
+    # per (row, query head): o is one step of N rows
+    head_errors(host(o)[None], np.asarray(o_ref)[None]).check(what="attn full size")
 
 
 def test_attn_long_single_row(orc):

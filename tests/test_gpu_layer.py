@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import gdn_inputs as gi
-from gpu_helpers import assert_parity, dev, host, rel_l2, say, torch_dtype
+from gpu_helpers import assert_parity, dev, head_errors, host, rel_l2, say, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -176,6 +176,27 @@ def test_layer_full_size_gva(orc):
     assert_parity(host(o), host(pool), o_ref, pool_ref, what="layer full size")
     err = rel_l2(host(y), y_ref)
     print(f"[parity] layer full size y: rel-L2 {err:.3e}")
+    assert err <= 2e-3
+    head_errors(host(y), y_ref).check(what="layer full size y")
+
+
+def test_layer_bf16_gates_odd_count(orc):
+    """bf16 raw gates whose count N HV is odd, on the streamed schedule (1025
+    rows of one head: 1025 workgroups).  The last row's gates come in by a
+    16-bit load, since the dword holding them would reach past the array;
+    every row, the last included, against the oracle."""
+    N = 1025
+    d = gi.make_decode_raw(2, N, 1, 1, 128, 128, seed=78, gate_dtype="bf16")
+    S0 = (np.random.default_rng(78).standard_normal((N, 1, 128, 128)) * 0.02).astype(np.float32)
+    say("layer bf16 gates, odd count 1025 x 1 head (streamed)")
+    o, S, y = _gpu_chain(d, S0, None, scale=128 ** -0.5, l2norm=True, norm=True)
+    o_ref, S_ref = _oracle_chain(orc, d, S0, None, scale=128 ** -0.5, l2norm=True)
+    y_ref = orc.rmsnorm_gated(o_ref, d.z, d.w)
+    assert_parity(host(o), host(S), o_ref, S_ref, what="layer bf16 gates odd count")
+    oh = host(o)
+    assert rel_l2(oh[:, N - 1], o_ref[:, N - 1]) <= 1e-3  # the last row on its own
+    err = rel_l2(host(y), y_ref)
+    print(f"[parity] layer bf16 gates odd count y: rel-L2 {err:.3e}")
     assert err <= 2e-3
 
 

@@ -20,15 +20,16 @@ def test_prefill_varlen_at_the_token_cap(orc):
     shortest at the 256-token minimum, 16 key / 32 value heads, S0 ~ N(0, 0.02);
     the library's own choice of scan.  Compared sequence by sequence, so the
     fp64 outputs are never held whole."""
-    from gpu_helpers import O_REL_L2, S_MAX_ABS
-    lengths = [65536, 256, 30000, 12000, 9000, 8000, 5000, 1280]
-    assert sum(lengths) == 131072
+    from gpu_helpers import O_REL_L2, S_MAX_ABS, HeadErrors
+    lengths = list(gi.CAP_LENGTHS)
+    assert sum(lengths) == 131072 and max(lengths) == 65536 and min(lengths) == 256
     x = gi.make_prefill(lengths, 16, 32, 128, 128, s0_std=0.02, seed=131)
     say(f"prefill varlen at the token cap: lengths={lengths}")
     o, S = gpu_prefill(x)
     Sh = host(S)
     num = den = 0.0
     worst = 0.0
+    heads = HeadErrors()
     cu = x.cu_seqlens
     for n in range(x.N):
         a, e = int(cu[n]), int(cu[n + 1])
@@ -38,10 +39,13 @@ def test_prefill_varlen_at_the_token_cap(orc):
         num += float(np.sum((og - o_ref) ** 2))
         den += float(np.sum(o_ref ** 2))
         worst = max(worst, float(np.max(np.abs(Sh[n] - S_ref[0]))))
+        heads.outputs(og, o_ref, seq_offset=n)
+        heads.state(Sh[n:n + 1], S_ref, seq_offset=n)
         del o_ref, og
     ro = (num / den) ** 0.5
     print(f"[parity] token cap: o rel-L2 {ro:.3e}, state max-abs {worst:.3e}", flush=True)
     assert ro <= O_REL_L2 and worst <= S_MAX_ABS
+    heads.check(what="token cap")
 
 
 def test_prefill_tiny_d16_fp32(orc):
@@ -49,7 +53,8 @@ def test_prefill_tiny_d16_fp32(orc):
     say("prefill tiny d=16 fp32")
     o, S = gpu_prefill(x)
     o_ref, S_ref = oracle_prefill(orc, x)
-    assert_parity(host(o), host(S), o_ref, S_ref, f32=True, what="prefill workload 0")
+    assert_parity(host(o), host(S), o_ref, S_ref, f32=True, what="prefill workload 0",
+                  cu=x.cu_seqlens)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4])
@@ -58,7 +63,7 @@ def test_prefill_full_workload(orc, cfg):
     say(f"prefill workload {cfg}: N={x.N} T={x.T} H={x.H} HV={x.HV} lengths={list(x.lengths)}")
     o, S = gpu_prefill(x)
     o_ref, S_ref = oracle_prefill(orc, x)
-    assert_parity(host(o), host(S), o_ref, S_ref, what=f"prefill workload {cfg}")
+    assert_parity(host(o), host(S), o_ref, S_ref, what=f"prefill workload {cfg}", cu=x.cu_seqlens)
 
 
 @pytest.mark.parametrize("scale", [1.0, 128 ** -0.5])
@@ -68,7 +73,7 @@ def test_prefill_ragged_and_empty(orc, scale):
     say(f"prefill ragged lengths={lengths} scale={scale}")
     o, S = gpu_prefill(x, scale=scale)
     o_ref, S_ref = oracle_prefill(orc, x, scale=scale)
-    assert_parity(host(o), host(S), o_ref, S_ref, what="ragged/empty")
+    assert_parity(host(o), host(S), o_ref, S_ref, what="ragged/empty", cu=x.cu_seqlens)
     # empty sequences return their initial state exactly
     Sh = S.cpu().numpy()
     assert np.array_equal(Sh[0], x.s0[0]) and np.array_equal(Sh[6], x.s0[6])
@@ -83,7 +88,7 @@ def test_prefill_head_sizes(orc, dk, dv, dtype):
     o, S = gpu_prefill(x, scale=dk ** -0.5)
     o_ref, S_ref = oracle_prefill(orc, x, scale=dk ** -0.5)
     assert_parity(host(o), host(S), o_ref, S_ref, f32=(dtype == "f32"),
-                  what=f"dk={dk} dv={dv} {dtype}")
+                  what=f"dk={dk} dv={dv} {dtype}", cu=x.cu_seqlens)
 
 
 def test_prefill_mild_decay_long_memory(orc):
@@ -93,7 +98,7 @@ def test_prefill_mild_decay_long_memory(orc):
     say("prefill mild decay")
     o, S = gpu_prefill(x, scale=128 ** -0.5)
     o_ref, S_ref = oracle_prefill(orc, x, scale=128 ** -0.5)
-    assert_parity(host(o), host(S), o_ref, S_ref, what="mild decay")
+    assert_parity(host(o), host(S), o_ref, S_ref, what="mild decay", cu=x.cu_seqlens)
 
 
 def test_prefill_gva_equals_repeated_heads():
@@ -138,8 +143,8 @@ def test_prefill_split_equals_whole(orc):
     o2, S2 = gpu_prefill(part(cut, 300, None), s0=S1)
     o_ref, S_ref = oracle_prefill(orc, x)
     o_split = np.concatenate([host(o1), host(o2)])
-    assert_parity(o_split, host(S2), o_ref, S_ref, what="split prefill")
-    assert_parity(host(o_all), host(S_all), o_ref, S_ref, what="whole prefill")
+    assert_parity(o_split, host(S2), o_ref, S_ref, what="split prefill", cu=x.cu_seqlens)
+    assert_parity(host(o_all), host(S_all), o_ref, S_ref, what="whole prefill", cu=x.cu_seqlens)
 
 
 def test_prefill_final_state_may_alias_initial():
@@ -214,14 +219,16 @@ def test_prefill_zero_tokens_copies_state():
 
 @pytest.mark.parametrize("ratio", [1, 4, 8])
 def test_prefill_value_heads_per_key_head(orc, ratio):
-    """GVA ratios up to 4 run the MFMA kernels (G, R and Z^T per value head of
-    a key head); 8 exercises the vector-unit path that larger ratios use."""
+    """1, 4 and 8 value heads per key head on the MFMA kernels, which take any
+    ratio (K K^T and Q K^T are formed again for every value head of a key
+    head)."""
     x = gi.make_prefill([130, 70, 1], 1, ratio, 128, 128, dtype="bf16", s0_std=0.05,
                         seed=40 + ratio)
     say(f"prefill value heads per key head = {ratio}")
     o, S = gpu_prefill(x)
     o_ref, S_ref = oracle_prefill(orc, x)
-    assert_parity(host(o), host(S), o_ref, S_ref, what=f"value heads per key head {ratio}")
+    assert_parity(host(o), host(S), o_ref, S_ref, what=f"value heads per key head {ratio}",
+                  cu=x.cu_seqlens)
 
 
 def _lengths_many(seed, n, hi):
@@ -240,7 +247,8 @@ def test_prefill_many_chains_matches_oracle(orc, H, HV, N):
     say(f"prefill many chains: N={N} H={H} HV={HV} T={sum(lengths)}")
     o, S = gpu_prefill(x, scale=128 ** -0.5)
     o_ref, S_ref = oracle_prefill(orc, x, scale=128 ** -0.5)
-    assert_parity(host(o), host(S), o_ref, S_ref, what=f"many chains H={H} HV={HV}")
+    assert_parity(host(o), host(S), o_ref, S_ref, what=f"many chains H={H} HV={HV}",
+                  cu=x.cu_seqlens)
 
 
 def test_prefill_many_chains_equals_per_tile_form():
@@ -271,4 +279,4 @@ def test_prefill_many_chains_forced_segments(orc):
     say(f"prefill many chains, segments of 32 chunks: T={sum(lengths)}")
     o, S = gpu_prefill(x, scale=128 ** -0.5, segment_chunks=32)
     o_ref, S_ref = oracle_prefill(orc, x, scale=128 ** -0.5)
-    assert_parity(host(o), host(S), o_ref, S_ref, what="many chains, segmented")
+    assert_parity(host(o), host(S), o_ref, S_ref, what="many chains, segmented", cu=x.cu_seqlens)

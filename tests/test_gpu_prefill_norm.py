@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 import gdn_inputs as gi
-from gpu_helpers import (O_REL_L2, S_MAX_ABS, dev, gpu_prefill, host, max_abs, oracle_prefill,
-                         rel_l2, say, torch_dtype)
+from gpu_helpers import (O_REL_L2, S_MAX_ABS, dev, gpu_prefill, head_errors, host, max_abs,
+                         oracle_prefill, rel_l2, say, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,7 @@ def test_prefill_norm_fused_matches_oracle(orc, kind, H, HV, N, zd, wd, yd):
     print(f"[parity] prefill+norm: y rel-L2 {ry:.3e} (<= {tol_y:.0e}), state max-abs {ms:.3e}",
           flush=True)
     assert ry <= tol_y and ms <= S_MAX_ABS
+    head_errors(host(y), y_ref, host(S), S_ref, cu=x.cu_seqlens).check(what="prefill+norm y")
 
 
 @pytest.mark.parametrize("kind", ["many", "long"])

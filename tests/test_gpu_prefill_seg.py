@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 
 import gdn_inputs as gi
-from gpu_helpers import (O_REL_L2, S_MAX_ABS, assert_parity, gpu_prefill, host, oracle_prefill,
-                         rel_l2, say)
+from gpu_helpers import (O_REL_L2, S_MAX_ABS, HeadErrors, assert_parity, gpu_prefill, host,
+                         oracle_prefill, rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def test_forced_segments_match_oracle(orc, lengths, H, HV, dk, dv, with_s0):
     say(f"prefill segments of 32 chunks: lengths={lengths} H={H} HV={HV} dk={dk} dv={dv} s0={with_s0}")
     o, S = gpu_prefill(x, scale=dk ** -0.5, segment_chunks=32)
     o_ref, S_ref = oracle_prefill(orc, x, scale=dk ** -0.5)
-    assert_parity(host(o), host(S), o_ref, S_ref, what=f"segmented {lengths}")
+    assert_parity(host(o), host(S), o_ref, S_ref, what=f"segmented {lengths}", cu=x.cu_seqlens)
 
 
 def test_segmented_equals_whole_scan(orc):
@@ -74,7 +74,7 @@ def test_segmented_final_state_may_alias_initial(orc):
     o, _ = gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=S, final_state=S,
                                segment_chunks=32)
     o_ref, S_ref = oracle_prefill(orc, x)
-    assert_parity(host(o), host(S), o_ref, S_ref, what="segmented in place")
+    assert_parity(host(o), host(S), o_ref, S_ref, what="segmented in place", cu=x.cu_seqlens)
 
 
 def test_long_prompt_automatic(orc):
@@ -84,7 +84,7 @@ def test_long_prompt_automatic(orc):
     say("prefill one 32768-token prompt, automatic segmentation")
     o, S = gpu_prefill(x, scale=128 ** -0.5)
     o_ref, S_ref = oracle_prefill(orc, x, scale=128 ** -0.5)
-    assert_parity(host(o), host(S), o_ref, S_ref, what="long prompt automatic")
+    assert_parity(host(o), host(S), o_ref, S_ref, what="long prompt automatic", cu=x.cu_seqlens)
 
 
 def _long_memory(x):
@@ -110,7 +110,8 @@ def test_long_memory_segments_match_oracle(orc, lengths, H, HV, dk, dv):
     say(f"prefill long memory, segments of 32 chunks: lengths={lengths} dk={dk} dv={dv}")
     o, S = gpu_prefill(x, scale=dk ** -0.5, segment_chunks=32)
     o_ref, S_ref = oracle_prefill(orc, x, scale=dk ** -0.5)
-    assert_parity(host(o), host(S), o_ref, S_ref, what=f"long memory segmented {lengths}")
+    assert_parity(host(o), host(S), o_ref, S_ref, what=f"long memory segmented {lengths}",
+                  cu=x.cu_seqlens)
     o2, S2 = gpu_prefill(x, scale=dk ** -0.5, segment_chunks=-1)
     r = rel_l2(host(o), host(o2))
     d = float(np.max(np.abs(host(S) - host(S2))))
@@ -136,8 +137,9 @@ def test_prefill_graph_replay_matches_eager(segment_chunks):
     T, N = int(x.cu_seqlens[-1]), len(x.cu_seqlens) - 1
     o = torch.empty(T, 4, 128, device="cuda")
     sf = torch.empty(N, 4, 128, 128, device="cuda")
-    ws = torch.empty(gdn.prefill_workspace_bytes(N, T, 2, 4, 128, 128), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(gdn.prefill_workspace_bytes(N, T, 2, 4, 128, 128,
+                                                 segment_chunks=segment_chunks),
+                     dtype=torch.uint8, device="cuda")
 
     def run():
         gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf, o=o,
@@ -176,6 +178,7 @@ def test_skewed_batch_automatic(orc, mode):
     o, S = gpu_prefill(x, segment_chunks=mode)
     Sh = host(S)
     num = den = worst = 0.0
+    heads = HeadErrors()
     cu = x.cu_seqlens
     for n in range(x.N):
         a, e = int(cu[n]), int(cu[n + 1])
@@ -185,6 +188,9 @@ def test_skewed_batch_automatic(orc, mode):
         num += float(np.sum((og - o_ref) ** 2))
         den += float(np.sum(o_ref ** 2))
         worst = max(worst, float(np.max(np.abs(Sh[n] - S_ref[0]))))
+        heads.outputs(og, o_ref, seq_offset=n)
+        heads.state(Sh[n:n + 1], S_ref, seq_offset=n)
     ro = (num / den) ** 0.5
     print(f"[parity] skewed batch: o rel-L2 {ro:.3e}, state max-abs {worst:.3e}", flush=True)
+    heads.check(what=f"skewed batch mode {mode}")
     assert ro <= O_REL_L2 and worst <= S_MAX_ABS
