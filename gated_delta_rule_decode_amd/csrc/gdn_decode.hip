@@ -88,19 +88,27 @@ __device__ __forceinline__ float ld_any_nb(const void* p, size_t i, bool bf16) {
 
 // Per-head scalars (uniform over the workgroup, never written by the kernel):
 // read through the constant address space so they come in by scalar loads,
-// which the vector-memory counter does not wait for.  ld_uniform_any reads the
-// aligned dword holding the element, like ld_any_nb: callers keep the last
-// element of an odd-length bf16 array off it.
+// which the vector-memory counter does not wait for.
 typedef const __attribute__((address_space(4))) float cfloat_t;
 typedef const __attribute__((address_space(4))) uint32_t cu32_t;
 __device__ __forceinline__ float ld_uniform(const float* p, size_t i) {
     return ((cfloat_t*)(uintptr_t)p)[i];
 }
-__device__ __forceinline__ float ld_uniform_any(const void* p, size_t i, bool bf16) {
-    const size_t byte = bf16 ? i * 2 : i * 4;
-    const uint32_t w = *(cu32_t*)((uintptr_t)p + (byte & ~size_t(3)));
-    const uint32_t hi = (byte & 2) ? (w & 0xffff0000u) : (w << 16);
-    return __uint_as_float(bf16 ? hi : w);
+// Element i of an element-aligned fp32 or bf16 array of n elements.  A bf16
+// element comes from a scalar load of the dword that holds it, its half chosen
+// by the element's address (a bf16 array need only be 2-byte aligned, e.g. a
+// per-step slice of an odd-length buffer), when that dword lies inside the
+// array; the first or last element of an array whose ends are not
+// dword-aligned takes a 16-bit vector load instead.
+__device__ __forceinline__ float ld_gate(const void* p, size_t i, size_t n, bool bf16) {
+    if (!bf16) return ld_uniform(static_cast<const float*>(p), i);
+    const uintptr_t base = (uintptr_t)p, a = base + 2 * i;
+    const uintptr_t a4 = a & ~(uintptr_t)3;
+    if (a4 >= base && a4 + 4 <= base + 2 * n) {
+        const uint32_t w = *(cu32_t*)a4;
+        return __uint_as_float((a & 2) ? (w & 0xffff0000u) : (w << 16));
+    }
+    return bf16_to_f32(static_cast<const bf16_t*>(p)[i]);
 }
 template <typename T>
 __device__ __forceinline__ void st_any(void* p, size_t i, float v, bool bf16) {
@@ -178,17 +186,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecodeArgs A) {
             wmine = ld_any_nb(A.w, (size_t)lr + (owner ? lc : 0) * RPP, A.w_bf16);
         }
         if (EXT && A.a_raw) {
-            // the dword holding a bf16 gate reaches past an array of odd length
-            // at its last element: that element takes a 16-bit load instead
             const size_t ngate = (size_t)A.N * HV;
-            if (A.gate_bf16 && (ngate & 1) && (size_t)nh + 1 == ngate) {
-                graw = ld_any<float>(A.a_raw, nh, true);
-                braw = ld_any<float>(A.b_raw, nh, true);
-            } else {
-                graw = ld_uniform_any(A.a_raw, nh, A.gate_bf16);
-                braw = ld_uniform_any(A.b_raw, nh, A.gate_bf16);
-            }
-            graw += A.dt_bias ? ld_uniform(A.dt_bias, h) : 0.f;
+            graw = ld_gate(A.a_raw, nh, ngate, A.gate_bf16) +
+                   (A.dt_bias ? ld_uniform(A.dt_bias, h) : 0.f);
+            braw = ld_gate(A.b_raw, nh, ngate, A.gate_bf16);
         } else {
             graw = ld_uniform(A.g, nh);
             braw = ld_uniform(A.beta, nh);

@@ -182,9 +182,12 @@ def test_layer_full_size_gva(orc):
 
 def test_layer_bf16_gates_odd_count(orc):
     """bf16 raw gates whose count N HV is odd, on the streamed schedule (1025
-    rows of one head: 1025 workgroups).  The last row's gates come in by a
-    16-bit load, since the dword holding them would reach past the array;
-    every row, the last included, against the oracle."""
+    rows of one head: 1025 workgroups), over two steps.  The first step's
+    gates start dword-aligned, and the dword holding the last one would reach
+    past the array; the second step's are a slice that starts 2 bytes into a
+    dword (2050 bytes into the buffer), so every row's gate sits in the other
+    half of its dword and the first row's dword would start before the array.
+    Every row of both steps against the oracle."""
     N = 1025
     d = gi.make_decode_raw(2, N, 1, 1, 128, 128, seed=78, gate_dtype="bf16")
     S0 = (np.random.default_rng(78).standard_normal((N, 1, 128, 128)) * 0.02).astype(np.float32)
@@ -194,7 +197,8 @@ def test_layer_bf16_gates_odd_count(orc):
     y_ref = orc.rmsnorm_gated(o_ref, d.z, d.w)
     assert_parity(host(o), host(S), o_ref, S_ref, what="layer bf16 gates odd count")
     oh = host(o)
-    assert rel_l2(oh[:, N - 1], o_ref[:, N - 1]) <= 1e-3  # the last row on its own
+    for t in range(d.steps):  # the first and last rows on their own
+        assert rel_l2(oh[t, 0], o_ref[t, 0]) <= 1e-3 and rel_l2(oh[t, N - 1], o_ref[t, N - 1]) <= 1e-3
     err = rel_l2(host(y), y_ref)
     print(f"[parity] layer bf16 gates odd count y: rel-L2 {err:.3e}")
     assert err <= 2e-3
