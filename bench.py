@@ -86,8 +86,8 @@ ATTN_TRAFFIC = {"kernel_source_sha256": "307e9311a1db99216f64ad4f2a186d5037925cb
                 "bytes_per_launch": 2185084533}
 # The fused decode at the 35B-A3B shape, batch 128 (gdn_decode.hip;
 # profiles/decode_traffic_35b.md)
-DECODE3_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
-                   "bytes_per_launch": 543840264}
+DECODE3_TRAFFIC = {"kernel_source_sha256": "1c35490b31acb0404bf63d73b3ebbd29605982bfb3ae7ed5fbe19560722a3b0d",
+                   "bytes_per_launch": 543826905}
 # RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
 # profiles/rmsnorm_gated_traffic.md)
 NORM_TRAFFIC = {"kernel_source_sha256": "8014073d5bbde2fe478883ec30d9322ab0c7f7757ad23136244750031bf4a1ce",
