@@ -35,7 +35,7 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 EXPORTS = ("gdn_version", "gdn_status_string", "gdn_last_hip_error", "gdn_decode_step",
            "gdn_decode_step_norm", "gdn_decode_layer_args_size", "gdn_decode_layer",
            "gdn_prefill_workspace_bytes", "gdn_prefill_workspace_bytes_seg",
-           "gdn_prefill_chunked", "gdn_prefill_chunked_seg",
+           "gdn_prefill_chunked", "gdn_prefill_chunked_seg", "gdn_prefill_chunked_noalloc",
            "gdn_prefill_norm_workspace_bytes", "gdn_prefill_chunked_norm",
            "gdn_attn_decode_args_size", "gdn_attn_decode_workspace_bytes", "gdn_attn_decode",
            "gdn_rmsnorm_gated")
@@ -130,6 +130,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill_chunked.restype = _i
         L.gdn_prefill_chunked.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _vp,
                                           _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]
+        L.gdn_prefill_chunked_noalloc.restype = _i
+        L.gdn_prefill_chunked_noalloc.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp,
+                                                  _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp]
         L.gdn_prefill_norm_workspace_bytes.restype = _sz
         L.gdn_prefill_norm_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
         L.gdn_prefill_chunked_norm.restype = _i

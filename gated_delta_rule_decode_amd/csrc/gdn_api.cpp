@@ -449,6 +449,29 @@ gdn_status gdn_prefill_chunked_seg(const void* q, const void* k, const void* v,
                         workspace, workspace_bytes, stream);
 }
 
+gdn_status gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       gdn_dtype in_dtype, const float* g, const float* beta,
+                                       const int32_t* cu_seqlens, int N, int T_total,
+                                       const float* initial_state, float* final_state, void* o,
+                                       gdn_dtype o_dtype, int H, int HV, int dk, int dv,
+                                       int chunk, float scale, void* stream) {
+    // the size check is host-only and comes first: a call beyond the array
+    // fails before any HIP call (sizes the prefill rejects give need == 0
+    // and fail its own validation below)
+    const size_t need = gdn_prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk);
+    if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERROR_WORKSPACE;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (need > 0) {
+        clear_pending();
+        const gdn_status st = from_hip(gdn::noalloc_scratch(&ws, &ws_bytes));
+        if (st != GDN_SUCCESS) return st;
+    }
+    return prefill_impl(q, k, v, in_dtype, g, beta, cu_seqlens, N, T_total, initial_state,
+                        final_state, o, o_dtype, H, HV, dk, dv, chunk, scale, 0, ws, ws_bytes,
+                        stream);
+}
+
 size_t gdn_prefill_norm_workspace_bytes(int N, int T_total, int H, int HV, int dk, int dv,
                                         int chunk) {
     const size_t base = gdn_prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk);

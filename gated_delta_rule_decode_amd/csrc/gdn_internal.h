@@ -160,6 +160,10 @@ struct AttnArgs {
 void attn_plan(int N, int Hq, int Hkv, int D, int Lmax, int& split, int& nsplit, size_t& bytes);
 hipError_t launch_attn_decode(const AttnArgs& a);
 
+// Device address (on the current device) and size of the static array that
+// gdn_prefill_chunked_noalloc uses as its workspace; looked up once per device.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 bool prefill_mfma_eligible(const PrefillArgs& a);

@@ -268,6 +268,35 @@ gdn_status gdn_prefill_chunked_seg(const void* q, const void* k, const void* v,
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_prefill_chunked_noalloc -- gdn_prefill_chunked for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace is a static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES inside the library, one per GPU it runs on, held
+ * until the process ends; its device address is looked up on the first call
+ * on each device.  The call allocates nothing.  `stream` must belong to the
+ * device current on the calling thread (the array of that device is used).
+ *
+ *   every argument as gdn_prefill_chunked (automatic segmentation), minus the
+ *   workspace.
+ * Returns GDN_ERROR_WORKSPACE, before any HIP call, when
+ * gdn_prefill_workspace_bytes(N, T_total, H, HV, dk, dv, chunk) exceeds
+ * GDN_NOALLOC_SCRATCH_BYTES; GDN_ERROR_HIP if the array's address cannot be
+ * found.  Every call on one GPU uses that GPU's one array: calls that overlap
+ * on one GPU (on different streams, or from different threads without an
+ * order between their streams) race and give wrong results.  Nothing in the
+ * array needs to start at zero, so the contents left by an earlier call do
+ * not matter.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (256u * 1024u * 1024u)
+
+gdn_status gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       gdn_dtype in_dtype, const float* g, const float* beta,
+                                       const int32_t* cu_seqlens, int N, int T_total,
+                                       const float* initial_state, float* final_state, void* o,
+                                       gdn_dtype o_dtype, int H, int HV, int dk, int dv,
+                                       int chunk, float scale, void* stream);
+
+/*
  * gdn_prefill_chunked_norm -- gdn_prefill_chunked followed by RMSNormGated of
  * each (token, value head)'s outputs: the prompt pass of the token mixer up to
  * the norm that closes the DeltaNet layer (Qwen3.5-0.8B chat guide, section
