@@ -376,6 +376,7 @@ gdn_status prefill_setup(const void* q, const void* k, const void* v, gdn_dtype 
     a.ws_Rl = reinterpret_cast<uint16_t*>(ws + L.ws_Rl);
     a.ws_Zh = reinterpret_cast<uint16_t*>(ws + L.ws_Zh);
     a.ws_Zl = reinterpret_cast<uint16_t*>(ws + L.ws_Zl);
+    a.ws_Tp = reinterpret_cast<uint16_t*>(ws + L.ws_Rh);
     a.max_chunks = L.max_chunks;
     a.seg_req = segment_chunks;
     a.seg_bound = L.seg_bound;

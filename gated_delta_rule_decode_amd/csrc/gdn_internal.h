@@ -70,6 +70,9 @@ struct PrefillArgs {
     uint16_t* ws_Rl;
     uint16_t* ws_Zh;
     uint16_t* ws_Zl;
+    // T'-only path (same memory): T' = (I + A)^-1 diag(b) as ten 16 x 16
+    // blocks per (chunk, value head), hi / lo bf16 in the scan's operand order
+    uint16_t* ws_Tp;
     int max_chunks;
     // segment-parallel scan (MFMA path).  A sequence is cut into segments of
     // whole chunks; the plan is made on the device from cu_seqlens.
@@ -168,6 +171,9 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 bool prefill_mfma_eligible(const PrefillArgs& a);
 hipError_t launch_prefill_mfma(const PrefillArgs& a);
+// T'-only prep and the chain / helper scan (d_k = 128)
+hipError_t launch_prep_tp(const PrefillArgs& a);
+hipError_t launch_scan_tp(const PrefillArgs& a, size_t grid, int items);
 hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream);
 hipError_t launch_rmsnorm_gated(const NormArgs& a);
 

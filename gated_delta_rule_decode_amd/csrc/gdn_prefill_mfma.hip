@@ -1811,9 +1811,14 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
     if (!may) A.seg_req = -1;
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK,
                        rows ? 1 : 0);
-    hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.HV), dim3(256), 0,
-                       A.stream, A);
-    hipError_t err = hipGetLastError();
+    // d_k = 128 without the per-chain scan: the T'-only prep and the chain /
+    // helper scan (gdn_prefill_tp.hip); otherwise the prep with R and Z^T
+    const bool tp = DK == 128 && !rows;
+    hipError_t err = tp ? launch_prep_tp(A) : hipSuccess;
+    if (!tp)
+        hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.HV), dim3(256), 0,
+                           A.stream, A);
+    if (err == hipSuccess) err = hipGetLastError();
     if (err != hipSuccess) return err;
     // value items of up to seg_bound segments (N without segmentation), then
     // the transition items; the kernel splits the grid at seg_bound
@@ -1835,8 +1840,13 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
         const size_t items = may ? chains8 * (TV + TK) : chains8 * TV;
         const size_t unseg = (size_t)((A.N * A.HV + 7) / 8) * 8 * TV;
         const size_t grid = (may && (size_t)A.N * A.HV * TV < 256) ? items : unseg;
-        hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)grid), dim3(256), 0,
-                           A.stream, A, (int)items);
+        if (tp) {
+            err = launch_scan_tp(A, grid, (int)items);
+            if (err != hipSuccess) return err;
+        } else {
+            hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)grid), dim3(256), 0,
+                               A.stream, A, (int)items);
+        }
     }
     if (may) {
         const int cgrid = (int)std::min<size_t>((size_t)A.N * A.HV * TV, 512);

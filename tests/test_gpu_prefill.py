@@ -253,8 +253,9 @@ def test_prefill_many_chains_matches_oracle(orc, H, HV, N):
 
 def test_prefill_many_chains_equals_per_tile_form():
     """The per-chain scan (N HV >= 512) and the per-32-row scan (the same
-    sequences in two calls of fewer chains) perform the same products in the
-    same order: outputs and final states agree bit for bit."""
+    sequences in two calls of fewer chains) compute the same chunked form with
+    the products grouped differently (R X and Z^T X against U = T' X): outputs
+    and final states agree to fp32 rounding."""
     lengths = _lengths_many(7, 32, 400)
     x = gi.make_prefill(lengths, 16, 16, 128, 128, s0_std=0.02, decay="mild", seed=102)
     say("prefill per-chain form vs per-tile form")
@@ -267,8 +268,10 @@ def test_prefill_many_chains_equals_per_tile_form():
                              (cu[half.start:half.stop + 1] - a).astype(np.int32), x.s0[half],
                              x.dtype, 16, 16, 128, 128)
         oh, Sh = gpu_prefill(y, scale=128 ** -0.5)
-        assert np.array_equal(o[a:e], host(oh))
-        assert np.array_equal(S[half], host(Sh))
+        r = rel_l2(host(oh), o[a:e])
+        d = float(np.max(np.abs(host(Sh) - S[half])))
+        print(f"[parity] per-chain vs per-tile: o rel-L2 {r:.3e}, state max-abs {d:.3e}")
+        assert r <= 2e-5 and d <= 2e-5
 
 
 def test_prefill_many_chains_forced_segments(orc):
