@@ -54,7 +54,24 @@ namespace gdn {
 constexpr int kTpBlocks = 10;
 constexpr int kTpBlockElems = 512;                          // uint16 per block (hi + lo)
 constexpr int kTpElems = kTpBlocks * kTpBlockElems;         // per (chunk, value head)
-__device__ __forceinline__ int tp_block(int tb, int sb) { return tb * (tb + 1) / 2 + sb; }
+__host__ __device__ constexpr int tp_block(int tb, int sb) { return tb * (tb + 1) / 2 + sb; }
+
+template <int V>
+struct TokenBlock {
+    static constexpr int value = V;
+};
+// Runs f(TokenBlock<tb>{}) for a wavefront-uniform tb in 0..3, so that the
+// triangular loops of a token block unroll with compile-time bounds: no
+// branch splits their LDS reads from one another.
+template <typename F>
+__device__ __forceinline__ void with_token_block(int tb, F&& f) {
+    switch (tb) {
+    case 0: f(TokenBlock<0>{}); break;
+    case 1: f(TokenBlock<1>{}); break;
+    case 2: f(TokenBlock<2>{}); break;
+    default: f(TokenBlock<3>{}); break;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // prep: G and T' per (chunk, value head)
@@ -312,19 +329,22 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
 // of a chain get the same b % 8 and neighbouring dispatch slots (workgroup b
 // runs on XCD b % 8), so their shared K, Q reads meet in one L2.
 //
-// Chain wavefront c (0..3): token block tb = c in phases A and U, state
-// columns j in 16 (2 c) .. 16 (2 c) + 31 in phase S; its accumulators hold
+// Chain wavefront c (0..3): token block tb = c in phases A and U (K S^T,
+// Q S^T, X; U = T' X), state columns j in 32 c .. 32 c + 31 in phase S; its
+// accumulators hold
 //   sacc[x][ib][r] = S'^T[j = 16 (2 c + x) + 4 lg + r][i = 16 ib + lr].
-// Helper wavefront 4 + tb: token block tb of P, Q S^T and O, and a quarter of
-// every staging copy.  Chunk c's K, Q and G sit in the buffers of parity
-// c % 2 from phase U of step c - 1 (staged) to phase S of step c (last read).
+// Helper wavefront 4 + c: token block tb = 3 - c of P and O (so that the
+// triangular work of a chain and a helper on one SIMD adds up to about the
+// same on every SIMD), and a quarter of every staging copy.
+// Chunk c's K, Q, G, V and T' sit in the buffers of parity c % 2 from
+// phase A of step c - 1 (staged) to phase S of step c (last read).
 template <int DK, typename Tout>
 __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) {
     static_assert(DK == 128, "the chain / helper scan is written for d_k = 128");
     constexpr int C = kChunk;
     constexpr int BV = 32;       // state rows per workgroup
     constexpr int KP = DK + 8;   // padded bf16 row: state, K and Q tiles
-    constexpr int TP = C + 8;    // padded bf16 row of the token-major tiles (X^T, U^T, U'^T, K^T, V^T)
+    constexpr int TP = C + 8;    // padded bf16 row of the token-major tiles (X^T, U^T, U'^T, V^T)
     constexpr int NKK = DK / 32;
     constexpr int NJB = DK / 64;  // state column blocks per chain wavefront
     __shared__ __attribute__((aligned(16))) __bf16 Sh[BV * KP];   // S, hi / lo
@@ -335,11 +355,12 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     __shared__ __attribute__((aligned(16))) __bf16 Ul[BV * TP];
     __shared__ __attribute__((aligned(16))) __bf16 Wh[BV * TP];   // U'^T [i][t]
     __shared__ __attribute__((aligned(16))) __bf16 Wl[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C * KP]; // K [t][j] of chunks of each parity
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C * KP]; // K [t][j], by chunk parity
     __shared__ __attribute__((aligned(16))) __bf16 Qs[2][C * KP]; // Q [t][j]
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[BV * TP];   // V^T [i][t] of the tile
-    __shared__ __attribute__((aligned(16))) uint16_t Tp[kTpElems];
-    __shared__ __attribute__((aligned(16))) float Gs[2][C];       // G of chunks of each parity
+    __shared__ __attribute__((aligned(16))) __bf16 Vt[2][BV * TP];  // V^T [i][t] of the tile
+    __shared__ __attribute__((aligned(16))) uint16_t Tp[2][kTpElems];
+    __shared__ __attribute__((aligned(16))) float Gs[2][C];
+    __shared__ __attribute__((aligned(16))) f4_t QSs[4][2][64];   // gamma (S Q^T) per token block, O^T lane order
     typedef short v4s_t __attribute__((ext_vector_type(4)));
 
     const int H = A.H, HV = A.HV, dv = A.dv;
@@ -347,7 +368,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     __builtin_assume(w >= 0 && w < 8);
     const bool is_chain = w < 4;
-    const int tb = w & 3;
+    const int tb = is_chain ? w : 7 - w;  // token block of the wavefront
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
     const int hp = tid & 255;  // a helper's lane among the 256 helper lanes
 
@@ -469,7 +490,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     float gst = 0.f;
     auto chunk_t0 = [&](int jc) { return sq + jc * C; };
     auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
-    auto load_kqvg = [&](int jc) {
+    auto load_chunk = [&](int jc) {
         const int t0 = chunk_t0(jc), L = chunk_L(jc);
         const __amdgpu_buffer_rsrc_t rk =
             in_rsrc(static_cast<const bf16_t*>(A.k) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
@@ -483,117 +504,83 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
             qst[q] = bload8(rq, kq_off[q]);
         }
         vst = bload8(rv, v_off);
-        if (hp < C) gst = A.ws_G[((size_t)(c_first + jc) * HV + h) * C + hp];
-    };
-    auto load_tp = [&](int jc) {
         const uint16_t* tp = A.ws_Tp + ((size_t)(c_first + jc) * HV + h) * kTpElems;
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
             const int pi = hp + 256 * q;
             if (pi < kTpElems / 8) tst[q] = gld8(tp + 8 * pi);
         }
+        if (hp < C) gst = A.ws_G[((size_t)(c_first + jc) * HV + h) * C + hp];
     };
-    auto stage_kqvg = [&](int jc) {
+    auto stage_chunk = [&](int jc) {
+        const int pb = jc & 1;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<bf8_t*>(&Ks[jc & 1][kq_st[q]]) = kst[q];
-            *reinterpret_cast<bf8_t*>(&Qs[jc & 1][kq_st[q]]) = qst[q];
+            *reinterpret_cast<bf8_t*>(&Ks[pb][kq_st[q]]) = kst[q];
+            *reinterpret_cast<bf8_t*>(&Qs[pb][kq_st[q]]) = qst[q];
         }
         // V^T: the piece's 8 rows of one token, one element per row
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Vt[(v_row0 + e) * TP + v_tok] = vst[e];
-        if (hp < C) Gs[jc & 1][hp] = gst;
-    };
-    auto stage_tp = [&]() {
+        for (int e = 0; e < 8; ++e) Vt[pb][(v_row0 + e) * TP + v_tok] = vst[e];
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
             const int pi = hp + 256 * q;
-            if (pi < kTpElems / 8) *reinterpret_cast<bf8_t*>(&Tp[8 * pi]) = tst[q];
+            if (pi < kTpElems / 8) *reinterpret_cast<bf8_t*>(&Tp[pb][8 * pi]) = tst[q];
         }
-    };
-
-    // helpers: P of chunk jc for this token block, decayed and masked, as B
-    // operands in the slot order s = 32 k2 + 16 half + 4 lg + r (slot 4 half + r):
-    // pq[sb][r] = (K Q^T)[s = 16 sb + 4 lg + r][t = 16 tb + lr]
-    bf8_t ph[2], pl[2];   // P fragments of the current chunk
-    auto make_p = [&](int jc) {
-        const __bf16* K_ = Ks[jc & 1];
-        const __bf16* Q_ = Qs[jc & 1];
-        const float* G_ = Gs[jc & 1];
-        f4_t pq[4];
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) pq[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const bf8_t qb = lds8(&Q_[(16 * tb + lr) * KP + 32 * kk + 8 * lg]);
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb)
-                if (sb <= tb) pq[sb] = mfma(lds8(&K_[(16 * sb + lr) * KP + 32 * kk + 8 * lg]), qb, pq[sb]);
-        }
-        const int t = 16 * tb + lr;
-        const float Gt = G_[t];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            float pv[8];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int sb = 2 * k2 + half;
-                const float4 g4 = *reinterpret_cast<const float4*>(&G_[16 * sb + 4 * lg]);
-                const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s_ = 16 * sb + 4 * lg + r;
-                    pv[4 * half + r] = (s_ <= t) ? pq[sb][r] * exp2f_(fminf(Gt - gs[r], 0.f)) : 0.f;
-                }
-            }
-            split8(pv, ph[k2], pl[k2]);
-        }
+        if (hp < C) Gs[pb][hp] = gst;
     };
 
     // prologue: chunk 0 staged, chunk 1 in flight, the state in LDS
     if (!is_chain) {
-        load_kqvg(0);
-        load_tp(0);
-        stage_kqvg(0);
-        stage_tp();
-        load_kqvg(min(1, nch - 1));
-        load_tp(min(1, nch - 1));
+        load_chunk(0);
+        stage_chunk(0);
+        if (nch > 1) load_chunk(1);
     } else {
         state_to_lds();
     }
     __syncthreads();
-    if (!is_chain) make_p(0);
 
-    f4_t oacc[2];  // helpers: O^T tiles [i = 16 ib + 4 lg + r][t = 16 tb + lr]
+    bf8_t ph[2], pl[2];  // helpers: P fragments of the chunk (B operand, slot order)
 
     for (int jc = 0; jc < nch; ++jc) {
         const int t0 = chunk_t0(jc), L = chunk_L(jc);
-        const float* Gc = Gs[jc & 1];
+        const int pb = jc & 1;
+        const float* Gc = Gs[pb];
         // ===== phase A =====
         if (is_chain) {
-            // K S^T for token block tb, both 16-row halves; X = V - diag(gamma) K S^T
-            f4_t kh[2], kl[2];
+            // K S^T (tokens of block tb, both 16-row halves) and S Q^T (its
+            // transposed O^T layout), sharing the state fragments; the hi and
+            // lo parts accumulate separately (four independent chains each)
+            f4_t kh[2], kl[2], qh[2], ql[2];
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
                 kh[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
                 kl[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+                qh[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+                ql[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const int col = 32 * kk + 8 * lg;
-                const bf8_t ka = lds8(&Ks[jc & 1][(16 * tb + lr) * KP + col]);
+                const bf8_t ka = lds8(&Ks[pb][(16 * tb + lr) * KP + col]);
+                const bf8_t qa = lds8(&Qs[pb][(16 * tb + lr) * KP + col]);
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
-                    kh[ib] = mfma(ka, lds8(&Sh[(16 * ib + lr) * KP + col]), kh[ib]);
-                    kl[ib] = mfma(ka, lds8(&Sl[(16 * ib + lr) * KP + col]), kl[ib]);
+                    const bf8_t sh = lds8(&Sh[(16 * ib + lr) * KP + col]);
+                    const bf8_t sl = lds8(&Sl[(16 * ib + lr) * KP + col]);
+                    kh[ib] = mfma(ka, sh, kh[ib]);
+                    kl[ib] = mfma(ka, sl, kl[ib]);
+                    qh[ib] = mfma(sh, qa, qh[ib]);
+                    ql[ib] = mfma(sl, qa, ql[ib]);
                 }
             }
             const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * tb + 4 * lg]);
             const float gam[4] = {exp2f_(g4.x), exp2f_(g4.y), exp2f_(g4.z), exp2f_(g4.w)};
+            // X = V - diag(gamma) K S^T, rows [i][t] hi / lo
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
                 const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
-                const uint2 vr = *reinterpret_cast<const uint2*>(&Vt[off]);
+                const uint2 vr = *reinterpret_cast<const uint2*>(&Vt[pb][off]);
                 const float vf[4] = {__uint_as_float(vr.x << 16), __uint_as_float(vr.x & 0xffff0000u),
                                      __uint_as_float(vr.y << 16), __uint_as_float(vr.y & 0xffff0000u)};
                 float xv[4];
@@ -604,35 +591,21 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                 *reinterpret_cast<uint2*>(&Xh[off]) = hi;
                 *reinterpret_cast<uint2*>(&Xl[off]) = lo;
             }
-        } else {
-            // O^T = diag(gamma) part: S Q^T for this token block
-            const int t = 16 * tb + lr;
-            const float Gt = Gc[t];
-            bf8_t qb[NKK];
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) qb[kk] = lds8(&Qs[jc & 1][t * KP + 32 * kk + 8 * lg]);
-            f4_t oh[2], ol[2];
+            // gamma_t (S Q^T)[i][t], t = 16 tb + lr: the O^T tiles' first part
+            const float gt = exp2f_(Gc[16 * tb + lr]);
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
-                oh[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-                ol[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+                f4_t v_;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v_[r] = gt * (qh[ib][r] + ql[ib][r]);
+                QSs[tb][ib][l] = v_;
             }
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int col = 32 * kk + 8 * lg;
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    oh[ib] = mfma(lds8(&Sh[(16 * ib + lr) * KP + col]), qb[kk], oh[ib]);
-                    ol[ib] = mfma(lds8(&Sl[(16 * ib + lr) * KP + col]), qb[kk], ol[ib]);
-                }
-            }
-            const float gt = exp2f_(Gt);
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) oacc[ib][r] = gt * (oh[ib][r] + ol[ib][r]);
+        } else {
+            // the next chunk into the other buffers; the one after it in flight
+            if (jc + 1 < nch) stage_chunk(jc + 1);
+            if (jc + 2 < nch) load_chunk(jc + 2);
         }
-        __syncthreads();  // B1: X of the chunk complete; K, Q, V of the chunk no longer read
+        __syncthreads();  // B1: X, gamma S Q^T of the chunk in LDS; the next chunk staged
 
         // ===== phase U =====
         if (is_chain) {
@@ -640,28 +613,38 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
             f4_t ua[2];
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) ua[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
+            with_token_block(tb, [&](auto TB) {
+                constexpr int tbc = decltype(TB)::value;
+                bf8_t th[2], tl[2], xh[2][2], xl[2][2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk <= (tb >> 1)) {
+                for (int kk = 0; kk <= (tbc >> 1); ++kk) {
+                    // lanes of the upper half-step (sb = tb + 1) read block 0
+                    // and are zeroed below
                     const int sb = 2 * kk + (lg >> 1);
-                    const int bi = (sb <= tb) ? tp_block(tb, sb) : 0;
+                    const int bi = (sb <= tbc) ? tp_block(tbc, sb) : 0;
                     const int at = bi * kTpBlockElems + (lr + 16 * (lg & 1)) * 8;
-                    bf8_t th = *reinterpret_cast<const bf8_t*>(&Tp[at]);
-                    bf8_t tl = *reinterpret_cast<const bf8_t*>(&Tp[at + 256]);
-                    if (sb > tb) {  // an upper block: zero
-                        th = zero8();
-                        tl = zero8();
+                    th[kk] = *reinterpret_cast<const bf8_t*>(&Tp[pb][at]);
+                    tl[kk] = *reinterpret_cast<const bf8_t*>(&Tp[pb][at + 256]);
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        xh[kk][ib] = lds8(&Xh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+                        xl[kk][ib] = lds8(&Xl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk <= (tbc >> 1); ++kk) {
+                    if ((tbc & 1) == 0 && kk == (tbc >> 1) && (lg >> 1)) {  // an upper block: zero
+                        th[kk] = zero8();
+                        tl[kk] = zero8();
                     }
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib) {
-                        const bf8_t xh = lds8(&Xh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                        const bf8_t xl = lds8(&Xl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                        ua[ib] = mfma(th, xh, ua[ib]);
-                        ua[ib] = mfma(th, xl, ua[ib]);
-                        ua[ib] = mfma(tl, xh, ua[ib]);
+                        ua[ib] = mfma(th[kk], xh[kk][ib], ua[ib]);
+                        ua[ib] = mfma(th[kk], xl[kk][ib], ua[ib]);
+                        ua[ib] = mfma(tl[kk], xh[kk][ib], ua[ib]);
                     }
                 }
-            }
+            });
             // ua[ib][r] = U[t = 16 tb + 4 lg + r][i = 16 ib + lr]; U' = diag(e^{G_n - G}) U
             const float Gn = Gc[L - 1];
             const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * tb + 4 * lg]);
@@ -682,29 +665,79 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                 *reinterpret_cast<uint2*>(&Wl[off]) = lo;
             }
         } else {
-            // the next chunk's K, Q, V, G into LDS; the one after it in flight
-            stage_kqvg(jc + 1);
-            load_kqvg(min(jc + 2, nch - 1));
+            // P of this chunk for token block tb, decayed and masked, as B
+            // operands in the slot order s = 32 k2 + 16 half + 4 lg + r (slot
+            // 4 half + r): pq[sb][r] = (K Q^T)[s = 16 sb + 4 lg + r][t = 16 tb + lr]
+            // (blocks sb > tb are zero: their fragments stay unset and unread)
+            with_token_block(tb, [&](auto TB) {
+                constexpr int tbc = decltype(TB)::value;
+                f4_t pq[tbc + 1];
+#pragma unroll
+                for (int sb = 0; sb <= tbc; ++sb) pq[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const bf8_t qb = lds8(&Qs[pb][(16 * tbc + lr) * KP + 32 * kk + 8 * lg]);
+                    bf8_t kb[tbc + 1];
+#pragma unroll
+                    for (int sb = 0; sb <= tbc; ++sb) kb[sb] = lds8(&Ks[pb][(16 * sb + lr) * KP + 32 * kk + 8 * lg]);
+#pragma unroll
+                    for (int sb = 0; sb <= tbc; ++sb) pq[sb] = mfma(kb[sb], qb, pq[sb]);
+                }
+                const int t = 16 * tbc + lr;
+                const float Gt = Gc[t];
+#pragma unroll
+                for (int k2 = 0; k2 <= (tbc >> 1); ++k2) {
+                    float pv[8];
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int sb = 2 * k2 + half;
+                        if (sb > tbc) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) pv[4 * half + r] = 0.f;
+                            continue;
+                        }
+                        const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * sb + 4 * lg]);
+                        const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            // Gt - gs <= 0 for s <= t, so the factor is at most 1; the
+                            // diagonal block masks s > t by a 0 / 1 factor
+                            float f = exp2f_(fminf(Gt - gs[r], 0.f));
+                            if (sb == tbc) f *= (4 * lg + r <= lr) ? 1.f : 0.f;
+                            pv[4 * half + r] = pq[sb][r] * f;
+                        }
+                    }
+                    split8(pv, ph[k2], pl[k2]);
+                }
+            });
         }
-        __syncthreads();  // B2: U, U' of the chunk complete; the next chunk's K, Q, V, G staged
+        __syncthreads();  // B2: U, U' of the chunk in LDS
 
         // ===== phase S =====
         if (is_chain) {
             // S'^T = gamma_n S^T + K^T U' for the wavefront's column blocks
             const float gn = exp2f_(Gc[L - 1]);
 #pragma unroll
-            for (int x = 0; x < NJB; ++x) {
-                const int jb = NJB * tb + x;
+            for (int x = 0; x < NJB; ++x)
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sacc[x][ib][r] *= gn;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
+            for (int kk = 0; kk < 2; ++kk) {
+                bf8_t wh[2], wl[2];
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    wh[ib] = lds8(&Wh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+                    wl[ib] = lds8(&Wl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+                }
+#pragma unroll
+                for (int x = 0; x < NJB; ++x) {
+                    const int jb = NJB * tb + x;
                     // K^T rows j = 16 jb + lr, tokens 32 kk + 8 lg .. + 7: two
                     // transpose reads; lane m of each 16-lane group points at
                     // row 32 kk + 8 lg + m / 4 (+ 4), columns 16 jb + 4 (m % 4) ..
-                    const __bf16* kp_ = &Ks[jc & 1][(32 * kk + 8 * lg + (lr >> 2)) * KP + 16 * jb + 4 * (lr & 3)];
+                    const __bf16* kp_ = &Ks[pb][(32 * kk + 8 * lg + (lr >> 2)) * KP + 16 * jb + 4 * (lr & 3)];
                     const v4s_t k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) v4s_t*)(kp_));
                     const v4s_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -712,19 +745,22 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                     const bf8_t kt = __builtin_bit_cast(bf8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib) {
-                        sacc[x][ib] = mfma(kt, lds8(&Wh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]), sacc[x][ib]);
-                        sacc[x][ib] = mfma(kt, lds8(&Wl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]), sacc[x][ib]);
+                        sacc[x][ib] = mfma(kt, wh[ib], sacc[x][ib]);
+                        sacc[x][ib] = mfma(kt, wl[ib], sacc[x][ib]);
                     }
                 }
             }
             // the next chunk's state (S of this chunk was last read in phase A)
             state_to_lds();
         } else {
-            // O^T += U^T P^T (P lower: k-steps kk <= tb / 2); U^T read in the
-            // slot order of the P fragments
+            // O^T = gamma S Q^T + U^T P^T (P lower: k-steps kk <= tb / 2); U^T
+            // read in the slot order of the P fragments
+            f4_t oacc[2] = {QSs[tb][0][l], QSs[tb][1][l]};
+            with_token_block(tb, [&](auto TB) {
+                constexpr int tbc = decltype(TB)::value;
+                bf8_t uh[2][2], ul[2][2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk <= (tb >> 1)) {
+                for (int kk = 0; kk <= (tbc >> 1); ++kk)
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib) {
                         const int off = (16 * ib + lr) * TP + 32 * kk + 4 * lg;
@@ -732,14 +768,18 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                         const uint2 h1 = *reinterpret_cast<const uint2*>(&Uh[off + 16]);
                         const uint2 l0 = *reinterpret_cast<const uint2*>(&Ul[off]);
                         const uint2 l1 = *reinterpret_cast<const uint2*>(&Ul[off + 16]);
-                        const bf8_t uh = __builtin_bit_cast(bf8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
-                        const bf8_t ul = __builtin_bit_cast(bf8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
-                        oacc[ib] = mfma(uh, ph[kk], oacc[ib]);
-                        oacc[ib] = mfma(ul, ph[kk], oacc[ib]);
-                        oacc[ib] = mfma(uh, pl[kk], oacc[ib]);
+                        uh[kk][ib] = __builtin_bit_cast(bf8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
+                        ul[kk][ib] = __builtin_bit_cast(bf8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
                     }
-                }
-            }
+#pragma unroll
+                for (int kk = 0; kk <= (tbc >> 1); ++kk)
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        oacc[ib] = mfma(uh[kk][ib], ph[kk], oacc[ib]);
+                        oacc[ib] = mfma(ul[kk][ib], ph[kk], oacc[ib]);
+                        oacc[ib] = mfma(uh[kk][ib], pl[kk], oacc[ib]);
+                    }
+            });
             // oacc[ib][r] = O[t = 16 tb + lr][i = 16 ib + 4 lg + r]; rows t >= L land
             // at or past the resource end and are dropped.  A transition item
             // writes w (fp32, d_k per token and head) instead of o.
@@ -763,13 +803,8 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                     out_store4(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * ib + 4 * lg), ov, op);
                 }
             }
-            // the next chunk's T' into LDS (this chunk's was last read in phase U)
-            stage_tp();
-            load_tp(min(jc + 2, nch - 1));
-            // P of the next chunk (its K, Q and G were staged in phase U)
-            make_p(min(jc + 1, nch - 1));
         }
-        __syncthreads();  // B3: the next chunk's state and T' are in LDS
+        __syncthreads();  // B3: the next chunk's state in LDS; U, gamma S Q^T read
     }
     if (is_chain) store_state();
 }
