@@ -344,7 +344,8 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     constexpr int C = kChunk;
     constexpr int BV = 32;       // state rows per workgroup
     constexpr int KP = DK + 8;   // padded bf16 row: state, K and Q tiles
-    constexpr int TP = C + 8;    // padded bf16 row of the token-major tiles (X^T, U^T, U'^T, V^T)
+    constexpr int TP = C + 8;    // padded bf16 row of the transposed tiles (X^T, U^T, U'^T)
+    constexpr int VP = BV + 16;  // padded bf16 row of V: the four rows of a transpose read fall in disjoint banks
     constexpr int NKK = DK / 32;
     constexpr int NJB = DK / 64;  // state column blocks per chain wavefront
     __shared__ __attribute__((aligned(16))) __bf16 Sh[BV * KP];   // S, hi / lo
@@ -357,7 +358,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     __shared__ __attribute__((aligned(16))) __bf16 Wl[BV * TP];
     __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C * KP]; // K [t][j], by chunk parity
     __shared__ __attribute__((aligned(16))) __bf16 Qs[2][C * KP]; // Q [t][j]
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[2][BV * TP];  // V^T [i][t] of the tile
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][C * VP];   // V [t][i] of the tile
     __shared__ __attribute__((aligned(16))) uint16_t Tp[2][kTpElems];
     __shared__ __attribute__((aligned(16))) float Gs[2][C];
     __shared__ __attribute__((aligned(16))) f4_t QSs[4][2][64];   // gamma (S Q^T) per token block, O^T lane order
@@ -519,9 +520,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
             *reinterpret_cast<bf8_t*>(&Ks[pb][kq_st[q]]) = kst[q];
             *reinterpret_cast<bf8_t*>(&Qs[pb][kq_st[q]]) = qst[q];
         }
-        // V^T: the piece's 8 rows of one token, one element per row
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Vt[pb][(v_row0 + e) * TP + v_tok] = vst[e];
+        *reinterpret_cast<bf8_t*>(&Vs[pb][v_tok * VP + v_row0]) = vst;
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
             const int pi = hp + 256 * q;
@@ -530,24 +529,17 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
         if (hp < C) Gs[pb][hp] = gst;
     };
 
-    // prologue: chunk 0 staged, chunk 1 in flight, the state in LDS
-    if (!is_chain) {
-        load_chunk(0);
-        stage_chunk(0);
-        if (nch > 1) load_chunk(1);
-    } else {
+    // The chain and the helpers run separate loops with the same three
+    // barriers per chunk, so that neither role's registers are held live
+    // across the other's code.
+    if (is_chain) {
         state_to_lds();
-    }
-    __syncthreads();
-
-    bf8_t ph[2], pl[2];  // helpers: P fragments of the chunk (B operand, slot order)
-
-    for (int jc = 0; jc < nch; ++jc) {
-        const int t0 = chunk_t0(jc), L = chunk_L(jc);
-        const int pb = jc & 1;
-        const float* Gc = Gs[pb];
-        // ===== phase A =====
-        if (is_chain) {
+        __syncthreads();  // B0: the state and chunk 0 in LDS
+        for (int jc = 0; jc < nch; ++jc) {
+            const int L = chunk_L(jc);
+            const int pb = jc & 1;
+            const float* Gc = Gs[pb];
+            // ===== phase A =====
             // K S^T (tokens of block tb, both 16-row halves) and S Q^T (its
             // transposed O^T layout), sharing the state fragments; the hi and
             // lo parts accumulate separately (four independent chains each)
@@ -559,30 +551,45 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                 qh[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
                 ql[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
             }
+            // every fragment is read before the first product
+            bf8_t ka[NKK], qa[NKK], sh[NKK][2], sl[NKK][2];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const int col = 32 * kk + 8 * lg;
-                const bf8_t ka = lds8(&Ks[pb][(16 * tb + lr) * KP + col]);
-                const bf8_t qa = lds8(&Qs[pb][(16 * tb + lr) * KP + col]);
+                ka[kk] = lds8(&Ks[pb][(16 * tb + lr) * KP + col]);
+                qa[kk] = lds8(&Qs[pb][(16 * tb + lr) * KP + col]);
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
-                    const bf8_t sh = lds8(&Sh[(16 * ib + lr) * KP + col]);
-                    const bf8_t sl = lds8(&Sl[(16 * ib + lr) * KP + col]);
-                    kh[ib] = mfma(ka, sh, kh[ib]);
-                    kl[ib] = mfma(ka, sl, kl[ib]);
-                    qh[ib] = mfma(sh, qa, qh[ib]);
-                    ql[ib] = mfma(sl, qa, ql[ib]);
+                    sh[kk][ib] = lds8(&Sh[(16 * ib + lr) * KP + col]);
+                    sl[kk][ib] = lds8(&Sl[(16 * ib + lr) * KP + col]);
                 }
             }
+            // V[t = 16 tb + 4 lg + r][i = 16 ib + lr], r = 0..3, by transpose
+            // reads: lane m of each 16-lane group points at row 16 tb + 4 lg + m / 4,
+            // columns 16 ib + 4 (m % 4) ..
+            v4s_t vr[2];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+                vr[ib] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(
+                    &Vs[pb][(16 * tb + 4 * lg + (lr >> 2)) * VP + 16 * ib + 4 * (lr & 3)]));
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    kh[ib] = mfma(ka[kk], sh[kk][ib], kh[ib]);
+                    kl[ib] = mfma(ka[kk], sl[kk][ib], kl[ib]);
+                    qh[ib] = mfma(sh[kk][ib], qa[kk], qh[ib]);
+                    ql[ib] = mfma(sl[kk][ib], qa[kk], ql[ib]);
+                }
             const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * tb + 4 * lg]);
             const float gam[4] = {exp2f_(g4.x), exp2f_(g4.y), exp2f_(g4.z), exp2f_(g4.w)};
             // X = V - diag(gamma) K S^T, rows [i][t] hi / lo
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
                 const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
-                const uint2 vr = *reinterpret_cast<const uint2*>(&Vt[pb][off]);
-                const float vf[4] = {__uint_as_float(vr.x << 16), __uint_as_float(vr.x & 0xffff0000u),
-                                     __uint_as_float(vr.y << 16), __uint_as_float(vr.y & 0xffff0000u)};
+                float vf[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vf[r] = __uint_as_float((uint32_t)(uint16_t)vr[ib][r] << 16);
                 float xv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) xv[r] = vf[r] - gam[r] * (kh[ib][r] + kl[ib][r]);
@@ -600,15 +607,8 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                 for (int r = 0; r < 4; ++r) v_[r] = gt * (qh[ib][r] + ql[ib][r]);
                 QSs[tb][ib][l] = v_;
             }
-        } else {
-            // the next chunk into the other buffers; the one after it in flight
-            if (jc + 1 < nch) stage_chunk(jc + 1);
-            if (jc + 2 < nch) load_chunk(jc + 2);
-        }
-        __syncthreads();  // B1: X, gamma S Q^T of the chunk in LDS; the next chunk staged
-
-        // ===== phase U =====
-        if (is_chain) {
+            __syncthreads();  // B1: X, gamma S Q^T of the chunk in LDS; the next chunk staged
+            // ===== phase U =====
             // U = T' X for token block tb (T' lower: k-steps kk <= tb / 2)
             f4_t ua[2];
 #pragma unroll
@@ -646,8 +646,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                 }
             });
             // ua[ib][r] = U[t = 16 tb + 4 lg + r][i = 16 ib + lr]; U' = diag(e^{G_n - G}) U
-            const float Gn = Gc[L - 1];
-            const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * tb + 4 * lg]);
+            const float Gn = Gc[L - 1];  // g4: G of the wavefront's tokens, read in phase A
             const float dd[4] = {exp2f_(Gn - g4.x), exp2f_(Gn - g4.y), exp2f_(Gn - g4.z),
                                  exp2f_(Gn - g4.w)};
 #pragma unroll
@@ -664,7 +663,64 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                 *reinterpret_cast<uint2*>(&Wh[off]) = hi;
                 *reinterpret_cast<uint2*>(&Wl[off]) = lo;
             }
-        } else {
+            __syncthreads();  // B2: U, U' of the chunk in LDS
+            // ===== phase S =====
+            // S'^T = gamma_n S^T + K^T U' for the wavefront's column blocks
+            const float gn = exp2f_(Gc[L - 1]);
+#pragma unroll
+            for (int x = 0; x < NJB; ++x)
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sacc[x][ib][r] *= gn;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf8_t wh[2], wl[2];
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    wh[ib] = lds8(&Wh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+                    wl[ib] = lds8(&Wl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
+                }
+#pragma unroll
+                for (int x = 0; x < NJB; ++x) {
+                    const int jb = NJB * tb + x;
+                    // K^T rows j = 16 jb + lr, tokens 32 kk + 8 lg .. + 7: two
+                    // transpose reads; lane m of each 16-lane group points at
+                    // row 32 kk + 8 lg + m / 4 (+ 4), columns 16 jb + 4 (m % 4) ..
+                    const __bf16* kp_ = &Ks[pb][(32 * kk + 8 * lg + (lr >> 2)) * KP + 16 * jb + 4 * (lr & 3)];
+                    const v4s_t k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s_t*)(kp_));
+                    const v4s_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s_t*)(kp_ + 4 * KP));
+                    const bf8_t kt = __builtin_bit_cast(bf8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        sacc[x][ib] = mfma(kt, wh[ib], sacc[x][ib]);
+                        sacc[x][ib] = mfma(kt, wl[ib], sacc[x][ib]);
+                    }
+                }
+            }
+            // the next chunk's state (S of this chunk was last read in phase A)
+            state_to_lds();
+            __syncthreads();  // B3: the next chunk's state in LDS; U, gamma S Q^T read
+        }
+        store_state();
+    } else {
+        load_chunk(0);
+        stage_chunk(0);
+        if (nch > 1) load_chunk(1);
+        __syncthreads();  // B0
+        bf8_t ph[2], pl[2];  // P fragments of the chunk (B operand, slot order)
+        for (int jc = 0; jc < nch; ++jc) {
+            const int t0 = chunk_t0(jc), L = chunk_L(jc);
+            const int pb = jc & 1;
+            const float* Gc = Gs[pb];
+            // ===== phase A =====
+            // the next chunk into the other buffers; the one after it in flight
+            if (jc + 1 < nch) stage_chunk(jc + 1);
+            if (jc + 2 < nch) load_chunk(jc + 2);
+            __syncthreads();  // B1
+            // ===== phase U =====
             // P of this chunk for token block tb, decayed and masked, as B
             // operands in the slot order s = 32 k2 + 16 half + 4 lg + r (slot
             // 4 half + r): pq[sb][r] = (K Q^T)[s = 16 sb + 4 lg + r][t = 16 tb + lr]
@@ -710,49 +766,8 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                     split8(pv, ph[k2], pl[k2]);
                 }
             });
-        }
-        __syncthreads();  // B2: U, U' of the chunk in LDS
-
-        // ===== phase S =====
-        if (is_chain) {
-            // S'^T = gamma_n S^T + K^T U' for the wavefront's column blocks
-            const float gn = exp2f_(Gc[L - 1]);
-#pragma unroll
-            for (int x = 0; x < NJB; ++x)
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sacc[x][ib][r] *= gn;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf8_t wh[2], wl[2];
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    wh[ib] = lds8(&Wh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                    wl[ib] = lds8(&Wl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                }
-#pragma unroll
-                for (int x = 0; x < NJB; ++x) {
-                    const int jb = NJB * tb + x;
-                    // K^T rows j = 16 jb + lr, tokens 32 kk + 8 lg .. + 7: two
-                    // transpose reads; lane m of each 16-lane group points at
-                    // row 32 kk + 8 lg + m / 4 (+ 4), columns 16 jb + 4 (m % 4) ..
-                    const __bf16* kp_ = &Ks[pb][(32 * kk + 8 * lg + (lr >> 2)) * KP + 16 * jb + 4 * (lr & 3)];
-                    const v4s_t k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s_t*)(kp_));
-                    const v4s_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s_t*)(kp_ + 4 * KP));
-                    const bf8_t kt = __builtin_bit_cast(bf8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        sacc[x][ib] = mfma(kt, wh[ib], sacc[x][ib]);
-                        sacc[x][ib] = mfma(kt, wl[ib], sacc[x][ib]);
-                    }
-                }
-            }
-            // the next chunk's state (S of this chunk was last read in phase A)
-            state_to_lds();
-        } else {
+            __syncthreads();  // B2
+            // ===== phase S =====
             // O^T = gamma S Q^T + U^T P^T (P lower: k-steps kk <= tb / 2); U^T
             // read in the slot order of the P fragments
             f4_t oacc[2] = {QSs[tb][0][l], QSs[tb][1][l]};
@@ -803,10 +818,9 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                     out_store4(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * ib + 4 * lg), ov, op);
                 }
             }
+            __syncthreads();  // B3
         }
-        __syncthreads();  // B3: the next chunk's state in LDS; U, gamma S Q^T read
     }
-    if (is_chain) store_state();
 }
 
 // Persistent over work items, as the per-tile scan: workgroup blockIdx.x takes
