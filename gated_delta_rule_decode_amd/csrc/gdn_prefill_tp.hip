@@ -45,33 +45,32 @@
 
 namespace gdn {
 
-// T' of one (chunk, value head): block (tb, sb), sb <= tb, at index
-// tb (tb + 1) / 2 + sb; a block is 1 KiB, 512 bytes of hi then 512 of lo.
-// Inside a block, the 16 bytes at lane-in-block lb = row + 16 half hold
-// columns 8 half .. 8 half + 7 of that row: an MFMA A operand for rows
-// 16 tb .. + 15 and contraction slots 32 kk .. + 31 reads, in lane
-// l = lr + 16 lg, block (tb, 2 kk + lg / 2) at lb = lr + 16 (lg % 2).
-constexpr int kTpBlocks = 10;
-constexpr int kTpBlockElems = 512;                          // uint16 per block (hi + lo)
-constexpr int kTpElems = kTpBlocks * kTpBlockElems;         // per (chunk, value head)
+// Contraction slots.  The state, X, U and P enter the MFMAs straight from
+// the accumulators of the products that made them: an accumulator lane
+// (lg, lr) holds rows 4 lg .. 4 lg + 3 of a 16-row block.  So a 32-long
+// contraction step kk gives the lane of group lg the eight slots
+//   e = 0..7  ->  index 32 kk + 16 (e / 4) + 4 lg + e % 4,
+// the lane's own rows of two adjacent 16-blocks, and every operand read
+// from memory (K, Q, T') is laid out in that order too.
+__host__ __device__ constexpr int slot_index(int kk, int lg, int e) { return 32 * kk + 16 * (e >> 2) + 4 * lg + (e & 3); }
+
+// T' of one (chunk, value head) in A-operand order: one tile per (token
+// block tb, contraction step kk <= tb / 2), tile tp_tile(tb, kk); a tile is
+// 512 bf16 of hi then 512 of lo, lane l's 8 slots at 8 l: row t = 16 tb + l % 16,
+// columns slot_index(kk, l / 16, e).  Columns past the diagonal hold zeros.
+constexpr int kTpTiles = 6;
+constexpr int kTpTileElems = 1024;                       // uint16 per tile (hi + lo)
+constexpr int kTpElems = kTpTiles * kTpTileElems;        // per (chunk, value head)
+__host__ __device__ constexpr int tp_tile(int tb, int kk) { return (tb < 3 ? tb : 4) + kk; }
+// (K Q^T) block (tb, sb), sb <= tb, among the ten on or below the diagonal
 __host__ __device__ constexpr int tp_block(int tb, int sb) { return tb * (tb + 1) / 2 + sb; }
 
+// A token block as a compile-time constant (triangular loops over token
+// blocks unroll with fixed bounds).
 template <int V>
 struct TokenBlock {
     static constexpr int value = V;
 };
-// Runs f(TokenBlock<tb>{}) for a wavefront-uniform tb in 0..3, so that the
-// triangular loops of a token block unroll with compile-time bounds: no
-// branch splits their LDS reads from one another.
-template <typename F>
-__device__ __forceinline__ void with_token_block(int tb, F&& f) {
-    switch (tb) {
-    case 0: f(TokenBlock<0>{}); break;
-    case 1: f(TokenBlock<1>{}); break;
-    case 2: f(TokenBlock<2>{}); break;
-    default: f(TokenBlock<3>{}); break;
-    }
-}
 
 // ---------------------------------------------------------------------------
 // prep: G and T' per (chunk, value head)
@@ -287,32 +286,33 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
                 Tm[(32 + 16 * tbm + 4 * lg + r) * AP + 16 * jb + lr] = -ta[r];
         }
         __syncthreads();
-        // T' = T diag(b), the ten blocks on or below the diagonal, hi / lo in
-        // operand order: unit u = (block, lane-in-block), 8 columns each.  A
-        // select, not a 0/1 factor, keeps the zero upper half of a diagonal
-        // block (T's other upper blocks hold scratch data and are not read).
+        // T' = T diag(b) in tile order (unit u = (tile, lane)), hi / lo.  A
+        // select, not a 0/1 factor, zeroes the slots past the diagonal (T's
+        // upper blocks hold scratch data).
         uint16_t* const tp = A.ws_Tp + ((size_t)c * HV + hv) * kTpElems;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int u = tid + 256 * q;
-            if (u < kTpBlocks * 32) {
-                const int blk = u >> 5, lb = u & 31;
-                const int tb = blk >= 6 ? 3 : (blk >= 3 ? 2 : (blk >= 1 ? 1 : 0));
-                const int sb = blk - tp_block(tb, 0);
-                const int t = 16 * tb + (lb & 15), s = 16 * sb + 8 * (lb >> 4);
-                const float4 x0 = *reinterpret_cast<const float4*>(&Tm[t * AP + s]);
-                const float4 x1 = *reinterpret_cast<const float4*>(&Tm[t * AP + s + 4]);
-                const float4 b0 = *reinterpret_cast<const float4*>(&Bs[s]);
-                const float4 b1 = *reinterpret_cast<const float4*>(&Bs[s + 4]);
-                const float tv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            if (u < kTpTiles * 64) {
+                const int ti = u >> 6, ul = u & 63, ulr = ul & 15, ulg = ul >> 4;
+                const int tb = ti < 2 ? ti : (ti < 4 ? 2 : 3);
+                const int kk = ti - tp_tile(tb, 0);
+                const int t = 16 * tb + ulr;
                 float pv[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = (s + e <= t) ? tv[e] * bb[e] : 0.f;
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int s0 = slot_index(kk, ulg, 4 * hh);
+                    const float4 x4 = *reinterpret_cast<const float4*>(&Tm[t * AP + s0]);
+                    const float4 b4 = *reinterpret_cast<const float4*>(&Bs[s0]);
+                    const float tv[4] = {x4.x, x4.y, x4.z, x4.w};
+                    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pv[4 * hh + r] = (s0 + r <= t) ? tv[r] * bb[r] : 0.f;
+                }
                 bf8_t hi, lo;
                 split8(pv, hi, lo);
-                *reinterpret_cast<bf8_t*>(tp + blk * kTpBlockElems + lb * 8) = hi;
-                *reinterpret_cast<bf8_t*>(tp + blk * kTpBlockElems + 256 + lb * 8) = lo;
+                *reinterpret_cast<bf8_t*>(tp + ti * kTpTileElems + ul * 8) = hi;
+                *reinterpret_cast<bf8_t*>(tp + ti * kTpTileElems + 512 + ul * 8) = lo;
             }
         }
         __syncthreads();  // Tm, Gs and Bs are rewritten for the next value head
@@ -320,7 +320,8 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// scan: sequential over chunks, chain and helper wavefronts
+// scan: sequential over chunks; state rows split over chain wavefronts, the
+// output over output wavefronts
 // ---------------------------------------------------------------------------
 // Work items as in the per-tile scan: (segment, value head, 32-row tile of
 // S) value items first, then the transition items of later segments (the same
@@ -329,49 +330,47 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
 // of a chain get the same b % 8 and neighbouring dispatch slots (workgroup b
 // runs on XCD b % 8), so their shared K, Q reads meet in one L2.
 //
-// Chain wavefront c (0..3): token block tb = c in phases A and U (K S^T,
-// Q S^T, X; U = T' X), state columns j in 32 c .. 32 c + 31 in phase S; its
-// accumulators hold
-//   sacc[x][ib][r] = S'^T[j = 16 (2 c + x) + 4 lg + r][i = 16 ib + lr].
-// Helper wavefront 4 + c: token block tb = 3 - c of P and O (so that the
-// triangular work of a chain and a helper on one SIMD adds up to about the
-// same on every SIMD), and a quarter of every staging copy.
-// Chunk c's K, Q, G, V and T' sit in the buffers of parity c % 2 from
-// phase A of step c - 1 (staged) to phase S of step c (last read).
+// The rows of S evolve independently.  Chain wavefront a (0, 1) owns rows
+// i = 16 a .. 16 a + 15 of the tile:
+//   sacc[jb][r] = S^T[j = 16 jb + 4 lg + r][i = 16 a + lr]
+// are the B operand of K S^T, and K S^T, X, U and U' come out of one product
+// in the lane layout the next one takes (the contraction slots above), so the
+// chain step needs nothing from other wavefronts.  Per chunk, with
+// gamma_t = e^{G_t}:
+//   X = V - diag(gamma) K S^T,  U = T' X,  U' = diag(e^{G_n - G}) U,
+//   S'^T = gamma_n S^T + K^T U'.
+// Output wavefront 2 + a takes the chain's S and U operands from LDS and forms
+//   O^T = scale (S Q^T diag(gamma) + U^T P^T),  P = (Q K^T) o e^{G_t - G_s} [s <= t],
+// each output wavefront computing the P tiles of two token blocks for both.
+// Wavefronts 4 and 5 stage the next chunk's K, Q, V, T' and G into the other
+// LDS buffers.  A chunk step has two phases:
+//   1: chain K S^T, X, U = T' X, U to LDS;  output S Q^T, its P tiles to LDS;
+//   2: chain S' and its operands to LDS;     output U^T P^T and the stores.
+// K and Q rows are stored with their columns in slot order (an operand read
+// is 16 contiguous bytes); a K^T operand is two transpose reads.
 template <int DK, typename Tout>
 __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) {
-    static_assert(DK == 128, "the chain / helper scan is written for d_k = 128");
+    static_assert(DK == 128, "the row-split scan is written for d_k = 128");
     constexpr int C = kChunk;
-    constexpr int BV = 32;       // state rows per workgroup
-    constexpr int KP = DK + 8;   // padded bf16 row: state, K and Q tiles
-    constexpr int TP = C + 8;    // padded bf16 row of the transposed tiles (X^T, U^T, U'^T)
-    constexpr int VP = BV + 16;  // padded bf16 row of V: the four rows of a transpose read fall in disjoint banks
-    constexpr int NKK = DK / 32;
-    constexpr int NJB = DK / 64;  // state column blocks per chain wavefront
-    __shared__ __attribute__((aligned(16))) __bf16 Sh[BV * KP];   // S, hi / lo
-    __shared__ __attribute__((aligned(16))) __bf16 Sl[BV * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 Xh[BV * TP];   // X^T [i][t]
-    __shared__ __attribute__((aligned(16))) __bf16 Xl[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Uh[BV * TP];   // U^T [i][t]
-    __shared__ __attribute__((aligned(16))) __bf16 Ul[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Wh[BV * TP];   // U'^T [i][t]
-    __shared__ __attribute__((aligned(16))) __bf16 Wl[BV * TP];
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C * KP]; // K [t][j], by chunk parity
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[2][C * KP]; // Q [t][j]
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][C * VP];   // V [t][i] of the tile
+    constexpr int BV = 32;        // state rows per workgroup
+    constexpr int KR = DK + 16;   // bf16 per K / Q row in LDS (288 bytes)
+    constexpr int VR = BV + 16;   // bf16 per V row in LDS (96 bytes)
+    constexpr int NJB = DK / 16;  // 16-column blocks of the state
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C * KR];  // K [t][slot order], by chunk parity
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[2][C * KR];  // Q [t][slot order]
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][C * VR];  // V [t][i] of the tile
     __shared__ __attribute__((aligned(16))) uint16_t Tp[2][kTpElems];
-    __shared__ __attribute__((aligned(16))) float Gs[2][C];
-    __shared__ __attribute__((aligned(16))) f4_t QSs[4][2][64];   // gamma (S Q^T) per token block, O^T lane order
+    __shared__ __attribute__((aligned(16))) float Gs[2][3][C];     // G, e^{G}, e^{G_n - G}
+    __shared__ __attribute__((aligned(16))) bf8_t Sx[2][4][2][64]; // chain S operands [a][kk][hi, lo][lane]
+    __shared__ __attribute__((aligned(16))) bf8_t Ux[2][2][2][64]; // chain U operands [a][kk][hi, lo][lane]
+    __shared__ __attribute__((aligned(16))) bf8_t Px[kTpTiles][2][64];  // P tiles [tile][hi, lo][lane]
     typedef short v4s_t __attribute__((ext_vector_type(4)));
 
     const int H = A.H, HV = A.HV, dv = A.dv;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __builtin_assume(w >= 0 && w < 8);
-    const bool is_chain = w < 4;
-    const int tb = is_chain ? w : 7 - w;  // token block of the wavefront
+    __builtin_assume(w >= 0 && w < 6);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int hp = tid & 255;  // a helper's lane among the 256 helper lanes
 
     const int TV = dv / BV;
     const int nb1 = ((A.seg_bound * HV + 7) / 8) * 8 * TV;
@@ -388,77 +387,6 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     const int sidx = __builtin_amdgcn_readfirstlane(A.seg_idx[sg]);
     if (trans && sidx == 0) return;
     const int hk = h / (HV / H);
-    Tout* op = static_cast<Tout*>(A.o);
-    const float* init = nullptr;  // null: zero state (or the identity for a transition item)
-    float* fin;
-    size_t ibase = 0, fbase;
-    if (trans) {
-        fin = A.ws_Phi;
-        fbase = ((size_t)(sg * HV + h) * DK + (size_t)tile * BV) * DK;
-    } else if (sidx == 0) {
-        init = A.s0;
-        ibase = ((size_t)(n * HV + h) * dv + (size_t)tile * BV) * DK;
-        const bool whole = __builtin_amdgcn_readfirstlane(A.seq_nseg[n]) == 1;
-        fin = whole ? A.s_final : A.ws_E;
-        fbase = whole ? ibase : ((size_t)(sg * HV + h) * dv + (size_t)tile * BV) * DK;
-    } else {
-        fin = A.ws_E;
-        fbase = ((size_t)(sg * HV + h) * dv + (size_t)tile * BV) * DK;
-    }
-
-    // chain: the state of its column blocks
-    f4_t sacc[NJB][2];
-    if (is_chain) {
-#pragma unroll
-        for (int x = 0; x < NJB; ++x)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int i = 16 * ib + lr, j = 16 * (NJB * tb + x) + 4 * lg;
-                if (init) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(init + ibase + (size_t)i * DK + j);
-                    sacc[x][ib] = f4_t{v4.x, v4.y, v4.z, v4.w};
-                } else if (trans) {
-                    const int d = tile * BV + i - j;  // identity: 1 where row == column
-                    sacc[x][ib] = f4_t{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f,
-                                       d == 3 ? 1.f : 0.f};
-                } else {
-                    sacc[x][ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-                }
-            }
-    }
-    auto store_state = [&]() {
-        if (!fin) return;
-#pragma unroll
-        for (int x = 0; x < NJB; ++x)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int i = 16 * ib + lr, j = 16 * (NJB * tb + x) + 4 * lg;
-                if (trans) {
-                    // Phi is stored transposed (Phi^T[j][i]): the combine pass
-                    // reads it as an MFMA B operand, 8 consecutive i per lane
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        fin[(size_t)(sg * HV + h) * DK * DK + (size_t)(j + r) * DK + tile * BV + i] =
-                            sacc[x][ib][r];
-                } else {
-                    *reinterpret_cast<float4*>(fin + fbase + (size_t)i * DK + j) =
-                        make_float4(sacc[x][ib][0], sacc[x][ib][1], sacc[x][ib][2], sacc[x][ib][3]);
-                }
-            }
-    };
-    auto state_to_lds = [&]() {
-#pragma unroll
-        for (int x = 0; x < NJB; ++x)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int off = (16 * ib + lr) * KP + 16 * (NJB * tb + x) + 4 * lg;
-                float sv[4] = {sacc[x][ib][0], sacc[x][ib][1], sacc[x][ib][2], sacc[x][ib][3]};
-                uint2 hi, lo;
-                split4(sv, hi, lo);
-                *reinterpret_cast<uint2*>(&Sh[off]) = hi;
-                *reinterpret_cast<uint2*>(&Sl[off]) = lo;
-            }
-    };
 
     int sq, eq;
     seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
@@ -466,31 +394,352 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     int nch = __builtin_amdgcn_readfirstlane(A.seg_nch[sg]);
     sq += (c_first - min(A.chunk_off[n], A.max_chunks)) * C;  // the segment's first token
     if (c_first + nch > A.max_chunks) nch = max(0, A.max_chunks - c_first);
-    if (nch <= 0) {
-        if (is_chain) store_state();
+    auto chunk_t0 = [&](int jc) { return sq + jc * C; };
+    auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
+
+    if (w < 2) {
+        // ===================== chain wavefront =====================
+        const float* init = nullptr;  // null: zero state (or the identity for a transition item)
+        float* fin;
+        size_t ibase = 0, fbase;
+        if (trans) {
+            fin = A.ws_Phi;
+            fbase = ((size_t)(sg * HV + h) * DK + (size_t)tile * BV) * DK;
+        } else if (sidx == 0) {
+            init = A.s0;
+            ibase = ((size_t)(n * HV + h) * dv + (size_t)tile * BV) * DK;
+            const bool whole = __builtin_amdgcn_readfirstlane(A.seq_nseg[n]) == 1;
+            fin = whole ? A.s_final : A.ws_E;
+            fbase = whole ? ibase : ((size_t)(sg * HV + h) * dv + (size_t)tile * BV) * DK;
+        } else {
+            fin = A.ws_E;
+            fbase = ((size_t)(sg * HV + h) * dv + (size_t)tile * BV) * DK;
+        }
+        const int il = 16 * w + lr;  // the lane's state row in the tile
+        f4_t sacc[NJB];
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            const int j = 16 * jb + 4 * lg;
+            if (init) {
+                const float4 v4 = *reinterpret_cast<const float4*>(init + ibase + (size_t)il * DK + j);
+                sacc[jb] = f4_t{v4.x, v4.y, v4.z, v4.w};
+            } else if (trans) {
+                const int d = tile * BV + il - j;  // identity: 1 where row == column
+                sacc[jb] = f4_t{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f, d == 3 ? 1.f : 0.f};
+            } else {
+                sacc[jb] = f4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        // the state as split-bf16 operands, one per contraction step; also
+        // handed to the output wavefront of these rows
+        bf8_t sh[4], sl[4];
+        auto state_operands = [&]() {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                float sv[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sv[r] = sacc[2 * kk][r];
+                    sv[4 + r] = sacc[2 * kk + 1][r];
+                }
+                split8(sv, sh[kk], sl[kk]);
+                Sx[w][kk][0][l] = sh[kk];
+                Sx[w][kk][1][l] = sl[kk];
+            }
+        };
+        if (nch > 0) {
+            state_operands();
+            __syncthreads();  // B0: chunk 0 staged, the state operands in LDS
+        }
+        for (int jc = 0; jc < nch; ++jc) {
+            const int pb = jc & 1;
+            const int L = chunk_L(jc);
+            const float* G1 = Gs[pb][1];
+            const float* G2 = Gs[pb][2];
+            // ---- phase 1: K S^T [t][i] ----
+            f4_t aks[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) aks[x] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf8_t kf[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) kf[x] = lds8(&Ks[pb][(16 * x + lr) * KR + 32 * kk + 8 * lg]);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    aks[tb] = mfma(kf[tb], sh[kk], aks[tb]);
+                    aks[tb] = mfma(kf[tb], sl[kk], aks[tb]);
+                }
+            }
+            // X = V - diag(gamma) K S^T: V[t = 16 tb + 4 lg + r][i] by a transpose
+            // read (lane m of a 16-lane group points at row 16 tb + 4 lg + m / 4,
+            // columns 16 a + 4 (m % 4) ..)
+            float xv[4][4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const float4 g4 = *reinterpret_cast<const float4*>(&G1[16 * tb + 4 * lg]);
+                const float gam[4] = {g4.x, g4.y, g4.z, g4.w};
+                const v4s_t vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(
+                    &Vs[pb][(16 * tb + 4 * lg + (lr >> 2)) * VR + 16 * w + 4 * (lr & 3)]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    xv[tb][r] = __uint_as_float((uint32_t)(uint16_t)vv[r] << 16) - gam[r] * aks[tb][r];
+            }
+            bf8_t xh[2], xl[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                float v8[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v8[r] = xv[2 * kk][r];
+                    v8[4 + r] = xv[2 * kk + 1][r];
+                }
+                split8(v8, xh[kk], xl[kk]);
+            }
+            // U = T' X (T' lower: steps kk <= tb / 2)
+            f4_t ua[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                ua[tb] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk <= (tb >> 1); ++kk) {
+                    const uint16_t* tt = &Tp[pb][tp_tile(tb, kk) * kTpTileElems + 8 * l];
+                    const bf8_t th = *reinterpret_cast<const bf8_t*>(tt);
+                    const bf8_t tl = *reinterpret_cast<const bf8_t*>(tt + 512);
+                    ua[tb] = mfma(th, xh[kk], ua[tb]);
+                    ua[tb] = mfma(th, xl[kk], ua[tb]);
+                    ua[tb] = mfma(tl, xh[kk], ua[tb]);
+                }
+            }
+            // U to the output wavefront; U' = diag(e^{G_n - G}) U kept
+            bf8_t wh[2], wl[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                float uv[8], wv[8];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int tb = 2 * kk + hh;
+                    const float4 d4 = *reinterpret_cast<const float4*>(&G2[16 * tb + 4 * lg]);
+                    const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        uv[4 * hh + r] = ua[tb][r];
+                        wv[4 * hh + r] = ua[tb][r] * dd[r];
+                    }
+                }
+                bf8_t uh, ul;
+                split8(uv, uh, ul);
+                Ux[w][kk][0][l] = uh;
+                Ux[w][kk][1][l] = ul;
+                split8(wv, wh[kk], wl[kk]);
+            }
+            __syncthreads();  // B1
+            // ---- phase 2: S'^T = gamma_n S^T + K^T U'.  K^T rows j = 16 jb + lr
+            // over the step's token slots: two transpose reads (tokens
+            // 32 kk + 4 lg + m / 4 and 16 more), lane m pointing at the stored
+            // column of j-group 16 jb + 4 (m % 4) ----
+            const float gn = G1[L - 1];
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[jb][r] *= gn;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf8_t kt[NJB];
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+                    const int col = 32 * (jb >> 1) + 8 * (lr & 3) + 4 * (jb & 1);
+                    const __bf16* kp = &Ks[pb][(32 * kk + 4 * lg + (lr >> 2)) * KR + col];
+                    const v4s_t k0 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(kp));
+                    const v4s_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s_t*)(kp + 16 * KR));
+                    kt[jb] = __builtin_bit_cast(bf8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+                    sacc[jb] = mfma(kt[jb], wh[kk], sacc[jb]);
+                    sacc[jb] = mfma(kt[jb], wl[kk], sacc[jb]);
+                }
+            }
+            if (jc + 1 < nch) state_operands();
+            __syncthreads();  // B2
+        }
+        if (fin) {
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int j = 16 * jb + 4 * lg;
+                if (trans) {
+                    // Phi is stored transposed (Phi^T[j][i]): the combine pass
+                    // reads it as an MFMA B operand, 8 consecutive i per lane
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        fin[(size_t)(sg * HV + h) * DK * DK + (size_t)(j + r) * DK + tile * BV + il] = sacc[jb][r];
+                } else {
+                    *reinterpret_cast<float4*>(fin + fbase + (size_t)il * DK + j) =
+                        make_float4(sacc[jb][0], sacc[jb][1], sacc[jb][2], sacc[jb][3]);
+                }
+            }
+        }
         return;
     }
 
-    // ---- helpers: loads of a chunk (into registers) and their staging ----
+    if (nch <= 0) return;
+    if (w < 4) {
+        // ===================== output wavefront =====================
+        const int a = w - 2;  // the chain (rows 16 a ..) whose output this is
+        Tout* op = static_cast<Tout*>(A.o);
+        __syncthreads();  // B0
+        // P tiles of token blocks T0 and T1 (compile-time), from the
+        // (K Q^T)^T blocks pq[x][sb][r] = (K Q^T)^T[s = 16 sb + 4 lg + r][t = 16 T + lr]
+        auto output_step = [&](auto T0c, auto T1c, int jc) {
+            constexpr int T0 = decltype(T0c)::value, T1 = decltype(T1c)::value;
+            const int pb = jc & 1;
+            const int t0 = chunk_t0(jc), L = chunk_L(jc);
+            const float* G0 = Gs[pb][0];
+            const float* G1 = Gs[pb][1];
+            // ---- phase 1: S Q^T [i][t] and the P tiles ----
+            bf8_t sh[4], sl[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                sh[kk] = Sx[a][kk][0][l];
+                sl[kk] = Sx[a][kk][1][l];
+            }
+            f4_t aqs[4], pq0[T0 + 1], pq1[T1 + 1];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) aqs[x] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x <= T0; ++x) pq0[x] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x <= T1; ++x) pq1[x] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf8_t qf[4], kf[T1 + 1];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) qf[x] = lds8(&Qs[pb][(16 * x + lr) * KR + 32 * kk + 8 * lg]);
+#pragma unroll
+                for (int x = 0; x <= T1; ++x) kf[x] = lds8(&Ks[pb][(16 * x + lr) * KR + 32 * kk + 8 * lg]);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    aqs[tb] = mfma(sh[kk], qf[tb], aqs[tb]);
+                    aqs[tb] = mfma(sl[kk], qf[tb], aqs[tb]);
+                }
+#pragma unroll
+                for (int sb = 0; sb <= T0; ++sb) pq0[sb] = mfma(kf[sb], qf[T0], pq0[sb]);
+#pragma unroll
+                for (int sb = 0; sb <= T1; ++sb) pq1[sb] = mfma(kf[sb], qf[T1], pq1[sb]);
+            }
+            auto p_tiles = [&](auto Tc, const f4_t* pq) {
+                constexpr int tb = decltype(Tc)::value;
+                const int t = 16 * tb + lr;
+                const float Gt = G0[t];
+#pragma unroll
+                for (int kk = 0; kk <= (tb >> 1); ++kk) {
+                    float pv[8];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int sb = 2 * kk + hh;
+                        if (sb > tb) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) pv[4 * hh + r] = 0.f;
+                            continue;
+                        }
+                        const float4 g4 = *reinterpret_cast<const float4*>(&G0[16 * sb + 4 * lg]);
+                        const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            // G_t - G_s <= 0 for s <= t; the diagonal block masks
+                            // s > t by a 0 / 1 factor (the factor is finite)
+                            float f = exp2f_(fminf(Gt - gs[r], 0.f));
+                            if (sb == tb) f *= (4 * lg + r <= lr) ? 1.f : 0.f;
+                            pv[4 * hh + r] = pq[sb][r] * f;
+                        }
+                    }
+                    bf8_t ph, pl;
+                    split8(pv, ph, pl);
+                    Px[tp_tile(tb, kk)][0][l] = ph;
+                    Px[tp_tile(tb, kk)][1][l] = pl;
+                }
+            };
+            p_tiles(T0c, pq0);
+            p_tiles(T1c, pq1);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const float gt = G1[16 * tb + lr];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) aqs[tb][r] *= gt;
+            }
+            __syncthreads();  // B1
+            // ---- phase 2: + U^T P^T, then stored: aqs[tb][r] =
+            // O[t = 16 tb + lr][i = 16 a + 4 lg + r]; rows t >= L land at or past
+            // the resource end and are dropped.  A transition item writes w
+            // (fp32, d_k per token and head) instead of o. ----
+            bf8_t uh[2], ul[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uh[kk] = Ux[a][kk][0][l];
+                ul[kk] = Ux[a][kk][1][l];
+            }
+            const __amdgpu_buffer_rsrc_t orsrc =
+                trans ? out_rsrc(A.ws_W + (size_t)t0 * HV * DK, (uint32_t)(L * HV * DK * 4))
+                      : out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int kk = 0; kk <= (tb >> 1); ++kk) {
+                    const bf8_t ph = Px[tp_tile(tb, kk)][0][l];
+                    const bf8_t pl = Px[tp_tile(tb, kk)][1][l];
+                    aqs[tb] = mfma(uh[kk], ph, aqs[tb]);
+                    aqs[tb] = mfma(ul[kk], ph, aqs[tb]);
+                    aqs[tb] = mfma(uh[kk], pl, aqs[tb]);
+                }
+                const int t = 16 * tb + lr;
+                const float ov[4] = {A.scale * aqs[tb][0], A.scale * aqs[tb][1], A.scale * aqs[tb][2],
+                                     A.scale * aqs[tb][3]};
+                if (trans)
+                    out_store4(orsrc, (uint32_t)((t * HV + h) * DK + tile * BV + 16 * a + 4 * lg), ov, A.ws_W);
+                else
+                    out_store4(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * a + 4 * lg), ov, op);
+            }
+            __syncthreads();  // B2
+        };
+        for (int jc = 0; jc < nch; ++jc) {
+            if (a == 0)
+                output_step(TokenBlock<0>{}, TokenBlock<3>{}, jc);
+            else
+                output_step(TokenBlock<1>{}, TokenBlock<2>{}, jc);
+        }
+        return;
+    }
+
+    // ===================== staging wavefronts =====================
+    const int hp = tid - 256;                      // 0..127
     const uint32_t qk_row = (uint32_t)H * DK * 2;  // bytes per token of q, k
     const uint32_t v_row = (uint32_t)HV * dv * 2;  // bytes per token of v
     const uint32_t v_on = trans ? 0u : 1u;         // a transition item reads V as zero
-    // K and Q: piece pi = hp + 256 q of the 64 x 256-byte tile (row pi / 16)
-    uint32_t kq_off[4];
-    int kq_st[4];
+    // K and Q: piece p = hp + 128 q, row p / 16, 16-byte column chunk c = p % 16
+    // holding columns 8 c .. 8 c + 7, stored as two 8-byte halves at their slots
+    uint32_t kq_off[8];
+    int kq_st[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int pi = hp + 256 * q, row = pi >> 4, c16 = pi & 15;
+    for (int q = 0; q < 8; ++q) {
+        const int p = hp + 128 * q, row = p >> 4, c16 = p & 15;
         kq_off[q] = ((uint32_t)row * H + hk) * DK * 2 + 16 * c16;
-        kq_st[q] = row * KP + 8 * c16;
+        // columns 8 c .. 8 c + 3 are slots 4 h + 0..3 of lane group 2 (c % 2)
+        // in step c / 4 (h = (c / 2) % 2), stored at 32 kk + 8 lg + 4 h
+        kq_st[q] = row * KR + 32 * (c16 >> 2) + 16 * (c16 & 1) + 4 * ((c16 >> 1) & 1);
     }
-    // V: token hp / 4, rows 8 (hp % 4) .. + 7 of the tile
-    const int v_tok = hp >> 2, v_row0 = 8 * (hp & 3);
-    const uint32_t v_off = ((uint32_t)v_tok * HV + h) * (uint32_t)dv * 2 + (uint32_t)(tile * BV + v_row0) * 2;
-    bf8_t kst[4], qst[4], vst, tst[3];
-    float gst = 0.f;
-    auto chunk_t0 = [&](int jc) { return sq + jc * C; };
-    auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
+    // V: piece p = hp + 128 q (q < 2): token p / 4, rows 8 (p % 4) .. + 7 of the tile
+    uint32_t v_off[2];
+    int v_st[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int p = hp + 128 * q, tok = p >> 2, part = p & 3;
+        v_off[q] = ((uint32_t)tok * HV + h) * (uint32_t)dv * 2 + (uint32_t)(tile * BV + 8 * part) * 2;
+        v_st[q] = tok * VR + 8 * part;
+    }
+    bf8_t kst[8], qst[8], vst[2], tst[6];
+    float gst = 0.f, gnst = 0.f;
     auto load_chunk = [&](int jc) {
         const int t0 = chunk_t0(jc), L = chunk_L(jc);
         const __amdgpu_buffer_rsrc_t rk =
@@ -500,326 +749,51 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
         const __amdgpu_buffer_rsrc_t rv =
             in_rsrc(static_cast<const bf16_t*>(A.v) + (size_t)t0 * HV * dv, v_on * L * v_row);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 8; ++q) {
             kst[q] = bload8(rk, kq_off[q]);
             qst[q] = bload8(rq, kq_off[q]);
         }
-        vst = bload8(rv, v_off);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) vst[q] = bload8(rv, v_off[q]);
         const uint16_t* tp = A.ws_Tp + ((size_t)(c_first + jc) * HV + h) * kTpElems;
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int pi = hp + 256 * q;
-            if (pi < kTpElems / 8) tst[q] = gld8(tp + 8 * pi);
-        }
-        if (hp < C) gst = A.ws_G[((size_t)(c_first + jc) * HV + h) * C + hp];
+        for (int q = 0; q < 6; ++q) tst[q] = gld8(tp + 8 * (hp + 128 * q));
+        const float* gp = A.ws_G + ((size_t)(c_first + jc) * HV + h) * C;
+        if (hp < C) gst = gp[hp];
+        gnst = gp[L - 1];
     };
     auto stage_chunk = [&](int jc) {
         const int pb = jc & 1;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<bf8_t*>(&Ks[pb][kq_st[q]]) = kst[q];
-            *reinterpret_cast<bf8_t*>(&Qs[pb][kq_st[q]]) = qst[q];
+        for (int q = 0; q < 8; ++q) {
+            const uint4 k4 = __builtin_bit_cast(uint4, kst[q]);
+            const uint4 q4 = __builtin_bit_cast(uint4, qst[q]);
+            *reinterpret_cast<uint2*>(&Ks[pb][kq_st[q]]) = make_uint2(k4.x, k4.y);
+            *reinterpret_cast<uint2*>(&Ks[pb][kq_st[q] + 8]) = make_uint2(k4.z, k4.w);
+            *reinterpret_cast<uint2*>(&Qs[pb][kq_st[q]]) = make_uint2(q4.x, q4.y);
+            *reinterpret_cast<uint2*>(&Qs[pb][kq_st[q] + 8]) = make_uint2(q4.z, q4.w);
         }
-        *reinterpret_cast<bf8_t*>(&Vs[pb][v_tok * VP + v_row0]) = vst;
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int pi = hp + 256 * q;
-            if (pi < kTpElems / 8) *reinterpret_cast<bf8_t*>(&Tp[pb][8 * pi]) = tst[q];
+        for (int q = 0; q < 2; ++q) *reinterpret_cast<bf8_t*>(&Vs[pb][v_st[q]]) = vst[q];
+#pragma unroll
+        for (int q = 0; q < 6; ++q) *reinterpret_cast<bf8_t*>(&Tp[pb][8 * (hp + 128 * q)]) = tst[q];
+        if (hp < C) {
+            Gs[pb][0][hp] = gst;
+            Gs[pb][1][hp] = exp2f_(gst);
+            Gs[pb][2][hp] = exp2f_(gnst - gst);
         }
-        if (hp < C) Gs[pb][hp] = gst;
     };
-
-    // The chain and the helpers run separate loops with the same three
-    // barriers per chunk, so that neither role's registers are held live
-    // across the other's code.
-    if (is_chain) {
-        state_to_lds();
-        __syncthreads();  // B0: the state and chunk 0 in LDS
-        for (int jc = 0; jc < nch; ++jc) {
-            const int L = chunk_L(jc);
-            const int pb = jc & 1;
-            const float* Gc = Gs[pb];
-            // ===== phase A =====
-            // K S^T (tokens of block tb, both 16-row halves) and S Q^T (its
-            // transposed O^T layout), sharing the state fragments; the hi and
-            // lo parts accumulate separately (four independent chains each)
-            f4_t kh[2], kl[2], qh[2], ql[2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                kh[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-                kl[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-                qh[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-                ql[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-            }
-            // every fragment is read before the first product
-            bf8_t ka[NKK], qa[NKK], sh[NKK][2], sl[NKK][2];
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int col = 32 * kk + 8 * lg;
-                ka[kk] = lds8(&Ks[pb][(16 * tb + lr) * KP + col]);
-                qa[kk] = lds8(&Qs[pb][(16 * tb + lr) * KP + col]);
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    sh[kk][ib] = lds8(&Sh[(16 * ib + lr) * KP + col]);
-                    sl[kk][ib] = lds8(&Sl[(16 * ib + lr) * KP + col]);
-                }
-            }
-            // V[t = 16 tb + 4 lg + r][i = 16 ib + lr], r = 0..3, by transpose
-            // reads: lane m of each 16-lane group points at row 16 tb + 4 lg + m / 4,
-            // columns 16 ib + 4 (m % 4) ..
-            v4s_t vr[2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-                vr[ib] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(
-                    &Vs[pb][(16 * tb + 4 * lg + (lr >> 2)) * VP + 16 * ib + 4 * (lr & 3)]));
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    kh[ib] = mfma(ka[kk], sh[kk][ib], kh[ib]);
-                    kl[ib] = mfma(ka[kk], sl[kk][ib], kl[ib]);
-                    qh[ib] = mfma(sh[kk][ib], qa[kk], qh[ib]);
-                    ql[ib] = mfma(sl[kk][ib], qa[kk], ql[ib]);
-                }
-            const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * tb + 4 * lg]);
-            const float gam[4] = {exp2f_(g4.x), exp2f_(g4.y), exp2f_(g4.z), exp2f_(g4.w)};
-            // X = V - diag(gamma) K S^T, rows [i][t] hi / lo
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
-                float vf[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) vf[r] = __uint_as_float((uint32_t)(uint16_t)vr[ib][r] << 16);
-                float xv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) xv[r] = vf[r] - gam[r] * (kh[ib][r] + kl[ib][r]);
-                uint2 hi, lo;
-                split4(xv, hi, lo);
-                *reinterpret_cast<uint2*>(&Xh[off]) = hi;
-                *reinterpret_cast<uint2*>(&Xl[off]) = lo;
-            }
-            // gamma_t (S Q^T)[i][t], t = 16 tb + lr: the O^T tiles' first part
-            const float gt = exp2f_(Gc[16 * tb + lr]);
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                f4_t v_;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v_[r] = gt * (qh[ib][r] + ql[ib][r]);
-                QSs[tb][ib][l] = v_;
-            }
-            __syncthreads();  // B1: X, gamma S Q^T of the chunk in LDS; the next chunk staged
-            // ===== phase U =====
-            // U = T' X for token block tb (T' lower: k-steps kk <= tb / 2)
-            f4_t ua[2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) ua[ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-            with_token_block(tb, [&](auto TB) {
-                constexpr int tbc = decltype(TB)::value;
-                bf8_t th[2], tl[2], xh[2][2], xl[2][2];
-#pragma unroll
-                for (int kk = 0; kk <= (tbc >> 1); ++kk) {
-                    // lanes of the upper half-step (sb = tb + 1) read block 0
-                    // and are zeroed below
-                    const int sb = 2 * kk + (lg >> 1);
-                    const int bi = (sb <= tbc) ? tp_block(tbc, sb) : 0;
-                    const int at = bi * kTpBlockElems + (lr + 16 * (lg & 1)) * 8;
-                    th[kk] = *reinterpret_cast<const bf8_t*>(&Tp[pb][at]);
-                    tl[kk] = *reinterpret_cast<const bf8_t*>(&Tp[pb][at + 256]);
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        xh[kk][ib] = lds8(&Xh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                        xl[kk][ib] = lds8(&Xl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                    }
-                }
-#pragma unroll
-                for (int kk = 0; kk <= (tbc >> 1); ++kk) {
-                    if ((tbc & 1) == 0 && kk == (tbc >> 1) && (lg >> 1)) {  // an upper block: zero
-                        th[kk] = zero8();
-                        tl[kk] = zero8();
-                    }
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        ua[ib] = mfma(th[kk], xh[kk][ib], ua[ib]);
-                        ua[ib] = mfma(th[kk], xl[kk][ib], ua[ib]);
-                        ua[ib] = mfma(tl[kk], xh[kk][ib], ua[ib]);
-                    }
-                }
-            });
-            // ua[ib][r] = U[t = 16 tb + 4 lg + r][i = 16 ib + lr]; U' = diag(e^{G_n - G}) U
-            const float Gn = Gc[L - 1];  // g4: G of the wavefront's tokens, read in phase A
-            const float dd[4] = {exp2f_(Gn - g4.x), exp2f_(Gn - g4.y), exp2f_(Gn - g4.z),
-                                 exp2f_(Gn - g4.w)};
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
-                float uv[4] = {ua[ib][0], ua[ib][1], ua[ib][2], ua[ib][3]};
-                uint2 hi, lo;
-                split4(uv, hi, lo);
-                *reinterpret_cast<uint2*>(&Uh[off]) = hi;
-                *reinterpret_cast<uint2*>(&Ul[off]) = lo;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) uv[r] *= dd[r];
-                split4(uv, hi, lo);
-                *reinterpret_cast<uint2*>(&Wh[off]) = hi;
-                *reinterpret_cast<uint2*>(&Wl[off]) = lo;
-            }
-            __syncthreads();  // B2: U, U' of the chunk in LDS
-            // ===== phase S =====
-            // S'^T = gamma_n S^T + K^T U' for the wavefront's column blocks
-            const float gn = exp2f_(Gc[L - 1]);
-#pragma unroll
-            for (int x = 0; x < NJB; ++x)
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sacc[x][ib][r] *= gn;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf8_t wh[2], wl[2];
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    wh[ib] = lds8(&Wh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                    wl[ib] = lds8(&Wl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                }
-#pragma unroll
-                for (int x = 0; x < NJB; ++x) {
-                    const int jb = NJB * tb + x;
-                    // K^T rows j = 16 jb + lr, tokens 32 kk + 8 lg .. + 7: two
-                    // transpose reads; lane m of each 16-lane group points at
-                    // row 32 kk + 8 lg + m / 4 (+ 4), columns 16 jb + 4 (m % 4) ..
-                    const __bf16* kp_ = &Ks[pb][(32 * kk + 8 * lg + (lr >> 2)) * KP + 16 * jb + 4 * (lr & 3)];
-                    const v4s_t k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s_t*)(kp_));
-                    const v4s_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s_t*)(kp_ + 4 * KP));
-                    const bf8_t kt = __builtin_bit_cast(bf8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        sacc[x][ib] = mfma(kt, wh[ib], sacc[x][ib]);
-                        sacc[x][ib] = mfma(kt, wl[ib], sacc[x][ib]);
-                    }
-                }
-            }
-            // the next chunk's state (S of this chunk was last read in phase A)
-            state_to_lds();
-            __syncthreads();  // B3: the next chunk's state in LDS; U, gamma S Q^T read
-        }
-        store_state();
-    } else {
-        load_chunk(0);
-        stage_chunk(0);
-        if (nch > 1) load_chunk(1);
-        __syncthreads();  // B0
-        bf8_t ph[2], pl[2];  // P fragments of the chunk (B operand, slot order)
-        for (int jc = 0; jc < nch; ++jc) {
-            const int t0 = chunk_t0(jc), L = chunk_L(jc);
-            const int pb = jc & 1;
-            const float* Gc = Gs[pb];
-            // ===== phase A =====
-            // the next chunk into the other buffers; the one after it in flight
-            if (jc + 1 < nch) stage_chunk(jc + 1);
-            if (jc + 2 < nch) load_chunk(jc + 2);
-            __syncthreads();  // B1
-            // ===== phase U =====
-            // P of this chunk for token block tb, decayed and masked, as B
-            // operands in the slot order s = 32 k2 + 16 half + 4 lg + r (slot
-            // 4 half + r): pq[sb][r] = (K Q^T)[s = 16 sb + 4 lg + r][t = 16 tb + lr]
-            // (blocks sb > tb are zero: their fragments stay unset and unread)
-            with_token_block(tb, [&](auto TB) {
-                constexpr int tbc = decltype(TB)::value;
-                f4_t pq[tbc + 1];
-#pragma unroll
-                for (int sb = 0; sb <= tbc; ++sb) pq[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const bf8_t qb = lds8(&Qs[pb][(16 * tbc + lr) * KP + 32 * kk + 8 * lg]);
-                    bf8_t kb[tbc + 1];
-#pragma unroll
-                    for (int sb = 0; sb <= tbc; ++sb) kb[sb] = lds8(&Ks[pb][(16 * sb + lr) * KP + 32 * kk + 8 * lg]);
-#pragma unroll
-                    for (int sb = 0; sb <= tbc; ++sb) pq[sb] = mfma(kb[sb], qb, pq[sb]);
-                }
-                const int t = 16 * tbc + lr;
-                const float Gt = Gc[t];
-#pragma unroll
-                for (int k2 = 0; k2 <= (tbc >> 1); ++k2) {
-                    float pv[8];
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const int sb = 2 * k2 + half;
-                        if (sb > tbc) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) pv[4 * half + r] = 0.f;
-                            continue;
-                        }
-                        const float4 g4 = *reinterpret_cast<const float4*>(&Gc[16 * sb + 4 * lg]);
-                        const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            // Gt - gs <= 0 for s <= t, so the factor is at most 1; the
-                            // diagonal block masks s > t by a 0 / 1 factor
-                            float f = exp2f_(fminf(Gt - gs[r], 0.f));
-                            if (sb == tbc) f *= (4 * lg + r <= lr) ? 1.f : 0.f;
-                            pv[4 * half + r] = pq[sb][r] * f;
-                        }
-                    }
-                    split8(pv, ph[k2], pl[k2]);
-                }
-            });
-            __syncthreads();  // B2
-            // ===== phase S =====
-            // O^T = gamma S Q^T + U^T P^T (P lower: k-steps kk <= tb / 2); U^T
-            // read in the slot order of the P fragments
-            f4_t oacc[2] = {QSs[tb][0][l], QSs[tb][1][l]};
-            with_token_block(tb, [&](auto TB) {
-                constexpr int tbc = decltype(TB)::value;
-                bf8_t uh[2][2], ul[2][2];
-#pragma unroll
-                for (int kk = 0; kk <= (tbc >> 1); ++kk)
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        const int off = (16 * ib + lr) * TP + 32 * kk + 4 * lg;
-                        const uint2 h0 = *reinterpret_cast<const uint2*>(&Uh[off]);
-                        const uint2 h1 = *reinterpret_cast<const uint2*>(&Uh[off + 16]);
-                        const uint2 l0 = *reinterpret_cast<const uint2*>(&Ul[off]);
-                        const uint2 l1 = *reinterpret_cast<const uint2*>(&Ul[off + 16]);
-                        uh[kk][ib] = __builtin_bit_cast(bf8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
-                        ul[kk][ib] = __builtin_bit_cast(bf8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
-                    }
-#pragma unroll
-                for (int kk = 0; kk <= (tbc >> 1); ++kk)
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        oacc[ib] = mfma(uh[kk][ib], ph[kk], oacc[ib]);
-                        oacc[ib] = mfma(ul[kk][ib], ph[kk], oacc[ib]);
-                        oacc[ib] = mfma(uh[kk][ib], pl[kk], oacc[ib]);
-                    }
-            });
-            // oacc[ib][r] = O[t = 16 tb + lr][i = 16 ib + 4 lg + r]; rows t >= L land
-            // at or past the resource end and are dropped.  A transition item
-            // writes w (fp32, d_k per token and head) instead of o.
-            const int t = 16 * tb + lr;
-            if (trans) {
-                float* wp = A.ws_W + (size_t)t0 * HV * DK;
-                const __amdgpu_buffer_rsrc_t wr = out_rsrc(wp, (uint32_t)(L * HV * DK * 4));
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const float ov[4] = {A.scale * oacc[ib][0], A.scale * oacc[ib][1],
-                                         A.scale * oacc[ib][2], A.scale * oacc[ib][3]};
-                    out_store4(wr, (uint32_t)((t * HV + h) * DK + tile * BV + 16 * ib + 4 * lg), ov, wp);
-                }
-            } else {
-                const __amdgpu_buffer_rsrc_t orsrc =
-                    out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const float ov[4] = {A.scale * oacc[ib][0], A.scale * oacc[ib][1],
-                                         A.scale * oacc[ib][2], A.scale * oacc[ib][3]};
-                    out_store4(orsrc, (uint32_t)((t * HV + h) * dv + tile * BV + 16 * ib + 4 * lg), ov, op);
-                }
-            }
-            __syncthreads();  // B3
-        }
+    load_chunk(0);
+    stage_chunk(0);
+    if (nch > 1) load_chunk(1);
+    __syncthreads();  // B0
+    for (int jc = 0; jc < nch; ++jc) {
+        // the next chunk into the other buffers (their last reader finished
+        // before the previous step's second barrier); the one after it in flight
+        if (jc + 1 < nch) stage_chunk(jc + 1);
+        if (jc + 2 < nch) load_chunk(jc + 2);
+        __syncthreads();  // B1
+        __syncthreads();  // B2
     }
 }
 
@@ -827,7 +801,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
 // items blockIdx.x, blockIdx.x + gridDim.x, ... (the grid is a multiple of 8,
 // so an item keeps its XCD).
 template <int DK, typename Tout>
-__global__ __launch_bounds__(512) void scan_tp_kernel(const PrefillArgs A, int items) {
+__global__ __launch_bounds__(384) void scan_tp_kernel(const PrefillArgs A, int items) {
     for (int b = blockIdx.x; b < items; b += gridDim.x) {
         __syncthreads();  // the previous item has finished with the LDS
         scan_tp_item<DK, Tout>(A, b);
@@ -841,10 +815,10 @@ hipError_t launch_prep_tp(const PrefillArgs& A) {
 
 hipError_t launch_scan_tp(const PrefillArgs& A, size_t grid, int items) {
     if (A.o_bf16)
-        hipLaunchKernelGGL((scan_tp_kernel<128, bf16_t>), dim3((unsigned)grid), dim3(512), 0,
+        hipLaunchKernelGGL((scan_tp_kernel<128, bf16_t>), dim3((unsigned)grid), dim3(384), 0,
                            A.stream, A, items);
     else
-        hipLaunchKernelGGL((scan_tp_kernel<128, float>), dim3((unsigned)grid), dim3(512), 0,
+        hipLaunchKernelGGL((scan_tp_kernel<128, float>), dim3((unsigned)grid), dim3(384), 0,
                            A.stream, A, items);
     return hipGetLastError();
 }
