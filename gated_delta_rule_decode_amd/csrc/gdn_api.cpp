@@ -512,16 +512,6 @@ gdn_status gdn_prefill_chunked_norm(const void* q, const void* k, const void* v,
                                   workspace_bytes, need, stream, a, &done);
     if (st != GDN_SUCCESS || done) return st;
     clear_pending();
-    gdn::PrefillArgs f = a;  // the fused form: y in place of o
-    f.o = y;
-    f.o_bf16 = y_dtype == GDN_BF16;
-    f.nz = z;
-    f.nw = w;
-    f.nz_bf16 = z_dtype == GDN_BF16;
-    f.nw_bf16 = w_dtype == GDN_BF16;
-    f.eps = eps;
-    f.ws_o = static_cast<float*>(o_fp32);  // raw outputs of later segments
-    if (!o && gdn::prefill_fuses_norm(f)) return from_hip(gdn::launch_prefill(f));
     st = from_hip(gdn::launch_prefill(a));
     if (st != GDN_SUCCESS) return st;
     const long groups = (long)T_total * HV;

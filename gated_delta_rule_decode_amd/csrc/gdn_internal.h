@@ -94,14 +94,6 @@ struct PrefillArgs {
     float* ws_Phi;       // [seg_bound, HV, dk, dk] transition of a segment
     float* ws_Sin;       // [seg_bound, HV, dv, dk] state entering a segment
     float* ws_W;         // [T, HV, dk] scale Phi_t q_t for tokens of later segments
-    // RMSNormGated fused into the scan (gdn_prefill_chunked_norm): with nz set,
-    // o receives y = o / sqrt(mean(o^2) + eps) * w * silu(z) instead of o
-    const void* nz;      // [T, HV, dv] gate input, or null for no norm
-    const void* nw;      // [dv] weight
-    bool nz_bf16, nw_bf16;
-    float eps;
-    float* ws_o;         // [T, HV, dv] fp32: with the norm and segments, the raw
-                         // outputs of later segments until the correction pass
     hipStream_t stream;
 };
 
@@ -137,10 +129,6 @@ PrefillLayout prefill_layout(int N, int T, int H, int HV, int dk, int dv, bool s
 // (the bf16 MFMA path with segments forced, or allowed and useful by the
 // host's rule); the device plan then decides from the lengths.
 bool prefill_may_segment(int N, int T, int HV, int dk, int dv, bool in_bf16, int seg_req);
-// true when launch_prefill, given nz (and ws_o), writes the normed outputs
-// itself (the per-chain scan, and with segments the correction pass);
-// otherwise nz must be null and the norm runs as its own launch
-bool prefill_fuses_norm(const PrefillArgs& A);
 
 // One decode step of gated full attention (gdn_attn_decode).
 struct AttnArgs {

@@ -848,469 +848,6 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillArgs A, int
 }
 
 // ---------------------------------------------------------------------------
-// scan by rows: one workgroup per chain, a wavefront per 32 state rows
-// ---------------------------------------------------------------------------
-// The same chunk step as scan_mfma (same products, same rounding), arranged
-// so that the workgroup owns a whole head (d_k = d_v = 128: four wavefronts of
-// 32 state rows) and every wavefront runs the full chunk for its rows:
-//   (A) K S^T and S Q^T for all 64 tokens of the chunk and its 32 rows,
-//   X = V - diag(gamma) K S^T, kept in the wavefront's own LDS area,
-//   (B) O^T = scale (S Q^T diag(gamma) + X^T R^T), S'^T = gamma_n S^T + Z^T X.
-// Rows never interact, so the wavefronts need each other only for the
-// chunk's shared operands: K, Q, V rows and the Z^T fragments are loaded once
-// per workgroup (a chunk ahead, into registers) and staged in LDS between two
-// barriers; the R fragments come straight from memory into registers, a chunk
-// ahead.  The state of the wavefront's rows lives in MFMA accumulators
-// (S'^T tiles) and in its LDS area as hi / lo bf16 for the next chunk's (A);
-// X takes the same area while the state is in the accumulators.
-//
-// With a gate type Tz (bf16_t or float; void for none) the workgroup, which
-// holds all d_v outputs of its head, also applies RMSNormGated to them
-// (Qwen3.5-0.8B chat guide, section "Architektur"): per token,
-// y = o / sqrt(mean(o^2) + eps) * w * silu(z), the sum of squares taken over
-// the four wavefronts' rows through LDS, and y is written in place of o.
-// That holds for a sequence's first segment, whose outputs are final; a later
-// segment writes its raw fp32 outputs to ws_o, and the correction pass adds
-// the entering state's part and applies the norm.
-template <typename Tout, typename Tz>
-__device__ __forceinline__ void scan_rows_item(const PrefillArgs& A, const int b) {
-    constexpr bool NORM = !std::is_void_v<Tz>;
-    constexpr int DK = 128, DV = 128, C = kChunk;
-    constexpr int KP = DK + 8;  // padded bf16 row of K, Q and the state
-    constexpr int VP = DV + 8;  // padded bf16 row of the V tile
-    constexpr int TP = C + 8;   // padded bf16 row of X (tokens)
-    constexpr int NJB = DK / 16;
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[C * VP];
-    __shared__ __attribute__((aligned(16))) bf8_t Zf[2][2 * NJB][64];  // Z^T fragments hi, lo
-    __shared__ __attribute__((aligned(16))) float Gs[C];
-    __shared__ __attribute__((aligned(16))) __bf16 Sp[4][2][32 * KP];  // per wavefront: S hi, lo / X
-    __shared__ __attribute__((aligned(16))) float Wn[NORM ? DV : 1];      // norm weight
-    __shared__ __attribute__((aligned(16))) float Nss[NORM ? C * 4 : 1];  // [token][wavefront] sums of o^2
-
-    const int H = A.H, HV = A.HV;
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // rows 32 w .. 32 w + 31
-    __builtin_assume(w >= 0 && w < 4);
-    const int l = tid & 63, lr = l & 15, lg = l >> 4;
-    // value items (segment, head) first, then the transition items of later segments
-    const int nb1 = A.seg_bound * HV;
-    const bool trans = b >= nb1;
-    const int chain = trans ? b - nb1 : b;
-    const int nseg = __builtin_amdgcn_readfirstlane(A.plan[0]);
-    if (chain >= nseg * HV) return;
-    const int sg = chain / HV, h = chain - sg * HV;
-    const int n = __builtin_amdgcn_readfirstlane(A.seg_seq[sg]);
-    const int sidx = __builtin_amdgcn_readfirstlane(A.seg_idx[sg]);
-    if (trans && sidx == 0) return;
-    const int hk = h / (HV / H);
-    Tout* op = static_cast<Tout*>(A.o);
-    if constexpr (NORM) {
-        if (tid < DV)  // read after the first barrier of the chunk loop
-            Wn[tid] = A.nw_bf16 ? bf16_to_f32(static_cast<const bf16_t*>(A.nw)[tid])
-                                : static_cast<const float*>(A.nw)[tid];
-    }
-    const float* init = nullptr;  // null: zero state (or the identity for a transition item)
-    float* fin;
-    size_t ibase = 0, fbase;
-    if (trans) {
-        fin = A.ws_Phi;
-        fbase = (size_t)(sg * HV + h) * DK * DK;
-    } else if (sidx == 0) {
-        init = A.s0;
-        ibase = (size_t)(n * HV + h) * DV * DK;
-        const bool whole = __builtin_amdgcn_readfirstlane(A.seq_nseg[n]) == 1;
-        fin = whole ? A.s_final : A.ws_E;
-        fbase = whole ? ibase : (size_t)(sg * HV + h) * DV * DK;
-    } else {
-        fin = A.ws_E;
-        fbase = (size_t)(sg * HV + h) * DV * DK;
-    }
-
-    // state: sacc[jb][ib][r] = S[i = 32 w + 16 ib + lr][j = 16 jb + 4 lg + r]
-    f4_t sacc[NJB][2];
-#pragma unroll
-    for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const int i = 32 * w + 16 * ib + lr, j = 16 * jb + 4 * lg;
-            if (init) {
-                const float4 v4 = *reinterpret_cast<const float4*>(init + ibase + (size_t)i * DK + j);
-                sacc[jb][ib] = f4_t{v4.x, v4.y, v4.z, v4.w};
-            } else if (trans) {
-                const int d = i - j;  // identity
-                sacc[jb][ib] = f4_t{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f,
-                                    d == 3 ? 1.f : 0.f};
-            } else {
-                sacc[jb][ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-    auto store_state = [&]() {
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int i = 32 * w + 16 * ib + lr, j = 16 * jb + 4 * lg;
-                if (trans) {
-                    // Phi stored transposed (Phi^T[j][i]), as the combine pass reads it
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) fin[fbase + (size_t)(j + r) * DK + i] = sacc[jb][ib][r];
-                } else {
-                    *reinterpret_cast<float4*>(fin + fbase + (size_t)i * DK + j) =
-                        make_float4(sacc[jb][ib][0], sacc[jb][ib][1], sacc[jb][ib][2], sacc[jb][ib][3]);
-                }
-            }
-    };
-    __bf16* const Sh = Sp[w][0];
-    __bf16* const Sl = Sp[w][1];
-    __bf16* const Xh = Sp[w][0];           // X [32 rows][64 tokens] hi, in the state's place
-    __bf16* const Xl = Sp[w][0] + 32 * TP;  // and lo (both inside the hi plane)
-    auto state_to_lds = [&]() {
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int off = (16 * ib + lr) * KP + 16 * jb + 4 * lg;
-                float sv[4] = {sacc[jb][ib][0], sacc[jb][ib][1], sacc[jb][ib][2], sacc[jb][ib][3]};
-                uint2 hi, lo;
-                split4(sv, hi, lo);
-                *reinterpret_cast<uint2*>(&Sh[off]) = hi;
-                *reinterpret_cast<uint2*>(&Sl[off]) = lo;
-            }
-    };
-
-    int sq, eq;
-    seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
-    const int c_first = __builtin_amdgcn_readfirstlane(A.seg_c0[sg]);
-    int nch = __builtin_amdgcn_readfirstlane(A.seg_nch[sg]);
-    sq += (c_first - min(A.chunk_off[n], A.max_chunks)) * C;  // the segment's first token
-    if (c_first + nch > A.max_chunks) nch = max(0, A.max_chunks - c_first);
-    if (nch <= 0) {
-        store_state();
-        return;
-    }
-
-    // ---- loads of a chunk (issued a chunk ahead) ----
-    const uint32_t qk_row = (uint32_t)H * DK * 2;       // bytes per token of q, k
-    const uint32_t v_row = (uint32_t)HV * DV * 2;       // bytes per token of v
-    const uint32_t v_on = trans ? 0u : 1u;              // a transition item reads V as zero
-    // cooperative pieces: 16 bytes, piece p = tid + 256 q of a 64 x 256-byte tile
-    uint32_t kq_off[4], v_off[4];
-    int st_off[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int p = tid + 256 * q, row = p >> 4, c16 = p & 15;
-        kq_off[q] = ((uint32_t)row * H + hk) * DK * 2 + 16 * c16;
-        v_off[q] = ((uint32_t)row * HV + h) * DV * 2 + 16 * c16;
-        st_off[q] = row * KP + 8 * c16;  // KP == VP
-    }
-    bf8_t kst[4], qst[4], vst[4], zst[2][4];
-    float gst = 0.f;
-    struct RF {
-        bf8_t h[4][2], lo[4][2];  // R fragments (row block tb, k-step kk), hi / lo
-    };
-    RF rn, rc;  // next chunk's, this chunk's
-    auto chunk_t0 = [&](int jc) { return sq + jc * C; };
-    auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
-    auto load_chunk = [&](int jc) {
-        const int t0 = chunk_t0(jc), L = chunk_L(jc);
-        const __amdgpu_buffer_rsrc_t rk =
-            in_rsrc(static_cast<const bf16_t*>(A.k) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
-        const __amdgpu_buffer_rsrc_t rq =
-            in_rsrc(static_cast<const bf16_t*>(A.q) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
-        const __amdgpu_buffer_rsrc_t rv =
-            in_rsrc(static_cast<const bf16_t*>(A.v) + (size_t)t0 * HV * DV, v_on * L * v_row);
-        const size_t cc = (size_t)(c_first + jc) * HV + h;
-        const __amdgpu_buffer_rsrc_t zh = in_rsrc(A.ws_Zh + cc * DK * C, DK * C * 2);
-        const __amdgpu_buffer_rsrc_t zl = in_rsrc(A.ws_Zl + cc * DK * C, DK * C * 2);
-        const __amdgpu_buffer_rsrc_t rh = in_rsrc(A.ws_Rh + cc * C * C, C * C * 2);
-        const __amdgpu_buffer_rsrc_t rl = in_rsrc(A.ws_Rl + cc * C * C, C * C * 2);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            kst[q] = bload8(rk, kq_off[q]);
-            qst[q] = bload8(rq, kq_off[q]);
-            vst[q] = bload8(rv, v_off[q]);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            zst[0][q] = bload8(zh, (uint32_t)(tid + 256 * q) * 16);
-            zst[1][q] = bload8(zl, (uint32_t)(tid + 256 * q) * 16);
-        }
-        if (tid < C) gst = A.ws_G[cc * C + tid];
-        // R: fragment (tb, kk) is 1 KiB at 1024 (2 tb + kk); row blocks 0, 1 need k-step 0 only
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk <= (tb >> 1)) {
-                    rn.h[tb][kk] = bload8(rh, (uint32_t)(1024 * (2 * tb + kk) + 16 * l));
-                    rn.lo[tb][kk] = bload8(rl, (uint32_t)(1024 * (2 * tb + kk) + 16 * l));
-                } else {
-                    rn.h[tb][kk] = zero8();
-                    rn.lo[tb][kk] = zero8();
-                }
-            }
-    };
-    auto stage_chunk = [&]() {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<bf8_t*>(&Ks[st_off[q]]) = kst[q];
-            *reinterpret_cast<bf8_t*>(&Qs[st_off[q]]) = qst[q];
-            *reinterpret_cast<bf8_t*>(&Vs[st_off[q]]) = vst[q];
-            const int p = tid + 256 * q;
-            Zf[0][p >> 6][p & 63] = zst[0][q];
-            Zf[1][p >> 6][p & 63] = zst[1][q];
-        }
-        if (tid < C) Gs[tid] = gst;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                rc.h[tb][kk] = rn.h[tb][kk];
-                rc.lo[tb][kk] = rn.lo[tb][kk];
-            }
-    };
-
-    load_chunk(0);
-    state_to_lds();
-    for (int jc = 0; jc < nch; ++jc) {
-        const int t0 = chunk_t0(jc), L = chunk_L(jc);
-        __syncthreads();  // every wavefront is done with the previous chunk's shared operands
-        stage_chunk();
-        __syncthreads();
-        load_chunk(min(jc + 1, nch - 1));  // the last chunk loads itself again
-
-        // decays of this chunk (G in log2 units)
-        float gt[4], gam[4][4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            gt[tb] = exp2f_(Gs[16 * tb + lr]);
-            const float4 g4 = *reinterpret_cast<const float4*>(&Gs[16 * tb + 4 * lg]);
-            gam[tb][0] = exp2f_(g4.x);
-            gam[tb][1] = exp2f_(g4.y);
-            gam[tb][2] = exp2f_(g4.z);
-            gam[tb][3] = exp2f_(g4.w);
-        }
-        const float gn = exp2f_(Gs[L - 1]);
-
-        // (A) ksa[tb][ib][r] = (K S^T)[t = 16 tb + 4 lg + r][i = 16 ib + lr]
-        //     qsa[tb][ib][r] = (S Q^T)[i = 16 ib + 4 lg + r][t = 16 tb + lr]
-        f4_t ksa[4][2], qsa[4][2];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                ksa[tb][ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-                qsa[tb][ib] = f4_t{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            const int col = 32 * kk + 8 * lg;
-            bf8_t sh[2], sl[2], ka[4], qa[4];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                sh[ib] = lds8(&Sh[(16 * ib + lr) * KP + col]);
-                sl[ib] = lds8(&Sl[(16 * ib + lr) * KP + col]);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                ka[tb] = lds8(&Ks[(16 * tb + lr) * KP + col]);
-                qa[tb] = lds8(&Qs[(16 * tb + lr) * KP + col]);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    ksa[tb][ib] = mfma(ka[tb], sh[ib], ksa[tb][ib]);
-                    qsa[tb][ib] = mfma(sh[ib], qa[tb], qsa[tb][ib]);
-                    ksa[tb][ib] = mfma(ka[tb], sl[ib], ksa[tb][ib]);
-                    qsa[tb][ib] = mfma(sl[ib], qa[tb], qsa[tb][ib]);
-                }
-        }
-        // X = V - diag(gamma) K S^T (zero in rows past the end: V and K read as zero),
-        // into the wavefront's area as X[i][t] hi / lo
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                float xv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float vv = static_cast<float>(Vs[(16 * tb + 4 * lg + r) * VP + 32 * w + 16 * ib + lr]);
-                    xv[r] = vv - gam[tb][r] * ksa[tb][ib][r];
-                }
-                uint2 hi, lo;
-                split4(xv, hi, lo);
-                const int off = (16 * ib + lr) * TP + 16 * tb + 4 * lg;
-                *reinterpret_cast<uint2*>(&Xh[off]) = hi;
-                *reinterpret_cast<uint2*>(&Xl[off]) = lo;
-            }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // the norm's gate inputs for this lane's outputs (zero past the end),
-        // in flight during (B)
-        typedef std::conditional_t<std::is_same_v<Tz, float>, float4, uint2> zraw_t;
-        zraw_t zr[4][2];
-        if constexpr (NORM) {
-            const __amdgpu_buffer_rsrc_t zrs = in_rsrc(static_cast<const Tz*>(A.nz) + (size_t)t0 * HV * DV,
-                                                       (uint32_t)(L * HV * DV * sizeof(Tz)));
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const int off = (int)((((16 * tb + lr) * HV + h) * DV + 32 * w + 16 * ib + 4 * lg) * sizeof(Tz));
-                    if constexpr (std::is_same_v<Tz, float>)
-                        zr[tb][ib] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(zrs, off, 0, 0));
-                    else
-                        zr[tb][ib] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zrs, off, 0, 0));
-                }
-        }
-        // (B) X fragments: k-step kk (tokens 32 kk + 8 lg ..), rows 16 ib + lr
-        bf8_t xh[2][2], xl[2][2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                xh[kk][ib] = lds8(&Xh[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-                xl[kk][ib] = lds8(&Xl[(16 * ib + lr) * TP + 32 * kk + 8 * lg]);
-            }
-        // O^T = scale (S Q^T diag(gamma) + X^T R^T); R is lower triangular, so
-        // row block tb needs the k-steps up to tb / 2
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) qsa[tb][ib][r] *= gt[tb];
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (kk <= (tb >> 1)) {
-                        qsa[tb][ib] = mfma(xh[kk][ib], rc.h[tb][kk], qsa[tb][ib]);
-                        qsa[tb][ib] = mfma(xl[kk][ib], rc.h[tb][kk], qsa[tb][ib]);
-                        qsa[tb][ib] = mfma(xh[kk][ib], rc.lo[tb][kk], qsa[tb][ib]);
-                    }
-                }
-            }
-        // S'^T = gamma_n S^T + Z^T X
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
-            bf8_t zh[2], zl[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                zh[kk] = Zf[0][2 * jb + kk][l];
-                zl[kk] = Zf[1][2 * jb + kk][l];
-            }
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sacc[jb][ib][r] *= gn;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    sacc[jb][ib] = mfma(zh[kk], xh[kk][ib], sacc[jb][ib]);
-                    sacc[jb][ib] = mfma(zh[kk], xl[kk][ib], sacc[jb][ib]);
-                    sacc[jb][ib] = mfma(zl[kk], xh[kk][ib], sacc[jb][ib]);
-                }
-            }
-        }
-        // outputs: qsa[tb][ib][r] = O[t = 16 tb + lr][i = 32 w + 16 ib + 4 lg + r]
-        // (w for a transition item); rows t >= L land past the resource end
-        {
-            const int trow = lr;
-            if (trans) {
-                float* wp = A.ws_W + (size_t)t0 * HV * DK;
-                const __amdgpu_buffer_rsrc_t wr = out_rsrc(wp, (uint32_t)(L * HV * DK * 4));
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        const float ov[4] = {A.scale * qsa[tb][ib][0], A.scale * qsa[tb][ib][1],
-                                             A.scale * qsa[tb][ib][2], A.scale * qsa[tb][ib][3]};
-                        out_store4(wr, (uint32_t)(((16 * tb + trow) * HV + h) * DK + 32 * w + 16 * ib + 4 * lg),
-                                   ov, wp);
-                    }
-            } else {
-                // with the norm, a later segment's raw outputs go to ws_o for the
-                // correction pass (fp32 outputs only: the host fuses the norm
-                // into segmented runs only then)
-                const bool normed = NORM && sidx == 0;
-                Tout* const dst = (NORM && !normed) ? reinterpret_cast<Tout*>(A.ws_o) : op;
-                const __amdgpu_buffer_rsrc_t orsrc =
-                    out_rsrc(dst + (size_t)t0 * HV * DV, (uint32_t)(L * HV * DV * sizeof(Tout)));
-                float inv[4] = {1.f, 1.f, 1.f, 1.f};
-                if (normed) {
-                    // sum of o^2 over this wavefront's 32 rows of token 16 tb + lr
-                    // (the four lane groups lg), then over the wavefronts
-#pragma unroll
-                    for (int tb = 0; tb < 4; ++tb) {
-                        float ss = 0.f;
-#pragma unroll
-                        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float o = A.scale * qsa[tb][ib][r];
-                                ss = __builtin_fmaf(o, o, ss);
-                            }
-                        ss += swz_xor16(ss);
-                        ss += xor32(ss);
-                        if (lg == 0) Nss[(16 * tb + lr) * 4 + w] = ss;
-                    }
-                    __syncthreads();
-#pragma unroll
-                    for (int tb = 0; tb < 4; ++tb) {
-                        const float4 p = *reinterpret_cast<const float4*>(&Nss[(16 * tb + lr) * 4]);
-                        inv[tb] = 1.0f / sqrtf((((p.x + p.y) + p.z) + p.w) * (1.0f / DV) + A.eps);
-                    }
-                }
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        float ov[4] = {A.scale * qsa[tb][ib][0], A.scale * qsa[tb][ib][1],
-                                       A.scale * qsa[tb][ib][2], A.scale * qsa[tb][ib][3]};
-                        if (normed) {
-                            float zv[4];
-                            if constexpr (std::is_same_v<Tz, float>) {
-                                zv[0] = zr[tb][ib].x; zv[1] = zr[tb][ib].y;
-                                zv[2] = zr[tb][ib].z; zv[3] = zr[tb][ib].w;
-                            } else {
-                                zv[0] = __uint_as_float(zr[tb][ib].x << 16);
-                                zv[1] = __uint_as_float(zr[tb][ib].x & 0xffff0000u);
-                                zv[2] = __uint_as_float(zr[tb][ib].y << 16);
-                                zv[3] = __uint_as_float(zr[tb][ib].y & 0xffff0000u);
-                            }
-                            const float4 wv = *reinterpret_cast<const float4*>(&Wn[32 * w + 16 * ib + 4 * lg]);
-                            const float wr[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                ov[r] = ov[r] * inv[tb] * wr[r] * silu_hw(zv[r]);
-                        }
-                        out_store4(orsrc,
-                                   (uint32_t)(((16 * tb + trow) * HV + h) * DV + 32 * w + 16 * ib + 4 * lg),
-                                   ov, dst);
-                    }
-            }
-        }
-        // the next chunk's state (X is no longer read: same wavefront, in order)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        state_to_lds();
-    }
-    store_state();
-}
-
-// One item per workgroup (a loop over items, as in scan_mfma_kernel, costs
-// this kernel registers it does not have: values hoisted out of the loop
-// spill at 512 VGPRs).
-template <typename Tout, typename Tz>
-__global__ __launch_bounds__(256) void scan_rows_kernel(const PrefillArgs A) {
-    scan_rows_item<Tout, Tz>(A, blockIdx.x);
-}
-
-// ---------------------------------------------------------------------------
 // segment-parallel scan: plan, combine, correction
 // ---------------------------------------------------------------------------
 // The chunk map of a segment is affine in the state entering it:
@@ -1371,7 +908,7 @@ constexpr int kNCand = 7;
 constexpr int kPlanCache = 2048;
 
 __global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A, int TV, int TK,
-                                                            int rows) {
+                                                            int tp) {
     __shared__ int ibuf[256];
     __shared__ int cnt_sh[kPlanCache], off_sh[kPlanCache];
     __shared__ float acc[3][kNCand];  // items, chain steps, tokens of later segments
@@ -1453,9 +990,12 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A,
             const float dk = (float)A.dk, dv = (float)A.dv;
             float best = 0.f;
             int bestL = 0;
-            const float thr = rows ? 46.f : 110.f;
+            // chain steps per microsecond over the whole GPU, and the time of one
+            // chain step (us) for a number of items; the d_k = 128 scan holds one
+            // workgroup per CU, so its step does not grow with the items
+            const float thr = tp ? 120.f : 110.f;
             auto step_of = [&](float items) {
-                return rows ? 5.6f : (items <= 64.f ? 2.2f : (items <= 256.f ? 2.6f : 4.5f));
+                return tp ? 2.1f : (items <= 64.f ? 2.2f : (items <= 256.f ? 2.6f : 4.5f));
             };
             const bool skewed = (float)cm * step_of(acc[0][0]) > 2.f * acc[1][0] / thr;
             for (int k = 0; k < (acc[0][0] < 256.f || skewed ? kNCand : 1); ++k) {
@@ -1645,13 +1185,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const PrefillArgs A) {
 // is (group of kCorrChunks chunks of one segment, value head); S_in of the
 // item is staged in LDS once, wavefront w takes tokens 16 w .. 16 w + 15 of
 // each chunk.  Persistent over items.
-// With a gate type Tz (d_v = 128; void for none) the raw outputs come from
-// ws_o and leave as RMSNormGated's y: a wavefront holds every output of its
-// 16 tokens (the 4 lane groups lg times the 8 blocks nb), so the sum of
-// squares is a sum over lg and needs no LDS.
-template <int DK, typename Tout, typename Tz>
+template <int DK, typename Tout>
 __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
-    constexpr bool NORM = !std::is_void_v<Tz>;
     constexpr int C = kChunk;
     constexpr int KP = DK + 8;
     constexpr int NKK = DK / 32;
@@ -1701,88 +1236,26 @@ __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
                 split8(x, wh[kk], wl[kk]);
             }
             const __amdgpu_buffer_rsrc_t orr = out_rsrc(op + (size_t)t0 * HV * dv, (uint32_t)(L * HV * dv * sizeof(Tout)));
-            if constexpr (NORM) {
-                constexpr int NB = 128 / 16;  // d_v = 128
-                float* rp = A.ws_o + (size_t)t0 * HV * 128;
-                const __amdgpu_buffer_rsrc_t rr = out_rsrc(rp, (uint32_t)(L * HV * 128 * 4));
-                const __amdgpu_buffer_rsrc_t zrs = in_rsrc(static_cast<const Tz*>(A.nz) + (size_t)t0 * HV * 128,
-                                                           (uint32_t)(L * HV * 128 * sizeof(Tz)));
-                float ov[NB][4];
-                float ss = 0.f;
+            for (int nb = 0; nb < dv / 16; ++nb) {
+                f4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    f4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < NKK; ++kk) {
-                        const bf8_t ah = lds8(&Sh[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
-                        const bf8_t al = lds8(&Sl[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
-                        d = mfma(ah, wh[kk], d);
-                        d = mfma(al, wh[kk], d);
-                        d = mfma(ah, wl[kk], d);
-                    }
-                    const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * 128 + 16 * nb + 4 * lg;
-                    load4_any(rr, off, ov[nb], rp);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        ov[nb][r] += d[r];
-                        ss = __builtin_fmaf(ov[nb][r], ov[nb][r], ss);
-                    }
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const bf8_t ah = lds8(&Sh[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
+                    const bf8_t al = lds8(&Sl[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
+                    d = mfma(ah, wh[kk], d);
+                    d = mfma(al, wh[kk], d);
+                    d = mfma(ah, wl[kk], d);
                 }
-                ss += swz_xor16(ss);
-                ss += xor32(ss);
-                const float inv = 1.0f / sqrtf(ss * (1.0f / 128) + A.eps);
+                // d[r] = (S_in W^T)[i = 16 nb + 4 lg + r][t = 16 w + lr]
+                const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * dv + 16 * nb + 4 * lg;
+                float ov[4];
+                load4_any(orr, off, ov, op);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * 128 + 16 * nb + 4 * lg;
-                    float zv[4];
-                    load4_any(zrs, off, zv, static_cast<Tz*>(nullptr));
-                    float y[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = 16 * nb + 4 * lg + r;
-                        const float wi = A.nw_bf16 ? bf16_to_f32(static_cast<const bf16_t*>(A.nw)[i])
-                                                   : static_cast<const float*>(A.nw)[i];
-                        y[r] = ov[nb][r] * inv * wi * silu_hw(zv[r]);
-                    }
-                    out_store4(orr, off, y, op);
-                }
-            } else {
-                for (int nb = 0; nb < dv / 16; ++nb) {
-                    f4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < NKK; ++kk) {
-                        const bf8_t ah = lds8(&Sh[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
-                        const bf8_t al = lds8(&Sl[(16 * nb + lr) * KP + 32 * kk + 8 * lg]);
-                        d = mfma(ah, wh[kk], d);
-                        d = mfma(al, wh[kk], d);
-                        d = mfma(ah, wl[kk], d);
-                    }
-                    // d[r] = (S_in W^T)[i = 16 nb + 4 lg + r][t = 16 w + lr]
-                    const uint32_t off = (uint32_t)((16 * w + lr) * HV + h) * dv + 16 * nb + 4 * lg;
-                    float ov[4];
-                    load4_any(orr, off, ov, op);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ov[r] += d[r];
-                    out_store4(orr, off, ov, op);
-                }
+                for (int r = 0; r < 4; ++r) ov[r] += d[r];
+                out_store4(orr, off, ov, op);
             }
         }
     }
-}
-
-constexpr size_t kRowsMinChains = 512;
-constexpr size_t kRowsMinTokensPerSeq = 16384;
-
-// At d_k = d_v = 128, one workgroup per chain (scan_rows_kernel: more work
-// per CU and chunk step) when there are many chains, or when long sequences
-// on fewer chains than CUs may be segmented (the segments then fill the CUs);
-// otherwise one workgroup per 32 state rows of a chain (scan_mfma_kernel, the
-// shorter chunk step)
-static bool use_rows(const PrefillArgs& A, int dk) {
-    return dk == 128 && A.dv == 128 &&
-           ((size_t)A.N * A.HV >= kRowsMinChains ||
-            (A.seg_req != -1 && (size_t)A.N * A.HV < 256 &&
-             (size_t)A.T >= kRowsMinTokensPerSeq * (size_t)A.N));
 }
 
 // Segmentation is possible when asked for; automatically (seg_req 0) when
@@ -1793,8 +1266,8 @@ static bool use_rows(const PrefillArgs& A, int dk) {
 // lengths).  Otherwise the plan is fixed to one segment per sequence and the
 // later passes are not launched: a possible plan costs their two launches
 // even when it turns out to be unsegmented.
-static bool may_segment(const PrefillArgs& A, int dk) {
-    const size_t TV = use_rows(A, dk) ? 1 : (size_t)A.dv / 32;
+static bool may_segment(const PrefillArgs& A) {
+    const size_t TV = (size_t)A.dv / 32;
     const bool longer = (A.T + kChunk - 1) / kChunk > kSegMinChunks;
     return A.seg_req > 0 || (A.seg_req == kSegAutoSkewed && longer) ||
            (A.seg_req == 0 && longer && (size_t)A.N * A.HV * TV < 256);
@@ -1804,16 +1277,14 @@ static bool may_segment(const PrefillArgs& A, int dk) {
 // Without segmentation the last two find no work and exit.
 template <int DK, typename Tout>
 static hipError_t launch_mfma_t(const PrefillArgs& A0) {
-    const bool rows = use_rows(A0, DK);
-    const int TV = rows ? 1 : A0.dv / 32, TK = rows ? 1 : DK / 32;
+    const int TV = A0.dv / 32, TK = DK / 32;
     PrefillArgs A = A0;
-    const bool may = may_segment(A0, DK);
+    const bool may = may_segment(A0);
     if (!may) A.seg_req = -1;
-    hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK,
-                       rows ? 1 : 0);
-    // d_k = 128 without the per-chain scan: the T'-only prep and the chain /
-    // helper scan (gdn_prefill_tp.hip); otherwise the prep with R and Z^T
-    const bool tp = DK == 128 && !rows;
+    // d_k = 128: the T'-only prep and the four-role scan (gdn_prefill_tp.hip);
+    // d_k = 64: the prep with R and Z^T and the per-tile scan
+    const bool tp = DK == 128;
+    hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, A.stream, A, TV, TK, tp ? 1 : 0);
     hipError_t err = tp ? launch_prep_tp(A) : hipSuccess;
     if (!tp)
         hipLaunchKernelGGL((prep_mfma_kernel<DK>), dim3(A.max_chunks, A.HV), dim3(256), 0,
@@ -1821,47 +1292,27 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
     if (err == hipSuccess) err = hipGetLastError();
     if (err != hipSuccess) return err;
     // value items of up to seg_bound segments (N without segmentation), then
-    // the transition items; the kernel splits the grid at seg_bound
-    // the grid of the per-tile scan: every possible item when the
-    // unsegmented items leave CUs idle, otherwise just the unsegmented items
-    // (any segments' items are then taken by the same workgroups in turn, and
-    // when there are none no workgroup is launched only to exit)
-    if (rows) {
-        const size_t items = may ? (size_t)2 * A.seg_bound * A.HV : (size_t)A.N * A.HV;
-        const dim3 grid((unsigned)items);
-        if (A.nz && A.nz_bf16)
-            hipLaunchKernelGGL((scan_rows_kernel<Tout, bf16_t>), grid, dim3(256), 0, A.stream, A);
-        else if (A.nz)
-            hipLaunchKernelGGL((scan_rows_kernel<Tout, float>), grid, dim3(256), 0, A.stream, A);
-        else
-            hipLaunchKernelGGL((scan_rows_kernel<Tout, void>), grid, dim3(256), 0, A.stream, A);
+    // the transition items; the kernel splits the grid at seg_bound.  The grid
+    // takes every possible item when the unsegmented items leave CUs idle,
+    // otherwise just the unsegmented items (any segments' items are then taken
+    // by the same workgroups in turn, and when there are none no workgroup is
+    // launched only to exit)
+    const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * A.HV + 7) / 8) * 8;
+    const size_t items = may ? chains8 * (TV + TK) : chains8 * TV;
+    const size_t unseg = (size_t)((A.N * A.HV + 7) / 8) * 8 * TV;
+    const size_t grid = (may && (size_t)A.N * A.HV * TV < 256) ? items : unseg;
+    if (tp) {
+        err = launch_scan_tp(A, grid, (int)items);
+        if (err != hipSuccess) return err;
     } else {
-        const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * A.HV + 7) / 8) * 8;
-        const size_t items = may ? chains8 * (TV + TK) : chains8 * TV;
-        const size_t unseg = (size_t)((A.N * A.HV + 7) / 8) * 8 * TV;
-        const size_t grid = (may && (size_t)A.N * A.HV * TV < 256) ? items : unseg;
-        if (tp) {
-            err = launch_scan_tp(A, grid, (int)items);
-            if (err != hipSuccess) return err;
-        } else {
-            hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)grid), dim3(256), 0,
-                               A.stream, A, (int)items);
-        }
+        hipLaunchKernelGGL((scan_mfma_kernel<DK, Tout>), dim3((unsigned)grid), dim3(256), 0,
+                           A.stream, A, (int)items);
     }
     if (may) {
         const int cgrid = (int)std::min<size_t>((size_t)A.N * A.HV * TV, 512);
         hipLaunchKernelGGL((combine_kernel<DK>), dim3(cgrid), dim3(256), 0, A.stream, A);
         const int rgrid = (int)std::min<size_t>((size_t)A.corr_bound * A.HV, 512);
-        if constexpr (DK == 128) {
-            if (A.nz && A.nz_bf16)
-                hipLaunchKernelGGL((correct_kernel<DK, Tout, bf16_t>), dim3(rgrid), dim3(256), 0, A.stream, A);
-            else if (A.nz)
-                hipLaunchKernelGGL((correct_kernel<DK, Tout, float>), dim3(rgrid), dim3(256), 0, A.stream, A);
-            else
-                hipLaunchKernelGGL((correct_kernel<DK, Tout, void>), dim3(rgrid), dim3(256), 0, A.stream, A);
-        } else {
-            hipLaunchKernelGGL((correct_kernel<DK, Tout, void>), dim3(rgrid), dim3(256), 0, A.stream, A);
-        }
+        hipLaunchKernelGGL((correct_kernel<DK, Tout>), dim3(rgrid), dim3(256), 0, A.stream, A);
     }
     return hipGetLastError();
 }
@@ -1873,13 +1324,7 @@ bool prefill_mfma_eligible(const PrefillArgs& A) {
 bool prefill_may_segment(int N, int T, int HV, int dk, int dv, bool in_bf16, int seg_req) {
     PrefillArgs A{};
     A.N = N; A.T = T; A.HV = HV; A.dk = dk; A.dv = dv; A.in_bf16 = in_bf16; A.seg_req = seg_req;
-    return prefill_mfma_eligible(A) && may_segment(A, dk);
-}
-
-bool prefill_fuses_norm(const PrefillArgs& A) {
-    // with segments the later segments' raw outputs pass through the output
-    // type: fused then only for fp32 outputs
-    return prefill_mfma_eligible(A) && use_rows(A, A.dk) && (!A.o_bf16 || !may_segment(A, A.dk));
+    return prefill_mfma_eligible(A) && may_segment(A);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& A) {

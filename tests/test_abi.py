@@ -107,13 +107,11 @@ def test_prefill_validation(L):
 
 def _may_segment(N, T, HV, dk, dv, seg_req):
     """The host's rule for whether a bf16 call can take the segment-parallel
-    scan (the per-chain scan at d = 128 with many chains or long prompts on
-    few; segments when forced, or when the chains leave CUs idle)."""
+    scan: segments when forced, always possible under the skewed automatic
+    mode, or automatically when the (chain, 32-row tile) items leave CUs idle."""
     if dk not in (64, 128) or dv % 32:
         return False
-    rows = dk == 128 and dv == 128 and (N * HV >= 512 or (seg_req != -1 and N * HV < 256
-                                                           and T >= 16384 * N))
-    TV = 1 if rows else dv // 32
+    TV = dv // 32
     longer = (T + 63) // 64 > 32
     return seg_req > 0 or (seg_req == -2 and longer) or (seg_req == 0 and longer
                                                           and N * HV * TV < 256)
