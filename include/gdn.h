@@ -312,13 +312,9 @@ gdn_status gdn_prefill_chunked_noalloc(const void* q, const void* k, const void*
  *   eps >= 0; chunk must be 64
  *   workspace device memory of workspace_bytes >=
  *             gdn_prefill_norm_workspace_bytes(...) (256-byte aligned)
- * Where the scan runs one workgroup per head (d_k = d_v = 128, with at least
- * 512 (sequence, value head) chains or long prompts on fewer) and o is NULL,
- * the norm is applied inside the scan and o never reaches memory; when such a
- * prompt is cut into segments (fp32 y only), the later segments' raw outputs
- * pass through the workspace in fp32 and the correction pass applies the norm.
- * Otherwise the raw outputs go to o (or, in fp32, to the workspace) and a
- * second launch applies the norm.  y may not be o.  Errors as
+ * The raw outputs go to o (or, when o is NULL, in fp32 to the workspace) and
+ * a second launch applies the norm: a head's outputs come from four
+ * workgroups, one per 32 state rows.  y may not be o.  Errors as
  * gdn_prefill_chunked, plus GDN_ERROR_INVALID_VALUE for a missing or
  * misaligned z, w or y, y == o or a negative eps.
  */
