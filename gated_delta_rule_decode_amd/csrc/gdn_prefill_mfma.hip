@@ -1297,9 +1297,12 @@ static hipError_t launch_mfma_t(const PrefillArgs& A0) {
     // otherwise just the unsegmented items (any segments' items are then taken
     // by the same workgroups in turn, and when there are none no workgroup is
     // launched only to exit)
-    const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * A.HV + 7) / 8) * 8;
+    // (the four-role scan counts chains by key head, R value heads each)
+    const size_t R = tp ? (size_t)(A.HV / A.H) : 1;
+    const size_t CH = tp ? (size_t)A.H : (size_t)A.HV;
+    const size_t chains8 = (size_t)(((may ? A.seg_bound : A.N) * CH + 7) / 8) * 8 * R;
     const size_t items = may ? chains8 * (TV + TK) : chains8 * TV;
-    const size_t unseg = (size_t)((A.N * A.HV + 7) / 8) * 8 * TV;
+    const size_t unseg = (size_t)((A.N * CH + 7) / 8) * 8 * R * TV;
     const size_t grid = (may && (size_t)A.N * A.HV * TV < 256) ? items : unseg;
     if (tp) {
         err = launch_scan_tp(A, grid, (int)items);

@@ -323,12 +323,13 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
 // scan: sequential over chunks; state rows split over chain wavefronts, the
 // output over output wavefronts
 // ---------------------------------------------------------------------------
-// Work items as in the per-tile scan: (segment, value head, 32-row tile of
-// S) value items first, then the transition items of later segments (the same
-// scan from the identity with V read as zero: d_k rows, writing
-// w = scale Phi_t q_t instead of o and Phi^T instead of the state).  All tiles
-// of a chain get the same b % 8 and neighbouring dispatch slots (workgroup b
-// runs on XCD b % 8), so their shared K, Q reads meet in one L2.
+// Work items: (segment, value head, 32-row tile of S) value items first, then
+// the transition items of later segments (the same scan from the identity
+// with V read as zero: d_k rows, writing w = scale Phi_t q_t instead of o and
+// Phi^T instead of the state).  Items are numbered by key chain (segment, key
+// head): every tile of every value head of a key head gets the same b % 8 and
+// neighbouring dispatch slots (workgroup b runs on XCD b % 8), so their shared
+// K, Q reads meet in one L2.
 //
 // The rows of S evolve independently.  Chain wavefront a (0, 1) owns rows
 // i = 16 a .. 16 a + 15 of the tile:
@@ -372,21 +373,27 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     __builtin_assume(w >= 0 && w < 6);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
 
+    // items by key chain (segment, key head): the R value heads of a key head
+    // times the tiles, all on XCD kc % 8 in neighbouring dispatch slots, share
+    // one L2 for their K and Q
+    const int R = HV / H;
     const int TV = dv / BV;
-    const int nb1 = ((A.seg_bound * HV + 7) / 8) * 8 * TV;
+    const int nb1 = ((A.seg_bound * H + 7) / 8) * 8 * R * TV;
     const bool trans = b >= nb1;
     const int bb = trans ? b - nb1 : b;
     const int TT = trans ? DK / BV : TV;
     const int slot = bb >> 3;
-    const int tile = slot % TT;
-    const int chn = (slot / TT) * 8 + (bb & 7);
+    const int per = R * TT;
+    const int kc = (slot / per) * 8 + (bb & 7);
+    const int rem = slot - (slot / per) * per;
+    const int tile = rem % TT;
     const int nseg = __builtin_amdgcn_readfirstlane(A.plan[0]);
-    if (chn >= nseg * HV) return;
-    const int sg = chn / HV, h = chn - sg * HV;
+    if (kc >= nseg * H) return;
+    const int sg = kc / H, hk = kc - sg * H;
+    const int h = hk * R + rem / TT;
     const int n = __builtin_amdgcn_readfirstlane(A.seg_seq[sg]);
     const int sidx = __builtin_amdgcn_readfirstlane(A.seg_idx[sg]);
     if (trans && sidx == 0) return;
-    const int hk = h / (HV / H);
 
     int sq, eq;
     seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
