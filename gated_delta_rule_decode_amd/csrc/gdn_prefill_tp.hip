@@ -101,7 +101,11 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
     float* const Xm = Tm + 32;  // 32-block merge: X [32 x 32] in the upper-right block
 
     const int H = A.H, HV = A.HV, R = HV / H;
-    const int c = blockIdx.x, hk = blockIdx.y, tid = threadIdx.x;
+    // workgroup id -> (chunk, key head): the key heads of a chunk on one XCD
+    // (id % 8) in neighbouring slots, so the cache lines of g and beta that
+    // they share (every value head of a token in one line) come from one L2
+    const int id = blockIdx.x, slot = id >> 3;
+    const int c = (slot / H) * 8 + (id & 7), hk = slot - (slot / H) * H, tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     __builtin_assume(w >= 0 && w < 4);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
@@ -816,7 +820,8 @@ __global__ __launch_bounds__(384) void scan_tp_kernel(const PrefillArgs A, int i
 }
 
 hipError_t launch_prep_tp(const PrefillArgs& A) {
-    hipLaunchKernelGGL((prep_tp_kernel<128>), dim3(A.max_chunks, A.H), dim3(256), 0, A.stream, A);
+    const unsigned grid = (unsigned)((A.max_chunks + 7) / 8) * 8u * (unsigned)A.H;
+    hipLaunchKernelGGL((prep_tp_kernel<128>), dim3(grid), dim3(256), 0, A.stream, A);
     return hipGetLastError();
 }
 
