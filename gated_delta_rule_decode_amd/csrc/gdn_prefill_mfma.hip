@@ -1015,6 +1015,25 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(const PrefillArgs A,
     }
     __syncthreads();
     const int Ls = s_len;
+    if (Ls == 0) {
+        // one segment per sequence: the tables need no scans, and there are
+        // no later segments, hence no combine or correction work
+        for (int n = threadIdx.x; n < N; n += 256) {
+            A.seq_seg0[n] = n;
+            A.seq_nseg[n] = 1;
+            A.seg_seq[n] = n;
+            A.seg_c0[n] = first_chunk(n);
+            A.seg_nch[n] = nchunks(n);
+            A.seg_idx[n] = 0;
+        }
+        if (threadIdx.x == 0) {
+            A.plan[0] = N;
+            A.plan[1] = 0;
+            A.plan[2] = 0;
+            A.plan[3] = 0;
+        }
+        return;
+    }
     auto nseg_of = [&](int n) {
         const int c = nchunks(n);
         return (Ls > 0 && c > 0) ? (c + Ls - 1) / Ls : 1;
