@@ -544,19 +544,13 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                 Ux[w][kk][1][l] = ul;
                 split8(wv, wh[kk], wl[kk]);
             }
-            __syncthreads();  // B1
-            // ---- phase 2: S'^T = gamma_n S^T + K^T U'.  K^T rows j = 16 jb + lr
-            // over the step's token slots: two transpose reads (tokens
-            // 32 kk + 4 lg + m / 4 and 16 more), lane m pointing at the stored
-            // column of j-group 16 jb + 4 (m % 4) ----
-            const float gn = G1[L - 1];
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sacc[jb][r] *= gn;
+            // the K^T operands of phase 2, read while the barrier waits: K^T rows
+            // j = 16 jb + lr over the step's token slots, two transpose reads
+            // (tokens 32 kk + 4 lg + m / 4 and 16 more), lane m pointing at the
+            // stored column of j-group 16 jb + 4 (m % 4)
+            bf8_t ktp[2][NJB];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                bf8_t kt[NJB];
 #pragma unroll
                 for (int jb = 0; jb < NJB; ++jb) {
                     const int col = 32 * (jb >> 1) + 8 * (lr & 3) + 4 * (jb & 1);
@@ -565,12 +559,22 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(kp));
                     const v4s_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) v4s_t*)(kp + 16 * KR));
-                    kt[jb] = __builtin_bit_cast(bf8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    ktp[kk][jb] = __builtin_bit_cast(bf8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
+            }
+            __syncthreads();  // B1
+            // ---- phase 2: S'^T = gamma_n S^T + K^T U' ----
+            const float gn = G1[L - 1];
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[jb][r] *= gn;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
                 for (int jb = 0; jb < NJB; ++jb) {
-                    sacc[jb] = mfma(kt[jb], wh[kk], sacc[jb]);
-                    sacc[jb] = mfma(kt[jb], wl[kk], sacc[jb]);
+                    sacc[jb] = mfma(ktp[kk][jb], wh[kk], sacc[jb]);
+                    sacc[jb] = mfma(ktp[kk][jb], wl[kk], sacc[jb]);
                 }
             }
             if (jc + 1 < nch) state_operands();
