@@ -32,12 +32,12 @@
 namespace gdn {
 
 constexpr int kAttnWG = 256;       // threads of a split workgroup (4 wavefronts)
-constexpr int kAttnTarget = 1024;  // split workgroups a launch aims at (one round, 4 per CU)
+constexpr int kAttnTarget = 512;   // split workgroups a launch aims at (one round, 2 per CU)
 constexpr int kAttnMinSplit = 256; // positions per split, at least
 
-// Split size: about kAttnTarget workgroups over the batch (measured: 1024
-// beats 2048 and more at 128 rows x 8192 positions), each at least
-// kAttnMinSplit positions.  Workspace: one partial result per split,
+// Split size: about kAttnTarget workgroups over the batch (measured at 128
+// rows x 8192 positions with two blocks in flight per wavefront: 512 beats
+// 1024), each at least kAttnMinSplit positions.  Workspace: one partial result per split,
 // [N, Hkv, nsplit, G, D + 2] fp32 (o relative to m, m, the sum).
 void attn_plan(int N, int Hq, int Hkv, int D, int Lmax, int& split, int& nsplit, size_t& bytes) {
     const long pairs = (long)N * Hkv;
@@ -156,14 +156,18 @@ __global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
         for (int j = 0; j < DPL; ++j) acc[g][j] = 0.f;
 
     const int nblk = (t1 - t0 + 15) / 16;
-    for (int b = w; b < nblk; b += 4) {
+    // Blocks b = w, w + 4, ... of this wavefront, two in flight: the loads of
+    // the next block are issued before the current one is computed.  Loads of
+    // a block past the split read positions >= pe, which the buffer resources
+    // return as zero (no access), so they are issued unconditionally and the
+    // wait counts stay static.
+    typedef uint32_t vraw_t[16][(DPL + 1) / 2];
+    auto load_block = [&](int b, bf8_t* kf, vraw_t& vraw) {
         const int P0 = t0 + 16 * b;
         // key fragments of 16 positions and the 16 value rows, all in flight
-        bf8_t kf[NKK];
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
             kf[kk] = bload8(kr, (uint32_t)((P0 + lr) * D + 32 * kk + 8 * lg) * 2);
-        uint32_t vraw[16][(DPL + 1) / 2];
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
             const uint32_t off = (uint32_t)((P0 + p) * D + DPL * l) * 2;
@@ -178,6 +182,9 @@ __global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
                 vraw[p][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, (int)off, 0, 0);
             }
         }
+    };
+    auto compute_block = [&](int b, const bf8_t* kf, const vraw_t& vraw) {
+        const int P0 = t0 + 16 * b;
         f4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -243,6 +250,15 @@ __global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
             }
         }
         __builtin_amdgcn_wave_barrier();  // pb and al are rewritten by the next block
+    };
+    bf8_t kfa[NKK], kfb[NKK];
+    vraw_t va, vb;
+    load_block(w, kfa, va);
+    for (int b = w; b < nblk; b += 8) {
+        load_block(b + 4, kfb, vb);
+        compute_block(b, kfa, va);
+        load_block(b + 8, kfa, va);
+        if (b + 4 < nblk) compute_block(b + 4, kfb, vb);
     }
 
     // merge the four wavefronts through LDS in two rounds (3 -> 1, 2 -> 0,
