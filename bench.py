@@ -73,32 +73,41 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # profiles/decode_traffic_qwen35_08b.md together with the sha256 of the kernel
 # source (and the local headers it includes) it was measured on.  Reported only
 # while those sources are unchanged.
-DECODE_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
-                  "bytes_per_launch": 68046342}
+DECODE_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
+                  "bytes_per_launch": 68046657}
 
 
 # The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
 # profiles/serving_decode_traffic.md) and the attention decode step
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
-SERVE_TRAFFIC = {"kernel_source_sha256": "24bfd10d65b39d707d47dbcb0815db74c8fd3560f7f7a51b30a1e1920abdd0b2",
-                 "bytes_per_launch": 543594255}
-ATTN_TRAFFIC = {"kernel_source_sha256": "307e9311a1db99216f64ad4f2a186d5037925cb4b7bb87d0d6756a8c362ee5c5",
-                "bytes_per_launch": 2185084533}
+SERVE_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
+                 "bytes_per_launch": 543598759}
+ATTN_TRAFFIC = {"kernel_source_sha256": "002352711e68de838ae6bfc13bfd9239b44fe796c7f2b54e0a772f89d9d3d1f1",
+                "bytes_per_launch": 2200967381}
 # The fused decode at the 35B-A3B shape, batch 128 (gdn_decode.hip;
 # profiles/decode_traffic_35b.md)
-DECODE3_TRAFFIC = {"kernel_source_sha256": "1c35490b31acb0404bf63d73b3ebbd29605982bfb3ae7ed5fbe19560722a3b0d",
-                   "bytes_per_launch": 543826905}
+DECODE3_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
+                   "bytes_per_launch": 543835208}
 # RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
 # profiles/rmsnorm_gated_traffic.md)
-NORM_TRAFFIC = {"kernel_source_sha256": "8014073d5bbde2fe478883ec30d9322ab0c7f7757ad23136244750031bf4a1ce",
-                "bytes_per_launch": 335592899}
+NORM_TRAFFIC = {"kernel_source_sha256": "b0b3d77d30c3ba96ec26fc908b4dc725c66a3ba8c8134a1e04f2f40ec0e10449",
+                "bytes_per_launch": 335594667}
 
 
 # Prefill counters from rocprofv3 runs of the bench lines (per call: issued
 # bf16 MFMA flops from SQ_INSTS_VALU_MFMA_MOPS_BF16, and HBM bytes from
 # FETCH_SIZE / WRITE_SIZE scaled by the copy calibration), keyed on the
-# prefill kernel sources they were measured on; profiles/ holds the runs.
-PREFILL_COUNTERS = {"kernel_source_sha256": None, "issued_mfma_flops": {}, "traffic_bytes": {}}
+# prefill kernel sources they were measured on (profiles/
+# prefill_traffic_and_mfma.md).  The job's prefill call is workload 3's shape
+# without an initial state, the cap phase is prefill4cap's.
+PREFILL_SOURCES = ("gdn_prefill_mfma.hip", "gdn_prefill_tp.hip")
+PREFILL_COUNTERS = {
+    "kernel_source_sha256": "497fd1577a52cae56696022ed8dd048ea3f26205ad1a2bb00a5344b2bd89716d",
+    "issued_mfma_flops": {"prefill2": 86704652288, "prefill3": 173409304576,
+                          "prefill4cap": 1388629196800, "job35b": 173409304576,
+                          "cap": 1388629196800},
+    "traffic_bytes": {"prefill2": 512113283, "prefill3": 818290745, "prefill4cap": 7373602342,
+                      "job35b": 818290745, "cap": 7373602342}}
 
 
 def recorded(record, source):
@@ -108,8 +117,8 @@ def recorded(record, source):
 
 
 def kernel_sources_sha256(source):
-    """sha256 over a kernel source and the local headers it includes (and
-    theirs), in include order."""
+    """sha256 over a kernel source (or a tuple of them) and the local headers
+    they include (and theirs), in include order."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc")
@@ -125,7 +134,8 @@ def kernel_sources_sha256(source):
         for inc in re.findall(rb'#include "([^"]+)"', data):
             visit(inc.decode())
 
-    visit(source)
+    for src in (source if isinstance(source, tuple) else (source,)):
+        visit(src)
     return h.hexdigest()
 
 
@@ -431,7 +441,7 @@ def run_job35b(args):
         workspace=ws_p), 5, s)
     del o32, o16, ws_p
     copy_ref = copy_same_bytes(Nd * HV * d * d * 4, copies=L, reps=8)
-    rec = recorded(PREFILL_COUNTERS, "gdn_prefill_mfma.hip")
+    rec = recorded(PREFILL_COUNTERS, PREFILL_SOURCES)
     pf_line = prefill_roofline(us_f32, N * T, N, H, HV, d,
                                issued=rec and rec["issued_mfma_flops"].get("job35b"),
                                traffic=rec and rec["traffic_bytes"].get("job35b"))
@@ -510,7 +520,7 @@ def prefill_cap_phase(args):
                                                      final_state=sf, o=o, workspace=ws), 3, s)
         res[name] = us
         del o
-    rec = recorded(PREFILL_COUNTERS, "gdn_prefill_mfma.hip")
+    rec = recorded(PREFILL_COUNTERS, PREFILL_SOURCES)
     out = {"workload": "long-context-varlen-prefill at the 131,072-token cap",
            "lengths": [int(x) for x in lengths], "qk_heads": H, "v_heads": HV,
            "roofline": prefill_roofline(res["f32"], T, N, H, HV, d, s0=True,
@@ -742,7 +752,7 @@ def run_prefill(args, cfg: str):
     pb = prefill_bytes(T, N, H, HV, d, d, s0=s0 is not None)
     pfl = prefill_flops(T, H, HV, d, d)
     key = f"prefill{cfg}"
-    rec = recorded(PREFILL_COUNTERS, "gdn_prefill_mfma.hip")
+    rec = recorded(PREFILL_COUNTERS, PREFILL_SOURCES)
     issued = rec and rec["issued_mfma_flops"].get(key)
     out = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s (one layer)",
