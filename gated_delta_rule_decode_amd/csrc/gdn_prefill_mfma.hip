@@ -1278,18 +1278,24 @@ __global__ __launch_bounds__(256) void correct_kernel(const PrefillArgs A) {
 }
 
 // Segmentation is possible when asked for; automatically (seg_req 0) when
-// the unsegmented scan leaves CUs idle (fewer than 256 workgroups) and some
-// sequence may be longer than one segment; and with kSegAutoSkewed whenever
+// the unsegmented scan leaves CUs idle and some sequence may be longer than
+// one segment; and with kSegAutoSkewed whenever
 // some sequence may be longer than one segment (one long prompt among short
 // ones, whose chains already fill the CUs: the planner decides from the
 // lengths).  Otherwise the plan is fixed to one segment per sequence and the
 // later passes are not launched: a possible plan costs their two launches
 // even when it turns out to be unsegmented.
+// "Idle" is fewer than 256 items for the per-tile scan (d_k = 64), and fewer
+// than 128 for the d_k = 128 scan: it holds one workgroup per CU, and a later
+// segment's value and transition items double its work, which paid only while
+// most CUs would otherwise idle (one 32768-token prompt, 64 items: 1.10 ->
+// 0.86 ms segmented; 128 items: 1.13 -> 1.37 ms).
 static bool may_segment(const PrefillArgs& A) {
     const size_t TV = (size_t)A.dv / 32;
+    const size_t idle = A.dk == 128 ? 128 : 256;
     const bool longer = (A.T + kChunk - 1) / kChunk > kSegMinChunks;
     return A.seg_req > 0 || (A.seg_req == kSegAutoSkewed && longer) ||
-           (A.seg_req == 0 && longer && (size_t)A.N * A.HV * TV < 256);
+           (A.seg_req == 0 && longer && (size_t)A.N * A.HV * TV < idle);
 }
 
 // plan -> prep -> scan (value and transition items) -> combine -> correction.

@@ -108,13 +108,15 @@ def test_prefill_validation(L):
 def _may_segment(N, T, HV, dk, dv, seg_req):
     """The host's rule for whether a bf16 call can take the segment-parallel
     scan: segments when forced, always possible under the skewed automatic
-    mode, or automatically when the (chain, 32-row tile) items leave CUs idle."""
+    mode, or automatically when the (chain, 32-row tile) items leave CUs idle
+    (fewer than 128 items at d_k = 128, 256 at d_k = 64)."""
     if dk not in (64, 128) or dv % 32:
         return False
     TV = dv // 32
+    idle = 128 if dk == 128 else 256
     longer = (T + 63) // 64 > 32
     return seg_req > 0 or (seg_req == -2 and longer) or (seg_req == 0 and longer
-                                                          and N * HV * TV < 256)
+                                                          and N * HV * TV < idle)
 
 
 def _want_bytes(N, T, HV, dk, dv, seg):
