@@ -309,13 +309,19 @@ def cpu_baseline_prefill(lengths, H, HV, d, s0_std=0.0, seed=0):
     return int(np.sum(lengths)) / secs, secs, orc.max_threads()
 
 
-def timed_calls(fn, reps, stream):
+def timed_calls(fn, reps, stream, settle_s=0.25):
     """Average time of ``reps`` back-to-back calls of fn on ``stream``
-    (HIP events on that stream), in microseconds."""
+    (HIP events on that stream), in microseconds, after at least ``settle_s``
+    seconds of untimed calls so that the clocks have settled."""
     import torch
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        fn()
+        t_end = time.perf_counter() + settle_s
+        while True:
+            fn()
+            stream.synchronize()
+            if time.perf_counter() >= t_end:
+                break
         e0.record(stream)
         for _ in range(reps):
             fn()
