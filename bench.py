@@ -74,24 +74,24 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # source (and the local headers it includes) it was measured on.  Reported only
 # while those sources are unchanged.
 DECODE_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
-                  "bytes_per_launch": 68046973}
+                  "bytes_per_launch": 68046261}
 
 
 # The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
 # profiles/serving_decode_traffic.md) and the attention decode step
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
 SERVE_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
-                 "bytes_per_launch": 543602924}
+                 "bytes_per_launch": 543600878}
 ATTN_TRAFFIC = {"kernel_source_sha256": "002352711e68de838ae6bfc13bfd9239b44fe796c7f2b54e0a772f89d9d3d1f1",
-                "bytes_per_launch": 2201065169}
+                "bytes_per_launch": 2201017645}
 # The fused decode at the 35B-A3B shape, batch 128 (gdn_decode.hip;
 # profiles/decode_traffic_35b.md)
 DECODE3_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
-                   "bytes_per_launch": 543841391}
+                   "bytes_per_launch": 543836680}
 # RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
 # profiles/rmsnorm_gated_traffic.md)
 NORM_TRAFFIC = {"kernel_source_sha256": "b0b3d77d30c3ba96ec26fc908b4dc725c66a3ba8c8134a1e04f2f40ec0e10449",
-                "bytes_per_launch": 335589889}
+                "bytes_per_launch": 335595940}
 
 
 # Prefill counters from rocprofv3 runs of the bench lines (per call: issued
@@ -102,12 +102,12 @@ NORM_TRAFFIC = {"kernel_source_sha256": "b0b3d77d30c3ba96ec26fc908b4dc725c66a3ba
 # without an initial state, the cap phase is prefill4cap's.
 PREFILL_SOURCES = ("gdn_prefill_mfma.hip", "gdn_prefill_tp.hip")
 PREFILL_COUNTERS = {
-    "kernel_source_sha256": "e57cdcb993aa71cb9ac72cb4dd7a00014740698edebcaf43058500ba1525f5dc",
+    "kernel_source_sha256": "aff3090db1350df35ed6dd849c263065f5d5e753248afb30360264d16fcb319f",
     "issued_mfma_flops": {"prefill2": 86704652288, "prefill3": 173409304576,
                           "prefill4cap": 1388629196800, "job35b": 173409304576,
                           "cap": 1388629196800},
-    "traffic_bytes": {"prefill2": 512117675, "prefill3": 818297569, "prefill4cap": 7503290326,
-                      "job35b": 818297569, "cap": 7503290326}}
+    "traffic_bytes": {"prefill2": 512129689, "prefill3": 818297384, "prefill4cap": 6636260600,
+                      "job35b": 818297384, "cap": 6636260600}}
 
 
 def recorded(record, source):

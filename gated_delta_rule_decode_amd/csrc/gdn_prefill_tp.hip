@@ -12,26 +12,24 @@
 //     S'   = gamma_n S + U'^T K                      U' = diag(e^{G_n - G}) U
 //
 // prep_tp_kernel (chunk-parallel, one workgroup per (chunk, key head), its
-// value heads in turn) writes G and T' -- 10 KiB per (chunk, value head), the
-// ten 16 x 16 blocks of T' on or below the diagonal, split into hi and lo
-// bf16 in the order the scan's MFMA operands read them -- and nothing else.
-// scan_tp_kernel (sequential over chunks) forms P, K^T, Q S^T and the rest
-// on the chip from K, Q and V, so no product of the chunk makes a round trip
-// through memory.
+// value heads in turn) writes G and T' -- 12 KiB per (chunk, value head): the
+// lower part of T' as six 16 x 32 tiles, split into hi and lo bf16 in the
+// order the scan's MFMA operands read them -- and nothing else.
+// scan_tp_kernel (sequential over chunks) forms P, Q S^T and every other
+// product on the chip from K, Q and V, so no product of the chunk makes a
+// round trip through memory.
 //
-// The scan splits a workgroup's eight wavefronts into two roles.  The four
-// chain wavefronts carry only the state's dependency chain,
+// The scan gives a workgroup's six wavefronts three roles.  Two chain
+// wavefronts carry only the state's dependency chain,
 //     S -> K S^T -> X -> U = T' X -> S' = gamma_n S + U'^T K,
-// with the state in MFMA accumulators; the K^T operand of the last product is
-// read from the row-major K tile with the LDS transpose read
-// (ds_read_b64_tr_b16).  The four helper wavefronts do what the chain does not
-// wait for: they stage the next chunk's K, Q, V, G and T' into LDS (loads
-// issued a chunk ahead), form P of the next chunk and Q S^T, and finish and
-// store the outputs.  A chain and a helper wavefront share each SIMD, so the
-// helpers' products, loads and stores fill the issue slots the chain leaves
-// while it waits on its own dependences.  Three barriers per chunk separate
-// the phases A (K S^T, X; Q S^T), U (U = T' X; staging of the next chunk) and
-// S (S'; O = scale (gamma Q S^T + P U), stores, P of the next chunk).
+// for 16 state rows each, with the state in MFMA accumulators; the K^T
+// operand of the last product is read from the row-major K tile with the LDS
+// transpose read (ds_read_b64_tr_b16).  Two output wavefronts form P and
+// Q S^T and finish and store the outputs.  Two staging wavefronts stage the
+// next chunk's K, Q, V, G and T' into LDS (loads issued a chunk ahead).  The
+// chain and output wavefronts run on different SIMDs; two barriers per chunk
+// separate phase 1 (K S^T, X, U; Q S^T and P) from phase 2 (S'; U P and the
+// stores).
 //
 // Precision as in the other MFMA kernels: q, k, v enter the products
 // exactly; every fp32 operand (S, X, U, U', P, T') is split into hi + lo
@@ -344,7 +342,7 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
 // gamma_t = e^{G_t}:
 //   X = V - diag(gamma) K S^T,  U = T' X,  U' = diag(e^{G_n - G}) U,
 //   S'^T = gamma_n S^T + K^T U'.
-// Output wavefront 2 + a takes the chain's S and U operands from LDS and forms
+// Output wavefront 2 + a takes the chain's S operands and U from LDS and forms
 //   O^T = scale (S Q^T diag(gamma) + U^T P^T),  P = (Q K^T) o e^{G_t - G_s} [s <= t],
 // each output wavefront computing the P tiles of two token blocks for both.
 // Wavefronts 4 and 5 stage the next chunk's K, Q, V, T' and G into the other
@@ -367,7 +365,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
     __shared__ __attribute__((aligned(16))) uint16_t Tp[2][kTpElems];
     __shared__ __attribute__((aligned(16))) float Gs[2][3][C];     // G, e^{G}, e^{G_n - G}
     __shared__ __attribute__((aligned(16))) bf8_t Sx[2][4][2][64]; // chain S operands [a][kk][hi, lo][lane]
-    __shared__ __attribute__((aligned(16))) bf8_t Ux[2][2][2][64]; // chain U operands [a][kk][hi, lo][lane]
+    __shared__ __attribute__((aligned(16))) float4 Uf[2][2][2][64];  // chain U, fp32 [a][kk][half][lane]
     __shared__ __attribute__((aligned(16))) bf8_t Px[kTpTiles][2][64];  // P tiles [tile][hi, lo][lane]
     typedef short v4s_t __attribute__((ext_vector_type(4)));
 
@@ -467,6 +465,20 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
             const int L = chunk_L(jc);
             const float* G1 = Gs[pb][1];
             const float* G2 = Gs[pb][2];
+            // the LDS operands of X, U' and phase 2 first, so that their latency
+            // passes under the K S^T products (pinned here: the scheduler would
+            // otherwise sink each read to its first use)
+            v4s_t vv[4];
+            float4 g1v[4], g2v[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                vv[tb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(
+                    &Vs[pb][(16 * tb + 4 * lg + (lr >> 2)) * VR + 16 * w + 4 * (lr & 3)]));
+                g1v[tb] = *reinterpret_cast<const float4*>(&G1[16 * tb + 4 * lg]);
+                g2v[tb] = *reinterpret_cast<const float4*>(&G2[16 * tb + 4 * lg]);
+            }
+            const float gn = G1[L - 1];
+            __builtin_amdgcn_sched_barrier(0);
             // ---- phase 1: K S^T [t][i] ----
             f4_t aks[4];
 #pragma unroll
@@ -482,19 +494,25 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                     aks[tb] = mfma(kf[tb], sl[kk], aks[tb]);
                 }
             }
+            // T' read before X is formed, so that its latency passes under the
+            // X arithmetic (pinned as above)
+            bf8_t tph[kTpTiles], tpl[kTpTiles];
+#pragma unroll
+            for (int ti = 0; ti < kTpTiles; ++ti) {
+                tph[ti] = *reinterpret_cast<const bf8_t*>(&Tp[pb][ti * kTpTileElems + 8 * l]);
+                tpl[ti] = *reinterpret_cast<const bf8_t*>(&Tp[pb][ti * kTpTileElems + 512 + 8 * l]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             // X = V - diag(gamma) K S^T: V[t = 16 tb + 4 lg + r][i] by a transpose
             // read (lane m of a 16-lane group points at row 16 tb + 4 lg + m / 4,
             // columns 16 a + 4 (m % 4) ..)
             float xv[4][4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const float4 g4 = *reinterpret_cast<const float4*>(&G1[16 * tb + 4 * lg]);
-                const float gam[4] = {g4.x, g4.y, g4.z, g4.w};
-                const v4s_t vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(
-                    &Vs[pb][(16 * tb + 4 * lg + (lr >> 2)) * VR + 16 * w + 4 * (lr & 3)]));
+                const float gam[4] = {g1v[tb].x, g1v[tb].y, g1v[tb].z, g1v[tb].w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    xv[tb][r] = __uint_as_float((uint32_t)(uint16_t)vv[r] << 16) - gam[r] * aks[tb][r];
+                    xv[tb][r] = __uint_as_float((uint32_t)(uint16_t)vv[tb][r] << 16) - gam[r] * aks[tb][r];
             }
             bf8_t xh[2], xl[2];
 #pragma unroll
@@ -514,34 +532,27 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                 ua[tb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk <= (tb >> 1); ++kk) {
-                    const uint16_t* tt = &Tp[pb][tp_tile(tb, kk) * kTpTileElems + 8 * l];
-                    const bf8_t th = *reinterpret_cast<const bf8_t*>(tt);
-                    const bf8_t tl = *reinterpret_cast<const bf8_t*>(tt + 512);
+                    const bf8_t th = tph[tp_tile(tb, kk)];
+                    const bf8_t tl = tpl[tp_tile(tb, kk)];
                     ua[tb] = mfma(th, xh[kk], ua[tb]);
                     ua[tb] = mfma(th, xl[kk], ua[tb]);
                     ua[tb] = mfma(tl, xh[kk], ua[tb]);
                 }
             }
-            // U to the output wavefront; U' = diag(e^{G_n - G}) U kept
+            // U to the output wavefront (fp32: it splits U itself); U' =
+            // diag(e^{G_n - G}) U kept
             bf8_t wh[2], wl[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                float uv[8], wv[8];
+                float wv[8];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int tb = 2 * kk + hh;
-                    const float4 d4 = *reinterpret_cast<const float4*>(&G2[16 * tb + 4 * lg]);
-                    const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+                    const float dd[4] = {g2v[tb].x, g2v[tb].y, g2v[tb].z, g2v[tb].w};
+                    Uf[w][kk][hh][l] = make_float4(ua[tb][0], ua[tb][1], ua[tb][2], ua[tb][3]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        uv[4 * hh + r] = ua[tb][r];
-                        wv[4 * hh + r] = ua[tb][r] * dd[r];
-                    }
+                    for (int r = 0; r < 4; ++r) wv[4 * hh + r] = ua[tb][r] * dd[r];
                 }
-                bf8_t uh, ul;
-                split8(uv, uh, ul);
-                Ux[w][kk][0][l] = uh;
-                Ux[w][kk][1][l] = ul;
                 split8(wv, wh[kk], wl[kk]);
             }
             // the K^T operands of phase 2, read while the barrier waits: K^T rows
@@ -564,7 +575,6 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
             }
             __syncthreads();  // B1
             // ---- phase 2: S'^T = gamma_n S^T + K^T U' ----
-            const float gn = G1[L - 1];
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
@@ -577,7 +587,9 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
                     sacc[jb] = mfma(ktp[kk][jb], wl[kk], sacc[jb]);
                 }
             }
-            if (jc + 1 < nch) state_operands();
+            // (after the last chunk too, where nothing reads them: no branch
+            // between the products and the split)
+            state_operands();
             __syncthreads();  // B2
         }
         if (fin) {
@@ -692,8 +704,9 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
             bf8_t uh[2], ul[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                uh[kk] = Ux[a][kk][0][l];
-                ul[kk] = Ux[a][kk][1][l];
+                const float4 u0 = Uf[a][kk][0][l], u1 = Uf[a][kk][1][l];
+                float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                split8(uv, uh[kk], ul[kk]);
             }
             const __amdgpu_buffer_rsrc_t orsrc =
                 trans ? out_rsrc(A.ws_W + (size_t)t0 * HV * DK, (uint32_t)(L * HV * DK * 4))
