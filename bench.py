@@ -749,12 +749,36 @@ def run_prefill(args, cfg: str):
         call(-1)
         torch.cuda.synchronize()
         n_w += 1
+    # ten timed runs of the library's choice and three with segmentation off,
+    # interleaved; the line reports medians and the spread of the ten
     runs = {0: [], -1: []}
-    for _ in range(3):
-        for seg in (0, -1):
-            runs[seg].append(timed(seg))
+    for i in range(10):
+        runs[0].append(timed(0))
+        if i % 3 == 0:
+            runs[-1].append(timed(-1))
     ms = float(np.median(runs[0]))
     ms_whole = float(np.median(runs[-1]))
+    one = np.array(runs[0]) * 1e3
+    stats = {"runs": len(one), "calls_per_run": args.steps,
+             "median_us": round(float(np.median(one)), 2), "min_us": round(float(one.min()), 2),
+             "p90_us": round(float(np.percentile(one, 90)), 2)}
+    # the same call writing o in bf16 (median of three timed runs)
+    o16 = torch.empty(T, HV, d, device=dev, dtype=torch.bfloat16)
+
+    def timed16():
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf, o=o16,
+                                workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    timed16()
+    ms16 = float(np.median([timed16() for _ in range(3)]))
+    del o16
     pb = prefill_bytes(T, N, H, HV, d, d, s0=s0 is not None)
     pfl = prefill_flops(T, H, HV, d, d)
     key = f"prefill{cfg}"
@@ -780,13 +804,18 @@ def run_prefill(args, cfg: str):
                      "issued_mfma_bf16_frac": issued and round(issued / (ms * 1e-3) / 1e12 /
                                                                BF16_PEAK_TFLOPS, 5)},
         "unsegmented_ms_per_step": round(ms_whole, 4),
+        "call_us_stats": stats,
+        "bf16_o": {k_: v_ for k_, v_ in prefill_roofline(ms16 * 1e3, T, N, H, HV, d,
+                                                          s0=s0 is not None, o_bytes=2).items()
+                   if k_ in ("call_us", "tokens_per_s", "hbm_frac", "mfma_bf16_frac")},
     }
     del q, k, v, g, b, o, sf, ws
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        # a bounded sample of the same workload: its first 4096 tokens (of the
-        # first sequences), all heads, prefill + RMSNormGated
-        sample, left = [], 4096
+        # a bounded sample of the same workload: its first 32768 tokens (of the
+        # first sequences; all of workloads 2 and 3), all heads, prefill +
+        # RMSNormGated
+        sample, left = [], 32768
         for x in lengths:
             if left <= 0:
                 break
