@@ -73,25 +73,25 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # profiles/decode_traffic_qwen35_08b.md together with the sha256 of the kernel
 # source (and the local headers it includes) it was measured on.  Reported only
 # while those sources are unchanged.
-DECODE_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
-                  "bytes_per_launch": 68046261}
+DECODE_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b27696c883c62b2e249ee88187c7",
+                  "bytes_per_launch": 68037471}
 
 
 # The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
 # profiles/serving_decode_traffic.md) and the attention decode step
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
-SERVE_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
-                 "bytes_per_launch": 543600878}
-ATTN_TRAFFIC = {"kernel_source_sha256": "002352711e68de838ae6bfc13bfd9239b44fe796c7f2b54e0a772f89d9d3d1f1",
-                "bytes_per_launch": 2201017645}
+SERVE_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b27696c883c62b2e249ee88187c7",
+                 "bytes_per_launch": 543599970}
+ATTN_TRAFFIC = {"kernel_source_sha256": "58ee111cbc773dab6033ea4a953afb6fbe2393f307f6e74b13ee4d56cb222c10",
+                "bytes_per_launch": 2201072093}
 # The fused decode at the 35B-A3B shape, batch 128 (gdn_decode.hip;
 # profiles/decode_traffic_35b.md)
-DECODE3_TRAFFIC = {"kernel_source_sha256": "f43e5ffb3b0508e381591768a84f6f6bdf5564c52c569747481a49243eaaf6ff",
-                   "bytes_per_launch": 543836680}
+DECODE3_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b27696c883c62b2e249ee88187c7",
+                   "bytes_per_launch": 543826013}
 # RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
 # profiles/rmsnorm_gated_traffic.md)
-NORM_TRAFFIC = {"kernel_source_sha256": "b0b3d77d30c3ba96ec26fc908b4dc725c66a3ba8c8134a1e04f2f40ec0e10449",
-                "bytes_per_launch": 335595940}
+NORM_TRAFFIC = {"kernel_source_sha256": "8bba89fa6e221f323599e1e67999eda741660ccbc6dc39ab4157f42bfae53472",
+                "bytes_per_launch": 335588844}
 
 
 # Prefill counters from rocprofv3 runs of the bench lines (per call: issued
@@ -102,12 +102,12 @@ NORM_TRAFFIC = {"kernel_source_sha256": "b0b3d77d30c3ba96ec26fc908b4dc725c66a3ba
 # without an initial state, the cap phase is prefill4cap's.
 PREFILL_SOURCES = ("gdn_prefill_mfma.hip", "gdn_prefill_tp.hip")
 PREFILL_COUNTERS = {
-    "kernel_source_sha256": "aff3090db1350df35ed6dd849c263065f5d5e753248afb30360264d16fcb319f",
+    "kernel_source_sha256": "afa7f93323f2ccb10ad302930f48b83845fce32251989aa484600e15d5b3c3b1",
     "issued_mfma_flops": {"prefill2": 86704652288, "prefill3": 173409304576,
                           "prefill4cap": 1388629196800, "job35b": 173409304576,
                           "cap": 1388629196800},
-    "traffic_bytes": {"prefill2": 512129689, "prefill3": 818297384, "prefill4cap": 6636260600,
-                      "job35b": 818297384, "cap": 6636260600}}
+    "traffic_bytes": {"prefill2": 512130244, "prefill3": 818298630, "prefill4cap": 6584467165,
+                      "job35b": 818298630, "cap": 6584467165}}
 
 
 def recorded(record, source):
@@ -720,64 +720,51 @@ def run_prefill(args, cfg: str):
     if w.get("s0_std"):
         s0 = torch.randn(N, HV, d, d, device=dev) * w["s0_std"]
     o = torch.empty(T, HV, d, device=dev)
+    o16 = torch.empty(T, HV, d, device=dev, dtype=torch.bfloat16)  # the bf16-o call
     sf = torch.empty(N, HV, d, d, device=dev)
     ws = torch.empty(gdn.prefill_workspace_bytes(N, T, H, HV, d, d), dtype=torch.uint8, device=dev)
-    def call(seg):
-        gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf, o=o,
-                            workspace=ws, segment_chunks=seg)
+    def call(seg, out=None):
+        gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf,
+                            o=o if out is None else out, workspace=ws, segment_chunks=seg)
 
-    def timed(seg):
+    def timed(seg, out=None):
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record()
         for _ in range(args.steps):
-            call(seg)
+            call(seg, out)
         e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return max(e0.elapsed_time(e1), wall * 1e3) / args.steps
 
     # warm-up: the requested calls, and at least a quarter second of calls so
-    # that the clocks have settled; then the library's own choice of the
-    # segment-parallel scan (0) and one chain per (sequence, head, tile) (-1),
-    # alternately, three times each (medians)
+    # that the clocks have settled (each form in turn); then ten timed runs of
+    # the library's own choice of the segment-parallel scan (0), interleaved
+    # with ten of the same call writing bf16 o and three with segmentation off
+    # (-1); the line reports medians and the spread of the ten
     t_end = time.perf_counter() + 0.25
     n_w = 0
     while n_w < args.warmup or time.perf_counter() < t_end:
         call(0)
         call(-1)
+        call(0, o16)
         torch.cuda.synchronize()
         n_w += 1
-    # ten timed runs of the library's choice and three with segmentation off,
-    # interleaved; the line reports medians and the spread of the ten
-    runs = {0: [], -1: []}
+    runs = {0: [], -1: [], "bf16": []}
     for i in range(10):
         runs[0].append(timed(0))
+        runs["bf16"].append(timed(0, o16))
         if i % 3 == 0:
             runs[-1].append(timed(-1))
     ms = float(np.median(runs[0]))
     ms_whole = float(np.median(runs[-1]))
+    ms16 = float(np.median(runs["bf16"]))
     one = np.array(runs[0]) * 1e3
     stats = {"runs": len(one), "calls_per_run": args.steps,
              "median_us": round(float(np.median(one)), 2), "min_us": round(float(one.min()), 2),
              "p90_us": round(float(np.percentile(one, 90)), 2)}
-    # the same call writing o in bf16 (median of three timed runs)
-    o16 = torch.empty(T, HV, d, device=dev, dtype=torch.bfloat16)
-
-    def timed16():
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            gdn.prefill_chunked(q, k, v, g, b, cu, initial_state=s0, final_state=sf, o=o16,
-                                workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    timed16()
-    ms16 = float(np.median([timed16() for _ in range(3)]))
     del o16
     pb = prefill_bytes(T, N, H, HV, d, d, s0=s0 is not None)
     pfl = prefill_flops(T, H, HV, d, d)

@@ -20,12 +20,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// round to nearest, ties to even (finite inputs; NaN stays NaN)
+// round to nearest, ties to even; NaN stays NaN (the hardware conversion,
+// one instruction)
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 // ---- element-type traits -------------------------------------------------

@@ -1,7 +1,7 @@
 // gdn_prefill_common.h -- device helpers shared by the chunked-prefill
 // kernels on MFMA (gfx950): LDS and buffer-resource loads and stores, the
-// hardware exp2 of log2-unit decays, SiLU from the hardware exp2 and
-// reciprocal, and the sequence / chunk lookups of a packed batch.
+// hardware exp2 of log2-unit decays, and the sequence / chunk lookups of a
+// packed batch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,26 +39,19 @@ __device__ __forceinline__ void out_store4(__amdgpu_buffer_rsrc_t r, uint32_t of
                     __float_as_uint(v[3])};
     __builtin_amdgcn_raw_buffer_store_b128(d, r, (int)(off * 4), 0, 0);
 }
+// (bf16: the hardware's packed round-to-nearest-even conversion, the same
+// result as f32_to_bf16 for every number, a quiet NaN for a NaN)
 __device__ __forceinline__ void out_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v, bf16_t*) {
     typedef unsigned u2_t __attribute__((ext_vector_type(2)));
-    const u2_t d = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+    const u2_t d = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{v[0], v[1]}, bf2_t)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{v[2], v[3]}, bf2_t))};
     __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)(off * 2), 0, 0);
 }
-
-__device__ __forceinline__ bf8_t zero8() { return __builtin_bit_cast(bf8_t, make_uint4(0, 0, 0, 0)); }
 
 // exponentials of log-decay differences: G is kept in log2 units (g log2 e),
 // so e^{G_t - G_s} is one hardware exp2
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// silu(z) = z / (1 + e^-z) from the hardware exp2 and reciprocal (about 1 ulp
-// each): a few instructions where the library forms take tens, which the
-// per-chain scan, with one wavefront per SIMD, would wait for
-__device__ __forceinline__ float silu_hw(float z) {
-    return z * __builtin_amdgcn_rcpf(1.0f + exp2f_(-kLog2e * z));
-}
 
 
 __device__ __forceinline__ void seq_bounds_m(const int32_t* cu, int n, int T, int& s, int& e) {

@@ -60,8 +60,6 @@ constexpr int kTpTiles = 6;
 constexpr int kTpTileElems = 1024;                       // uint16 per tile (hi + lo)
 constexpr int kTpElems = kTpTiles * kTpTileElems;        // per (chunk, value head)
 __host__ __device__ constexpr int tp_tile(int tb, int kk) { return (tb < 3 ? tb : 4) + kk; }
-// (K Q^T) block (tb, sb), sb <= tb, among the ten on or below the diagonal
-__host__ __device__ constexpr int tp_block(int tb, int sb) { return tb * (tb + 1) / 2 + sb; }
 
 // A token block as a compile-time constant (triangular loops over token
 // blocks unroll with fixed bounds).
