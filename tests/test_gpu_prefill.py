@@ -80,7 +80,7 @@ def test_prefill_ragged_and_empty(orc, scale):
 
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (16, 128), (32, 64), (64, 32), (64, 64),
-                                   (128, 16), (128, 128)])
+                                   (128, 16), (128, 32), (128, 64), (128, 128)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_head_sizes(orc, dk, dv, dtype):
     x = gi.make_prefill([70, 5, 129], 2, 4, dk, dv, dtype=dtype, s0_std=0.05, seed=dk + dv)
