@@ -72,16 +72,17 @@ struct TokenBlock {
 // prep: G and T' per (chunk, value head)
 // ---------------------------------------------------------------------------
 // One workgroup (4 wavefronts) per (chunk, key head): the chunk's K rows are
-// read once and serve every value head of the key head in turn.  Per value
-// head: G (a wave prefix sum, log2 units), A = strictly lower
-// diag(b) (K K^T o e^{G_t - G_s}) from K K^T on MFMA (row block w per
-// wavefront), T = (I + A)^-1 by forward substitution on the 16 x 16 diagonal
-// blocks and block merges on split-bf16 MFMA, then T' = T diag(b) written out
-// as hi / lo blocks.  Rows past a sequence end read K, g and b as zero, so
-// T' has zero rows there and its valid block is the inverse of the valid
-// part alone.
+// read once and K K^T is formed once on MFMA (row block w per wavefront, kept
+// in registers) for every value head of the key head; the K tile's LDS then
+// holds A and T.  Per value head: G (a wave prefix sum, log2 units), A =
+// strictly lower diag(b) (K K^T o e^{G_t - G_s}), T = (I + A)^-1 by forward
+// substitution on the 16 x 16 diagonal blocks and block merges on split-bf16
+// MFMA, then T' = T diag(b) written out as hi / lo blocks.  Rows past a
+// sequence end read K, g and b as zero, so T' has zero rows there and its
+// valid block is the inverse of the valid part alone.  At most 128 VGPRs
+// keep four workgroups on a CU (a tighter bound spills and measured slower).
 template <int DK>
-__global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
+__global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
     constexpr int KP = DK + 8;   // padded bf16 row of the K tile
     constexpr int AP = C + 4;    // padded fp32 row (16-byte aligned rows)
@@ -89,8 +90,9 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
     constexpr int PPR = DK / 8;  // 16-byte pieces per row
     constexpr int RPI = 64 / PPR;
     constexpr int NLD = 16 / RPI;
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) float Tm[C * AP];  // A, then T written over it
+    static_assert(C * KP * 2 <= C * AP * 4, "the K tile fits the A / T buffer");
+    __shared__ __attribute__((aligned(16))) float Tm[C * AP];  // K, then A, then T written over it
+    __bf16* const Ks = reinterpret_cast<__bf16*>(Tm);
     __shared__ __attribute__((aligned(16))) float Gs[C];
     __shared__ __attribute__((aligned(16))) float Bs[C];
     float* const Am = Tm;
@@ -135,6 +137,21 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
 #pragma unroll
     for (int p = 0; p < NLD; ++p)
         *reinterpret_cast<bf8_t*>(&Ks[(16 * w + RPI * p + l / PPR) * KP + 8 * (l % PPR)]) = kst[p];
+    __syncthreads();  // K is in LDS
+    // K K^T of row block w, once for all value heads of the key head:
+    // kk[sb][r] = (K K^T)[t = 16 w + 4 lg + r][s = 16 sb + lr]
+    f4_t kk[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) kk[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKK; ++ks) {
+        const int col = 32 * ks + 8 * lg;
+        const bf8_t ka = lds8(&Ks[(16 * w + lr) * KP + col]);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+            if (sb <= w) kk[sb] = mfma(ka, lds8(&Ks[(16 * sb + lr) * KP + col]), kk[sb]);
+    }
+    __syncthreads();  // every wavefront has read K: its buffer holds A and T from here
 
     for (int v = 0; v < R; ++v) {
         const int hv = hk * R + v;
@@ -152,22 +169,10 @@ __global__ __launch_bounds__(256) void prep_tp_kernel(const PrefillArgs A) {
             Bs[l] = bv;
             A.ws_G[((size_t)c * HV + hv) * C + l] = gs;
         }
-        __syncthreads();  // K (first value head), G and b are in LDS
+        __syncthreads();  // G and b are in LDS
 
         // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s}), row block w
         {
-            f4_t kk[4];
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) kk[sb] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKK; ++ks) {
-                const int col = 32 * ks + 8 * lg;
-                const bf8_t ka = lds8(&Ks[(16 * w + lr) * KP + col]);
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    if (sb <= w) kk[sb] = mfma(ka, lds8(&Ks[(16 * sb + lr) * KP + col]), kk[sb]);
-            }
-            // kk[sb][r] = (K K^T)[t = 16 w + 4 lg + r][s = 16 sb + lr]
             const float4 g4 = *reinterpret_cast<const float4*>(&Gs[16 * w + 4 * lg]);
             const float4 b4 = *reinterpret_cast<const float4*>(&Bs[16 * w + 4 * lg]);
             const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
