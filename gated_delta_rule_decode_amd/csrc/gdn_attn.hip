@@ -34,6 +34,10 @@ namespace gdn {
 constexpr int kAttnWG = 256;       // threads of a split workgroup (4 wavefronts)
 constexpr int kAttnTarget = 512;   // split workgroups a launch aims at (one round, 2 per CU)
 constexpr int kAttnMinSplit = 256; // positions per split, at least
+// The cache rows are read once per step: non-temporal loads (buffer cache
+// policy nt) keep them from displacing other lines, measured ~2.5 % faster at
+// the 35B-A3B shape
+constexpr int kCacheNt = 2;
 
 // Split size: about kAttnTarget workgroups over the batch (measured at 128
 // rows x 8192 positions with two blocks in flight per wavefront: 512 beats
@@ -167,19 +171,20 @@ __global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
         // key fragments of 16 positions and the 16 value rows, all in flight
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
-            kf[kk] = bload8(kr, (uint32_t)((P0 + lr) * D + 32 * kk + 8 * lg) * 2);
+            kf[kk] = __builtin_bit_cast(bf8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                kr, (int)(((P0 + lr) * D + 32 * kk + 8 * lg) * 2), 0, kCacheNt));
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
             const uint32_t off = (uint32_t)((P0 + p) * D + DPL * l) * 2;
             if constexpr (DPL == 4) {
                 typedef unsigned u2_t __attribute__((ext_vector_type(2)));
-                const u2_t u = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(vr, (int)off, 0, 0));
+                const u2_t u = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(vr, (int)off, 0, kCacheNt));
                 vraw[p][0] = u.x;
                 vraw[p][1] = u.y;
             } else if constexpr (DPL == 2) {
-                vraw[p][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, (int)off, 0, 0);
+                vraw[p][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, (int)off, 0, kCacheNt);
             } else {
-                vraw[p][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, (int)off, 0, 0);
+                vraw[p][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, (int)off, 0, kCacheNt);
             }
         }
     };
