@@ -74,24 +74,24 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
 # source (and the local headers it includes) it was measured on.  Reported only
 # while those sources are unchanged.
 DECODE_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b27696c883c62b2e249ee88187c7",
-                  "bytes_per_launch": 68037243}
+                  "bytes_per_launch": 68036973}
 
 
 # The same for the serving decode step (gdn_decode.hip, 35B-A3B serving shape;
 # profiles/serving_decode_traffic.md) and the attention decode step
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
 SERVE_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b27696c883c62b2e249ee88187c7",
-                 "bytes_per_launch": 543599111}
+                 "bytes_per_launch": 543596916}
 ATTN_TRAFFIC = {"kernel_source_sha256": "a55f1f0128c3ac52654a854205401ab99f01d37fd95e47543e585655e3b6859b",
-                "bytes_per_launch": 2201187582}
+                "bytes_per_launch": 2201579868}
 # The fused decode at the 35B-A3B shape, batch 128 (gdn_decode.hip;
 # profiles/decode_traffic_35b.md)
 DECODE3_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b27696c883c62b2e249ee88187c7",
-                   "bytes_per_launch": 543827777}
+                   "bytes_per_launch": 543826119}
 # RMSNormGated on its own (gdn_rmsnorm.hip, 0.8B prefill output shape;
 # profiles/rmsnorm_gated_traffic.md)
 NORM_TRAFFIC = {"kernel_source_sha256": "8bba89fa6e221f323599e1e67999eda741660ccbc6dc39ab4157f42bfae53472",
-                "bytes_per_launch": 335595342}
+                "bytes_per_launch": 335594827}
 
 
 # Prefill counters from rocprofv3 runs of the bench lines (per call: issued
@@ -102,12 +102,12 @@ NORM_TRAFFIC = {"kernel_source_sha256": "8bba89fa6e221f323599e1e67999eda741660cc
 # without an initial state, the cap phase is prefill4cap's.
 PREFILL_SOURCES = ("gdn_prefill_mfma.hip", "gdn_prefill_tp.hip")
 PREFILL_COUNTERS = {
-    "kernel_source_sha256": "7d178e037f017e474348d4702c20733b96c1faa7a27a419dc0c3355b9f5ab53f",
+    "kernel_source_sha256": "76d68db5956286242da9fc858ac19e80cddceadb53388b766b9f19c6291e315a",
     "issued_mfma_flops": {"prefill2": 86704652288, "prefill3": 170724950016,
                           "prefill4cap": 1367133388800, "job35b": 170724950016,
                           "cap": 1367133388800},
-    "traffic_bytes": {"prefill2": 512124438, "prefill3": 818292238, "prefill4cap": 6600328566,
-                      "job35b": 818292238, "cap": 6600328566}}
+    "traffic_bytes": {"prefill2": 512164959, "prefill3": 818332505, "prefill4cap": 6546191989,
+                      "job35b": 818332505, "cap": 6546191989}}
 
 
 def recorded(record, source):

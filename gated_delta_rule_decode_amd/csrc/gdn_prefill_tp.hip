@@ -26,7 +26,8 @@
 // operand of the last product is read from the row-major K tile with the LDS
 // transpose read (ds_read_b64_tr_b16).  Two output wavefronts form P and
 // Q S^T and finish and store the outputs.  Two staging wavefronts stage the
-// next chunk's K, Q, V, G and T' into LDS (loads issued a chunk ahead).  The
+// next chunk's K, Q, V, G and T' into LDS (loads issued a chunk ahead, and
+// the workgroup's next item's first chunk during an item's last steps).  The
 // chain and output wavefronts run on different SIMDs; two barriers per chunk
 // separate phase 1 (K S^T, X, U; Q S^T and P) from phase 2 (S'; U P and the
 // stores).
@@ -328,6 +329,21 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
 // scan: sequential over chunks; state rows split over chain wavefronts, the
 // output over output wavefronts
 // ---------------------------------------------------------------------------
+// The scan workgroup's LDS, declared once in the kernel: the chain and output
+// wavefronts and the staging wavefronts run separate item loops over it.
+template <int DK>
+struct ScanLds {
+    static constexpr int C = kChunk, KR = DK + 16, VR = 32 + 16;
+    __attribute__((aligned(16))) __bf16 Ks[2][C * KR];  // K [t][slot order], by chunk parity
+    __attribute__((aligned(16))) __bf16 Qs[2][C * KR];  // Q [t][slot order]
+    __attribute__((aligned(16))) __bf16 Vs[2][C * VR];  // V [t][i] of the tile
+    __attribute__((aligned(16))) uint16_t Tp[2][kTpElems];
+    __attribute__((aligned(16))) float Gs[2][3][C];     // G, e^{G}, e^{G_n - G}
+    __attribute__((aligned(16))) bf8_t Sx[2][4][2][64]; // chain S operands [a][kk][hi, lo][lane]
+    __attribute__((aligned(16))) float4 Uf[2][2][2][64];  // chain U, fp32 [a][kk][half][lane]
+    __attribute__((aligned(16))) bf8_t Px[kTpTiles][2][64];  // P tiles [tile][hi, lo][lane]
+};
+
 // Work items: (segment, value head, 32-row tile of S) value items first, then
 // the transition items of later segments (the same scan from the identity
 // with V read as zero: d_k rows, writing w = scale Phi_t q_t instead of o and
@@ -336,6 +352,62 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
 // neighbouring dispatch slots (workgroup b runs on XCD b % 8), so their shared
 // K, Q reads meet in one L2.
 //
+// One work item's coordinates, every field wavefront-uniform; valid 0: an
+// item with nothing to do (a key chain past the plan's segments, or the
+// transition item of a first segment); live: valid with chunks to scan.
+struct ScanItem {
+    int valid, live, trans, sg, hk, h, tile, n, sidx, whole, c_first, nch, sq, eq;
+};
+
+// Item b's coordinates.  The table reads take two dependent rounds: the segment's entries (its index
+// clamped into the tables, so that an item past the plan reads in bounds),
+// then its sequence's; an item's validity is decided after both.
+template <int DK>
+__device__ __forceinline__ ScanItem scan_item(const PrefillArgs& A, const int b) {
+    constexpr int C = kChunk, BV = 32;
+    const int H = A.H, HV = A.HV, dv = A.dv;
+    const int R = HV / H;
+    const int TV = dv / BV;
+    const int nb1 = ((A.seg_bound * H + 7) / 8) * 8 * R * TV;
+    const bool trans = b >= nb1;
+    const int bb = trans ? b - nb1 : b;
+    const int TT = trans ? DK / BV : TV;
+    const int slot = bb >> 3;
+    const int per = R * TT;
+    const int kc = (slot / per) * 8 + (bb & 7);
+    const int rem = slot - (slot / per) * per;
+    const int sg = kc / H;
+    const int sgc = min(sg, A.seg_bound - 1);
+    const int nseg = __builtin_amdgcn_readfirstlane(A.plan[0]);
+    const int n0 = __builtin_amdgcn_readfirstlane(A.seg_seq[sgc]);
+    const int sidx = __builtin_amdgcn_readfirstlane(A.seg_idx[sgc]);
+    const int c_first = __builtin_amdgcn_readfirstlane(A.seg_c0[sgc]);
+    int nch = __builtin_amdgcn_readfirstlane(A.seg_nch[sgc]);
+    const int n = min(max(n0, 0), A.N - 1);
+    int sq, eq;
+    seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
+    const int coff = __builtin_amdgcn_readfirstlane(A.chunk_off[n]);
+    const int nsq = __builtin_amdgcn_readfirstlane(A.seq_nseg[n]);
+    sq += (c_first - min(coff, A.max_chunks)) * C;  // the segment's first token
+    if (c_first + nch > A.max_chunks) nch = max(0, A.max_chunks - c_first);
+    ScanItem it;
+    it.valid = (kc < nseg * H && !(trans && sidx == 0)) ? 1 : 0;
+    it.live = (it.valid && nch > 0) ? 1 : 0;
+    it.trans = trans ? 1 : 0;
+    it.sg = sg;
+    it.hk = kc - sg * H;
+    it.h = it.hk * R + rem / TT;
+    it.tile = rem % TT;
+    it.n = n;
+    it.sidx = sidx;
+    it.whole = nsq == 1 ? 1 : 0;
+    it.c_first = c_first;
+    it.nch = nch;
+    it.sq = __builtin_amdgcn_readfirstlane(sq);
+    it.eq = __builtin_amdgcn_readfirstlane(eq);
+    return it;
+}
+
 // The rows of S evolve independently.  Chain wavefront a (0, 1) owns rows
 // i = 16 a .. 16 a + 15 of the tile:
 //   sacc[jb][r] = S^T[j = 16 jb + 4 lg + r][i = 16 a + lr]
@@ -355,57 +427,34 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
 // K and Q rows are stored with their columns in slot order (an operand read
 // is 16 contiguous bytes); a K^T operand is two transpose reads.
 template <int DK, typename Tout>
-__device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) {
+__device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b, ScanLds<DK>& S) {
     static_assert(DK == 128, "the row-split scan is written for d_k = 128");
     constexpr int C = kChunk;
     constexpr int BV = 32;        // state rows per workgroup
     constexpr int KR = DK + 16;   // bf16 per K / Q row in LDS (288 bytes)
     constexpr int VR = BV + 16;   // bf16 per V row in LDS (96 bytes)
     constexpr int NJB = DK / 16;  // 16-column blocks of the state
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C * KR];  // K [t][slot order], by chunk parity
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[2][C * KR];  // Q [t][slot order]
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][C * VR];  // V [t][i] of the tile
-    __shared__ __attribute__((aligned(16))) uint16_t Tp[2][kTpElems];
-    __shared__ __attribute__((aligned(16))) float Gs[2][3][C];     // G, e^{G}, e^{G_n - G}
-    __shared__ __attribute__((aligned(16))) bf8_t Sx[2][4][2][64]; // chain S operands [a][kk][hi, lo][lane]
-    __shared__ __attribute__((aligned(16))) float4 Uf[2][2][2][64];  // chain U, fp32 [a][kk][half][lane]
-    __shared__ __attribute__((aligned(16))) bf8_t Px[kTpTiles][2][64];  // P tiles [tile][hi, lo][lane]
+    auto& Ks = S.Ks;
+    auto& Qs = S.Qs;
+    auto& Vs = S.Vs;
+    auto& Tp = S.Tp;
+    auto& Gs = S.Gs;
+    auto& Sx = S.Sx;
+    auto& Uf = S.Uf;
+    auto& Px = S.Px;
     typedef short v4s_t __attribute__((ext_vector_type(4)));
 
-    const int H = A.H, HV = A.HV, dv = A.dv;
+    const int HV = A.HV, dv = A.dv;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __builtin_assume(w >= 0 && w < 6);
+    __builtin_assume(w >= 0 && w < 4);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
 
-    // items by key chain (segment, key head): the R value heads of a key head
-    // times the tiles, all on XCD kc % 8 in neighbouring dispatch slots, share
-    // one L2 for their K and Q
-    const int R = HV / H;
-    const int TV = dv / BV;
-    const int nb1 = ((A.seg_bound * H + 7) / 8) * 8 * R * TV;
-    const bool trans = b >= nb1;
-    const int bb = trans ? b - nb1 : b;
-    const int TT = trans ? DK / BV : TV;
-    const int slot = bb >> 3;
-    const int per = R * TT;
-    const int kc = (slot / per) * 8 + (bb & 7);
-    const int rem = slot - (slot / per) * per;
-    const int tile = rem % TT;
-    const int nseg = __builtin_amdgcn_readfirstlane(A.plan[0]);
-    if (kc >= nseg * H) return;
-    const int sg = kc / H, hk = kc - sg * H;
-    const int h = hk * R + rem / TT;
-    const int n = __builtin_amdgcn_readfirstlane(A.seg_seq[sg]);
-    const int sidx = __builtin_amdgcn_readfirstlane(A.seg_idx[sg]);
-    if (trans && sidx == 0) return;
-
-    int sq, eq;
-    seq_bounds_m(A.cu_seqlens, n, A.T, sq, eq);
-    const int c_first = __builtin_amdgcn_readfirstlane(A.seg_c0[sg]);
-    int nch = __builtin_amdgcn_readfirstlane(A.seg_nch[sg]);
-    sq += (c_first - min(A.chunk_off[n], A.max_chunks)) * C;  // the segment's first token
-    if (c_first + nch > A.max_chunks) nch = max(0, A.max_chunks - c_first);
+    const ScanItem it = scan_item<DK>(A, b);
+    if (!it.valid) return;
+    const bool trans = it.trans != 0;
+    const int sg = it.sg, h = it.h, tile = it.tile, n = it.n, sidx = it.sidx;
+    const int nch = it.nch, sq = it.sq, eq = it.eq;
     auto chunk_t0 = [&](int jc) { return sq + jc * C; };
     auto chunk_L = [&](int jc) { return min(C, eq - (sq + jc * C)); };
 
@@ -420,7 +469,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
         } else if (sidx == 0) {
             init = A.s0;
             ibase = ((size_t)(n * HV + h) * dv + (size_t)tile * BV) * DK;
-            const bool whole = __builtin_amdgcn_readfirstlane(A.seq_nseg[n]) == 1;
+            const bool whole = it.whole != 0;
             fin = whole ? A.s_final : A.ws_E;
             fbase = whole ? ibase : ((size_t)(sg * HV + h) * dv + (size_t)tile * BV) * DK;
         } else {
@@ -595,21 +644,21 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
             state_operands();
             __syncthreads();  // B2
         }
-        if (fin) {
+        // the final state (Phi^T for a transition item), from one base
+        // address per lane so that the stores issue back to back
+        if (fin && trans) {
+            // Phi is stored transposed (Phi^T[j][i]): the combine pass reads
+            // it as an MFMA B operand, 8 consecutive i per lane
+            float* const fp = fin + (size_t)(sg * HV + h) * DK * DK + (size_t)(4 * lg) * DK + tile * BV + il;
 #pragma unroll
-            for (int jb = 0; jb < NJB; ++jb) {
-                const int j = 16 * jb + 4 * lg;
-                if (trans) {
-                    // Phi is stored transposed (Phi^T[j][i]): the combine pass
-                    // reads it as an MFMA B operand, 8 consecutive i per lane
+            for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        fin[(size_t)(sg * HV + h) * DK * DK + (size_t)(j + r) * DK + tile * BV + il] = sacc[jb][r];
-                } else {
-                    *reinterpret_cast<float4*>(fin + fbase + (size_t)il * DK + j) =
-                        make_float4(sacc[jb][0], sacc[jb][1], sacc[jb][2], sacc[jb][3]);
-                }
-            }
+                for (int r = 0; r < 4; ++r) fp[(size_t)(16 * jb + r) * DK] = sacc[jb][r];
+        } else if (fin) {
+            float* const fp = fin + fbase + (size_t)il * DK + 4 * lg;
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+                *reinterpret_cast<float4*>(fp + 16 * jb) = make_float4(sacc[jb][0], sacc[jb][1], sacc[jb][2], sacc[jb][3]);
         }
         return;
     }
@@ -742,12 +791,24 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
         }
         return;
     }
+}
 
-    // ===================== staging wavefronts =====================
-    const int hp = tid - 256;                      // 0..127
+// The staging wavefronts' own item loop.  They stage each item's chunks one
+// step ahead and keep the chunk after it in flight, as in one item; during an
+// item's last steps they load the first chunk of the workgroup's next item,
+// so that item's first barrier does not wait on memory.  Per item they pass
+// the same barriers as the other roles: one at the item's top, then, for an
+// item with chunks, B0 and two per chunk.
+template <int DK>
+__device__ __forceinline__ void scan_tp_stage(const PrefillArgs& A, const int items, ScanLds<DK>& S) {
+    constexpr int C = kChunk;
+    constexpr int BV = 32;
+    constexpr int KR = DK + 16;
+    constexpr int VR = BV + 16;
+    const int H = A.H, HV = A.HV, dv = A.dv;
+    const int hp = threadIdx.x - 256;              // 0..127
     const uint32_t qk_row = (uint32_t)H * DK * 2;  // bytes per token of q, k
     const uint32_t v_row = (uint32_t)HV * dv * 2;  // bytes per token of v
-    const uint32_t v_on = trans ? 0u : 1u;         // a transition item reads V as zero
     // K and Q: piece p = hp + 128 q, row p / 16, 16-byte column chunk c = p % 16
     // holding columns 8 c .. 8 c + 7, stored as two 8-byte halves at their slots
     uint32_t kq_off[8];
@@ -755,7 +816,7 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int p = hp + 128 * q, row = p >> 4, c16 = p & 15;
-        kq_off[q] = ((uint32_t)row * H + hk) * DK * 2 + 16 * c16;
+        kq_off[q] = (uint32_t)row * qk_row + 16 * c16;
         // columns 8 c .. 8 c + 3 are slots 4 h + 0..3 of lane group 2 (c % 2)
         // in step c / 4 (h = (c / 2) % 2), stored at 32 kk + 8 lg + 4 h
         kq_st[q] = row * KR + 32 * (c16 >> 2) + 16 * (c16 & 1) + 4 * ((c16 >> 1) & 1);
@@ -766,13 +827,16 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int p = hp + 128 * q, tok = p >> 2, part = p & 3;
-        v_off[q] = ((uint32_t)tok * HV + h) * (uint32_t)dv * 2 + (uint32_t)(tile * BV + 8 * part) * 2;
+        v_off[q] = (uint32_t)tok * v_row + 16 * part;
         v_st[q] = tok * VR + 8 * part;
     }
     bf8_t kst[8], qst[8], vst[2], tst[6];
     float gst = 0.f, gnst = 0.f;
-    auto load_chunk = [&](int jc) {
-        const int t0 = chunk_t0(jc), L = chunk_L(jc);
+    auto load_chunk = [&](const ScanItem& it, const int jc) {
+        const int t0 = it.sq + jc * C, L = min(C, it.eq - t0);
+        const uint32_t kq_h = (uint32_t)it.hk * DK * 2;
+        const uint32_t v_h = ((uint32_t)it.h * dv + (uint32_t)it.tile * BV) * 2;
+        const uint32_t v_on = it.trans ? 0u : 1u;  // a transition item reads V as zero
         const __amdgpu_buffer_rsrc_t rk =
             in_rsrc(static_cast<const bf16_t*>(A.k) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
         const __amdgpu_buffer_rsrc_t rq =
@@ -781,16 +845,18 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
             in_rsrc(static_cast<const bf16_t*>(A.v) + (size_t)t0 * HV * dv, v_on * L * v_row);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            kst[q] = bload8(rk, kq_off[q]);
-            qst[q] = bload8(rq, kq_off[q]);
+            kst[q] = bload8(rk, kq_off[q] + kq_h);
+            qst[q] = bload8(rq, kq_off[q] + kq_h);
         }
 #pragma unroll
-        for (int q = 0; q < 2; ++q) vst[q] = bload8(rv, v_off[q]);
-        const uint16_t* tp = A.ws_Tp + ((size_t)(c_first + jc) * HV + h) * kTpElems;
+        for (int q = 0; q < 2; ++q) vst[q] = bload8(rv, v_off[q] + v_h);
+        const uint16_t* tp = A.ws_Tp + ((size_t)(it.c_first + jc) * HV + it.h) * kTpElems;
 #pragma unroll
         for (int q = 0; q < 6; ++q) tst[q] = gld8(tp + 8 * (hp + 128 * q));
-        const float* gp = A.ws_G + ((size_t)(c_first + jc) * HV + h) * C;
-        if (hp < C) gst = gp[hp];
+        const float* gp = A.ws_G + ((size_t)(it.c_first + jc) * HV + it.h) * C;
+        // every lane loads (lanes hp >= C a copy): a value defined on some
+        // lanes only would be copied between registers, which waits for it
+        gst = gp[hp & (C - 1)];
         gnst = gp[L - 1];
     };
     auto stage_chunk = [&](int jc) {
@@ -799,43 +865,75 @@ __device__ __forceinline__ void scan_tp_item(const PrefillArgs& A, const int b) 
         for (int q = 0; q < 8; ++q) {
             const uint4 k4 = __builtin_bit_cast(uint4, kst[q]);
             const uint4 q4 = __builtin_bit_cast(uint4, qst[q]);
-            *reinterpret_cast<uint2*>(&Ks[pb][kq_st[q]]) = make_uint2(k4.x, k4.y);
-            *reinterpret_cast<uint2*>(&Ks[pb][kq_st[q] + 8]) = make_uint2(k4.z, k4.w);
-            *reinterpret_cast<uint2*>(&Qs[pb][kq_st[q]]) = make_uint2(q4.x, q4.y);
-            *reinterpret_cast<uint2*>(&Qs[pb][kq_st[q] + 8]) = make_uint2(q4.z, q4.w);
+            *reinterpret_cast<uint2*>(&S.Ks[pb][kq_st[q]]) = make_uint2(k4.x, k4.y);
+            *reinterpret_cast<uint2*>(&S.Ks[pb][kq_st[q] + 8]) = make_uint2(k4.z, k4.w);
+            *reinterpret_cast<uint2*>(&S.Qs[pb][kq_st[q]]) = make_uint2(q4.x, q4.y);
+            *reinterpret_cast<uint2*>(&S.Qs[pb][kq_st[q] + 8]) = make_uint2(q4.z, q4.w);
         }
 #pragma unroll
-        for (int q = 0; q < 2; ++q) *reinterpret_cast<bf8_t*>(&Vs[pb][v_st[q]]) = vst[q];
+        for (int q = 0; q < 2; ++q) *reinterpret_cast<bf8_t*>(&S.Vs[pb][v_st[q]]) = vst[q];
 #pragma unroll
-        for (int q = 0; q < 6; ++q) *reinterpret_cast<bf8_t*>(&Tp[pb][8 * (hp + 128 * q)]) = tst[q];
+        for (int q = 0; q < 6; ++q) *reinterpret_cast<bf8_t*>(&S.Tp[pb][8 * (hp + 128 * q)]) = tst[q];
         if (hp < C) {
-            Gs[pb][0][hp] = gst;
-            Gs[pb][1][hp] = exp2f_(gst);
-            Gs[pb][2][hp] = exp2f_(gnst - gst);
+            S.Gs[pb][0][hp] = gst;
+            S.Gs[pb][1][hp] = exp2f_(gst);
+            S.Gs[pb][2][hp] = exp2f_(gnst - gst);
         }
     };
-    load_chunk(0);
-    stage_chunk(0);
-    if (nch > 1) load_chunk(1);
-    __syncthreads();  // B0
-    for (int jc = 0; jc < nch; ++jc) {
+    bool have = false;  // the registers hold item b's first chunk (loaded during the previous item)
+    for (int b = blockIdx.x; b < items; b += gridDim.x) {
+        __syncthreads();  // the previous item has finished with the LDS
+        const ScanItem it = scan_item<DK>(A, b);
+        if (!it.live) continue;
+        const int nch = it.nch;
+        ScanItem nx{};
+        if (b + (int)gridDim.x < items) nx = scan_item<DK>(A, b + gridDim.x);
+        if (!have) load_chunk(it, 0);
+        stage_chunk(0);
+        if (nch > 1)
+            load_chunk(it, 1);
+        else if (nx.live)
+            load_chunk(nx, 0);
+        __syncthreads();  // B0
         // the next chunk into the other buffers (their last reader finished
-        // before the previous step's second barrier); the one after it in flight
-        if (jc + 1 < nch) stage_chunk(jc + 1);
-        if (jc + 2 < nch) load_chunk(jc + 2);
-        __syncthreads();  // B1
+        // before the previous step's second barrier), the one after it in
+        // flight; every step of this loop stages and loads, so the registers'
+        // pending loads are the same on every path into it
+        int jc = 0;
+        for (; jc + 2 < nch; ++jc) {
+            stage_chunk(jc + 1);
+            load_chunk(it, jc + 2);
+            __syncthreads();  // B1
+            __syncthreads();  // B2
+        }
+        if (nch > 1) {
+            // the last chunk staged, the next item's first in flight
+            stage_chunk(nch - 1);
+            if (nx.live) load_chunk(nx, 0);
+            __syncthreads();  // B1
+            __syncthreads();  // B2
+        }
+        __syncthreads();  // B1 of the last step
         __syncthreads();  // B2
+        have = nx.live;
     }
 }
 
 // Persistent over work items, as the per-tile scan: workgroup blockIdx.x takes
 // items blockIdx.x, blockIdx.x + gridDim.x, ... (the grid is a multiple of 8,
-// so an item keeps its XCD).
+// so an item keeps its XCD).  The chain and output wavefronts run the item
+// loop here, the staging wavefronts their own (the same items and barriers),
+// which carries the next item's first chunk in registers.
 template <int DK, typename Tout>
 __global__ __launch_bounds__(384) void scan_tp_kernel(const PrefillArgs A, int items) {
+    __shared__ ScanLds<DK> S;
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= 4) {
+        scan_tp_stage<DK>(A, items, S);
+        return;
+    }
     for (int b = blockIdx.x; b < items; b += gridDim.x) {
         __syncthreads();  // the previous item has finished with the LDS
-        scan_tp_item<DK, Tout>(A, b);
+        scan_tp_item<DK, Tout>(A, b, S);
     }
 }
 
