@@ -78,11 +78,17 @@ struct TokenBlock {
 // holds A and T.  Per value head: G (a wave prefix sum, log2 units), A =
 // strictly lower diag(b) (K K^T o e^{G_t - G_s}), T = (I + A)^-1 by forward
 // substitution on the 16 x 16 diagonal blocks and block merges on split-bf16
-// MFMA, then T' = T diag(b) written out as hi / lo blocks.  Rows past a
-// sequence end read K, g and b as zero, so T' has zero rows there and its
-// valid block is the inverse of the valid part alone.  At most 128 VGPRs
-// keep four workgroups on a CU (a tighter bound spills and measured slower).
-template <int DK>
+// MFMA, then T' = T diag(b) written out as hi / lo blocks.  P value heads go
+// through these steps together, each in its own A / T buffer (P = 2 when a
+// key head has an even number of value heads): the diagonal blocks of value
+// head p take lanes 16 p .. 16 p + 15 of each wavefront, its 16-block merges
+// wavefronts 2 p and 2 p + 1, and every wavefront does its 32-block merge
+// products for each of them, so a pair costs about one value head's
+// latency.  Rows past a sequence end read K, g and b as zero, so T' has zero
+// rows there and its valid block is the inverse of the valid part alone.  At
+// most 128 VGPRs keep four workgroups on a CU (a tighter bound spills and
+// measured slower).
+template <int DK, int P>
 __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
     constexpr int KP = DK + 8;   // padded bf16 row of the K tile
@@ -91,13 +97,13 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
     constexpr int PPR = DK / 8;  // 16-byte pieces per row
     constexpr int RPI = 64 / PPR;
     constexpr int NLD = 16 / RPI;
+    static_assert(P == 1 || P == 2, "one or two value heads at a time");
     static_assert(C * KP * 2 <= C * AP * 4, "the K tile fits the A / T buffer");
-    __shared__ __attribute__((aligned(16))) float Tm[C * AP];  // K, then A, then T written over it
-    __bf16* const Ks = reinterpret_cast<__bf16*>(Tm);
-    __shared__ __attribute__((aligned(16))) float Gs[C];
-    __shared__ __attribute__((aligned(16))) float Bs[C];
-    float* const Am = Tm;
-    float* const Xm = Tm + 32;  // 32-block merge: X [32 x 32] in the upper-right block
+    // per value head in flight: A, then T written over it; buffer 0 first holds K
+    __shared__ __attribute__((aligned(16))) float Tm[P][C * AP];
+    __bf16* const Ks = reinterpret_cast<__bf16*>(Tm[0]);
+    __shared__ __attribute__((aligned(16))) float Gs[P][C];
+    __shared__ __attribute__((aligned(16))) float Bs[P][C];
 
     const int H = A.H, HV = A.HV, R = HV / H;
     // workgroup id -> (chunk, key head): the key heads of a chunk on one XCD
@@ -116,8 +122,8 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
     const int t0 = s0 + (c - A.chunk_off[n]) * C;
     const int L = min(C, e0 - t0);
 
-    // K rows of the key head (coalesced 16-byte pieces), g and b of the first
-    // value head for token l (wave 0; zero past the end)
+    // K rows of the key head (coalesced 16-byte pieces); g and b of value
+    // head p for token l on wavefront p (zero past the end)
     const uint32_t qk_row = (uint32_t)H * DK * 2;
     const __amdgpu_buffer_rsrc_t rk =
         in_rsrc(static_cast<const bf16_t*>(A.k) + (size_t)t0 * H * DK, (uint32_t)L * qk_row);
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
         bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)((l * HV + hv) * 4), 0, 0));
     };
     float gnext = 0.f, bnext = 0.f;
-    if (w == 0) load_gb(hk * R, gnext, bnext);
+    if (w < P) load_gb(hk * R + w, gnext, bnext);
 #pragma unroll
     for (int p = 0; p < NLD; ++p)
         *reinterpret_cast<bf8_t*>(&Ks[(16 * w + RPI * p + l / PPR) * KP + 8 * (l % PPR)]) = kst[p];
@@ -154,34 +160,36 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
     }
     __syncthreads();  // every wavefront has read K: its buffer holds A and T from here
 
-    for (int v = 0; v < R; ++v) {
-        const int hv = hk * R + v;
-        if (w == 0) {
-            // G (log2 units, inclusive in-chunk prefix sum) and b of this value head
+    for (int v0 = 0; v0 < R; v0 += P) {
+        if (w < P) {
+            // G (log2 units, inclusive in-chunk prefix sum) and b of value head v0 + w
+            const int hv = hk * R + v0 + w;
             float gs = gnext * kLog2e;
             const float bv = bnext;
-            if (v + 1 < R) load_gb(hv + 1, gnext, bnext);  // the next value head's, in flight
+            if (v0 + P < R) load_gb(hv + P, gnext, bnext);  // the next pass's, in flight
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float up = __shfl_up(gs, off, 64);
                 if (l >= off) gs += up;
             }
-            Gs[l] = gs;
-            Bs[l] = bv;
+            Gs[w][l] = gs;
+            Bs[w][l] = bv;
             A.ws_G[((size_t)c * HV + hv) * C + l] = gs;
         }
         __syncthreads();  // G and b are in LDS
 
         // A = strictly lower part of diag(b) (K K^T o e^{G_t - G_s}), row block w
-        {
-            const float4 g4 = *reinterpret_cast<const float4*>(&Gs[16 * w + 4 * lg]);
-            const float4 b4 = *reinterpret_cast<const float4*>(&Bs[16 * w + 4 * lg]);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            float* const Am = Tm[p];
+            const float4 g4 = *reinterpret_cast<const float4*>(&Gs[p][16 * w + 4 * lg]);
+            const float4 b4 = *reinterpret_cast<const float4*>(&Bs[p][16 * w + 4 * lg]);
             const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
             const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
                 if (sb <= w) {
-                    const float Gsb = Gs[16 * sb + lr];
+                    const float Gsb = Gs[p][16 * sb + lr];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = 16 * w + 4 * lg + r, s = 16 * sb + lr;
@@ -193,10 +201,11 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
             }
         }
         __syncthreads();
-        // diagonal blocks T_bb = (I + A_bb)^-1 by forward substitution: wave b,
-        // lane j < 16 owns column j
-        if (l < 16) {
+        // diagonal blocks T_bb = (I + A_bb)^-1 by forward substitution:
+        // wavefront b, lane 16 p + j of value head p owns column j
+        if (l < 16 * P) {
             const int o = 16 * w;
+            float* const Am = Tm[P == 1 ? 0 : (l >> 4)];
             float col[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
@@ -209,27 +218,28 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
                         arow[4 * q4 + 2] = a4.z; arow[4 * q4 + 3] = a4.w;
                     }
                 }
-                float v_ = (t == l) ? 1.f : 0.f;
+                float v_ = (t == lr) ? 1.f : 0.f;
 #pragma unroll
                 for (int x = 0; x < t; ++x) v_ -= arow[x] * col[x];
                 col[t] = v_;
             }
 #pragma unroll
-            for (int t = 0; t < 16; ++t) Tm[(o + t) * AP + o + l] = col[t];
+            for (int t = 0; t < 16; ++t) Am[(o + t) * AP + o + lr] = col[t];
         }
         __syncthreads();
-        // 16-block merges, one per wavefront 0 and 1:
+        // 16-block merges, value head p on wavefronts 2 p and 2 p + 1:
         //   T_{ii,j} = -T_{ii,ii} (A_{ii,j} T_{jj}),  (ii, j) = (1, 0), (3, 2)
         // (the 16-long contraction fills slots 0..3 of each lane group, slots
         // 4..7 are zero, so the first product's accumulators are the second
         // product's B operand)
-        if (w < 2) {
-            const int j = 2 * w, ii = j + 1;
-            const float4 a4 = *reinterpret_cast<const float4*>(&Am[(16 * ii + lr) * AP + 16 * j + 4 * lg]);
+        if (w < 2 * P) {
+            float* const Tb = Tm[P == 1 ? 0 : (w >> 1)];
+            const int j = 2 * (w & 1), ii = j + 1;
+            const float4 a4 = *reinterpret_cast<const float4*>(&Tb[(16 * ii + lr) * AP + 16 * j + 4 * lg]);
             float av[8] = {a4.x, a4.y, a4.z, a4.w, 0.f, 0.f, 0.f, 0.f};
             float bv8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int y = 0; y < 4; ++y) bv8[y] = Tm[(16 * j + 4 * lg + y) * AP + 16 * j + lr];
+            for (int y = 0; y < 4; ++y) bv8[y] = Tb[(16 * j + 4 * lg + y) * AP + 16 * j + lr];
             bf8_t ah, al, bh, bl;
             split8(av, ah, al);
             split8(bv8, bh, bl);
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
             xa = mfma(ah, bh, xa);
             xa = mfma(ah, bl, xa);
             xa = mfma(al, bh, xa);
-            const float4 t4 = *reinterpret_cast<const float4*>(&Tm[(16 * ii + lr) * AP + 16 * ii + 4 * lg]);
+            const float4 t4 = *reinterpret_cast<const float4*>(&Tb[(16 * ii + lr) * AP + 16 * ii + 4 * lg]);
             float tv[8] = {t4.x, t4.y, t4.z, t4.w, 0.f, 0.f, 0.f, 0.f};
             float xv[8] = {xa[0], xa[1], xa[2], xa[3], 0.f, 0.f, 0.f, 0.f};
             split8(tv, ah, al);
@@ -247,69 +257,90 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
             ta = mfma(ah, bl, ta);
             ta = mfma(al, bh, ta);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Tm[(16 * ii + 4 * lg + r) * AP + 16 * j + lr] = -ta[r];
+            for (int r = 0; r < 4; ++r) Tb[(16 * ii + 4 * lg + r) * AP + 16 * j + lr] = -ta[r];
         }
         __syncthreads();
-        // 32-block merge: X = A[32:64, 0:32] T[0:32, 0:32]; T[32:64, 0:32] = -T_B X
+        // 32-block merge: X = A[32:64, 0:32] T[0:32, 0:32] into the upper-right
+        // block; T[32:64, 0:32] = -T_B X.  Wavefront w: row block w >> 1,
+        // column block w & 1, for each value head in flight.
+        const int tbm = w >> 1, jb = w & 1;
         {
-            const int tbm = w >> 1, jb = w & 1;
-            float av[8], bv8[8];
+            f4_t xa[P];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                av[x] = Am[(32 + 16 * tbm + lr) * AP + 8 * lg + x];
-                const int xr = 8 * lg + x, cc = 16 * jb + lr;
-                bv8[x] = (xr >= cc) ? Tm[xr * AP + cc] : 0.f;
+            for (int p = 0; p < P; ++p) {
+                const float* const Tb = Tm[p];
+                float av[8], bv8[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    av[x] = Tb[(32 + 16 * tbm + lr) * AP + 8 * lg + x];
+                    const int xr = 8 * lg + x, cc = 16 * jb + lr;
+                    bv8[x] = (xr >= cc) ? Tb[xr * AP + cc] : 0.f;
+                }
+                bf8_t ah, al, bh, bl;
+                split8(av, ah, al);
+                split8(bv8, bh, bl);
+                xa[p] = f4_t{0.f, 0.f, 0.f, 0.f};
+                xa[p] = mfma(ah, bh, xa[p]);
+                xa[p] = mfma(ah, bl, xa[p]);
+                xa[p] = mfma(al, bh, xa[p]);
             }
-            bf8_t ah, al, bh, bl;
-            split8(av, ah, al);
-            split8(bv8, bh, bl);
-            f4_t xa = f4_t{0.f, 0.f, 0.f, 0.f};
-            xa = mfma(ah, bh, xa);
-            xa = mfma(ah, bl, xa);
-            xa = mfma(al, bh, xa);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Xm[(16 * tbm + 4 * lg + r) * AP + 16 * jb + lr] = xa[r];
+            for (int p = 0; p < P; ++p) {
+                float* const Xm = Tm[p] + 32;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Xm[(16 * tbm + 4 * lg + r) * AP + 16 * jb + lr] = xa[p][r];
+            }
         }
         __syncthreads();
         {
-            const int tbm = w >> 1, jb = w & 1;
-            float av[8], bv8[8];
+            f4_t ta[P];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const int rr = 16 * tbm + lr, xc = 8 * lg + x;  // T_B row rr, column xc (lower)
-                av[x] = (xc <= rr) ? Tm[(32 + rr) * AP + 32 + xc] : 0.f;
-                bv8[x] = Xm[(8 * lg + x) * AP + 16 * jb + lr];
+            for (int p = 0; p < P; ++p) {
+                const float* const Tb = Tm[p];
+                const float* const Xm = Tb + 32;
+                float av[8], bv8[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const int rr = 16 * tbm + lr, xc = 8 * lg + x;  // T_B row rr, column xc (lower)
+                    av[x] = (xc <= rr) ? Tb[(32 + rr) * AP + 32 + xc] : 0.f;
+                    bv8[x] = Xm[(8 * lg + x) * AP + 16 * jb + lr];
+                }
+                bf8_t ah, al, bh, bl;
+                split8(av, ah, al);
+                split8(bv8, bh, bl);
+                ta[p] = f4_t{0.f, 0.f, 0.f, 0.f};
+                ta[p] = mfma(ah, bh, ta[p]);
+                ta[p] = mfma(ah, bl, ta[p]);
+                ta[p] = mfma(al, bh, ta[p]);
             }
-            bf8_t ah, al, bh, bl;
-            split8(av, ah, al);
-            split8(bv8, bh, bl);
-            f4_t ta = f4_t{0.f, 0.f, 0.f, 0.f};
-            ta = mfma(ah, bh, ta);
-            ta = mfma(ah, bl, ta);
-            ta = mfma(al, bh, ta);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Tm[(32 + 16 * tbm + 4 * lg + r) * AP + 16 * jb + lr] = -ta[r];
+            for (int p = 0; p < P; ++p) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Tm[p][(32 + 16 * tbm + 4 * lg + r) * AP + 16 * jb + lr] = -ta[p][r];
+            }
         }
         __syncthreads();
-        // T' = T diag(b) in tile order (unit u = (tile, lane)), hi / lo.  A
-        // select, not a 0/1 factor, zeroes the slots past the diagonal (T's
-        // upper blocks hold scratch data).
-        uint16_t* const tp = A.ws_Tp + ((size_t)c * HV + hv) * kTpElems;
+        // T' = T diag(b) in tile order (unit u = (value head, tile, lane)), hi /
+        // lo.  A select, not a 0/1 factor, zeroes the slots past the diagonal
+        // (T's upper blocks hold scratch data).
+        constexpr int kUnits = kTpTiles * 64;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < (P * kUnits + 255) / 256; ++q) {
             const int u = tid + 256 * q;
-            if (u < kTpTiles * 64) {
-                const int ti = u >> 6, ul = u & 63, ulr = ul & 15, ulg = ul >> 4;
+            if (u < P * kUnits) {
+                const int p = P == 1 ? 0 : u / kUnits, uu = u - p * kUnits;
+                const int ti = uu >> 6, ul = uu & 63, ulr = ul & 15, ulg = ul >> 4;
                 const int tb = ti < 2 ? ti : (ti < 4 ? 2 : 3);
                 const int kk = ti - tp_tile(tb, 0);
                 const int t = 16 * tb + ulr;
+                const float* const Tb = Tm[p];
                 float pv[8];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int s0 = slot_index(kk, ulg, 4 * hh);
-                    const float4 x4 = *reinterpret_cast<const float4*>(&Tm[t * AP + s0]);
-                    const float4 b4 = *reinterpret_cast<const float4*>(&Bs[s0]);
+                    const float4 x4 = *reinterpret_cast<const float4*>(&Tb[t * AP + s0]);
+                    const float4 b4 = *reinterpret_cast<const float4*>(&Bs[p][s0]);
                     const float tv[4] = {x4.x, x4.y, x4.z, x4.w};
                     const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
@@ -317,11 +348,12 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
                 }
                 bf8_t hi, lo;
                 split8(pv, hi, lo);
+                uint16_t* const tp = A.ws_Tp + ((size_t)c * HV + hk * R + v0 + p) * kTpElems;
                 *reinterpret_cast<bf8_t*>(tp + ti * kTpTileElems + ul * 8) = hi;
                 *reinterpret_cast<bf8_t*>(tp + ti * kTpTileElems + 512 + ul * 8) = lo;
             }
         }
-        __syncthreads();  // Tm, Gs and Bs are rewritten for the next value head
+        __syncthreads();  // Tm, Gs and Bs are rewritten for the next pass
     }
 }
 
@@ -939,7 +971,10 @@ __global__ __launch_bounds__(384) void scan_tp_kernel(const PrefillArgs A, int i
 
 hipError_t launch_prep_tp(const PrefillArgs& A) {
     const unsigned grid = (unsigned)((A.max_chunks + 7) / 8) * 8u * (unsigned)A.H;
-    hipLaunchKernelGGL((prep_tp_kernel<128>), dim3(grid), dim3(256), 0, A.stream, A);
+    if ((A.HV / A.H) % 2 == 0)
+        hipLaunchKernelGGL((prep_tp_kernel<128, 2>), dim3(grid), dim3(256), 0, A.stream, A);
+    else
+        hipLaunchKernelGGL((prep_tp_kernel<128, 1>), dim3(grid), dim3(256), 0, A.stream, A);
     return hipGetLastError();
 }
 
