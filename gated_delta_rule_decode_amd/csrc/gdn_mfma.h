@@ -21,11 +21,25 @@ __device__ __forceinline__ f4_t mfma(bf8_t a, bf8_t b, f4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// two floats -> packed hi and lo bf16 words (one conversion per word)
+// two floats -> packed hi and lo bf16 words: hi = bf16(x) (one packed
+// conversion); x - hi in fp32 straight from the packed hi, as a bf16 dot
+// product with (-1, 0) or (0, -1) accumulated onto x (one v_dot2c per value:
+// x - bf16(x) is exact in fp32, so the dot's rounding never acts); lo =
+// bf16(x - hi) (one conversion).  Four instructions per pair, against six
+// when hi is widened back to fp32 by a shift and a mask and subtracted.  The
+// two bf16 pairs are moved into scalar registers by hand: given as constants,
+// the compiler folds (-1, 0) into an inline immediate that the hardware reads
+// as (0, -1) (an in-bounds probe on gfx950: every lane wrong with the folded
+// constant, every lane equal to the subtraction with the register).
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{x0, x1}, bf2_t));
-    const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
-    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{x0 - h0, x1 - h1}, bf2_t));
+    uint32_t m0, m1;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(m0));      // bf16 (-1, 0)
+    asm("s_mov_b32 %0, 0xbf800000" : "=s"(m1));  // bf16 (0, -1)
+    const bf2_t h = __builtin_convertvector(f2_t{x0, x1}, bf2_t);
+    const float d0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2_t, m0), x0, false);
+    const float d1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2_t, m1), x1, false);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{d0, d1}, bf2_t));
 }
 // fp32 x -> (hi, lo) with hi = bf16(x), lo = bf16(x - hi): 4 or 8 values
 __device__ __forceinline__ void split4(const float* x, uint2& hi, uint2& lo) {
