@@ -100,7 +100,6 @@ struct PrefillArgs {
 constexpr int kSegMinChunks = 32;  // shortest segment of the segment-parallel scan
 constexpr int kSegAutoSkewed = -2; // segment_chunks: automatic, also when the chains fill the CUs
 constexpr int kCorrChunks = 4;     // chunks per item of the correction pass
-constexpr int kPrepPlanMaxSeqs = 256;  // d_k = 128: batches up to this size plan inside the prep launch
 constexpr int kPlanInts = 8;
 
 struct NormArgs {
@@ -161,7 +160,7 @@ hipError_t launch_prefill(const PrefillArgs& a);
 bool prefill_mfma_eligible(const PrefillArgs& a);
 hipError_t launch_prefill_mfma(const PrefillArgs& a);
 // T'-only prep and the chain / helper scan (d_k = 128)
-hipError_t launch_prep_tp(const PrefillArgs& a, int plan_tv);
+hipError_t launch_prep_tp(const PrefillArgs& a);
 hipError_t launch_scan_tp(const PrefillArgs& a, size_t grid, int items);
 hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream);
 hipError_t launch_rmsnorm_gated(const NormArgs& a);

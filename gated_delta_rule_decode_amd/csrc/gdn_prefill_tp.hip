@@ -41,7 +41,6 @@
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 #include "gdn_prefill_common.h"
-#include "gdn_prefill_plan.h"
 
 namespace gdn {
 
@@ -89,14 +88,8 @@ struct TokenBlock {
 // rows there and its valid block is the inverse of the valid part alone.  At
 // most 128 VGPRs keep four workgroups on a CU (a tighter bound spills and
 // measured slower).
-//
-// plan_tv > 0 (batches of at most kPrepPlanMaxSeqs sequences): the launch's
-// last workgroup is the segment planner (plan_tv value tiles per head), and
-// every other workgroup finds its chunk's sequence from cu_seqlens itself
-// instead of from the planner's chunk table, so the planner needs no launch
-// of its own.
 template <int DK, int P>
-__global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A, const int plan_tv) {
+__global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A) {
     constexpr int C = kChunk;
     constexpr int KP = DK + 8;   // padded bf16 row of the K tile
     constexpr int AP = C + 4;    // padded fp32 row (16-byte aligned rows)
@@ -112,14 +105,6 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A, co
     __shared__ __attribute__((aligned(16))) float Gs[P][C];
     __shared__ __attribute__((aligned(16))) float Bs[P][C];
 
-    if (plan_tv > 0 && blockIdx.x == gridDim.x - 1) {
-        // the planner, in this workgroup's LDS (the tables of at most
-        // kPrepPlanMaxSeqs sequences, 3 KiB, in the first A / T buffer)
-        int* const ib = reinterpret_cast<int*>(Tm[0]);
-        plan_segments(A, plan_tv, DK / 32, 1, ib, ib + 256, ib + 256 + kPrepPlanMaxSeqs,
-                      kPrepPlanMaxSeqs, Gs[0], reinterpret_cast<int*>(Bs[0]));
-        return;
-    }
     const int H = A.H, HV = A.HV, R = HV / H;
     // workgroup id -> (chunk, key head): the key heads of a chunk on one XCD
     // (id % 8) in neighbouring slots, so the cache lines of g and beta that
@@ -129,49 +114,12 @@ __global__ __launch_bounds__(256, 4) void prep_tp_kernel(const PrefillArgs A, co
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     __builtin_assume(w >= 0 && w < 4);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
-    int n, coff;
-    if (plan_tv > 0) {
-        // the first chunk of every sequence (N <= 256, thread n holding
-        // sequence n): wavefront prefix sums, then the wavefronts' totals
-        __shared__ int wsum[4], sel[2];
-        int cnt = 0;
-        if (tid < A.N) {
-            int s, e;
-            seq_bounds_m(A.cu_seqlens, tid, A.T, s, e);
-            cnt = (e - s + C - 1) / C;
-        }
-        int inc = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int up = __shfl_up(inc, off, 64);
-            if (l >= off) inc += up;
-        }
-        if (l == 63) wsum[w] = inc;
-        __syncthreads();
-        int before = 0, all = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            before += i < w ? wsum[i] : 0;
-            all += wsum[i];
-        }
-        // chunk c belongs to the one sequence whose chunks [excl, excl + cnt) hold it
-        const int excl = before + inc - cnt;
-        if (cnt > 0 && excl <= c && c < excl + cnt) {
-            sel[0] = tid;
-            sel[1] = excl;
-        }
-        if (c >= min(all, A.max_chunks)) return;  // uniform over the workgroup
-        __syncthreads();
-        n = sel[0];
-        coff = sel[1];
-    } else {
-        if (c >= min(A.chunk_off[A.N], A.max_chunks)) return;
-        n = find_seq_m(A.chunk_off, A.N, c);
-        coff = A.chunk_off[n];
-    }
+    const int total = min(A.chunk_off[A.N], A.max_chunks);
+    if (c >= total) return;
+    const int n = find_seq_m(A.chunk_off, A.N, c);
     int s0, e0;
     seq_bounds_m(A.cu_seqlens, n, A.T, s0, e0);
-    const int t0 = s0 + (c - coff) * C;
+    const int t0 = s0 + (c - A.chunk_off[n]) * C;
     const int L = min(C, e0 - t0);
 
     // K rows of the key head (coalesced 16-byte pieces); g and b of value
@@ -1021,13 +969,12 @@ __global__ __launch_bounds__(384) void scan_tp_kernel(const PrefillArgs A, int i
     }
 }
 
-hipError_t launch_prep_tp(const PrefillArgs& A, int plan_tv) {
-    const unsigned grid =
-        (unsigned)((A.max_chunks + 7) / 8) * 8u * (unsigned)A.H + (plan_tv > 0 ? 1u : 0u);
+hipError_t launch_prep_tp(const PrefillArgs& A) {
+    const unsigned grid = (unsigned)((A.max_chunks + 7) / 8) * 8u * (unsigned)A.H;
     if ((A.HV / A.H) % 2 == 0)
-        hipLaunchKernelGGL((prep_tp_kernel<128, 2>), dim3(grid), dim3(256), 0, A.stream, A, plan_tv);
+        hipLaunchKernelGGL((prep_tp_kernel<128, 2>), dim3(grid), dim3(256), 0, A.stream, A);
     else
-        hipLaunchKernelGGL((prep_tp_kernel<128, 1>), dim3(grid), dim3(256), 0, A.stream, A, plan_tv);
+        hipLaunchKernelGGL((prep_tp_kernel<128, 1>), dim3(grid), dim3(256), 0, A.stream, A);
     return hipGetLastError();
 }
 
