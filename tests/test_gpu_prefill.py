@@ -251,6 +251,20 @@ def test_prefill_many_chains_matches_oracle(orc, H, HV, N):
                   cu=x.cu_seqlens)
 
 
+@pytest.mark.parametrize("N", [255, 256, 257, 300])
+def test_prefill_batches_of_hundreds_of_sequences(orc, N):
+    """Batches of a few hundred short prompts at d = 128 (the planner's block
+    scans take 256 sequences per round, so both sides of that size), with
+    empty, one-token, whole-chunk and ragged prompts."""
+    lengths = _lengths_many(200 + N, N, 140)
+    x = gi.make_prefill(lengths, 2, 4, 128, 128, s0_std=0.02, seed=300 + N)
+    say(f"prefill batch of {N} sequences: T={sum(lengths)}")
+    o, S = gpu_prefill(x, scale=128 ** -0.5)
+    o_ref, S_ref = oracle_prefill(orc, x, scale=128 ** -0.5)
+    assert_parity(host(o), host(S), o_ref, S_ref, what=f"batch of {N} sequences",
+                  cu=x.cu_seqlens)
+
+
 def test_prefill_result_does_not_depend_on_the_batch():
     """Every (chain, 32-row tile) item runs the same code on its own data, so
     the same sequences give the same outputs and final states bit for bit in
