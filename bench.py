@@ -102,12 +102,12 @@ NORM_TRAFFIC = {"kernel_source_sha256": "8bba89fa6e221f323599e1e67999eda741660cc
 # without an initial state, the cap phase is prefill4cap's.
 PREFILL_SOURCES = ("gdn_prefill_mfma.hip", "gdn_prefill_tp.hip")
 PREFILL_COUNTERS = {
-    "kernel_source_sha256": "2d6aa1212c2ec11b93bdcc4d18dd863d1c3e4422dbcb66b726757156bfd5811b",
+    "kernel_source_sha256": "4ca8b49a8eaa23df991969aab3cdd2ae563bacb10cd19d39e94127e5e642e38c",
     "issued_mfma_flops": {"prefill2": 86704652288, "prefill3": 170724950016,
                           "prefill4cap": 1367133388800, "job35b": 170724950016,
                           "cap": 1367133388800},
-    "traffic_bytes": {"prefill2": 512165484, "prefill3": 818382981, "prefill4cap": 6547138987,
-                      "job35b": 818382981, "cap": 6547138987}}
+    "traffic_bytes": {"prefill2": 512143287, "prefill3": 818358760, "prefill4cap": 6544831466,
+                      "job35b": 818358760, "cap": 6544831466}}
 
 
 def recorded(record, source):
