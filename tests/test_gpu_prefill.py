@@ -217,11 +217,12 @@ def test_prefill_zero_tokens_copies_state():
     assert torch.count_nonzero(S).item() == 0
 
 
-@pytest.mark.parametrize("ratio", [1, 4, 8])
+@pytest.mark.parametrize("ratio", [1, 3, 4, 6, 8])
 def test_prefill_value_heads_per_key_head(orc, ratio):
-    """1, 4 and 8 value heads per key head on the MFMA kernels, which take any
-    ratio (K K^T and Q K^T are formed again for every value head of a key
-    head)."""
+    """1, 3, 4, 6 and 8 value heads per key head on the MFMA kernels, which
+    take any ratio: the prep forms K K^T once per key head and takes its value
+    heads one at a time for an odd count, two at a time for an even one (3:
+    three single passes; 6: three paired passes)."""
     x = gi.make_prefill([130, 70, 1], 1, ratio, 128, 128, dtype="bf16", s0_std=0.05,
                         seed=40 + ratio)
     say(f"prefill value heads per key head = {ratio}")
