@@ -481,6 +481,8 @@ def run_job35b(args):
                      "algorithmic_bytes_per_launch": bytes_launch},
         "copy_same_bytes": copy_ref,
         "roofline_prefill": pf_line,
+        "context": model_step_context(pf_tokens / (pf_ms / args.steps * 1e-3),
+                                      dec_tokens / (dec_ms / args.steps * 1e-3), 30),
     }
     if not args.no_cap:
         out["phases"]["long_context_varlen_cap"] = prefill_cap_phase(args)
@@ -494,6 +496,18 @@ def run_job35b(args):
                                          f"rows x {steps} decode steps + RMSNormGated, fp64, "
                                          f"{secs:.1f} s"}
     return out
+
+
+def model_step_context(pf_tok_s, dec_tok_s, layers):
+    """Context only: the per-layer rates over the DeltaNet layers of a whole
+    model (18 of the 0.8B model's 24 layers; 30 of the 35B-A3B's 40: Core AI
+    card, introduction), i.e. a model step with nothing but its DeltaNet
+    mixers -- no attention, MoE, projections or sampling."""
+    return {"deltanet_layers": layers,
+            "gdn_only_prefill_tokens_per_s": round(pf_tok_s / layers, 1),
+            "gdn_only_decode_tokens_per_s": round(dec_tok_s / layers, 1),
+            "note": "per-layer rates divided by the model's DeltaNet layer count; "
+                    "not a whole-model figure"}
 
 
 def prefill_cap_phase(args):
@@ -679,6 +693,7 @@ def run_decode_job(args):
                              "mfma_bf16_frac": round(pf_f / (pf_call_us * 1e-6) / 1e12 /
                                                      BF16_PEAK_TFLOPS, 5),
                              "algorithmic_bytes": pf_b, "algorithmic_flops": pf_f},
+        "context": model_step_context(pf_tok_s, dec_tok_s, 18),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a sample of the job")
