@@ -20,9 +20,10 @@
 // for all G query heads of the group, so each cache row is read once.  Scores
 // on MFMA (v_mfma_f32_16x16x32_bf16, query heads as the 16 rows, q split into
 // hi + lo bf16 against the exact bf16 keys), an online softmax per head, and
-// P V on the vector units with every value row read as whole cache lines (one
-// 16-byte or smaller piece per lane).  A second kernel merges the splits and
-// applies the gate.
+// P V on MFMA as well (v_mfma_f32_16x16x16_bf16 per 16 value dimensions, the
+// block's value rows, read as whole cache lines, staged in the wavefront's
+// LDS area and read back transposed; P split into hi + lo).  A second kernel
+// merges the splits and applies the gate.
 #include <math.h>
 
 #include "gdn_device.h"
@@ -55,7 +56,8 @@ void attn_plan(int N, int Hq, int Hkv, int D, int Lmax, int& split, int& nsplit,
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
+// (at most 256 registers a lane: two workgroups on a CU)
+__global__ __launch_bounds__(kAttnWG, 2) void attn_split_kernel(const AttnArgs A) {
     constexpr int NKK = D / 32;   // MFMA k-steps over the head dimension
     constexpr int DPL = D / 64;   // value dimensions per lane in P V
     static_assert(G >= 1 && G <= 16 && D % 64 == 0, "shape");
@@ -71,6 +73,13 @@ __global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
     __shared__ float pb[4][16][16];    // per wavefront: P of a 16-position block [pos][head]
     __shared__ float al[4][16];        // per wavefront: rescale factors of a block [head]
     __shared__ float xm[2][G], xl[2][G];  // merging the wavefronts
+    // per wavefront: a block's value rows [16][VR] bf16 (VR = D + 16: padded
+    // rows keep the transposed reads off common banks), then, after the
+    // positions, its o [G][D] fp32 on the way to the merge's layout
+    constexpr int VR = D + 16;
+    constexpr int VXF = (16 * VR / 2 > G * D) ? 16 * VR / 2 : G * D;  // floats per wavefront
+    __shared__ __attribute__((aligned(16))) float vx[4][VXF];
+    constexpr int NT = D / 16;  // 16-dimension tiles of P V
 
     const int Hkv = A.Hkv;
     const int n = blockIdx.y / Hkv, kvh = blockIdx.y - n * Hkv;
@@ -153,11 +162,17 @@ __global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
         m[r] = -INFINITY;
         ls[r] = 0.f;
     }
-    float acc[G][DPL];  // o[head][dims DPL l ..] (unnormalised, relative to m)
+    // o^T on MFMA: oacc[t][r] = o[head lr][dim 16 t + 4 lg + r] (unnormalised,
+    // relative to m; lanes lr >= G hold padding heads)
+    f4_t oacc[NT];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int t = 0; t < NT; ++t) oacc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+    // the new position's value row, as the cache words of this lane's dims
+    uint32_t vnw[2] = {0u, 0u};
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) acc[g][j] = 0.f;
+    for (int j = 0; j < DPL; ++j) vnw[j / 2] |= (uint32_t)vnew[DPL * l + j] << (16 * (j & 1));
+    uint16_t* const vw = reinterpret_cast<uint16_t*>(vx[w]);
+    typedef short v4s_t __attribute__((ext_vector_type(4)));
 
     const int nblk = (t1 - t0 + 15) / 16;
     // Blocks b = w, w + 4, ... of this wavefront, two in flight: the loads of
@@ -226,33 +241,48 @@ __global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int j = 0; j < DPL; ++j) acc[g][j] *= al[w][g];
-        // the new position's value comes from v_new, not the cache
-        float vn[DPL];
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) vn[j] = bf16_to_f32(vnew[DPL * l + j]);
+        // the block's value rows into this wavefront's area (the new
+        // position's row from v_new; rows past pe read as zero)
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
-            float v[DPL];
-#pragma unroll
-            for (int j = 0; j < DPL; ++j) {
-                const uint32_t word = vraw[p][j / 2];
-                v[j] = (j & 1) ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
-            }
-            if (DPL == 1) v[0] = __uint_as_float(vraw[p][0] << 16);
+            uint32_t w0 = vraw[p][0], w1 = DPL == 4 ? vraw[p][DPL == 4 ? 1 : 0] : 0u;
             if (P0 + p == pe) {
-#pragma unroll
-                for (int j = 0; j < DPL; ++j) v[j] = vn[j];
+                w0 = vnw[0];
+                w1 = vnw[1];
             }
+            if constexpr (DPL == 4)
+                *reinterpret_cast<uint2*>(&vw[p * VR + 4 * l]) = make_uint2(w0, w1);
+            else if constexpr (DPL == 2)
+                *reinterpret_cast<uint32_t*>(&vw[p * VR + 2 * l]) = w0;
+            else
+                vw[p * VR + l] = (uint16_t)w0;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // rescale by the head's factor, then o^T += V^T P^T per tile: the B
+        // operand is P^T (column head lr, positions 4 lg ..), split hi / lo;
+        // the A operand V^T (row dim 16 t + lr, positions 4 lg ..) comes from
+        // a transpose read, lane c of each 16-lane group pointing at row
+        // 4 lg + c / 4, dims 16 t + 4 (c % 4) ..
+        const float ah = al[w][lr];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float pg = pb[w][p][g];
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int j = 0; j < DPL; ++j) acc[g][j] += pg * v[j];
-            }
+            for (int r = 0; r < 4; ++r) oacc[t][r] *= ah;
+        float pf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pf[i] = pb[w][4 * lg + i][lr];
+        uint2 phu, plu;
+        split4(pf, phu, plu);
+        const v4s_t ph = __builtin_bit_cast(v4s_t, phu), pl = __builtin_bit_cast(v4s_t, plu);
+        const uint16_t* const vt = &vw[(4 * lg + (lr >> 2)) * VR + 4 * (lr & 3)];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const v4s_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t*)(vt + 16 * t));
+            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, oacc[t], 0, 0, 0);
+            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, oacc[t], 0, 0, 0);
         }
         __builtin_amdgcn_wave_barrier();  // pb and al are rewritten by the next block
     };
@@ -265,6 +295,25 @@ __global__ __launch_bounds__(kAttnWG) void attn_split_kernel(const AttnArgs A) {
         load_block(b + 8, kfa, va);
         if (b + 4 < nblk) compute_block(b + 4, kfb, vb);
     }
+
+    // o back to the merge's layout, acc[g][j] = o[head g][dim DPL l + j],
+    // through this wavefront's area (its last block's reads are done: LDS
+    // operations of one wavefront complete in order)
+    float* const xw = vx[w];
+    if (lr < G) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xw[lr * D + 16 * t + 4 * lg + r] = oacc[t][r];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float acc[G][DPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[g][j] = xw[g * D + DPL * l + j];
 
     // merge the four wavefronts through LDS in two rounds (3 -> 1, 2 -> 0,
     // then 1 -> 0); a wavefront without positions holds m = -inf
