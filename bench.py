@@ -82,8 +82,8 @@ DECODE_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b
 # (gdn_attn.hip, split + combine kernels; profiles/attention_decode_traffic.md).
 SERVE_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b27696c883c62b2e249ee88187c7",
                  "bytes_per_launch": 543596916}
-ATTN_TRAFFIC = {"kernel_source_sha256": "4e36c55f9b776e277377f8cad262b9944853dfd9898c930e2d6e41923d494265",
-                "bytes_per_launch": 2197164917}
+ATTN_TRAFFIC = {"kernel_source_sha256": "b4c7bd0b8563d7f0d784dc692deadbfa4d08b1b3b87439910dda3ff64a06dbdf",
+                "bytes_per_launch": 2197192926}
 # The fused decode at the 35B-A3B shape, batch 128 (gdn_decode.hip;
 # profiles/decode_traffic_35b.md)
 DECODE3_TRAFFIC = {"kernel_source_sha256": "076fd1460782135513e283e43e4305599738b27696c883c62b2e249ee88187c7",

@@ -56,8 +56,9 @@ void attn_plan(int N, int Hq, int Hkv, int D, int Lmax, int& split, int& nsplit,
 }
 
 template <int D, int G>
-// (at most 256 registers a lane: two workgroups on a CU)
-__global__ __launch_bounds__(kAttnWG, 2) void attn_split_kernel(const AttnArgs A) {
+// (at most 256 registers a lane: two workgroups on a CU, where the LDS of
+// groups of up to 8 query heads allows two)
+__global__ __launch_bounds__(kAttnWG, G <= 8 ? 2 : 1) void attn_split_kernel(const AttnArgs A) {
     constexpr int NKK = D / 32;   // MFMA k-steps over the head dimension
     constexpr int DPL = D / 64;   // value dimensions per lane in P V
     static_assert(G >= 1 && G <= 16 && D % 64 == 0, "shape");
